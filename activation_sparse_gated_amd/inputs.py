@@ -1,0 +1,123 @@
+"""Seeded synthetic inputs for the gate-first sparse FFN.
+
+This module is shared by the HIP path's tests and bench and by the CPU oracle's
+tests. It holds no FFN arithmetic: only random draws, the bf16 rounding of the
+draws, and the constant that places a target fraction of gate pre-activations
+below zero. Every array is generated from
+``PCG64(SeedSequence([2026, cfg, layer, replica, stream]))``.
+
+Recipe (the pages fix the FFN shapes but print no inputs, so these are our
+choices, stated once here):
+
+* Standard gating ("Model casting: compute the gate, then skip most of the
+  FFN", section "What an FFN actually computes"): W1, W3 in R^{H x D} and W2 in
+  R^{D x H}, every entry N(0, 1/D). W2 is stored transposed, W2T = W2^T with
+  shape [H, D], so hidden unit i owns the contiguous row W2T[i].
+* Tokens: x[0] = 1 and x[1:] ~ N(0, 1). Column 0 of W1 is set to
+  c = -Phi^{-1}(s), so z_i = c + (a sum of D-1 terms of variance 1/D) and
+  P(z_i > 0) = Phi(c) = 1 - s. A tiny workload fixes c = -1.2816 for s = 0.9.
+* LoPA gating (same page, section "LoPA Gating: moving the ceiling"):
+  V [r, D] ~ N(0, 1/D), U [H', r] ~ N(0, 1/r), W3 ~ N(0, 1/D),
+  W2T [H', D] ~ N(0, 1/H'). The gate's bias rides on rank 0: V[0] = e_0 so
+  (Vx)_0 = x_0 = 1, and U[:, 0] = c.
+* Rounding: draw fp64, round to fp32, then round-to-nearest-even to bf16.
+  Everything downstream consumes the bf16 values, so the quantisation is part
+  of the input, not of the method.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import ndtri
+
+SEED_BASE = 2026
+# stream ids inside one (cfg, layer, replica) key
+S_X, S_W1, S_W3, S_W2T, S_V, S_U = 0, 1, 2, 3, 4, 5
+
+
+def rng(cfg: int, layer: int = 0, replica: int = 0, stream: int = 0) -> np.random.Generator:
+    return np.random.Generator(
+        np.random.PCG64(np.random.SeedSequence([SEED_BASE, cfg, layer, replica, stream])))
+
+
+def to_bf16_bits(a) -> np.ndarray:
+    """fp64 -> fp32 -> bf16 (round to nearest, ties to even) as uint16 bit patterns."""
+    f = np.ascontiguousarray(np.asarray(a, dtype=np.float32))
+    u = f.view(np.uint32)
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    out = ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Exact widening of bf16 bit patterns to fp32."""
+    b = np.ascontiguousarray(np.asarray(bits, dtype=np.uint16))
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def gate_offset(sparsity: float) -> float:
+    """c = -Phi^{-1}(s): with z ~ N(c, 1), P(z > 0) = 1 - s."""
+    return float(-ndtri(sparsity))
+
+
+def _finish(a64: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "bf16":
+        return to_bf16_bits(a64)
+    if dtype == "f32":
+        return np.ascontiguousarray(a64.astype(np.float32))
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def normal(shape, std: float, cfg: int, layer: int, replica: int, stream: int) -> np.ndarray:
+    return rng(cfg, layer, replica, stream).standard_normal(size=shape, dtype=np.float64) * std
+
+
+def tokens(D: int, n: int, cfg: int, layer: int = 0, replica: int = 0, dtype: str = "bf16",
+           stream: int = S_X) -> np.ndarray:
+    """n tokens [n, D]: x[:, 0] = 1, x[:, 1:] ~ N(0, 1)."""
+    x = normal((n, D), 1.0, cfg, layer, replica, stream)
+    x[:, 0] = 1.0
+    return _finish(x, dtype)
+
+
+def standard_weights(D: int, H: int, sparsity: float | None, cfg: int, layer: int = 0,
+                     replica: int = 0, dtype: str = "bf16", offset: float | None = None) -> dict:
+    """W1, W3, W2T, each [H, D], N(0, 1/D); W1[:, 0] = c sets the sparsity."""
+    std = 1.0 / np.sqrt(D)
+    W1 = normal((H, D), std, cfg, layer, replica, S_W1)
+    c = offset if offset is not None else (gate_offset(sparsity) if sparsity is not None else None)
+    if c is not None:
+        W1[:, 0] = c
+    W3 = normal((H, D), std, cfg, layer, replica, S_W3)
+    W2T = normal((H, D), std, cfg, layer, replica, S_W2T)
+    return {"W1": _finish(W1, dtype), "W3": _finish(W3, dtype), "W2T": _finish(W2T, dtype),
+            "offset": c}
+
+
+def lopa_weights(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, layer: int = 0,
+                 replica: int = 0, dtype: str = "bf16", offset: float | None = None) -> dict:
+    """V [r, D], U [Hp, r], W3 [Hp, D], W2T [Hp, D] with fan-in scaled variances."""
+    V = normal((r, D), 1.0 / np.sqrt(D), cfg, layer, replica, S_V)
+    U = normal((Hp, r), 1.0 / np.sqrt(r), cfg, layer, replica, S_U)
+    c = offset if offset is not None else (gate_offset(sparsity) if sparsity is not None else None)
+    if c is not None:
+        V[0, :] = 0.0
+        V[0, 0] = 1.0
+        U[:, 0] = c
+    W3 = normal((Hp, D), 1.0 / np.sqrt(D), cfg, layer, replica, S_W3)
+    W2T = normal((Hp, D), 1.0 / np.sqrt(Hp), cfg, layer, replica, S_W2T)
+    return {"V": _finish(V, dtype), "U": _finish(U, dtype), "W3": _finish(W3, dtype),
+            "W2T": _finish(W2T, dtype), "offset": c}
+
+
+def small_integers(shape, lo: int, hi: int, cfg: int, layer: int = 0, replica: int = 0,
+                   stream: int = 0, dtype: str = "bf16") -> np.ndarray:
+    """Integers uniform in [lo, hi]; exact in bf16 and fp32 for |v| <= 256."""
+    a = rng(cfg, layer, replica, stream).integers(lo, hi + 1, size=shape).astype(np.float64)
+    return _finish(a, dtype)
+
+
+def as_float(a: np.ndarray) -> np.ndarray:
+    """View generated data as fp32 values (bf16 bits are widened exactly)."""
+    if a.dtype == np.uint16:
+        return bf16_bits_to_f32(a)
+    return np.asarray(a, dtype=np.float32)
