@@ -1,0 +1,445 @@
+// C ABI of the gate-first sparse FFN (declared in include/sffn.h): handle
+// management, synchronous argument checks, and the launch plan of each
+// forward call. All arithmetic runs in the kernels of sffn_kernels.hip.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "sffn.h"
+#include "sffn_kernels.hip"
+
+using namespace sffn;
+
+namespace {
+
+enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GATE_UP_DENSE,
+            KIND_DOWN, KIND_LIVE_LIST, KIND_COUNT };
+const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
+                                            "k_gate_up_dense", "k_down", "k_live_list"};
+
+thread_local std::string g_thread_error = "no error";
+
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    return std::atoi(v);
+}
+
+}  // namespace
+
+struct sffn_handle {
+    int D = 0, H = 0, r = 0, max_tokens = 0, act = 0, dtype = 0;
+    unsigned flags = 0;
+    int device = 0;
+    float* a_buf = nullptr;      // [max_tokens x H] unit products a_i
+    uint8_t* live_buf = nullptr; // [max_tokens x H] live flags
+    float* t_buf = nullptr;      // [max_tokens x r] LoPA rank vectors
+    std::string err = "no error";
+    // launch plan
+    int gate_rows_per_wave = 4;
+    int down_lpr = 8;
+    // instrumentation
+    bool timing = false;
+    struct Rec { int kind; hipEvent_t start, stop; };
+    std::vector<Rec> pending;
+    std::vector<hipEvent_t> pool;
+    double total_ms[KIND_COUNT] = {};
+    int64_t launches[KIND_COUNT] = {};
+};
+
+namespace {
+
+sffn_status fail(sffn_handle* h, sffn_status code, const std::string& msg) {
+    if (h)
+        h->err = msg;
+    else
+        g_thread_error = msg;
+    return code;
+}
+
+sffn_status hip_fail(sffn_handle* h, hipError_t e, const char* what) {
+    return fail(h, SFFN_HIP_ERROR, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipEvent_t take_event(sffn_handle* h) {
+    if (!h->pool.empty()) {
+        hipEvent_t e = h->pool.back();
+        h->pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+template <typename... KArgs, typename... Args>
+sffn_status launch(sffn_handle* h, int kind, void (*kern)(KArgs...), dim3 grid, dim3 block,
+                   hipStream_t s, Args... args) {
+    if (grid.x == 0) return SFFN_OK;
+    if (h->timing) {
+        hipEvent_t e0 = take_event(h), e1 = take_event(h);
+        if (!e0 || !e1) return fail(h, SFFN_HIP_ERROR, "hipEventCreate failed");
+        hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, static_cast<KArgs>(args)...);
+        h->pending.push_back({kind, e0, e1});
+    } else {
+        hipLaunchKernelGGL(kern, grid, block, 0, s, static_cast<KArgs>(args)...);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(h, e, kKindNames[kind]);
+    return SFFN_OK;
+}
+
+// ------------------------------------------------------------------ dispatch
+// Register chunks per lane for a row of n elements (64 lanes x 16 bytes per chunk).
+int chunks_needed(int n, int dtype) {
+    const int cw = WAVE * (dtype == SFFN_BF16 ? 8 : 4);
+    return (n + cw - 1) / cw;
+}
+
+// The instantiated chunk counts; the smallest one that covers the row is used.
+constexpr int kNC[] = {1, 2, 3, 4, 5, 6, 8, 12, 16};
+constexpr int kNR[] = {1, 2, 4, 8};
+
+int pick(const int* set, int n, int need) {
+    for (int i = 0; i < n; ++i)
+        if (set[i] >= need) return set[i];
+    return -1;
+}
+
+#define SFFN_NC_SWITCH(NCV, BODY)            \
+    switch (NCV) {                           \
+        case 1: { constexpr int NC = 1; BODY; } break;   \
+        case 2: { constexpr int NC = 2; BODY; } break;   \
+        case 3: { constexpr int NC = 3; BODY; } break;   \
+        case 4: { constexpr int NC = 4; BODY; } break;   \
+        case 5: { constexpr int NC = 5; BODY; } break;   \
+        case 6: { constexpr int NC = 6; BODY; } break;   \
+        case 8: { constexpr int NC = 8; BODY; } break;   \
+        case 12: { constexpr int NC = 12; BODY; } break; \
+        case 16: { constexpr int NC = 16; BODY; } break; \
+        default: return fail(h, SFFN_INTERNAL, "no kernel for this width"); \
+    }
+
+#define SFFN_NR_SWITCH(NRV, BODY)            \
+    switch (NRV) {                           \
+        case 1: { constexpr int NR = 1; BODY; } break;   \
+        case 2: { constexpr int NR = 2; BODY; } break;   \
+        case 4: { constexpr int NR = 4; BODY; } break;   \
+        case 8: { constexpr int NR = 8; BODY; } break;   \
+        default: return fail(h, SFFN_INTERNAL, "no kernel for this rank"); \
+    }
+
+template <typename WT>
+sffn_status run_down(sffn_handle* h, const void* W2T, float* y, int T, int union_mode, int dense,
+                     hipStream_t s) {
+    const int vec = Elem<WT>::VEC;
+    if (h->down_lpr == 4) {
+        const int cb = 4 * vec;
+        const int nslices = (h->D + cb - 1) / cb;
+        const int nb = ((nslices + 7) / 8) * 8;
+        return launch(h, KIND_DOWN, k_down<WT, 4, 4>, dim3(nb), dim3(K2_THREADS), s, h->a_buf,
+                      (const WT*)W2T, y, h->D, h->H, T, union_mode, dense);
+    }
+    const int cb = 8 * vec;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nb = ((nslices + 7) / 8) * 8;
+    return launch(h, KIND_DOWN, k_down<WT, 8, 4>, dim3(nb), dim3(K2_THREADS), s, h->a_buf,
+                  (const WT*)W2T, y, h->D, h->H, T, union_mode, dense);
+}
+
+sffn_status run_live_list(sffn_handle* h, int T, int32_t* live_count, int32_t* live_idx,
+                          hipStream_t s) {
+    if (!live_count) return SFFN_OK;
+    return launch(h, KIND_LIVE_LIST, k_live_list, dim3(T), dim3(1024), s, h->live_buf, h->H,
+                  live_count, live_idx);
+}
+
+template <typename WT>
+sffn_status run_sparse(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                       const void* W2T, float* y, int T, int mode, int32_t* live_count,
+                       int32_t* live_idx, hipStream_t s) {
+    const int nc = pick(kNC, sizeof(kNC) / sizeof(int), chunks_needed(h->D, h->dtype));
+    const int rpw = h->gate_rows_per_wave;
+    const int rows_per_block = rpw * K1_WAVES;
+    const int nb = (h->H + rows_per_block - 1) / rows_per_block;
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    sffn_status st = SFFN_OK;
+    SFFN_NC_SWITCH(nc, st = launch(h, KIND_GATE_UP_SPARSE, k_gate_up_sparse<WT, NC>, dim3(nb),
+                                   dim3(K1_THREADS), s, (const WT*)x, (const WT*)W1,
+                                   (const WT*)W3, h->a_buf, live, h->D, h->H, T, h->act,
+                                   mode == SFFN_MODE_UNION ? 1 : 0, rpw));
+    if (st != SFFN_OK) return st;
+    st = run_down<WT>(h, W2T, y, T, mode == SFFN_MODE_UNION ? 1 : 0, 0, s);
+    if (st != SFFN_OK) return st;
+    return run_live_list(h, T, live_count, live_idx, s);
+}
+
+template <typename WT>
+sffn_status run_lopa(sffn_handle* h, const void* x, const void* V, const void* U, const void* W3,
+                     const void* W2T, float* y, int T, int mode, int32_t* live_count,
+                     int32_t* live_idx, hipStream_t s) {
+    const int nc = pick(kNC, sizeof(kNC) / sizeof(int), chunks_needed(h->D, h->dtype));
+    const int nr = pick(kNR, sizeof(kNR) / sizeof(int), chunks_needed(h->r, h->dtype));
+    sffn_status st = SFFN_OK;
+    {
+        const int rpw = 1;
+        const int nb = (h->r + K1_WAVES * rpw - 1) / (K1_WAVES * rpw);
+        SFFN_NC_SWITCH(nc, st = launch(h, KIND_RANK_PROJ, k_rank_proj<WT, NC>, dim3(nb),
+                                       dim3(K1_THREADS), s, (const WT*)x, (const WT*)V, h->t_buf,
+                                       h->D, h->r, T, rpw));
+        if (st != SFFN_OK) return st;
+    }
+    const int rpw = h->gate_rows_per_wave;
+    const int rows_per_block = rpw * K1_WAVES;
+    const int nb = (h->H + rows_per_block - 1) / rows_per_block;
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    SFFN_NC_SWITCH(nc, SFFN_NR_SWITCH(nr, st = launch(h, KIND_GATE_UP_LOPA,
+                                                      k_gate_up_lopa<WT, NC, NR>, dim3(nb),
+                                                      dim3(K1_THREADS), s, (const WT*)x,
+                                                      (const float*)h->t_buf, (const WT*)U,
+                                                      (const WT*)W3, h->a_buf, live, h->D, h->H,
+                                                      h->r, T, h->act,
+                                                      mode == SFFN_MODE_UNION ? 1 : 0, rpw)));
+    if (st != SFFN_OK) return st;
+    st = run_down<WT>(h, W2T, y, T, mode == SFFN_MODE_UNION ? 1 : 0, 0, s);
+    if (st != SFFN_OK) return st;
+    return run_live_list(h, T, live_count, live_idx, s);
+}
+
+template <typename WT>
+sffn_status run_dense(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                      const void* W2T, float* y, int T, hipStream_t s) {
+    const int nc = pick(kNC, sizeof(kNC) / sizeof(int), chunks_needed(h->D, h->dtype));
+    const int rpw = 2;
+    const int nb = (h->H + K1_WAVES * rpw - 1) / (K1_WAVES * rpw);
+    sffn_status st = SFFN_OK;
+    SFFN_NC_SWITCH(nc, st = launch(h, KIND_GATE_UP_DENSE, k_gate_up_dense<WT, NC>, dim3(nb),
+                                   dim3(K1_THREADS), s, (const WT*)x, (const WT*)W1,
+                                   (const WT*)W3, h->a_buf, h->D, h->H, T, h->act, rpw));
+    if (st != SFFN_OK) return st;
+    return run_down<WT>(h, W2T, y, T, 1, 1, s);
+}
+
+sffn_status check_common(sffn_handle* h, const void* x, const void* W3, const void* W2T,
+                         const float* y, int T, int32_t* live_count, int32_t* live_idx,
+                         hipStream_t* stream_out, void* stream) {
+    if (!h) return fail(nullptr, SFFN_INVALID_ARGUMENT, "null handle");
+    if (T < 0 || T > h->max_tokens)
+        return fail(h, SFFN_INVALID_ARGUMENT,
+                    "T=" + std::to_string(T) + " outside [0, max_tokens=" +
+                        std::to_string(h->max_tokens) + "]");
+    if (!x || !W3 || !W2T || !y) return fail(h, SFFN_INVALID_ARGUMENT, "null tensor pointer");
+    if (!aligned16(x) || !aligned16(W3) || !aligned16(W2T) || !aligned16(y))
+        return fail(h, SFFN_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+    if ((live_count == nullptr) != (live_idx == nullptr))
+        return fail(h, SFFN_INVALID_ARGUMENT, "live_count and live_idx must be both set or both NULL");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(h, e, "hipGetDevice");
+    if (dev != h->device)
+        return fail(h, SFFN_INVALID_ARGUMENT, "current device differs from the handle's device");
+    *stream_out = reinterpret_cast<hipStream_t>(stream);
+    return SFFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sffn_abi_version(void) { return 1; }
+
+const char* sffn_status_string(sffn_status s) {
+    switch (s) {
+        case SFFN_OK: return "SFFN_OK";
+        case SFFN_INVALID_ARGUMENT: return "SFFN_INVALID_ARGUMENT";
+        case SFFN_UNSUPPORTED: return "SFFN_UNSUPPORTED";
+        case SFFN_OUT_OF_MEMORY: return "SFFN_OUT_OF_MEMORY";
+        case SFFN_HIP_ERROR: return "SFFN_HIP_ERROR";
+        case SFFN_INTERNAL: return "SFFN_INTERNAL";
+        default: return "unknown status";
+    }
+}
+
+const char* sffn_last_error(const sffn_handle* h) {
+    return h ? h->err.c_str() : g_thread_error.c_str();
+}
+
+sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, int act,
+                        int dtype, unsigned flags) {
+    try {
+        if (!out) return fail(nullptr, SFFN_INVALID_ARGUMENT, "out is NULL");
+        *out = nullptr;
+        if (act != SFFN_ACT_RELU && act != SFFN_ACT_RSPLUS)
+            return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
+        if (dtype != SFFN_BF16 && dtype != SFFN_F32)
+            return fail(nullptr, SFFN_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+        if (flags != 0) return fail(nullptr, SFFN_UNSUPPORTED, "flags must be 0");
+        const int dmax = dtype == SFFN_BF16 ? 8192 : 4096;
+        if (D <= 0 || D % 8 != 0 || D > dmax)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT,
+                        "D must be a positive multiple of 8, at most " + std::to_string(dmax));
+        if (H <= 0 || H > (1 << 20))
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "H must be in [1, 2^20]");
+        const int rmax = dtype == SFFN_BF16 ? 2048 : 2048;
+        if (r != 0 && (r < 8 || r % 8 != 0 || r > rmax))
+            return fail(nullptr, SFFN_INVALID_ARGUMENT,
+                        "r must be 0 or a multiple of 8 in [8, 2048]");
+        if (max_tokens < 1 || max_tokens > MAXT)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "max_tokens must be in [1, 64]");
+
+        sffn_handle* h = new (std::nothrow) sffn_handle();
+        if (!h) return fail(nullptr, SFFN_OUT_OF_MEMORY, "host allocation failed");
+        h->D = D; h->H = H; h->r = r; h->max_tokens = max_tokens; h->act = act;
+        h->dtype = dtype; h->flags = flags;
+        hipError_t e = hipGetDevice(&h->device);
+        if (e != hipSuccess) {
+            delete h;
+            return fail(nullptr, SFFN_HIP_ERROR, std::string("hipGetDevice: ") + hipGetErrorString(e));
+        }
+        const size_t th = (size_t)max_tokens * (size_t)H;
+        e = hipMalloc(&h->a_buf, th * sizeof(float));
+        if (e == hipSuccess) e = hipMalloc(&h->live_buf, th);
+        if (e == hipSuccess && r > 0) e = hipMalloc(&h->t_buf, (size_t)max_tokens * r * sizeof(float));
+        if (e != hipSuccess) {
+            sffn_destroy(h);
+            return fail(nullptr, e == hipErrorOutOfMemory ? SFFN_OUT_OF_MEMORY : SFFN_HIP_ERROR,
+                        std::string("scratch allocation: ") + hipGetErrorString(e));
+        }
+        // launch plan: enough gate/up blocks to cover the 256 CUs several times over
+        int rpw = 4;
+        while (rpw > 1 && (H + rpw * K1_WAVES - 1) / (rpw * K1_WAVES) < 1024) rpw /= 2;
+        h->gate_rows_per_wave = rpw;
+        h->down_lpr = 8;
+        const int env_rpw = env_int("SFFN_GATE_ROWS_PER_WAVE", 0);
+        if (env_rpw >= 1 && env_rpw <= K1_MAX_ROWS / K1_WAVES) h->gate_rows_per_wave = env_rpw;
+        const int env_lpr = env_int("SFFN_DOWN_LANES_PER_ROW", 0);
+        if (env_lpr == 4 || env_lpr == 8) h->down_lpr = env_lpr;
+        *out = h;
+        return SFFN_OK;
+    } catch (...) {
+        return fail(nullptr, SFFN_INTERNAL, "exception in sffn_create");
+    }
+}
+
+void sffn_destroy(sffn_handle* h) {
+    if (!h) return;
+    for (auto& r : h->pending) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    for (auto e : h->pool) (void)hipEventDestroy(e);
+    if (h->a_buf) (void)hipFree(h->a_buf);
+    if (h->live_buf) (void)hipFree(h->live_buf);
+    if (h->t_buf) (void)hipFree(h->t_buf);
+    delete h;
+}
+
+sffn_status sffn_forward_dense(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                               const void* W2T, float* y, int T, void* stream) {
+    try {
+        hipStream_t s;
+        sffn_status st = check_common(h, x, W3, W2T, y, T, nullptr, nullptr, &s, stream);
+        if (st != SFFN_OK) return st;
+        if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "dense forward needs a standard-gating handle (r == 0)");
+        if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
+        if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
+        if (T == 0) return SFFN_OK;
+        return h->dtype == SFFN_BF16 ? run_dense<uint16_t>(h, x, W1, W3, W2T, y, T, s)
+                                     : run_dense<float>(h, x, W1, W3, W2T, y, T, s);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_dense");
+    }
+}
+
+sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                                const void* W2T, float* y, int T, int mode, int32_t* live_count,
+                                int32_t* live_idx, void* stream) {
+    try {
+        hipStream_t s;
+        sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
+        if (st != SFFN_OK) return st;
+        if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "sparse forward needs a standard-gating handle (r == 0)");
+        if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
+            return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
+        if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
+        if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
+        if (T == 0) return SFFN_OK;
+        return h->dtype == SFFN_BF16
+                   ? run_sparse<uint16_t>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s)
+                   : run_sparse<float>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_sparse");
+    }
+}
+
+sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, const void* U,
+                              const void* W3, const void* W2T, float* y, int T, int mode,
+                              int32_t* live_count, int32_t* live_idx, void* stream) {
+    try {
+        hipStream_t s;
+        sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
+        if (st != SFFN_OK) return st;
+        if (h->r == 0) return fail(h, SFFN_INVALID_ARGUMENT, "LoPA forward needs a handle with r > 0");
+        if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
+            return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
+        if (!V || !U) return fail(h, SFFN_INVALID_ARGUMENT, "null V or U");
+        if (!aligned16(V) || !aligned16(U))
+            return fail(h, SFFN_INVALID_ARGUMENT, "V and U must be 16-byte aligned");
+        if (T == 0) return SFFN_OK;
+        return h->dtype == SFFN_BF16
+                   ? run_lopa<uint16_t>(h, x, V, U, W3, W2T, y, T, mode, live_count, live_idx, s)
+                   : run_lopa<float>(h, x, V, U, W3, W2T, y, T, mode, live_count, live_idx, s);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_lopa");
+    }
+}
+
+sffn_status sffn_timing_enable(sffn_handle* h, int enable) {
+    if (!h) return fail(nullptr, SFFN_INVALID_ARGUMENT, "null handle");
+    h->timing = enable != 0;
+    return SFFN_OK;
+}
+
+sffn_status sffn_timing_read(sffn_handle* h, int kind, double* total_ms, int64_t* launches,
+                             int reset) {
+    if (!h) return fail(nullptr, SFFN_INVALID_ARGUMENT, "null handle");
+    if (kind < 0 || kind >= KIND_COUNT) return fail(h, SFFN_INVALID_ARGUMENT, "unknown kernel kind");
+    for (auto& rec : h->pending) {
+        hipError_t e = hipEventSynchronize(rec.stop);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
+        float ms = 0.0f;
+        e = hipEventElapsedTime(&ms, rec.start, rec.stop);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventElapsedTime");
+        h->total_ms[rec.kind] += ms;
+        h->launches[rec.kind] += 1;
+        h->pool.push_back(rec.start);
+        h->pool.push_back(rec.stop);
+    }
+    h->pending.clear();
+    if (total_ms) *total_ms = h->total_ms[kind];
+    if (launches) *launches = h->launches[kind];
+    if (reset) {
+        for (int k = 0; k < KIND_COUNT; ++k) {
+            h->total_ms[k] = 0.0;
+            h->launches[k] = 0;
+        }
+    }
+    return SFFN_OK;
+}
+
+int sffn_kernel_kinds(void) { return KIND_COUNT; }
+
+const char* sffn_kernel_name(int kind) {
+    if (kind < 0 || kind >= KIND_COUNT) return "unknown";
+    return kKindNames[kind];
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+"""Thin ctypes binding of libsffn.so (C ABI in include/sffn.h).
+
+The functions keep the C names and only marshal arguments: torch tensors (or
+raw integer addresses) become device pointers, and the current torch stream
+becomes the `stream` argument unless one is given. Every step of the forward
+pass runs in the library's HIP kernels; there is no fallback. If the library
+has not been built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+SFFN_OK = 0
+SFFN_INVALID_ARGUMENT = -1
+SFFN_UNSUPPORTED = -2
+SFFN_OUT_OF_MEMORY = -3
+SFFN_HIP_ERROR = -4
+SFFN_INTERNAL = -5
+
+SFFN_ACT_RELU, SFFN_ACT_RSPLUS = 0, 1
+SFFN_BF16, SFFN_F32 = 0, 1
+SFFN_MODE_PER_TOKEN, SFFN_MODE_UNION = 0, 1
+
+EXPORTED = (
+    "sffn_create", "sffn_destroy", "sffn_forward_dense", "sffn_forward_sparse",
+    "sffn_forward_lopa", "sffn_last_error", "sffn_status_string", "sffn_abi_version",
+    "sffn_timing_enable", "sffn_timing_read", "sffn_kernel_kinds", "sffn_kernel_name",
+)
+
+_lib = None
+
+
+class SffnError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{status_string(status)}: {message}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _build.LIB
+
+
+def load() -> ctypes.CDLL:
+    """Open libsffn.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = _build.LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P, I, U = ctypes.c_void_p, ctypes.c_int, ctypes.c_uint
+    PP = ctypes.POINTER(ctypes.c_void_p)
+    lib.sffn_create.restype = I
+    lib.sffn_create.argtypes = [PP, I, I, I, I, I, I, U]
+    lib.sffn_destroy.restype = None
+    lib.sffn_destroy.argtypes = [P]
+    lib.sffn_forward_dense.restype = I
+    lib.sffn_forward_dense.argtypes = [P, P, P, P, P, P, I, P]
+    lib.sffn_forward_sparse.restype = I
+    lib.sffn_forward_sparse.argtypes = [P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_forward_lopa.restype = I
+    lib.sffn_forward_lopa.argtypes = [P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_last_error.restype = ctypes.c_char_p
+    lib.sffn_last_error.argtypes = [P]
+    lib.sffn_status_string.restype = ctypes.c_char_p
+    lib.sffn_status_string.argtypes = [I]
+    lib.sffn_abi_version.restype = I
+    lib.sffn_abi_version.argtypes = []
+    lib.sffn_timing_enable.restype = I
+    lib.sffn_timing_enable.argtypes = [P, I]
+    lib.sffn_timing_read.restype = I
+    lib.sffn_timing_read.argtypes = [P, I, ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(ctypes.c_int64), I]
+    lib.sffn_kernel_kinds.restype = I
+    lib.sffn_kernel_kinds.argtypes = []
+    lib.sffn_kernel_name.restype = ctypes.c_char_p
+    lib.sffn_kernel_name.argtypes = [I]
+    _lib = lib
+    return lib
+
+
+def _ptr(t):
+    """Device address of a tensor (or an int address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def status_string(status: int) -> str:
+    return load().sffn_status_string(status).decode()
+
+
+def sffn_last_error(handle=None) -> str:
+    return load().sffn_last_error(handle).decode()
+
+
+def sffn_abi_version() -> int:
+    return load().sffn_abi_version()
+
+
+def _check(status: int, handle) -> None:
+    if status != SFFN_OK:
+        raise SffnError(status, sffn_last_error(handle))
+
+
+def sffn_create(D: int, H: int, r: int, max_tokens: int, act: int, dtype: int, flags: int = 0):
+    """Returns the handle (an opaque address); raises SffnError on failure."""
+    out = ctypes.c_void_p()
+    st = load().sffn_create(ctypes.byref(out), D, H, r, max_tokens, act, dtype, flags)
+    _check(st, None)
+    return out.value
+
+
+def sffn_create_status(D, H, r, max_tokens, act, dtype, flags=0):
+    """Raw status form of sffn_create: (status, handle or None)."""
+    out = ctypes.c_void_p()
+    st = load().sffn_create(ctypes.byref(out), D, H, r, max_tokens, act, dtype, flags)
+    return st, out.value
+
+
+def sffn_destroy(handle) -> None:
+    if handle:
+        load().sffn_destroy(handle)
+
+
+def sffn_forward_dense(handle, x, W1, W3, W2T, y, T: int, stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_dense(handle, _ptr(x), _ptr(W1), _ptr(W3), _ptr(W2T), _ptr(y), T,
+                                   _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_sparse(handle, x, W1, W3, W2T, y, T: int, mode: int = SFFN_MODE_PER_TOKEN,
+                        live_count=None, live_idx=None, stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_sparse(handle, _ptr(x), _ptr(W1), _ptr(W3), _ptr(W2T), _ptr(y), T,
+                                    mode, _ptr(live_count), _ptr(live_idx), _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_lopa(handle, x, V, U, W3, W2T, y, T: int, mode: int = SFFN_MODE_PER_TOKEN,
+                      live_count=None, live_idx=None, stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_lopa(handle, _ptr(x), _ptr(V), _ptr(U), _ptr(W3), _ptr(W2T), _ptr(y),
+                                  T, mode, _ptr(live_count), _ptr(live_idx), _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_timing_enable(handle, enable: bool) -> None:
+    _check(load().sffn_timing_enable(handle, int(bool(enable))), handle)
+
+
+def sffn_timing_read(handle, kind: int, reset: bool = False):
+    """(total milliseconds, launches) of kernel kind `kind` since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int64()
+    _check(load().sffn_timing_read(handle, kind, ctypes.byref(ms), ctypes.byref(n), int(reset)),
+           handle)
+    return ms.value, n.value
+
+
+def sffn_kernel_kinds() -> int:
+    return load().sffn_kernel_kinds()
+
+
+def sffn_kernel_name(kind: int) -> str:
+    return load().sffn_kernel_name(kind).decode()
+
+
+def kernel_kind(name: str) -> int:
+    for k in range(sffn_kernel_kinds()):
+        if sffn_kernel_name(k) == name:
+            return k
+    raise KeyError(name)
+
+
+class Handle:
+    """Owns one sffn handle; destroys it when closed or collected."""
+
+    def __init__(self, D, H, r=0, max_tokens=1, act=SFFN_ACT_RELU, dtype=SFFN_BF16, flags=0):
+        self.D, self.H, self.r, self.max_tokens = D, H, r, max_tokens
+        self.act, self.dtype = act, dtype
+        self.ptr = sffn_create(D, H, r, max_tokens, act, dtype, flags)
+
+    def close(self):
+        if self.ptr:
+            sffn_destroy(self.ptr)
+            self.ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+        return False

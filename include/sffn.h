@@ -1,0 +1,162 @@
+/*
+ * sffn.h - C ABI of the gate-first sparse FFN forward pass for AMD MI355X
+ * (gfx950). Library: libsffn.so, built from activation_sparse_gated_amd/csrc.
+ *
+ * The operation (page "Model casting: compute the gate, then skip most of the
+ * FFN", sections "What an FFN actually computes" and "The 3x ceiling, and why
+ * W1 is always on"): for each token x in R^D,
+ *
+ *     z = W1 x                     gate pre-activation, H entries
+ *     h = A(z)                     A = ReLU, or R-S+ (x*sigmoid(x) for x >= 0,
+ *                                  0 below; section "Model casting: make
+ *                                  sparsity a target")
+ *     L = { i : z_i > 0 }          the live hidden units
+ *     y = W2 (h (.) W3 x) = sum_{i in L} h_i (W3_i . x) W2[:, i]
+ *
+ * Only the rows of W3 and the columns of W2 of live units are read; the result
+ * is exact, not an approximation. Under LoPA gating (section "LoPA Gating:
+ * moving the ceiling") the gate pre-activation is z = U (V x) with a rank-r
+ * factorisation, U in R^{H x r}, V in R^{r x D}; H is then the widened
+ * hidden size H'.
+ *
+ * Layout (all row-major, element type given by the handle's dtype):
+ *   x    [T x D]   tokens, one row per token
+ *   W1   [H x D]   gate; row i belongs to hidden unit i
+ *   W3   [H x D]   up projection; row i belongs to hidden unit i
+ *   W2T  [H x D]   the down projection W2 (D x H) stored TRANSPOSED, so that
+ *                  unit i's column of W2 is the contiguous row W2T[i]
+ *   V    [r x D], U [H x r]   LoPA factors
+ *   y    [T x D]   fp32 output, overwritten
+ * Requirements: D % 8 == 0, D <= 8192; 1 <= H <= 1<<20; LoPA: r % 8 == 0 and
+ * 8 <= r <= 2048; 0 <= T <= max_tokens <= 64; every pointer 16-byte aligned
+ * and a device pointer (hipMalloc or torch CUDA tensors). T == 0 is a no-op.
+ *
+ * Ownership: the caller owns every tensor. The library borrows them only for
+ * the work it enqueues and keeps no pointer between calls, so the same handle
+ * can be used with different weight buffers on every call. The handle owns its
+ * device scratch (per-token unit products and LoPA rank vectors), allocated
+ * once in sffn_create and freed in sffn_destroy.
+ *
+ * Streams and errors: `stream` is a hipStream_t passed as void* (NULL = the
+ * default stream). Arguments are checked synchronously before anything is
+ * enqueued; the forward calls never synchronise the host. A launch failure is
+ * reported from hipGetLastError; a device fault surfaces at the caller's next
+ * synchronisation. One handle must not be used from two streams or threads at
+ * once. No C++ exception crosses this ABI.
+ */
+#ifndef SFFN_H
+#define SFFN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct sffn_handle sffn_handle;
+typedef int sffn_status;
+
+enum {
+    SFFN_OK = 0,
+    SFFN_INVALID_ARGUMENT = -1, /* null pointer, bad size, misalignment, T > max_tokens */
+    SFFN_UNSUPPORTED = -2,      /* unknown activation, dtype, mode or flag */
+    SFFN_OUT_OF_MEMORY = -3,    /* scratch allocation failed in sffn_create */
+    SFFN_HIP_ERROR = -4,        /* a HIP runtime call or launch failed */
+    SFFN_INTERNAL = -5          /* unexpected internal failure */
+};
+
+enum { SFFN_ACT_RELU = 0, SFFN_ACT_RSPLUS = 1 };
+enum { SFFN_BF16 = 0, SFFN_F32 = 1 };
+/* How a batch of T tokens moves data; never changes the result.
+ * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set.
+ * UNION:     the union of the tokens' live sets is read once and each row is
+ *            applied to the tokens for which it is live (batched decode: the
+ *            pages note the speedup is quoted at batch size 1 and erodes as
+ *            the batch grows, since the union fills up). */
+enum { SFFN_MODE_PER_TOKEN = 0, SFFN_MODE_UNION = 1 };
+
+/*
+ * Create a handle for one FFN shape.
+ *   D, H        model width and hidden width (H' for LoPA handles)
+ *   r           LoPA rank; 0 for a standard-gating handle
+ *   max_tokens  largest T any forward call on this handle will pass (1..64)
+ *   act         SFFN_ACT_RELU or SFFN_ACT_RSPLUS
+ *   dtype       SFFN_BF16 (weights and x as bf16 bit patterns; products in
+ *               fp32) or SFFN_F32
+ *   flags       must be 0 (bits reserved)
+ * On success *out receives the handle. Allocates device scratch on the
+ * current device: max_tokens * (H + r) floats plus max_tokens * H bytes.
+ */
+sffn_status sffn_create(sffn_handle **out, int D, int H, int r, int max_tokens, int act,
+                        int dtype, unsigned flags);
+
+/* Frees the handle and its scratch. NULL is ignored. The caller must make sure
+ * no work using the handle is still pending (synchronise the stream first). */
+void sffn_destroy(sffn_handle *h);
+
+/*
+ * Dense comparator: y = W2 (A(W1 x) (.) W3 x) over all H units, reading every
+ * row of W1, W3 and W2T (page "Model casting: compute the gate, then skip most
+ * of the FFN", section "What an FFN actually computes"). Standard-gating
+ * handles only.
+ */
+sffn_status sffn_forward_dense(sffn_handle *h, const void *x, const void *W1, const void *W3,
+                               const void *W2T, float *y, int T, void *stream);
+
+/*
+ * Gate-first sparse forward, standard gating (sections "The 3x ceiling, and
+ * why W1 is always on" and "Compute the gate first, then skip the dead
+ * units"): all of W1 is read; W3 rows and W2T rows are read only for live
+ * units.
+ *   mode        SFFN_MODE_PER_TOKEN or SFFN_MODE_UNION
+ *   live_count  nullable device int32 [T]: k_t = |L_t| per token
+ *   live_idx    nullable device int32 [T x H]: token t's live units in
+ *               live_idx[t*H : t*H + k_t] (ascending); entries past k_t are
+ *               unspecified. live_count and live_idx must be both set or both
+ *               NULL.
+ */
+sffn_status sffn_forward_sparse(sffn_handle *h, const void *x, const void *W1, const void *W3,
+                                const void *W2T, float *y, int T, int mode, int32_t *live_count,
+                                int32_t *live_idx, void *stream);
+
+/*
+ * Gate-first sparse forward, LoPA gating without the fixed G term:
+ * z = U (V x), then the same skip as sffn_forward_sparse. The rank vector
+ * V x is kept in fp32 up to the live test. LoPA handles (r > 0) only.
+ */
+sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, const void *U,
+                              const void *W3, const void *W2T, float *y, int T, int mode,
+                              int32_t *live_count, int32_t *live_idx, void *stream);
+
+/* Message of the last failure on this handle; with NULL, the calling thread's
+ * last failure that had no handle (e.g. in sffn_create). Never NULL. */
+const char *sffn_last_error(const sffn_handle *h);
+
+/* Name of a status code. Never NULL. */
+const char *sffn_status_string(sffn_status s);
+
+/* ABI version of the library (this header: 1). */
+int sffn_abi_version(void);
+
+/*
+ * Instrumentation, for measuring the kernels' own durations. While enabled,
+ * every kernel the forward calls enqueue is launched with a start/stop event
+ * pair recorded at the kernel's own begin and end. sffn_timing_read
+ * synchronises with those events and returns, for kernel kind `kind`, the
+ * summed duration in milliseconds and the number of launches since the last
+ * reset (reset != 0 clears the totals after reading). Kinds are numbered
+ * 0 .. sffn_kernel_kinds()-1 and named by sffn_kernel_name. Timing adds
+ * events between launches, so it is off by default and must stay off during
+ * stream capture.
+ */
+sffn_status sffn_timing_enable(sffn_handle *h, int enable);
+sffn_status sffn_timing_read(sffn_handle *h, int kind, double *total_ms, int64_t *launches,
+                             int reset);
+int sffn_kernel_kinds(void);
+const char *sffn_kernel_name(int kind);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SFFN_H */

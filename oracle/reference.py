@@ -17,7 +17,7 @@ import os
 
 import numpy as np
 
-from .build import LIB, SRC, build as _build_lib
+from .buildlib import LIB, SRC, build as _build_lib
 
 ACT_RELU, ACT_RSPLUS = 0, 1
 _DT = {np.dtype(np.uint16): 0, np.dtype(np.float32): 1, np.dtype(np.float64): 2}
