@@ -19,9 +19,14 @@ using namespace sffn;
 namespace {
 
 enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GATE_UP_DENSE,
-            KIND_DOWN, KIND_LIVE_LIST, KIND_COUNT };
+            KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_GATE_UP_DENSE_T1, KIND_DOWN_T1,
+            KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
+            KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
-                                            "k_gate_up_dense", "k_down", "k_live_list"};
+                                            "k_gate_up_dense", "k_down", "k_live_list",
+                                            "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
+                                            "k_ffn_t1", "k_ffn_dense_t1", "k_reduce_partials",
+                                            "k_rank_proj_t1", "k_gate_up_lopa_t1"};
 
 thread_local std::string g_thread_error = "no error";
 
@@ -44,6 +49,18 @@ struct sffn_handle {
     // launch plan
     int gate_rows_per_wave = 4;
     int down_lpr = 8;
+    // batch-1 bf16 path
+    int t1_rw = 1;            // units per wave in the gate pass
+    int t1_lpr = 8;           // lanes per W2T row slice in the down pass
+    int t1_splits_sparse = 4; // row splits of the down pass (sparse)
+    int t1_splits_dense = 16; // row splits of the down pass (dense, unfused)
+    int t1_fused_sparse = 0;  // sparse: fused gate/up/down pass + partial reduction
+    int t1_fused_dense = 1;   // dense: fused one-pass W1/W3/W2T + partial reduction
+    int t1_fused = 1;         // a fused plan exists for this shape
+    int f_rows_per_block = 0; // units per fused block
+    int f_rw = 0;             // units per wave in the fused pass
+    int f_blocks = 0;         // fused blocks (= partials)
+    float* part_buf = nullptr; // [f_blocks x D] partial outputs
     // instrumentation
     bool timing = false;
     struct Rec { int kind; hipEvent_t start, stop; };
@@ -78,6 +95,24 @@ hipEvent_t take_event(sffn_handle* h) {
     hipEvent_t e = nullptr;
     if (hipEventCreate(&e) != hipSuccess) return nullptr;
     return e;
+}
+
+template <typename... KArgs, typename... Args>
+sffn_status launch_shm(sffn_handle* h, int kind, void (*kern)(KArgs...), dim3 grid, dim3 block,
+                       size_t shm, hipStream_t s, Args... args) {
+    if (grid.x == 0) return SFFN_OK;
+    if (h->timing) {
+        hipEvent_t e0 = take_event(h), e1 = take_event(h);
+        if (!e0 || !e1) return fail(h, SFFN_HIP_ERROR, "hipEventCreate failed");
+        hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)shm, s, e0, e1, 0,
+                              static_cast<KArgs>(args)...);
+        h->pending.push_back({kind, e0, e1});
+    } else {
+        hipLaunchKernelGGL(kern, grid, block, shm, s, static_cast<KArgs>(args)...);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(h, e, kKindNames[kind]);
+    return SFFN_OK;
 }
 
 template <typename... KArgs, typename... Args>
@@ -162,6 +197,152 @@ sffn_status run_live_list(sffn_handle* h, int T, int32_t* live_count, int32_t* l
                   live_count, live_idx);
 }
 
+constexpr int kNC_T1[] = {1, 2, 3, 4, 5, 6, 8};
+constexpr int kPMAX[] = {4, 8, 16, 32};
+
+bool t1_ok(const sffn_handle* h, int T) {
+    return T == 1 && h->dtype == SFFN_BF16 &&
+           chunks_needed(h->D, h->dtype) <= 8 &&
+           (h->H + KD_THREADS - 1) / KD_THREADS <= 32;
+}
+
+#define SFFN_NCT1_SWITCH(NCV, BODY)                       \
+    switch (NCV) {                                        \
+        case 1: { constexpr int NC = 1; BODY; } break;    \
+        case 2: { constexpr int NC = 2; BODY; } break;    \
+        case 3: { constexpr int NC = 3; BODY; } break;    \
+        case 4: { constexpr int NC = 4; BODY; } break;    \
+        case 5: { constexpr int NC = 5; BODY; } break;    \
+        case 6: { constexpr int NC = 6; BODY; } break;    \
+        case 8: { constexpr int NC = 8; BODY; } break;    \
+        default: return fail(h, SFFN_INTERNAL, "no batch-1 kernel for this width"); \
+    }
+#define SFFN_RW_SWITCH(RWV, BODY)                         \
+    switch (RWV) {                                        \
+        case 1: { constexpr int RW = 1; BODY; } break;    \
+        case 2: { constexpr int RW = 2; BODY; } break;    \
+        case 4: { constexpr int RW = 4; BODY; } break;    \
+        default: return fail(h, SFFN_INTERNAL, "bad units per wave"); \
+    }
+#define SFFN_PMAX_SWITCH(PV, BODY)                        \
+    switch (PV) {                                         \
+        case 4: { constexpr int PMAX = 4; BODY; } break;  \
+        case 8: { constexpr int PMAX = 8; BODY; } break;  \
+        case 16: { constexpr int PMAX = 16; BODY; } break; \
+        case 32: { constexpr int PMAX = 32; BODY; } break; \
+        default: return fail(h, SFFN_INTERNAL, "hidden width too large for the down pass"); \
+    }
+
+// down pass, batch 1, bf16
+sffn_status run_down_t1(sffn_handle* h, const void* W2T, float* y, int splits, int dense,
+                        hipStream_t s) {
+    const int cb = h->t1_lpr * 8;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    sffn_status st = SFFN_OK;
+    if (h->t1_lpr == 4) {
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<4, PMAX>, dim3(nbx, splits),
+                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
+    } else {
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<8, PMAX>, dim3(nbx, splits),
+                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
+    }
+    return st;
+}
+
+#define SFFN_FRW_SWITCH(RWV, BODY)                        \
+    switch (RWV) {                                        \
+        case 1: { constexpr int RW = 1; BODY; } break;    \
+        case 2: { constexpr int RW = 2; BODY; } break;    \
+        case 4: { constexpr int RW = 4; BODY; } break;    \
+        case 8: { constexpr int RW = 8; BODY; } break;    \
+        default: return fail(h, SFFN_INTERNAL, "bad units per wave"); \
+    }
+
+// Fused batch-1 pass (gate, live W3 and W2T rows) + partial reduction.
+template <bool DENSE>
+sffn_status run_fused_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                         const void* W2T, float* y, int32_t* live_count, int32_t* live_idx,
+                         hipStream_t s) {
+    const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
+    const size_t shm = (size_t)KF_WAVES * h->D * sizeof(float);
+    uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
+    const int kind = DENSE ? KIND_FFN_DENSE_T1 : KIND_FFN_T1;
+    sffn_status st = SFFN_OK;
+    SFFN_NCT1_SWITCH(nc, SFFN_FRW_SWITCH(h->f_rw,
+        st = launch_shm(h, kind, k_ffn_t1<NC, RW, DENSE>, dim3(h->f_blocks), dim3(KF_THREADS),
+                        shm, s, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
+                        (const uint16_t*)W2T, h->part_buf, live, h->D, h->H,
+                        h->f_rows_per_block, h->act)));
+    if (st != SFFN_OK) return st;
+    st = launch(h, KIND_REDUCE, k_reduce_partials, dim3((h->D + 63) / 64), dim3(KR_THREADS), s,
+                (const float*)h->part_buf, y, h->D, h->f_blocks);
+    if (st != SFFN_OK) return st;
+    if (!DENSE) return run_live_list(h, 1, live_count, live_idx, s);
+    return SFFN_OK;
+}
+
+// Allow the fused kernels their dynamic LDS (one y slice per wave).
+sffn_status prepare_fused(sffn_handle* h) {
+    const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
+    const int shm = KF_WAVES * h->D * (int)sizeof(float);
+    hipError_t e = hipSuccess;
+    SFFN_NCT1_SWITCH(nc, SFFN_FRW_SWITCH(h->f_rw,
+        e = hipFuncSetAttribute((const void*)k_ffn_t1<NC, RW, false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, shm);
+        if (e == hipSuccess)
+            e = hipFuncSetAttribute((const void*)k_ffn_t1<NC, RW, true>,
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, shm)));
+    if (e != hipSuccess) return hip_fail(h, e, "hipFuncSetAttribute");
+    return SFFN_OK;
+}
+
+sffn_status run_sparse_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                          const void* W2T, float* y, int32_t* live_count, int32_t* live_idx,
+                          hipStream_t s) {
+    if (h->t1_fused && h->t1_fused_sparse)
+        return run_fused_t1<false>(h, x, W1, W3, W2T, y, live_count, live_idx, s);
+    const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
+    const int rw = h->t1_rw;
+    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
+    const int splits = h->t1_splits_sparse;
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    float* yz = splits > 1 ? y : nullptr;
+    sffn_status st = SFFN_OK;
+    SFFN_NCT1_SWITCH(nc, SFFN_RW_SWITCH(rw, st = launch(h, KIND_GATE_UP_T1, k_gate_up_t1<NC, RW>,
+                                                        dim3(nb), dim3(K1_THREADS), s,
+                                                        (const uint16_t*)x, (const uint16_t*)W1,
+                                                        (const uint16_t*)W3, h->a_buf, live, yz,
+                                                        h->D, h->H, h->act)));
+    if (st != SFFN_OK) return st;
+    st = run_down_t1(h, W2T, y, splits, 0, s);
+    if (st != SFFN_OK) return st;
+    return run_live_list(h, 1, live_count, live_idx, s);
+}
+
+sffn_status run_dense_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                         const void* W2T, float* y, hipStream_t s) {
+    if (h->t1_fused && h->t1_fused_dense)
+        return run_fused_t1<true>(h, x, W1, W3, W2T, y, nullptr, nullptr, s);
+    const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
+    const int rw = h->t1_rw;
+    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
+    const int splits = h->t1_splits_dense;
+    float* yz = splits > 1 ? y : nullptr;
+    sffn_status st = SFFN_OK;
+    SFFN_NCT1_SWITCH(nc, SFFN_RW_SWITCH(rw, st = launch(h, KIND_GATE_UP_DENSE_T1,
+                                                        k_gate_up_dense_t1<NC, RW>, dim3(nb),
+                                                        dim3(K1_THREADS), s, (const uint16_t*)x,
+                                                        (const uint16_t*)W1, (const uint16_t*)W3,
+                                                        h->a_buf, yz, h->D, h->H, h->act)));
+    if (st != SFFN_OK) return st;
+    return run_down_t1(h, W2T, y, splits, 1, s);
+}
+
 template <typename WT>
 sffn_status run_sparse(sffn_handle* h, const void* x, const void* W1, const void* W3,
                        const void* W2T, float* y, int T, int mode, int32_t* live_count,
@@ -180,6 +361,41 @@ sffn_status run_sparse(sffn_handle* h, const void* x, const void* W1, const void
     st = run_down<WT>(h, W2T, y, T, mode == SFFN_MODE_UNION ? 1 : 0, 0, s);
     if (st != SFFN_OK) return st;
     return run_live_list(h, T, live_count, live_idx, s);
+}
+
+#define SFFN_NRT1_SWITCH(NRV, BODY)                       \
+    switch (NRV) {                                        \
+        case 1: { constexpr int NR = 1; BODY; } break;    \
+        case 2: { constexpr int NR = 2; BODY; } break;    \
+        case 4: { constexpr int NR = 4; BODY; } break;    \
+        default: return fail(h, SFFN_INTERNAL, "no batch-1 kernel for this rank"); \
+    }
+
+sffn_status run_lopa_t1(sffn_handle* h, const void* x, const void* V, const void* U,
+                        const void* W3, const void* W2T, float* y, int32_t* live_count,
+                        int32_t* live_idx, hipStream_t s) {
+    const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
+    const int nr = pick(kNR, 3, chunks_needed(h->r, h->dtype));
+    const int splits = h->t1_splits_sparse;
+    float* yz = splits > 1 ? y : nullptr;
+    sffn_status st = SFFN_OK;
+    const int nbr = (h->r + K1_WAVES - 1) / K1_WAVES;
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_RANK_PROJ_T1, k_rank_proj_t1<NC>, dim3(nbr),
+                                     dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)V,
+                                     h->t_buf, yz, h->D, h->r));
+    if (st != SFFN_OK) return st;
+    const int rw = h->t1_rw;
+    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    SFFN_NCT1_SWITCH(nc, SFFN_NRT1_SWITCH(nr, SFFN_RW_SWITCH(rw,
+        st = launch(h, KIND_GATE_UP_LOPA_T1, k_gate_up_lopa_t1<NC, NR, RW>, dim3(nb),
+                    dim3(K1_THREADS), s, (const uint16_t*)x, (const float*)h->t_buf,
+                    (const uint16_t*)U, (const uint16_t*)W3, h->a_buf, live, h->D, h->H, h->r,
+                    h->act))));
+    if (st != SFFN_OK) return st;
+    st = run_down_t1(h, W2T, y, splits, 0, s);
+    if (st != SFFN_OK) return st;
+    return run_live_list(h, 1, live_count, live_idx, s);
 }
 
 template <typename WT>
@@ -322,6 +538,45 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if (env_rpw >= 1 && env_rpw <= K1_MAX_ROWS / K1_WAVES) h->gate_rows_per_wave = env_rpw;
         const int env_lpr = env_int("SFFN_DOWN_LANES_PER_ROW", 0);
         if (env_lpr == 4 || env_lpr == 8) h->down_lpr = env_lpr;
+        const int e_rw = env_int("SFFN_T1_ROWS_PER_WAVE", 0);
+        if (e_rw == 1 || e_rw == 2 || e_rw == 4) h->t1_rw = e_rw;
+        const int e_lpr = env_int("SFFN_T1_LANES_PER_ROW", 0);
+        if (e_lpr == 4 || e_lpr == 8) h->t1_lpr = e_lpr;
+        const int e_ss = env_int("SFFN_T1_SPLITS_SPARSE", 0);
+        if (e_ss >= 1 && e_ss <= 16) h->t1_splits_sparse = e_ss;
+        const int e_sd = env_int("SFFN_T1_SPLITS_DENSE", 0);
+        if (e_sd >= 1 && e_sd <= 16) h->t1_splits_dense = e_sd;
+        h->t1_fused = 1;
+        h->t1_fused_sparse = env_int("SFFN_T1_FUSED_SPARSE", h->t1_fused_sparse) != 0;
+        h->t1_fused_dense = env_int("SFFN_T1_FUSED_DENSE", h->t1_fused_dense) != 0;
+        // fused batch-1 plan: about one block per CU, at most 64 units per block
+        if (dtype == SFFN_BF16 && D <= KF_DMAX) {
+            int target = env_int("SFFN_T1_BLOCKS", 128);
+            if (target < 1) target = 256;
+            int rpb = (H + target - 1) / target;
+            // keep the W1 tiles of a wave (units x register chunks) within 32 x 16 bytes per lane
+            const int ncf = pick(kNC_T1, 7, chunks_needed(D, dtype));
+            int rw_max = 1;
+            while (rw_max * 2 <= 8 && rw_max * 2 * ncf <= 32) rw_max *= 2;
+            if (rpb > KF_WAVES * rw_max) rpb = KF_WAVES * rw_max;
+            int rw = 1;
+            while (rw * KF_WAVES < rpb) rw *= 2;
+            h->f_rows_per_block = rpb;
+            h->f_rw = rw;
+            h->f_blocks = (H + rpb - 1) / rpb;
+            e = hipMalloc(&h->part_buf, (size_t)h->f_blocks * D * sizeof(float));
+            if (e != hipSuccess) {
+                sffn_destroy(h);
+                return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
+            }
+            if (prepare_fused(h) != SFFN_OK) {
+                std::string m = h->err;
+                sffn_destroy(h);
+                return fail(nullptr, SFFN_HIP_ERROR, m);
+            }
+        } else {
+            h->t1_fused = 0;
+        }
         *out = h;
         return SFFN_OK;
     } catch (...) {
@@ -339,6 +594,7 @@ void sffn_destroy(sffn_handle* h) {
     if (h->a_buf) (void)hipFree(h->a_buf);
     if (h->live_buf) (void)hipFree(h->live_buf);
     if (h->t_buf) (void)hipFree(h->t_buf);
+    if (h->part_buf) (void)hipFree(h->part_buf);
     delete h;
 }
 
@@ -352,6 +608,7 @@ sffn_status sffn_forward_dense(sffn_handle* h, const void* x, const void* W1, co
         if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
         if (T == 0) return SFFN_OK;
+        if (t1_ok(h, T)) return run_dense_t1(h, x, W1, W3, W2T, y, s);
         return h->dtype == SFFN_BF16 ? run_dense<uint16_t>(h, x, W1, W3, W2T, y, T, s)
                                      : run_dense<float>(h, x, W1, W3, W2T, y, T, s);
     } catch (...) {
@@ -372,6 +629,7 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
         if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
         if (T == 0) return SFFN_OK;
+        if (t1_ok(h, T)) return run_sparse_t1(h, x, W1, W3, W2T, y, live_count, live_idx, s);
         return h->dtype == SFFN_BF16
                    ? run_sparse<uint16_t>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s)
                    : run_sparse<float>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
@@ -394,6 +652,8 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
         if (!aligned16(V) || !aligned16(U))
             return fail(h, SFFN_INVALID_ARGUMENT, "V and U must be 16-byte aligned");
         if (T == 0) return SFFN_OK;
+        if (t1_ok(h, T) && h->r <= 4 * WAVE * 8)
+            return run_lopa_t1(h, x, V, U, W3, W2T, y, live_count, live_idx, s);
         return h->dtype == SFFN_BF16
                    ? run_lopa<uint16_t>(h, x, V, U, W3, W2T, y, T, mode, live_count, live_idx, s)
                    : run_lopa<float>(h, x, V, U, W3, W2T, y, T, mode, live_count, live_idx, s);

@@ -484,6 +484,646 @@ __global__ __launch_bounds__(K2_THREADS) void k_down(const float* __restrict__ a
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batch-1 bf16 fast path.
+//
+// 64-lane sum with DPP: quad swaps, half-row and row mirrors give every lane
+// its 16-lane row sum; row_bcast15/31 fold the four rows into lane 63.
+__device__ inline float wave_sum_dpp(float v) {
+    int t;
+    t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    v += __int_as_float(t);
+    t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    v += __int_as_float(t);
+    t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false);  // row_half_mirror
+    v += __int_as_float(t);
+    t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false);  // row_mirror
+    v += __int_as_float(t);
+    t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false);  // row_bcast:15
+    v += __int_as_float(t);
+    t = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false);  // row_bcast:31
+    v += __int_as_float(t);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// sum over a 16-byte chunk pair of bf16x2 products, accumulated in fp32.
+// The vector elements are copied to scalars before the bit cast: a bit cast of
+// an element lvalue of an ext_vector_type reads element 0 with this compiler.
+__device__ inline float dot2_chunk(const u32x4& w, const u32x4& x, float s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q], xq = x[q];
+        s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, wq),
+                                            __builtin_bit_cast(bf16x2, xq), s, false);
+    }
+    return s;
+}
+
+// Gate and gathered up projection for one token, bf16. Each wave owns RW
+// consecutive units and issues all of their W1 loads before any arithmetic;
+// the grid is sized so every block is resident at once, so the whole of W1 is
+// requested in one round. y_zero (nullable): D floats this grid clears for a
+// down pass that accumulates.
+template <int NC, int RW>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, float* __restrict__ a_out, uint8_t* __restrict__ live_out,
+    float* __restrict__ y_zero, int D, int H, int act) {
+    constexpr int RPB = K1_WAVES * RW;
+    constexpr int CW = WAVE * 8;
+    __shared__ float zs[RPB];
+    __shared__ int list[RPB];
+    __shared__ int nlist;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int row0 = blockIdx.x * RPB;
+    const int nrows = min(RPB, H - row0);
+
+    u32x4 w[RW][NC];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int rl = wave * RW + r;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            w[r][c] = (rl < nrows && col < D) ? load_stream(W1 + (size_t)(row0 + rl) * D + col)
+                                              : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    u32x4 xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = dot2_chunk(w[r][c], xv[c], s);
+        s = wave_sum_dpp(s);
+        const int rl = wave * RW + r;
+        if (lane == 0 && rl < nrows) zs[rl] = s;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool in = lane < nrows;
+        const float z = in ? zs[lane] : 0.0f;
+        const bool live = in && z > 0.0f;
+        const uint64_t m = __ballot(live);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (live) list[pos] = lane;
+        if (lane == 0) nlist = __popcll(m);
+        if (in) {
+            if (!live) a_out[row0 + lane] = 0.0f;
+            if (live_out) live_out[row0 + lane] = live ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    const int n = nlist;
+    // this block's live units, RW per wave at most; all W3 loads first
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int e = wave + j * K1_WAVES;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            w[j][c] = (e < n && col < D) ? load_stream(W3 + (size_t)(row0 + list[e]) * D + col)
+                                         : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < RW; ++j) {
+        const int e = wave + j * K1_WAVES;
+        if (e < n) {
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) s = dot2_chunk(w[j][c], xv[c], s);
+            const float u = wave_sum_dpp(s);
+            const int rl = list[e];
+            if (lane == 0) a_out[row0 + rl] = activation(act, zs[rl]) * u;
+        }
+    }
+}
+
+// Dense comparator, batch-1 bf16: W1 and W3 rows of RW units per wave read
+// together (one merged pass), a_i = A(z_i) u_i for every unit.
+template <int NC, int RW>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_dense_t1(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, float* __restrict__ a_out, float* __restrict__ y_zero,
+    int D, int H, int act) {
+    constexpr int RPB = K1_WAVES * RW;
+    constexpr int CW = WAVE * 8;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int row0 = blockIdx.x * RPB;
+    u32x4 w1[RW][NC], w3[RW][NC];
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        const int row = row0 + wave * RW + r;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            const bool ok = row < H && col < D;
+            w1[r][c] = ok ? load_stream(W1 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
+            w3[r][c] = ok ? load_stream(W3 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    u32x4 xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+#pragma unroll
+    for (int r = 0; r < RW; ++r) {
+        float sz = 0.0f, su = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            sz = dot2_chunk(w1[r][c], xv[c], sz);
+            su = dot2_chunk(w3[r][c], xv[c], su);
+        }
+        sz = wave_sum_dpp(sz);
+        su = wave_sum_dpp(su);
+        const int row = row0 + wave * RW + r;
+        if (lane == 0 && row < H) a_out[row] = activation(act, sz) * su;
+    }
+}
+
+// LoPA batch-1 bf16: rank projection t = V x (fp32 out), one V row per wave,
+// products of bf16 pairs accumulated in fp32. Also clears y for a down pass
+// that accumulates.
+template <int NC>
+__global__ __launch_bounds__(K1_THREADS) void k_rank_proj_t1(const uint16_t* __restrict__ x,
+                                                             const uint16_t* __restrict__ V,
+                                                             float* __restrict__ t_out,
+                                                             float* __restrict__ y_zero, int D,
+                                                             int r) {
+    constexpr int CW = WAVE * 8;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int m = blockIdx.x * K1_WAVES + wave;
+    u32x4 w[NC], xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        w[c] = (m < r && col < D) ? load_stream(V + (size_t)m * D + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    float sacc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sacc = dot2_chunk(w[c], xv[c], sacc);
+    sacc = wave_sum_dpp(sacc);
+    if (lane == 0 && m < r) t_out[m] = sacc;
+}
+
+// LoPA batch-1 bf16 gate: z_i = U_i . t with t in fp32 (U rows widened exactly
+// from bf16), then the same compaction and live W3 rows as k_gate_up_t1.
+// NR = 16-byte register chunks of a U row (r <= NR * 512).
+template <int NC, int NR, int RW>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
+    const uint16_t* __restrict__ x, const float* __restrict__ t_in,
+    const uint16_t* __restrict__ U, const uint16_t* __restrict__ W3, float* __restrict__ a_out,
+    uint8_t* __restrict__ live_out, int D, int H, int r, int act) {
+    constexpr int RPB = K1_WAVES * RW;
+    constexpr int CW = WAVE * 8;
+    __shared__ float zs[RPB];
+    __shared__ int list[RPB];
+    __shared__ int nlist;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int row0 = blockIdx.x * RPB;
+    const int nrows = min(RPB, H - row0);
+
+    u32x4 u[RW][NR];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        const int rl = wave * RW + q;
+#pragma unroll
+        for (int c = 0; c < NR; ++c) {
+            const int col = c * CW + lane * 8;
+            u[q][c] = (rl < nrows && col < r) ? load_stream(U + (size_t)(row0 + rl) * r + col)
+                                              : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float tv[NR][8];
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+        const int col = c * CW + lane * 8;
+        if (col < r) {
+            const float4 a = *reinterpret_cast<const float4*>(t_in + col);
+            const float4 b = *reinterpret_cast<const float4*>(t_in + col + 4);
+            tv[c][0] = a.x; tv[c][1] = a.y; tv[c][2] = a.z; tv[c][3] = a.w;
+            tv[c][4] = b.x; tv[c][5] = b.y; tv[c][6] = b.z; tv[c][7] = b.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) tv[c][k] = 0.0f;
+        }
+    }
+    u32x4 xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s = fmaf(Elem<uint16_t>::get(u[q][c], k), tv[c][k], s);
+        s = wave_sum_dpp(s);
+        const int rl = wave * RW + q;
+        if (lane == 0 && rl < nrows) zs[rl] = s;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool in = lane < nrows;
+        const float z = in ? zs[lane] : 0.0f;
+        const bool live = in && z > 0.0f;
+        const uint64_t m = __ballot(live);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (live) list[pos] = lane;
+        if (lane == 0) nlist = __popcll(m);
+        if (in) {
+            if (!live) a_out[row0 + lane] = 0.0f;
+            if (live_out) live_out[row0 + lane] = live ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    const int n = nlist;
+    for (int e = wave; e < n; e += K1_WAVES) {
+        u32x4 w3[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            w3[c] = col < D ? load_stream(W3 + (size_t)(row0 + list[e]) * D + col)
+                            : u32x4{0u, 0u, 0u, 0u};
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = dot2_chunk(w3[c], xv[c], s);
+        const float uu = wave_sum_dpp(s);
+        const int rl = list[e];
+        if (lane == 0) a_out[row0 + rl] = activation(act, zs[rl]) * uu;
+    }
+}
+
+// Down projection for one token: y[slice] = sum_i a_i W2T[i, slice].
+// Grid = (column slices, remapped XCD-contiguous) x (row splits S). Every
+// thread first loads its share of a (one round trip for the whole vector),
+// the nonzero a_i are compacted into LDS with a ballot + prefix, and the W2T
+// row slices of all of them are loaded UF at a time per lane. With S > 1 each
+// block covers H/S units and adds its partial slice to y (cleared by the gate
+// pass); with S == 1 it stores. dense != 0 keeps every unit.
+constexpr int KD_THREADS = 512;
+constexpr int KD_WAVES = KD_THREADS / WAVE;
+constexpr int KD_LCAP = 4096;  // compacted entries held in LDS at once
+template <int LPR, int PMAX>
+__global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict__ a,
+                                                        const uint16_t* __restrict__ W2T,
+                                                        float* __restrict__ y, int D, int H,
+                                                        int splits, int dense) {
+    constexpr int VEC = 8;
+    constexpr int CB = LPR * VEC;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 8;
+    __shared__ int list[KD_LCAP];
+    __shared__ float av[KD_LCAP];
+    __shared__ int wcount[PMAX][KD_WAVES];
+    __shared__ float red[KD_WAVES][CB];
+
+    const int nslices = (D + CB - 1) / CB;
+    const int per_xcd = (nslices + 7) / 8;
+    const int bx = blockIdx.x;
+    const int slice = (bx & 7) * per_xcd + (bx >> 3);
+    if (slice >= nslices) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * VEC;
+    const bool col_ok = col < D;
+    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
+
+    float ar[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        ar[p] = (p < P && row < h1) ? a[row] : 0.0f;
+    }
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
+        mk[p] = __ballot(keep);
+        if (lane == 0 && p < P) wcount[p][wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+
+    float acc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
+
+    int p0 = 0;
+    while (p0 < P) {
+        // greedy chunk of row groups whose entries fit the LDS list
+        int p1 = p0, n = 0;
+        while (p1 < P) {
+            int c = 0;
+            for (int w2 = 0; w2 < KD_WAVES; ++w2) c += wcount[p1][w2];
+            if (n + c > KD_LCAP) break;
+            n += c;
+            ++p1;
+        }
+        int base = 0;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= p0 && p < p1) {
+                int off = base;
+                for (int w2 = 0; w2 < KD_WAVES; ++w2) {
+                    if (w2 == wave) off = base;
+                    base += wcount[p][w2];
+                }
+                const bool keep = (mk[p] >> lane) & 1ull;
+                if (keep) {
+                    const int pos = off + __builtin_amdgcn_mbcnt_hi(
+                                              (uint32_t)(mk[p] >> 32),
+                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                    list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+                    av[pos] = ar[p];
+                }
+            }
+        }
+        __syncthreads();
+        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+            u32x4 wv[UF];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)list[e] * D + col)
+                                          : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const float aval = e < n ? av[e] : 0.0f;
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc[k] = fmaf(aval, Elem<uint16_t>::get(wv[u], k), acc[k]);
+            }
+        }
+        __syncthreads();
+        p0 = p1;
+    }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        float v = acc[k];
+        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+        acc[k] = v;
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[k];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+        float s = 0.0f;
+        for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+        if (col0 + c < D) {
+            if (splits > 1)
+                atomicAdd(y + col0 + c, s);
+            else
+                y[col0 + c] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Batch-1 fused pass: gate, compaction, gathered W3 dot and W2T accumulation
+// in one block per group of consecutive units (about one block per CU).
+//
+// Each of the 8 waves owns up to RW units and issues all of their W1 loads
+// before any arithmetic. The live units of the block (z > 0 on the fp32
+// accumulator) are compacted into LDS by wave 0 (ballot + mbcnt); the waves
+// then take them two at a time and load the W3 row and the W2T row of each
+// together, so the up and down reads of a live unit cost one round trip. Each
+// lane keeps the slice of y that matches its slice of x in registers; the
+// waves' slices are summed into LDS and the block writes one partial y of D
+// floats. k_reduce_partials adds the partials. DENSE visits every unit (the
+// dense comparator: W1, W3 and W2T rows of every unit, one pass).
+constexpr int KF_THREADS = 512;
+constexpr int KF_WAVES = KF_THREADS / WAVE;
+constexpr int KF_DMAX = 4096;
+
+template <int NC>
+__device__ inline void axpy_chunks(float (&acc)[NC][8], float a, const u32x4 (&w)[NC]) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[c][k] = fmaf(a, Elem<uint16_t>::get(w[c], k), acc[c][k]);
+}
+
+template <int NC>
+__device__ inline void load_row(u32x4 (&w)[NC], const uint16_t* row, int D, int lane, bool ok) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * WAVE * 8 + lane * 8;
+        w[c] = (ok && col < D) ? load_stream(row + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+template <int NC>
+__device__ inline float dot_row(const u32x4 (&w)[NC], const u32x4 (&xv)[NC]) {
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s = dot2_chunk(w[c], xv[c], s);
+    return s;
+}
+
+template <int NC, int RW, bool DENSE>
+__global__ __launch_bounds__(KF_THREADS) void k_ffn_t1(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, const uint16_t* __restrict__ W2T,
+    float* __restrict__ part, uint8_t* __restrict__ live_out, int D, int H, int rows_per_block,
+    int act) {
+    extern __shared__ float ywave[];  // [KF_WAVES][D]: each wave's slice of y
+    __shared__ float zs[KF_WAVES * RW];
+    __shared__ int list[KF_WAVES * RW];
+    __shared__ int nlist;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int row0 = blockIdx.x * rows_per_block;
+    const int nrows = min(rows_per_block, H - row0);
+
+    u32x4 xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * WAVE * 8 + lane * 8;
+        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float acc[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[c][k] = 0.0f;
+
+    int nwaves_acc;  // waves 0 .. nwaves_acc-1 hold a y slice
+    if constexpr (DENSE) {
+        // every unit: W1, W3 and W2T rows together, one unit at a time per wave
+        for (int r = 0; r < RW; ++r) {
+            const int rl = wave * RW + r;
+            const bool ok = rl < nrows;
+            const size_t off = (size_t)(row0 + rl) * D;
+            u32x4 w1[NC], w3[NC], w2[NC];
+            load_row<NC>(w1, W1 + off, D, lane, ok);
+            load_row<NC>(w3, W3 + off, D, lane, ok);
+            load_row<NC>(w2, W2T + off, D, lane, ok);
+            const float z = wave_sum_dpp(dot_row<NC>(w1, xv));
+            const float u = wave_sum_dpp(dot_row<NC>(w3, xv));
+            const float a = ok ? activation(act, z) * u : 0.0f;
+            axpy_chunks<NC>(acc, a, w2);
+        }
+        nwaves_acc = KF_WAVES;
+    } else {
+        u32x4 w[RW][NC];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const int rl = wave * RW + r;
+            load_row<NC>(w[r], W1 + (size_t)(row0 + rl) * D, D, lane, rl < nrows);
+        }
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const float z = wave_sum_dpp(dot_row<NC>(w[r], xv));
+            const int rl = wave * RW + r;
+            if (lane == 0 && rl < nrows) zs[rl] = z;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            const bool in = lane < nrows;
+            const bool live = in && zs[lane] > 0.0f;
+            const uint64_t m = __ballot(live);
+            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            if (live) list[pos] = lane;
+            if (lane == 0) nlist = __popcll(m);
+            if (in && live_out) live_out[row0 + lane] = live ? 1 : 0;
+        }
+        __syncthreads();
+        const int n = nlist;
+        // live units two at a time per wave: W3 and W2T rows of both in flight together
+        for (int e = wave; e < n; e += 2 * KF_WAVES) {
+            const int e2 = e + KF_WAVES;
+            const bool ok2 = e2 < n;
+            const int ra = list[e], rb = ok2 ? list[e2] : ra;
+            u32x4 w3a[NC], w2a[NC], w3b[NC], w2b[NC];
+            load_row<NC>(w3a, W3 + (size_t)(row0 + ra) * D, D, lane, true);
+            load_row<NC>(w2a, W2T + (size_t)(row0 + ra) * D, D, lane, true);
+            load_row<NC>(w3b, W3 + (size_t)(row0 + rb) * D, D, lane, ok2);
+            load_row<NC>(w2b, W2T + (size_t)(row0 + rb) * D, D, lane, ok2);
+            const float ua = wave_sum_dpp(dot_row<NC>(w3a, xv));
+            const float ub = wave_sum_dpp(dot_row<NC>(w3b, xv));
+            const float aa = activation(act, zs[ra]) * ua;
+            const float ab = ok2 ? activation(act, zs[rb]) * ub : 0.0f;
+            axpy_chunks<NC>(acc, aa, w2a);
+            axpy_chunks<NC>(acc, ab, w2b);
+        }
+        nwaves_acc = min(n, KF_WAVES);
+    }
+    // waves with a y slice store it to LDS (16-byte stores, conflict-free),
+    // then every thread sums 8 columns over those waves and writes the partial
+    if (wave < nwaves_acc) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * WAVE * 8 + lane * 8;
+            if (col < D) {
+                float4* dst = reinterpret_cast<float4*>(ywave + (size_t)wave * D + col);
+                dst[0] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+                dst[1] = make_float4(acc[c][4], acc[c][5], acc[c][6], acc[c][7]);
+            }
+        }
+    }
+    __syncthreads();
+    float* pb = part + (size_t)blockIdx.x * D;
+    for (int j = threadIdx.x * 8; j < D; j += KF_THREADS * 8) {
+        float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
+        for (int w2 = 0; w2 < nwaves_acc; ++w2) {
+            const float4* src = reinterpret_cast<const float4*>(ywave + (size_t)w2 * D + j);
+            const float4 a0 = src[0], a1 = src[1];
+            s0.x += a0.x; s0.y += a0.y; s0.z += a0.z; s0.w += a0.w;
+            s1.x += a1.x; s1.y += a1.y; s1.z += a1.z; s1.w += a1.w;
+        }
+        reinterpret_cast<float4*>(pb + j)[0] = s0;
+        reinterpret_cast<float4*>(pb + j)[1] = s1;
+    }
+}
+
+// y = sum over the nb partials. Block: 64 columns; thread (pg, cq) adds the
+// partials pg, pg + 16, ... of columns 4cq .. 4cq+3 (16-byte loads, all issued
+// before any use), then the 16 partial groups are summed in LDS.
+constexpr int KR_THREADS = 256;
+__global__ __launch_bounds__(KR_THREADS) void k_reduce_partials(const float* __restrict__ part,
+                                                                float* __restrict__ y, int D,
+                                                                int nb) {
+    __shared__ float red[16][64];
+    const int cq = threadIdx.x & 15, pg = threadIdx.x >> 4;
+    const int c = blockIdx.x * 64 + cq * 4;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < D) {
+        constexpr int U = 16;
+        for (int b0 = pg; b0 < nb; b0 += 16 * U) {
+            float4 v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int b = b0 + u * 16;
+                v[u] = b < nb ? *reinterpret_cast<const float4*>(part + (size_t)b * D + c)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                s.x += v[u].x; s.y += v[u].y; s.z += v[u].z; s.w += v[u].w;
+            }
+        }
+    }
+    red[pg][cq * 4 + 0] = s.x;
+    red[pg][cq * 4 + 1] = s.y;
+    red[pg][cq * 4 + 2] = s.z;
+    red[pg][cq * 4 + 3] = s.w;
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        float t = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) t += red[g][threadIdx.x];
+        const int col = blockIdx.x * 64 + threadIdx.x;
+        if (col < D) y[col] = t;
+    }
+}
+
 // Ascending live lists from the live flags: one block per token.
 __global__ __launch_bounds__(1024) void k_live_list(const uint8_t* __restrict__ live, int H,
                                                     int32_t* __restrict__ count,

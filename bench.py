@@ -1,0 +1,372 @@
+"""Benchmark of the gate-first sparse FFN forward pass on one MI355X.
+
+Workload (the decode shape): D = 2560, H = 7168, bf16 weights with fp32
+accumulation, R-S+ gate, sparsity 0.9, batch 1, a stream of 1024 sequential
+tokens. One step = the 1024 tokens, each a separate sffn_forward_sparse call
+with T = 1, captured once into a HIP graph and replayed. Token t reads weight
+replica t % R (R = 16 byte-identical copies, 1.76 GB in all) so that the
+weights come from HBM and not from the 256 MB on-package cache.
+
+Prints one JSON line: tokens/s of the sparse path (`value`), touched-byte HBM
+GB/s, the dense comparator and LoPA on the same kind of stream, the roofline
+of the dominant kernel (the longest per-token launch) from its own measured launch
+durations, and the fp64 CPU oracle timed on a bounded sample of the same
+stream as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+CALIB_BYTES = 256 << 20   # the calibration copy reads and writes this many bytes
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in ("activation_sparse_gated_amd/csrc/sffn_kernels.hip",
+                "activation_sparse_gated_amd/csrc/sffn_api.hip"):
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_pmc.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def _rocpd_rows(db_dir, query):
+    import glob
+    import sqlite3
+    rows = []
+    for db in sorted(glob.glob(os.path.join(db_dir, "**", "*.db"), recursive=True)):
+        con = sqlite3.connect(db)
+        rows += con.execute(query).fetchall()
+        con.close()
+    return rows
+
+
+def summarize_trace(db_dir: str, out: str, command: str) -> None:
+    """Kernel-trace summary (count, mean/min/max duration) of a rocprofv3 run as markdown."""
+    rows = _rocpd_rows(db_dir, "select name, count(*), avg(duration), min(duration), max(duration), "
+                               "sum(duration) from kernels group by name order by sum(duration) desc")
+    lines = [f"# rocprofv3 kernel trace: {os.path.basename(out)}", "", "Command (from the repo root):",
+             "", "```", command, "```", "",
+             "| kernel | launches | mean us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+    for name, cnt, avg, mn, mx, tot in rows:
+        short = name.split("(")[0].replace("void ", "")
+        lines.append(f"| `{short}` | {cnt} | {avg / 1e3:.3f} | {mn / 1e3:.3f} | {mx / 1e3:.3f} | "
+                     f"{tot / 1e6:.3f} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
+def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command: str) -> None:
+    """HBM bytes per launch of `kernel` from FETCH_SIZE and WRITE_SIZE runs, each scaled by
+    what the same counter reads for the calibration copy of CALIB_BYTES in the same run."""
+    q = ("select kernel_name, counter_name, avg(value), count(*) from counters_collection "
+         "group by kernel_name, counter_name")
+    res = {}
+    for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
+        vals = {name: (v, c) for name, cn, v, c in _rocpd_rows(d, q) if cn == counter}
+        calib = [v for name, (v, c) in vals.items() if "elementwise" in name and v * 1024 > CALIB_BYTES / 8]
+        kern = [v for name, (v, c) in vals.items() if kernel + "<" in name or kernel + "(" in name]
+        if not calib or not kern:
+            raise SystemExit(f"{counter}: calibration copy or {kernel} not found in {d}")
+        scale = CALIB_BYTES / (max(calib) * 1024.0)
+        res[counter] = {"kib_per_dispatch": kern[0], "calib_kib": max(calib), "scale": scale,
+                        "bytes_per_launch": kern[0] * 1024.0 * scale}
+    d = {"kernel": kernel, "workload": "decode", "source_hash": kernel_source_hash(),
+         "command": command, "calibration_copy_bytes": CALIB_BYTES,
+         "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
+         "hbm_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_launch"]
+                                       + res["WRITE_SIZE"]["bytes_per_launch"], 0)}
+    with open(out, "w") as f:
+        json.dump(d, f, indent=2)
+
+
+def main() -> int:
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
+        summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4])
+        return 0
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
+        summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
+        return 0
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--tokens", type=int, default=1024)
+    ap.add_argument("--replicas", type=int, default=16)
+    ap.add_argument("--sparsity", type=float, default=0.9)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall-clock budget of the CPU oracle baseline sample")
+    ap.add_argument("--no-extras", action="store_true", help="skip the dense and LoPA streams")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+            "(the FFN path has no cross-GPU step in this build).")
+        return 2
+
+    import torch
+
+    from activation_sparse_gated_amd import inputs as gen
+    from activation_sparse_gated_amd import sffn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    sffn.load()
+    D, H, n, R, s = 2560, 7168, args.tokens, args.replicas, args.sparsity
+    act = sffn.SFFN_ACT_RSPLUS
+
+    # ---------------------------------------------------------------- inputs
+    t0 = time.time()
+    x_np = gen.tokens(D, n, cfg=2, dtype="bf16")
+    w_np = gen.standard_weights(D, H, s, cfg=2, dtype="bf16")
+    log(f"generated decode inputs in {time.time() - t0:.1f}s")
+
+    def to_dev(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+    x = to_dev(x_np)
+    W = {k: to_dev(w_np[k]) for k in ("W1", "W3", "W2T")}
+    reps = [{k: (W[k] if r == 0 else W[k].clone()) for k in W} for r in range(R)]
+    y = torch.zeros(n, D, dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(n, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(n, H, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+
+    hs = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_BF16)
+
+    # live counts of every token (outside the timed region)
+    for t in range(n):
+        rp = reps[t % R]
+        sffn.sffn_forward_sparse(hs.ptr, x[t], rp["W1"], rp["W3"], rp["W2T"], y[t], 1,
+                                 sffn.SFFN_MODE_PER_TOKEN, cnt[t:t + 1], idx[t])
+    torch.cuda.synchronize()
+    k = cnt.cpu().numpy().astype(np.int64)
+    meas_sparsity = 1.0 - k.mean() / H
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            fn()  # one eager pass on the capture stream before capturing
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(g, steps, warmup):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps  # ms per step
+
+    def sparse_stream():
+        for t in range(n):
+            rp = reps[t % R]
+            sffn.sffn_forward_sparse(hs.ptr, x[t], rp["W1"], rp["W3"], rp["W2T"], y[t], 1,
+                                     sffn.SFFN_MODE_PER_TOKEN)
+
+    g_sparse = capture(sparse_stream)
+    ms_step = time_graph(g_sparse, args.steps, args.warmup)
+    tok_s = n / (ms_step * 1e-3)
+    bytes_tok = 2 * (H * D + 2 * k * D) + 6 * D          # weights read + x in + y out
+    touched_gbps = bytes_tok.sum() / (ms_step * 1e-3) / 1e9
+    log(f"sparse: {ms_step:.3f} ms/step, {tok_s:,.0f} tokens/s, {touched_gbps:,.0f} GB/s touched")
+
+    # per-kernel durations, measured at each kernel's own begin/end on the same stream
+    sffn.sffn_timing_enable(hs.ptr, True)
+    sffn.sffn_timing_read(hs.ptr, 0, reset=True)
+    for _ in range(2):
+        sparse_stream()
+    torch.cuda.synchronize()
+    sffn.sffn_timing_enable(hs.ptr, False)
+    kt = {}
+    for kd in range(sffn.sffn_kernel_kinds()):
+        ms, launches = sffn.sffn_timing_read(hs.ptr, kd)
+        if launches:
+            kt[sffn.sffn_kernel_name(kd)] = ms * 1e3 / launches   # us per launch
+    sffn.sffn_timing_read(hs.ptr, 0, reset=True)
+    dom = max(kt, key=kt.get)
+    kmean = float(k.mean())
+    # algorithmic bytes per launch of each batch-1 kernel (bf16 weights, fp32 unit products)
+    algo_bytes = {
+        "k_gate_up_t1": 2 * (H * D + kmean * D) + 2 * D + 4 * H,     # W1, live W3 rows, x, a out
+        "k_down_t1": 2 * kmean * D + 4 * H + 4 * D,                  # live W2T rows, a in, y out
+        "k_ffn_t1": 2 * (H * D + 2 * kmean * D) + 2 * D + 4 * D * 0,  # W1, live W3 + W2T rows, x
+        "k_reduce_partials": 0.0,
+    }
+    gate_bytes = algo_bytes.get(dom, float("nan"))
+    achieved = gate_bytes / (kt[dom] * 1e-6) / 1e9
+    log("kernels (us/launch): " + ", ".join(f"{n_} {v:.2f}" for n_, v in kt.items()))
+    log(f"dominant {dom}: {gate_bytes / 1e6:.2f} MB algorithmic per launch, {achieved:,.0f} GB/s")
+
+    # a plain copy of known size, for scaling the HBM byte counters of a profile of this run
+    calib = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_out = torch.empty_like(calib)
+    torch.mul(calib, 1.0, out=calib_out)
+    torch.cuda.synchronize()
+    del calib, calib_out
+
+    extras = {}
+    if not args.no_extras:
+        def dense_stream():
+            for t in range(n):
+                rp = reps[t % R]
+                sffn.sffn_forward_dense(hs.ptr, x[t], rp["W1"], rp["W3"], rp["W2T"], y[t], 1)
+
+        g_dense = capture(dense_stream)
+        ms_dense = time_graph(g_dense, args.steps, args.warmup)
+        sffn.sffn_timing_enable(hs.ptr, True)
+        sffn.sffn_timing_read(hs.ptr, 0, reset=True)
+        dense_stream()
+        torch.cuda.synchronize()
+        sffn.sffn_timing_enable(hs.ptr, False)
+        kt_dense = {}
+        for kd in range(sffn.sffn_kernel_kinds()):
+            ms_, l_ = sffn.sffn_timing_read(hs.ptr, kd)
+            if l_:
+                kt_dense[sffn.sffn_kernel_name(kd)] = round(ms_ * 1e3 / l_, 3)
+        sffn.sffn_timing_read(hs.ptr, 0, reset=True)
+        dense_tok_s = n / (ms_dense * 1e-3)
+        dense_gbps = n * (2 * 3 * H * D + 6 * D) / (ms_dense * 1e-3) / 1e9
+        log(f"dense: {ms_dense:.3f} ms/step, {dense_tok_s:,.0f} tokens/s, {dense_gbps:,.0f} GB/s")
+        extras.update({"dense_kernel_us": kt_dense,
+                       "dense_tokens_per_s": round(dense_tok_s, 1),
+                       "dense_GBps": round(dense_gbps, 1),
+                       "speedup_vs_dense": round(tok_s / dense_tok_s, 3)})
+        del g_dense
+
+        # LoPA at constant parameter count: D = 2560, H' = 9787, r = 400
+        Hp, r = 9787, 400
+        wl = gen.lopa_weights(D, Hp, r, s, cfg=3, dtype="bf16")
+        xl = to_dev(gen.tokens(D, n, cfg=3, dtype="bf16"))
+        WL = {kk: to_dev(wl[kk]) for kk in ("V", "U", "W3", "W2T")}
+        repl = [{kk: (WL[kk] if rr == 0 else WL[kk].clone()) for kk in WL} for rr in range(R)]
+        hl = sffn.Handle(D, Hp, r, 1, act, sffn.SFFN_BF16)
+        cl = torch.zeros(n, dtype=torch.int32, device="cuda")
+        il = torch.zeros(n, Hp, dtype=torch.int32, device="cuda")
+        for t in range(n):
+            rp = repl[t % R]
+            sffn.sffn_forward_lopa(hl.ptr, xl[t], rp["V"], rp["U"], rp["W3"], rp["W2T"], y[t], 1,
+                                   sffn.SFFN_MODE_PER_TOKEN, cl[t:t + 1], il[t])
+        torch.cuda.synchronize()
+        kl = cl.cpu().numpy().astype(np.int64)
+
+        def lopa_stream():
+            for t in range(n):
+                rp = repl[t % R]
+                sffn.sffn_forward_lopa(hl.ptr, xl[t], rp["V"], rp["U"], rp["W3"], rp["W2T"], y[t], 1,
+                                       sffn.SFFN_MODE_PER_TOKEN)
+
+        g_lopa = capture(lopa_stream)
+        ms_lopa = time_graph(g_lopa, args.steps, args.warmup)
+        lopa_tok_s = n / (ms_lopa * 1e-3)
+        lopa_gbps = (2 * (r * (D + Hp) + 2 * kl * D) + 6 * D).sum() / (ms_lopa * 1e-3) / 1e9
+        log(f"lopa: {ms_lopa:.3f} ms/step, {lopa_tok_s:,.0f} tokens/s, {lopa_gbps:,.0f} GB/s touched")
+        extras.update({"lopa_tokens_per_s": round(lopa_tok_s, 1),
+                       "lopa_touched_GBps": round(lopa_gbps, 1),
+                       "lopa_measured_sparsity": round(float(1 - kl.mean() / Hp), 4),
+                       "lopa_speedup_vs_dense": round(lopa_tok_s / extras["dense_tokens_per_s"], 3)})
+        del g_lopa
+        hl.close()
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu:
+        from oracle import reference as ref
+        threads = ref.num_threads()
+        done, t0 = 0, time.time()
+        while time.time() - t0 < args.cpu_seconds and done < 64 * n:
+            ref.ffn_standard(x_np[done % n], w_np["W1"], w_np["W3"], w_np["W2T"],
+                             act=ref.ACT_RSPLUS)
+            done += 1
+        dt = time.time() - t0
+        cpu = {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{done} tokens of the {n}-token decode stream (cycled from token 0) "
+                         f"through the fp64 sparse oracle: {dt:.1f} s, OpenMP over {threads} "
+                         f"threads"}
+        log(f"cpu oracle: {cpu['value']} tokens/s on {threads} threads ({done} tokens)")
+
+    traffic = read_traffic(dom, "decode")
+    out = {
+        "metric": "sparse-FFN tokens/s + touched-bytes HBM GB/s vs dense, D=2560 H=7168 90% sparsity",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "decode: D=2560 H=7168, bf16 weights, fp32 accumulate, R-S+ gate, "
+                               f"sparsity {s}, batch 1, {n} sequential tokens per step, "
+                               f"{R} rotating weight replicas",
+                   "D": D, "H": H, "sparsity": s, "batch": 1, "tokens_per_step": n,
+                   "replicas": R, "parallelism": "single GPU"},
+        "touched_GBps": round(float(touched_gbps), 1),
+        "touched_frac_of_peak": round(float(touched_gbps) / HBM_PEAK_GBPS, 4),
+        "measured_sparsity": round(float(meas_sparsity), 4),
+        "k_mean": round(float(k.mean()), 1),
+        "k_std": round(float(k.std()), 1),
+        "us_per_token": round(ms_step * 1e3 / n, 3),
+        "kernel_us": {kk: round(v, 3) for kk, v in kt.items()},
+        "kernels_per_token": len(kt),
+        **extras,
+        "roofline": {"bound": "hbm", "achieved": round(float(achieved), 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(float(achieved) / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": dom,
+                     "bytes_per_launch": round(float(gate_bytes), 0),
+                     "avg_launch_us": round(kt[dom], 3)},
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    hs.close()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
