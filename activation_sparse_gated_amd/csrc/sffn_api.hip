@@ -51,8 +51,8 @@ struct sffn_handle {
     int down_lpr = 8;
     // batch-1 bf16 path
     int t1_rw = 1;            // units per wave in the gate pass
-    int t1_lpr = 8;           // lanes per W2T row slice in the down pass
-    int t1_splits_sparse = 4; // row splits of the down pass (sparse)
+    int t1_lpr = 32;          // lanes per W2T row slice in the down pass (512 B per row)
+    int t1_splits_sparse = 16; // row splits of the down pass (sparse)
     int t1_splits_dense = 16; // row splits of the down pass (dense, unfused)
     int t1_fused_sparse = 0;  // sparse: fused gate/up/down pass + partial reduction
     int t1_fused_dense = 1;   // dense: fused one-pass W1/W3/W2T + partial reduction
@@ -244,6 +244,14 @@ sffn_status run_down_t1(sffn_handle* h, const void* W2T, float* y, int splits, i
     sffn_status st = SFFN_OK;
     if (h->t1_lpr == 4) {
         SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<4, PMAX>, dim3(nbx, splits),
+                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
+    } else if (h->t1_lpr == 16) {
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<16, PMAX>, dim3(nbx, splits),
+                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
+    } else if (h->t1_lpr == 32) {
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<32, PMAX>, dim3(nbx, splits),
                                            dim3(KD_THREADS), s, (const float*)h->a_buf,
                                            (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
     } else {
@@ -541,9 +549,9 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         const int e_rw = env_int("SFFN_T1_ROWS_PER_WAVE", 0);
         if (e_rw == 1 || e_rw == 2 || e_rw == 4) h->t1_rw = e_rw;
         const int e_lpr = env_int("SFFN_T1_LANES_PER_ROW", 0);
-        if (e_lpr == 4 || e_lpr == 8) h->t1_lpr = e_lpr;
+        if (e_lpr == 4 || e_lpr == 8 || e_lpr == 16 || e_lpr == 32) h->t1_lpr = e_lpr;
         const int e_ss = env_int("SFFN_T1_SPLITS_SPARSE", 0);
-        if (e_ss >= 1 && e_ss <= 16) h->t1_splits_sparse = e_ss;
+        if (e_ss >= 1 && e_ss <= 64) h->t1_splits_sparse = e_ss;
         const int e_sd = env_int("SFFN_T1_SPLITS_DENSE", 0);
         if (e_sd >= 1 && e_sd <= 16) h->t1_splits_dense = e_sd;
         h->t1_fused = 1;

@@ -812,7 +812,8 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
     constexpr int UF = 8;
     __shared__ int list[KD_LCAP];
     __shared__ float av[KD_LCAP];
-    __shared__ int wcount[PMAX][KD_WAVES];
+    __shared__ int wcount[PMAX * KD_WAVES];   // kept entries per (row group p, wave)
+    __shared__ int woff[PMAX * KD_WAVES + 1]; // exclusive prefix of wcount in (p, wave) order
     __shared__ float red[KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
@@ -843,7 +844,27 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
         const int row = h0 + p * KD_THREADS + threadIdx.x;
         const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
         mk[p] = __ballot(keep);
-        if (lane == 0 && p < P) wcount[p][wave] = __popcll(mk[p]);
+        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    // exclusive prefix over the (p, wave) counts by wave 0: one independent LDS
+    // read per lane, then a wave-wide scan with DPP-free shuffles
+    if (wave == 0) {
+        constexpr int NCNT = PMAX * KD_WAVES;
+        int carry = 0;
+        for (int base = 0; base < NCNT; base += WAVE) {
+            const int i = base + lane;
+            const int v = i < NCNT ? wcount[i] : 0;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const int t = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += t;
+            }
+            if (i < NCNT) woff[i] = carry + incl - v;
+            carry += __shfl(incl, WAVE - 1, WAVE);
+        }
+        if (lane == 0) woff[NCNT] = carry;
     }
     __syncthreads();
 
@@ -854,31 +875,20 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
     int p0 = 0;
     while (p0 < P) {
         // greedy chunk of row groups whose entries fit the LDS list
-        int p1 = p0, n = 0;
-        while (p1 < P) {
-            int c = 0;
-            for (int w2 = 0; w2 < KD_WAVES; ++w2) c += wcount[p1][w2];
-            if (n + c > KD_LCAP) break;
-            n += c;
+        int p1 = p0 + 1;
+        while (p1 < P && woff[p1 * KD_WAVES] - woff[p0 * KD_WAVES] + 
+                         (woff[(p1 + 1) * KD_WAVES] - woff[p1 * KD_WAVES]) <= KD_LCAP)
             ++p1;
-        }
-        int base = 0;
+        const int ebase = woff[p0 * KD_WAVES];
+        const int n = woff[p1 * KD_WAVES] - ebase;
 #pragma unroll
         for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1) {
-                int off = base;
-                for (int w2 = 0; w2 < KD_WAVES; ++w2) {
-                    if (w2 == wave) off = base;
-                    base += wcount[p][w2];
-                }
-                const bool keep = (mk[p] >> lane) & 1ull;
-                if (keep) {
-                    const int pos = off + __builtin_amdgcn_mbcnt_hi(
-                                              (uint32_t)(mk[p] >> 32),
-                                              __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                    list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-                    av[pos] = ar[p];
-                }
+            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
+                const int pos = woff[p * KD_WAVES + wave] - ebase +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+                av[pos] = ar[p];
             }
         }
         __syncthreads();

@@ -107,6 +107,95 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command
         json.dump(d, f, indent=2)
 
 
+
+def _graph_time(torch, fn, steps, warmup):
+    """Capture fn once into a HIP graph; ms per replay."""
+    g = torch.cuda.CUDAGraph()
+    fn()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def bench_batched(torch, sffn, gen, to_dev, x1, reps, D, H, act, args):
+    """Token batches of T = 1, 4, 16, 64 at s = 0.9 (i.i.d. tokens, independent live sets):
+    per-token lists, union of live sets, and the dense comparator. 64 calls per replay."""
+    R = len(reps)
+    out = {}
+    xb = to_dev(gen.tokens(D, 64 * 64, cfg=4, dtype="bf16"))
+    for T in (1, 4, 16, 64):
+        h = sffn.Handle(D, H, 0, T, act, sffn.SFFN_BF16)
+        y = torch.zeros(64 * T, D, dtype=torch.float32, device="cuda")
+        calls = 64
+        res = {}
+        for name, mode in (("per_token", sffn.SFFN_MODE_PER_TOKEN), ("union", sffn.SFFN_MODE_UNION),
+                           ("dense", None)):
+            def fn():
+                for c in range(calls):
+                    rp = reps[c % R]
+                    xs, ys = xb[c * T:(c + 1) * T], y[c * T:(c + 1) * T]
+                    if mode is None:
+                        sffn.sffn_forward_dense(h.ptr, xs, rp["W1"], rp["W3"], rp["W2T"], ys, T)
+                    else:
+                        sffn.sffn_forward_sparse(h.ptr, xs, rp["W1"], rp["W3"], rp["W2T"], ys, T,
+                                                 mode)
+            ms = _graph_time(torch, fn, max(2, args.steps // 4), 1)
+            res[name + "_tokens_per_s"] = round(calls * T / (ms * 1e-3), 1)
+        res["union_vs_dense"] = round(res["union_tokens_per_s"] / res["dense_tokens_per_s"], 3)
+        out[f"T{T}"] = res
+        log(f"batched T={T}: " + ", ".join(f"{k} {v:,}" for k, v in res.items()))
+        h.close()
+    return out
+
+
+def bench_stacks(torch, sffn, gen, to_dev, act, args):
+    """32-layer stacks at s = 0.895, batch-1 decode of 256 tokens through all layers.
+    The 32 layers are byte-identical copies of one generated layer at distinct addresses
+    (2.4 GB and 9.7 GB): the weights stream from HBM exactly as 32 independent layers."""
+    out = {}
+    for (D, H) in ((2048, 6144), (4096, 12288)):
+        w = gen.standard_weights(D, H, 0.895, cfg=5, dtype="bf16")
+        W = {k: to_dev(w[k]) for k in ("W1", "W3", "W2T")}
+        layers = [{k: (W[k] if l == 0 else W[k].clone()) for k in W} for l in range(32)]
+        ntok = 256
+        xs = to_dev(gen.tokens(D, ntok * 32, cfg=5, dtype="bf16"))
+        h = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_BF16)
+        y = torch.zeros(ntok * 32, D, dtype=torch.float32, device="cuda")
+        res = {}
+        for name, dense in (("sparse", False), ("dense", True)):
+            def fn():
+                for t in range(ntok):
+                    for l in range(32):
+                        i = t * 32 + l
+                        L = layers[l]
+                        if dense:
+                            sffn.sffn_forward_dense(h.ptr, xs[i], L["W1"], L["W3"], L["W2T"], y[i], 1)
+                        else:
+                            sffn.sffn_forward_sparse(h.ptr, xs[i], L["W1"], L["W3"], L["W2T"], y[i], 1)
+            ms = _graph_time(torch, fn, 2, 1)
+            res[name + "_stack_tokens_per_s"] = round(ntok / (ms * 1e-3), 1)
+            res[name + "_layer_tokens_per_s"] = round(ntok * 32 / (ms * 1e-3), 1)
+        res["sparse_vs_dense"] = round(res["sparse_stack_tokens_per_s"] / res["dense_stack_tokens_per_s"], 3)
+        out[f"D{D}_H{H}"] = res
+        log(f"stack D={D} H={H}: " + ", ".join(f"{k} {v:,}" for k, v in res.items()))
+        h.close()
+        del layers, W
+        torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -306,6 +395,11 @@ def main() -> int:
                        "lopa_speedup_vs_dense": round(lopa_tok_s / extras["dense_tokens_per_s"], 3)})
         del g_lopa
         hl.close()
+
+    # ---------------------------------------------------------------- batched decode and stacks
+    if not args.no_extras:
+        extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
+        extras["stacks"] = bench_stacks(torch, sffn, gen, to_dev, act, args)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
