@@ -21,12 +21,13 @@ namespace {
 enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GATE_UP_DENSE,
             KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_GATE_UP_DENSE_T1, KIND_DOWN_T1,
             KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
-            KIND_COUNT };
+            KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
                                             "k_ffn_t1", "k_ffn_dense_t1", "k_reduce_partials",
-                                            "k_rank_proj_t1", "k_gate_up_lopa_t1"};
+                                            "k_rank_proj_t1", "k_gate_up_lopa_t1",
+                                            "k_gate_up_mfma", "k_down_mfma", "k_down_tb"};
 
 thread_local std::string g_thread_error = "no error";
 
@@ -61,6 +62,14 @@ struct sffn_handle {
     int f_rw = 0;             // units per wave in the fused pass
     int f_blocks = 0;         // fused blocks (= partials)
     float* part_buf = nullptr; // [f_blocks x D] partial outputs
+    // batched bf16 path on MFMA (union of live sets, dense)
+    int m_tp = 0;                  // padded token count (16 * token tiles) the buffers hold
+    int m_splits = 4;              // row splits of the MFMA down pass
+    int tb_splits = 16;            // row splits of the small-batch down pass
+    int tb_max = 8;                // batches up to this size use the small-batch down pass
+    float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
+    uint64_t* m_mask = nullptr;    // [H] tokens for which each unit is live
+
     // instrumentation
     bool timing = false;
     struct Rec { int kind; hipEvent_t start, stop; };
@@ -351,6 +360,78 @@ sffn_status run_dense_t1(sffn_handle* h, const void* x, const void* W1, const vo
     return run_down_t1(h, W2T, y, splits, 1, s);
 }
 
+// ---- batched bf16 path on MFMA
+bool mfma_ok(const sffn_handle* h, int T) {
+    return T >= 2 && h->dtype == SFFN_BF16 && h->m_a != nullptr && h->D <= 4096 &&
+           T <= h->m_tp;
+}
+
+#define SFFN_NT_SWITCH(NTV, BODY)                         \
+    switch (NTV) {                                        \
+        case 1: { constexpr int NT = 1; BODY; } break;    \
+        case 2: { constexpr int NT = 2; BODY; } break;    \
+        case 3: { constexpr int NT = 3; BODY; } break;    \
+        case 4: { constexpr int NT = 4; BODY; } break;    \
+        default: return fail(h, SFFN_INTERNAL, "bad token tile count"); \
+    }
+#define SFFN_KS_SWITCH(KSV, BODY)                         \
+    switch (KSV) {                                        \
+        case 2: { constexpr int KS = 2; BODY; } break;    \
+        case 4: { constexpr int KS = 4; BODY; } break;    \
+        case 8: { constexpr int KS = 8; BODY; } break;    \
+        case 16: { constexpr int KS = 16; BODY; } break;  \
+        case 20: { constexpr int KS = 20; BODY; } break;  \
+        case 32: { constexpr int KS = 32; BODY; } break;  \
+        default: return fail(h, SFFN_INTERNAL, "bad K steps"); \
+    }
+constexpr int kKS[] = {2, 4, 8, 16, 20, 32};
+
+template <bool DENSE>
+sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                     const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
+                     hipStream_t s) {
+    const int nt = (T + 15) / 16;
+    const int steps = (h->D + 31) / 32;
+    const int ks = pick(kKS, 6, (steps + 3) / 4);
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    sffn_status st = SFFN_OK;
+    const int nb = (h->H + 15) / 16;
+    const bool small = T <= h->tb_max && T <= 8;
+    const int splits = small ? h->tb_splits : h->m_splits;
+    float* yz = splits > 1 ? y : nullptr;
+    SFFN_NT_SWITCH(nt, SFFN_KS_SWITCH(ks,
+        st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NT, KS, DENSE>, dim3(nb),
+                    dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,
+                    (const uint16_t*)W3, h->m_a, h->m_mask, live, yz, h->D, h->H, T, h->act)));
+    if (st != SFFN_OK) return st;
+    if (small) {
+        // 512-byte row slices (32 lanes x 16 B), XCD-contiguous slice order
+        const int cb = 32 * 8;
+        const int nslices = (h->D + cb - 1) / cb;
+        const int nbx = ((nslices + 7) / 8) * 8;
+        const int hs = (h->H + splits - 1) / splits;
+        const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+        const int tt = T <= 2 ? 2 : (T <= 4 ? 4 : 8);
+#define SFFN_TB_LAUNCH(TTV)                                                                      \
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB, k_down_tb<32, PMAX, TTV>,            \
+                                           dim3(nbx, splits), dim3(KD_THREADS), s,               \
+                                           (const float*)h->m_a, (const uint64_t*)h->m_mask,     \
+                                           (const uint16_t*)W2T, y, h->D, h->H, T, 16 * nt,      \
+                                           splits))
+        if (tt == 2) { SFFN_TB_LAUNCH(2); } else if (tt == 4) { SFFN_TB_LAUNCH(4); } else { SFFN_TB_LAUNCH(8); }
+#undef SFFN_TB_LAUNCH
+    } else {
+        const int ntile = (h->D + 63) / 64;
+        SFFN_NT_SWITCH(nt,
+            st = launch(h, KIND_DOWN_MFMA, k_down_mfma<NT>, dim3(ntile, splits),
+                        dim3(KDM_THREADS), s, (const float*)h->m_a, (const uint64_t*)h->m_mask,
+                        (const uint16_t*)W2T, y, h->D, h->H, T, splits));
+    }
+    if (st != SFFN_OK) return st;
+    if (!DENSE) return run_live_list(h, T, live_count, live_idx, s);
+    return SFFN_OK;
+}
+
 template <typename WT>
 sffn_status run_sparse(sffn_handle* h, const void* x, const void* W1, const void* W3,
                        const void* W2T, float* y, int T, int mode, int32_t* live_count,
@@ -585,6 +666,25 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         } else {
             h->t1_fused = 0;
         }
+        // batched MFMA plan: unit-major products for up to 16*ceil(max_tokens/16) tokens
+        if (dtype == SFFN_BF16 && D <= 4096 && max_tokens >= 2) {
+            h->m_tp = 16 * ((max_tokens + 15) / 16);
+            int sp = env_int("SFFN_MFMA_SPLITS", 4);
+            if (sp < 1) sp = 4;
+            while ((H + sp - 1) / sp > KDM_LCAP) ++sp;
+            h->m_splits = sp;
+            const int tbs = env_int("SFFN_TB_SPLITS", 16);
+            if (tbs >= 1 && tbs <= 64) h->tb_splits = tbs;
+            const int tbm = env_int("SFFN_TB_MAX", 8);
+            if (tbm >= 0 && tbm <= 8) h->tb_max = tbm;
+            while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;
+            e = hipMalloc(&h->m_a, (size_t)H * h->m_tp * sizeof(float));
+            if (e == hipSuccess) e = hipMalloc(&h->m_mask, (size_t)H * sizeof(uint64_t));
+            if (e != hipSuccess) {
+                sffn_destroy(h);
+                return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
+            }
+        }
         *out = h;
         return SFFN_OK;
     } catch (...) {
@@ -603,6 +703,9 @@ void sffn_destroy(sffn_handle* h) {
     if (h->live_buf) (void)hipFree(h->live_buf);
     if (h->t_buf) (void)hipFree(h->t_buf);
     if (h->part_buf) (void)hipFree(h->part_buf);
+    if (h->m_a) (void)hipFree(h->m_a);
+    if (h->m_mask) (void)hipFree(h->m_mask);
+
     delete h;
 }
 
@@ -617,6 +720,7 @@ sffn_status sffn_forward_dense(sffn_handle* h, const void* x, const void* W1, co
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
         if (T == 0) return SFFN_OK;
         if (t1_ok(h, T)) return run_dense_t1(h, x, W1, W3, W2T, y, s);
+        if (mfma_ok(h, T)) return run_mfma<true>(h, x, W1, W3, W2T, y, T, nullptr, nullptr, s);
         return h->dtype == SFFN_BF16 ? run_dense<uint16_t>(h, x, W1, W3, W2T, y, T, s)
                                      : run_dense<float>(h, x, W1, W3, W2T, y, T, s);
     } catch (...) {
@@ -638,6 +742,8 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
         if (T == 0) return SFFN_OK;
         if (t1_ok(h, T)) return run_sparse_t1(h, x, W1, W3, W2T, y, live_count, live_idx, s);
+        if (mode == SFFN_MODE_UNION && mfma_ok(h, T))
+            return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
         return h->dtype == SFFN_BF16
                    ? run_sparse<uint16_t>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s)
                    : run_sparse<float>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);

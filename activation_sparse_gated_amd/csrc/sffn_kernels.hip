@@ -1134,6 +1134,509 @@ __global__ __launch_bounds__(KR_THREADS) void k_reduce_partials(const float* __r
     }
 }
 
+// ---------------------------------------------------------------------------
+// Batched bf16 path on MFMA (v_mfma_f32_16x16x32_bf16). Lane l of a wave holds
+// A[l%16][8(l/16) .. +8], B[8(l/16) .. +8][l%16] and C[4(l/16) .. +4][l%16].
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ inline bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ inline f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs)
+__device__ inline uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// acc[nt] = W[16 rows, steps s0..s1) x X^T[tokens nt*16 .. +16] over 32-column
+// MFMA steps. The weight rows are streamed from HBM with coalesced loads (a
+// wave-load covers 4 rows x 256 contiguous bytes), all issued up front, and
+// pass through a per-wave LDS tile (rows padded to 17 x 16 B, so both the
+// stores and the MFMA fragment reads are conflict-free). The token operand
+// runs PF steps ahead in a register ring. rows[r] is the matrix row of tile
+// row r (< 0: a zero row).
+constexpr int LA_STRIDE = 17;  // 16-byte units per staged row (16 + 1 pad)
+template <int NT, int KS>
+__device__ inline void mfma_rows_x_tokens(f32x4 (&acc)[NT], const uint16_t* __restrict__ W,
+                                          const int* rows, u32x4* la,
+                                          const uint16_t* __restrict__ x, int D, int T, int s0,
+                                          int s1, int lane) {
+    constexpr int PFW = NT >= 3 ? 2 : 4;  // token-operand ring depth
+    constexpr int PF = KS < PFW ? KS : PFW;
+    constexpr int NCH = (KS + 3) / 4;     // chunks of 4 steps (128 columns)
+    const int kq = 8 * (lane >> 4);
+    const int r16 = lane & 15;
+    // weight chunks: chunk c, wave-load j covers tile rows 4j .. 4j+3, 16 B units l%16
+    u32x4 w[NCH][4];
+#pragma unroll
+    for (int c = 0; c < NCH; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * j + (lane >> 4);
+            const int u = lane & 15;
+            const int step = s0 + 4 * c + (u >> 2);
+            const int col = (s0 + 4 * c) * 32 + u * 8;
+            const int row = rows[r];
+            w[c][j] = (row >= 0 && step < s1 && col < D) ? load_stream(W + (size_t)row * D + col)
+                                                        : u32x4{0u, 0u, 0u, 0u};
+        }
+    u32x4 b[PF][NT];
+#pragma unroll
+    for (int i = 0; i < PF; ++i) {
+        const int col = (s0 + i) * 32 + kq;
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int t = nt * 16 + r16;
+            b[i][nt] = (s0 + i < s1 && t < T && col < D) ? load_cached(x + (size_t)t * D + col)
+                                                        : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) la[(4 * j + (lane >> 4)) * LA_STRIDE + (lane & 15)] = w[c][j];
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int i = 4 * c + ii;
+            if (i < KS) {
+                const u32x4 af = la[r16 * LA_STRIDE + ii * 4 + (lane >> 4)];
+                if (s0 + i < s1) {
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(af, b[i % PF][nt], acc[nt]);
+                }
+                const int ip = i + PF;
+                if (ip < KS) {
+                    const int col = (s0 + ip) * 32 + kq;
+#pragma unroll
+                    for (int nt = 0; nt < NT; ++nt) {
+                        const int t = nt * 16 + r16;
+                        b[i % PF][nt] = (s0 + ip < s1 && t < T && col < D)
+                                            ? load_cached(x + (size_t)t * D + col)
+                                            : u32x4{0u, 0u, 0u, 0u};
+                    }
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Stage 1: gate and up projection of 16 units for T <= 16*NT tokens.
+// The 4 waves split the K = D dimension into contiguous ranges of 32-column
+// MFMA steps (at most KS steps each). The gate reads every W1 row of the
+// block; the up projection gathers only the W3 rows of units live for some
+// token (DENSE: all units). Writes a_rm[unit][16*NT] (unit-major; 0 for dead
+// (unit, token) pairs and padded tokens), umask[unit] (tokens for which the
+// unit is live; DENSE: all tokens), live flags [T x H] when requested, and
+// clears y (T x D) for the down pass that accumulates.
+constexpr int KM_THREADS = 256;
+template <int NT, int KS, bool DENSE>
+__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act) {
+    constexpr int TP = 16 * NT;
+    __shared__ float part[4][16][TP + 1];
+    __shared__ float zf[16][TP + 1];
+    __shared__ unsigned long long tmask[16];
+    __shared__ int ulist[16];
+    __shared__ int upos[16];
+    __shared__ int nu_s;
+    __shared__ int rows_g[16];
+    __shared__ int rows_u[16];
+    __shared__ u32x4 la_all[4][16 * LA_STRIDE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int u0 = blockIdx.x * 16;
+    const int S = (D + 31) / 32;
+    const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
+    const int kq = 8 * (lane >> 4);
+    const int r16 = lane & 15;
+
+    if (y_zero) {
+        for (int j = blockIdx.x * KM_THREADS + threadIdx.x; j < T * D; j += gridDim.x * KM_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    if (threadIdx.x < 16) {
+        tmask[threadIdx.x] = 0ull;
+        rows_g[threadIdx.x] = (u0 + (int)threadIdx.x < H) ? u0 + (int)threadIdx.x : -1;
+    }
+    __syncthreads();
+
+    // ---- gate: z[16 units][TP tokens]
+    {
+        f32x4 acc[NT];
+        mfma_rows_x_tokens<NT, KS>(acc, W1, rows_g, la_all[wave], x, D, T, s0, s1, lane);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[wave][4 * (lane >> 4) + j][nt * 16 + r16] = acc[nt][j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        const float z = part[0][i][t] + part[1][i][t] + part[2][i][t] + part[3][i][t];
+        zf[i][t] = z;
+        const bool ok = (u0 + i < H) && t < T;
+        const bool live = ok && (DENSE || z > 0.0f);
+        if (live) atomicOr(&tmask[i], 1ull << t);
+        if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool any = lane < 16 && tmask[lane] != 0ull;
+        const uint64_t m = __ballot(any);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (any) ulist[pos] = lane;
+        if (lane < 16) upos[lane] = any ? pos : -1;
+        if (lane < 16) rows_u[lane] = -1;
+        if (lane == 0) nu_s = __popcll(m);
+        if (lane < 16 && u0 + lane < H) umask[u0 + lane] = tmask[lane];
+    }
+    __syncthreads();
+    const int nu = nu_s;
+    if (threadIdx.x < 16 && (int)threadIdx.x < nu) rows_u[threadIdx.x] = u0 + ulist[threadIdx.x];
+    __syncthreads();
+
+    // ---- up projection over the gathered live units: u[p][token], p < nu
+    if (nu > 0) {
+        f32x4 acc[NT];
+        mfma_rows_x_tokens<NT, KS>(acc, W3, rows_u, la_all[wave], x, D, T, s0, s1, lane);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) part[wave][4 * (lane >> 4) + j][nt * 16 + r16] = acc[nt][j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        if (u0 + i >= H) continue;
+        const int p = upos[i];
+        float av = 0.0f;
+        if (p >= 0 && t < T && ((tmask[i] >> t) & 1ull)) {
+            const float u = part[0][p][t] + part[1][p][t] + part[2][p][t] + part[3][p][t];
+            av = activation(act, zf[i][t]) * u;
+        }
+        a_rm[(size_t)(u0 + i) * TP + t] = av;
+    }
+}
+
+// Stage 2: y[T x D] += sum over units of a_rm[unit][t] * W2T[unit][:], over the
+// units live for some token (y is cleared by stage 1). Grid: (column tiles of
+// 64, row splits). Each of the 4 waves takes its own 32-unit chunks of the
+// block's compacted unit list: it stages the chunk's W2T tile [32 x 64]
+// transposed in LDS and its unit products [TP x 32] in LDS, then runs MFMAs
+// with the products split into bf16 hi + lo parts (two MFMAs, close to fp32
+// accuracy). The global loads of the next two chunks are in flight while a
+// chunk is staged and multiplied. The waves' tiles are summed in LDS and each
+// block adds its tile to y with fp32 atomics (one add per split per output).
+constexpr int KDM_THREADS = 256;
+constexpr int KDM_LCAP = 2048;
+template <int NT>
+__global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
+    const float* __restrict__ a_rm, const uint64_t* __restrict__ umask,
+    const uint16_t* __restrict__ W2T, float* __restrict__ y, int D, int H, int T, int splits) {
+    constexpr int TP = 16 * NT;
+    constexpr int CWT = 64;  // columns per block
+    __shared__ int list[KDM_LCAP];
+    __shared__ int wcnt[KDM_THREADS / WAVE];
+    __shared__ int nlist_s;
+    __shared__ __attribute__((aligned(16))) uint16_t bt[4][CWT][32 + 8];  // W2T chunk, [col][unit]
+    __shared__ float at[4][TP][32 + 1];                                     // products, [token][unit]
+    __shared__ float ysum[TP][CWT + 1];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15;
+    const int kq = 8 * (lane >> 4);
+    const int col0 = blockIdx.x * CWT;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+
+    // compaction of the units live for some token, ascending within the block
+    if (threadIdx.x == 0) nlist_s = 0;
+    for (int e = threadIdx.x; e < TP * (CWT + 1); e += KDM_THREADS) (&ysum[0][0])[e] = 0.0f;
+    __syncthreads();
+    for (int base = h0; base < h1; base += KDM_THREADS) {
+        const int row = base + threadIdx.x;
+        const bool keep = row < h1 && umask[row] != 0ull;
+        const uint64_t m = __ballot(keep);
+        if (lane == 0) wcnt[wave] = __popcll(m);
+        __syncthreads();
+        int off = nlist_s;
+        for (int w = 0; w < wave; ++w) off += wcnt[w];
+        if (keep) {
+            const int pos = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+            list[pos] = row;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) nlist_s += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+        __syncthreads();
+    }
+    const int n = nlist_s;
+
+    f32x4 acc[NT][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    constexpr int AV = TP / 8;  // float4 loads of unit products per lane per chunk
+    constexpr int DEPTH = 3;    // chunks whose global loads are in flight
+    u32x4 wv[DEPTH][4];
+    float4 avv[DEPTH][AV];
+    auto fetch = [&](int slot, int c0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = c0 + q * 8 + (lane >> 3);
+            const int cc = (lane & 7) * 8;
+            wv[slot][q] = (e < n && col0 + cc < D)
+                              ? load_stream(W2T + (size_t)list[e] * D + col0 + cc)
+                              : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int v = 0; v < AV; ++v) {
+            const int idx = v * WAVE + lane;
+            const int uu = idx / (TP / 4), t4 = (idx % (TP / 4)) * 4;
+            const int e = c0 + uu;
+            avv[slot][v] = e < n ? *reinterpret_cast<const float4*>(a_rm + (size_t)list[e] * TP + t4)
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    const int cstep = 4 * 32;  // this wave's chunks are wave*32 + j*cstep
+    const int nch = (n > wave * 32) ? (n - wave * 32 + cstep - 1) / cstep : 0;
+#pragma unroll
+    for (int d = 0; d < DEPTH - 1; ++d)
+        if (d < nch) fetch(d, wave * 32 + d * cstep);
+    for (int j0 = 0; j0 < nch; j0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int j = j0 + d;
+            if (j < nch) {
+                const int jn = j + DEPTH - 1;
+                if (jn < nch) fetch((d + DEPTH - 1) % DEPTH, wave * 32 + jn * cstep);
+                // stage chunk j: W2T transposed [col][unit], products [token][unit]
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int uu = q * 8 + (lane >> 3);
+                    const int cc = (lane & 7) * 8;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const uint32_t w32 = wv[d][q][k >> 1];
+                        bt[wave][cc + k][uu] = (uint16_t)((k & 1) ? (w32 >> 16) : (w32 & 0xffffu));
+                    }
+                }
+#pragma unroll
+                for (int v = 0; v < AV; ++v) {
+                    const int idx = v * WAVE + lane;
+                    const int uu = idx / (TP / 4), t4 = (idx % (TP / 4)) * 4;
+                    at[wave][t4 + 0][uu] = avv[d][v].x;
+                    at[wave][t4 + 1][uu] = avv[d][v].y;
+                    at[wave][t4 + 2][uu] = avv[d][v].z;
+                    at[wave][t4 + 3][uu] = avv[d][v].w;
+                }
+                __builtin_amdgcn_wave_barrier();
+                u32x4 b[4];
+#pragma unroll
+                for (int ct = 0; ct < 4; ++ct)
+                    b[ct] = *reinterpret_cast<const u32x4*>(&bt[wave][ct * 16 + r16][kq]);
+#pragma unroll
+                for (int nt = 0; nt < NT; ++nt) {
+                    const float* srcA = &at[wave][nt * 16 + r16][kq];
+                    uint32_t hi[8], lo[8];
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float f = srcA[k];
+                        hi[k] = bf16_rne(f);
+                        lo[k] = bf16_rne(f - __uint_as_float(hi[k] << 16));
+                    }
+                    const u32x4 ahi = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                            hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+                    const u32x4 alo = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                            lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+#pragma unroll
+                    for (int ct = 0; ct < 4; ++ct) {
+                        acc[nt][ct] = mfma_bf16(ahi, b[ct], acc[nt][ct]);
+                        acc[nt][ct] = mfma_bf16(alo, b[ct], acc[nt][ct]);
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+        }
+    }
+    // sum the 4 waves' tiles in LDS, then add the block's tile to y
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                atomicAdd(&ysum[nt * 16 + 4 * (lane >> 4) + j][ct * 16 + r16], acc[nt][ct][j]);
+    __syncthreads();
+    for (int e = threadIdx.x; e < T * CWT; e += KDM_THREADS) {
+        const int t = e / CWT, c = e % CWT;
+        if (col0 + c < D) {
+            if (splits > 1)
+                atomicAdd(y + (size_t)t * D + col0 + c, ysum[t][c]);
+            else
+                y[(size_t)t * D + col0 + c] = ysum[t][c];
+        }
+    }
+}
+
+// Down projection for small batches (T <= TT <= 8), bf16: like k_down_t1, but
+// the units kept are those live for some token (umask != 0; DENSE: all), each
+// lane keeps TT x 8 accumulators, and a unit's TT products come from the
+// unit-major a_rm[unit][tp]. y is cleared by the gate pass when splits > 1.
+template <int LPR, int PMAX, int TT>
+__global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict__ a_rm,
+                                                        const uint64_t* __restrict__ umask,
+                                                        const uint16_t* __restrict__ W2T,
+                                                        float* __restrict__ y, int D, int H,
+                                                        int T, int tp, int splits) {
+    constexpr int VEC = 8;
+    constexpr int CB = LPR * VEC;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 4;
+    __shared__ int list[KD_LCAP];
+    __shared__ int wcount[PMAX * KD_WAVES];
+    __shared__ int woff[PMAX * KD_WAVES + 1];
+    __shared__ float red[KD_WAVES][CB];
+
+    const int nslices = (D + CB - 1) / CB;
+    const int per_xcd = (nslices + 7) / 8;
+    const int bx = blockIdx.x;
+    const int slice = (bx & 7) * per_xcd + (bx >> 3);
+    if (slice >= nslices) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * VEC;
+    const bool col_ok = col < D;
+    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;
+
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        const bool keep = p < P && row < h1 && umask[row] != 0ull;
+        mk[p] = __ballot(keep);
+        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int NCNT = PMAX * KD_WAVES;
+        int carry = 0;
+        for (int base = 0; base < NCNT; base += WAVE) {
+            const int i = base + lane;
+            const int v = i < NCNT ? wcount[i] : 0;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const int t = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += t;
+            }
+            if (i < NCNT) woff[i] = carry + incl - v;
+            carry += __shfl(incl, WAVE - 1, WAVE);
+        }
+        if (lane == 0) woff[NCNT] = carry;
+    }
+    __syncthreads();
+
+    float acc[TT][VEC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[t][k] = 0.0f;
+
+    int p0 = 0;
+    while (p0 < P) {
+        int p1 = p0 + 1;
+        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
+        const int ebase = woff[p0 * KD_WAVES];
+        const int n = woff[p1 * KD_WAVES] - ebase;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
+                const int pos = woff[p * KD_WAVES + wave] - ebase +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+            }
+        }
+        __syncthreads();
+        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+            u32x4 wv[UF];
+            float av[UF][TT];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const int row = e < n ? list[e] : 0;
+                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)row * D + col)
+                                          : u32x4{0u, 0u, 0u, 0u};
+                // TT <= 16 <= tp, and padded token slots of a_rm hold 0
+                const float* ar = a_rm + (size_t)row * tp;
+#pragma unroll
+                for (int t = 0; t < TT; t += 2) {
+                    const float2 v2 = e < n ? *reinterpret_cast<const float2*>(ar + t)
+                                            : make_float2(0.0f, 0.0f);
+                    av[u][t] = v2.x;
+                    av[u][t + 1] = v2.y;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) {
+                    const float w = Elem<uint16_t>::get(wv[u], k);
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) acc[t][k] = fmaf(av[u][t], w, acc[t][k]);
+                }
+        }
+        __syncthreads();
+        p0 = p1;
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            float v = acc[t][k];
+            for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+            acc[t][k] = v;
+        }
+        if (grp == 0) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[t][k];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+            float s2 = 0.0f;
+            for (int w2 = 0; w2 < KD_WAVES; ++w2) s2 += red[w2][c];
+            if (col0 + c < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + col0 + c, s2);
+                else
+                    y[(size_t)t * D + col0 + c] = s2;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Ascending live lists from the live flags: one block per token.
 __global__ __launch_bounds__(1024) void k_live_list(const uint8_t* __restrict__ live, int H,
                                                     int32_t* __restrict__ count,
