@@ -1257,7 +1257,6 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
     const int u0 = blockIdx.x * 16;
     const int S = (D + 31) / 32;
     const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
-    const int kq = 8 * (lane >> 4);
     const int r16 = lane & 15;
 
     if (y_zero) {
