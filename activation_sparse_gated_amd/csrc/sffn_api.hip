@@ -65,7 +65,9 @@ struct sffn_handle {
     float* part_buf = nullptr; // [f_blocks x D] partial outputs
     // batched bf16 path on MFMA (union of live sets, dense)
     int m_tp = 0;                  // padded token count (16 * token tiles) the buffers hold
-    int m_splits = 4;              // row splits of the MFMA down pass
+    int m_splits = 16;             // row splits of the MFMA down pass
+    int m_ut1 = 1, m_ut2 = 2, m_ut4 = 2;  // unit tiles per gate block for <=16, <=32, <=64 tokens
+    void* m_zero = nullptr;        // 4 KB of zeros (source of the staged pieces outside the operands)
     int tb_splits = 16;            // row splits of the small-batch down pass
     int tb_max = 8;                // batches up to this size use the small-batch down pass
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
@@ -363,47 +365,45 @@ sffn_status run_dense_t1(sffn_handle* h, const void* x, const void* W1, const vo
 
 // ---- batched bf16 path on MFMA
 bool mfma_ok(const sffn_handle* h, int T) {
-    return T >= 2 && h->dtype == SFFN_BF16 && h->m_a != nullptr && h->D <= 4096 &&
-           T <= h->m_tp;
+    return T >= 2 && h->dtype == SFFN_BF16 && h->m_a != nullptr && T <= h->max_tokens;
 }
 
 #define SFFN_NT_SWITCH(NTV, BODY)                         \
     switch (NTV) {                                        \
         case 1: { constexpr int NT = 1; BODY; } break;    \
         case 2: { constexpr int NT = 2; BODY; } break;    \
-        case 3: { constexpr int NT = 3; BODY; } break;    \
         case 4: { constexpr int NT = 4; BODY; } break;    \
         default: return fail(h, SFFN_INTERNAL, "bad token tile count"); \
     }
-#define SFFN_KS_SWITCH(KSV, BODY)                         \
-    switch (KSV) {                                        \
-        case 2: { constexpr int KS = 2; BODY; } break;    \
-        case 4: { constexpr int KS = 4; BODY; } break;    \
-        case 8: { constexpr int KS = 8; BODY; } break;    \
-        case 16: { constexpr int KS = 16; BODY; } break;  \
-        case 20: { constexpr int KS = 20; BODY; } break;  \
-        case 32: { constexpr int KS = 32; BODY; } break;  \
-        default: return fail(h, SFFN_INTERNAL, "bad K steps"); \
-    }
-constexpr int kKS[] = {2, 4, 8, 16, 20, 32};
+
+// token tiles of 16 for a batch of T tokens: 1, 2 or 4
+inline int token_tiles(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
 template <bool DENSE>
 sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* W3,
                      const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
                      hipStream_t s) {
-    const int nt = (T + 15) / 16;
-    const int steps = (h->D + 31) / 32;
-    const int ks = pick(kKS, 6, (steps + 3) / 4);
+    const int nt = token_tiles(T);
     uint8_t* live = live_count ? h->live_buf : nullptr;
     sffn_status st = SFFN_OK;
-    const int nb = (h->H + 15) / 16;
+    const int ut = nt == 4 ? h->m_ut4 : (nt == 2 ? h->m_ut2 : h->m_ut1);  // unit tiles per gate block
+    const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const bool small = T <= h->tb_max && T <= 8;
     const int splits = small ? h->tb_splits : h->m_splits;
     float* yz = splits > 1 ? y : nullptr;
-    SFFN_NT_SWITCH(nt, SFFN_KS_SWITCH(ks,
-        st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NT, KS, DENSE>, dim3(nb),
-                    dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,
-                    (const uint16_t*)W3, h->m_a, h->m_mask, live, yz, h->D, h->H, T, h->act)));
+#define SFFN_GATE_MFMA(NTV, UTV)                                                               \
+    st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NTV, UTV, DENSE>, dim3(nb),               \
+                dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
+                (const uint16_t*)W3, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, yz,   \
+                h->D, h->H, T, h->act)
+    if (nt == 1) {
+        if (ut == 4) { SFFN_GATE_MFMA(1, 4); } else if (ut == 2) { SFFN_GATE_MFMA(1, 2); } else { SFFN_GATE_MFMA(1, 1); }
+    } else if (nt == 2) {
+        if (ut == 4) { SFFN_GATE_MFMA(2, 4); } else if (ut == 2) { SFFN_GATE_MFMA(2, 2); } else { SFFN_GATE_MFMA(2, 1); }
+    } else {
+        if (ut == 4) { SFFN_GATE_MFMA(4, 4); } else if (ut == 2) { SFFN_GATE_MFMA(4, 2); } else { SFFN_GATE_MFMA(4, 1); }
+    }
+#undef SFFN_GATE_MFMA
     if (st != SFFN_OK) return st;
     if (small) {
         // 512-byte row slices (32 lanes x 16 B), XCD-contiguous slice order
@@ -422,7 +422,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
         if (tt == 2) { SFFN_TB_LAUNCH(2); } else if (tt == 4) { SFFN_TB_LAUNCH(4); } else { SFFN_TB_LAUNCH(8); }
 #undef SFFN_TB_LAUNCH
     } else {
-        const int ntile = (h->D + 63) / 64;
+        const int ntile = (h->D + KDM_NB - 1) / KDM_NB;
         SFFN_NT_SWITCH(nt,
             st = launch(h, KIND_DOWN_MFMA, k_down_mfma<NT>, dim3(ntile, splits),
                         dim3(KDM_THREADS), s, (const float*)h->m_a, (const uint64_t*)h->m_mask,
@@ -668,10 +668,17 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             h->t1_fused = 0;
         }
         // batched MFMA plan: unit-major products for up to 16*ceil(max_tokens/16) tokens
-        if (dtype == SFFN_BF16 && D <= 4096 && max_tokens >= 2) {
-            h->m_tp = 16 * ((max_tokens + 15) / 16);
-            int sp = env_int("SFFN_MFMA_SPLITS", 4);
-            if (sp < 1) sp = 4;
+        if (dtype == SFFN_BF16 && max_tokens >= 2) {
+            h->m_tp = 16 * token_tiles(max_tokens);
+            auto ut_env = [](const char* name, int dflt) {
+                const int v = env_int(name, dflt);
+                return (v == 1 || v == 2 || v == 4) ? v : dflt;
+            };
+            h->m_ut1 = ut_env("SFFN_MFMA_UT1", 1);
+            h->m_ut2 = ut_env("SFFN_MFMA_UT2", 2);
+            h->m_ut4 = ut_env("SFFN_MFMA_UT4", 2);
+            int sp = env_int("SFFN_MFMA_SPLITS", 16);
+            if (sp < 1) sp = 16;
             while ((H + sp - 1) / sp > KDM_LCAP) ++sp;
             h->m_splits = sp;
             const int tbs = env_int("SFFN_TB_SPLITS", 16);
@@ -681,6 +688,9 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;
             e = hipMalloc(&h->m_a, (size_t)H * h->m_tp * sizeof(float));
             if (e == hipSuccess) e = hipMalloc(&h->m_mask, (size_t)H * sizeof(uint64_t));
+            if (e == hipSuccess) e = hipMalloc(&h->m_zero, 4096);
+            if (e == hipSuccess) e = hipMemset(h->m_zero, 0, 4096);
+            if (e == hipSuccess) e = hipDeviceSynchronize();
             if (e != hipSuccess) {
                 sffn_destroy(h);
                 return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
@@ -706,6 +716,7 @@ void sffn_destroy(sffn_handle* h) {
     if (h->part_buf) (void)hipFree(h->part_buf);
     if (h->m_a) (void)hipFree(h->m_a);
     if (h->m_mask) (void)hipFree(h->m_mask);
+    if (h->m_zero) (void)hipFree(h->m_zero);
 
     delete h;
 }
@@ -743,6 +754,17 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
         if (T == 0) return SFFN_OK;
         if (t1_ok(h, T)) return run_sparse_t1(h, x, W1, W3, W2T, y, live_count, live_idx, s);
+        if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1)) {
+            // per-token lists: every token runs the whole batch-1 pass on its own live set
+            const size_t xb = (size_t)h->D * sizeof(uint16_t);
+            for (int t = 0; t < T; ++t) {
+                st = run_sparse_t1(h, (const char*)x + t * xb, W1, W3, W2T, y + (size_t)t * h->D,
+                                   live_count ? live_count + t : nullptr,
+                                   live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
+                if (st != SFFN_OK) return st;
+            }
+            return SFFN_OK;
+        }
         if (mode == SFFN_MODE_UNION && mfma_ok(h, T))
             return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
         return h->dtype == SFFN_BF16
@@ -769,6 +791,16 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
         if (T == 0) return SFFN_OK;
         if (t1_ok(h, T) && h->r <= 4 * WAVE * 8)
             return run_lopa_t1(h, x, V, U, W3, W2T, y, live_count, live_idx, s);
+        if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1) && h->r <= 4 * WAVE * 8) {
+            const size_t xb = (size_t)h->D * sizeof(uint16_t);
+            for (int t = 0; t < T; ++t) {
+                st = run_lopa_t1(h, (const char*)x + t * xb, V, U, W3, W2T, y + (size_t)t * h->D,
+                                 live_count ? live_count + t : nullptr,
+                                 live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
+                if (st != SFFN_OK) return st;
+            }
+            return SFFN_OK;
+        }
         return h->dtype == SFFN_BF16
                    ? run_lopa<uint16_t>(h, x, V, U, W3, W2T, y, T, mode, live_count, live_idx, s)
                    : run_lopa<float>(h, x, V, U, W3, W2T, y, T, mode, live_count, live_idx, s);

@@ -1152,136 +1152,212 @@ __device__ inline uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// acc[nt] = W[16 rows, steps s0..s1) x X^T[tokens nt*16 .. +16] over 32-column
-// MFMA steps. The weight rows are streamed from HBM with coalesced loads (a
-// wave-load covers 4 rows x 256 contiguous bytes), all issued up front, and
-// pass through a per-wave LDS tile (rows padded to 17 x 16 B, so both the
-// stores and the MFMA fragment reads are conflict-free). The token operand
-// runs PF steps ahead in a register ring. rows[r] is the matrix row of tile
-// row r (< 0: a zero row).
-constexpr int LA_STRIDE = 17;  // 16-byte units per staged row (16 + 1 pad)
-template <int NT, int KS>
-__device__ inline void mfma_rows_x_tokens(f32x4 (&acc)[NT], const uint16_t* __restrict__ W,
-                                          const int* rows, u32x4* la,
-                                          const uint16_t* __restrict__ x, int D, int T, int s0,
-                                          int s1, int lane) {
-    constexpr int PFW = NT >= 3 ? 2 : 4;  // token-operand ring depth
-    constexpr int PF = KS < PFW ? KS : PFW;
-    constexpr int NCH = (KS + 3) / 4;     // chunks of 4 steps (128 columns)
-    const int kq = 8 * (lane >> 4);
-    const int r16 = lane & 15;
-    // weight chunks: chunk c, wave-load j covers tile rows 4j .. 4j+3, 16 B units l%16
-    u32x4 w[NCH][4];
-#pragma unroll
-    for (int c = 0; c < NCH; ++c)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 4 * j + (lane >> 4);
-            const int u = lane & 15;
-            const int step = s0 + 4 * c + (u >> 2);
-            const int col = (s0 + 4 * c) * 32 + u * 8;
-            const int row = rows[r];
-            w[c][j] = (row >= 0 && step < s1 && col < D) ? load_stream(W + (size_t)row * D + col)
-                                                        : u32x4{0u, 0u, 0u, 0u};
-        }
-    u32x4 b[PF][NT];
-#pragma unroll
-    for (int i = 0; i < PF; ++i) {
-        const int col = (s0 + i) * 32 + kq;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            const int t = nt * 16 + r16;
-            b[i][nt] = (s0 + i < s1 && t < T && col < D) ? load_cached(x + (size_t)t * D + col)
-                                                        : u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) la[(4 * j + (lane >> 4)) * LA_STRIDE + (lane & 15)] = w[c][j];
-        __builtin_amdgcn_wave_barrier();
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int i = 4 * c + ii;
-            if (i < KS) {
-                const u32x4 af = la[r16 * LA_STRIDE + ii * 4 + (lane >> 4)];
-                if (s0 + i < s1) {
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_bf16(af, b[i % PF][nt], acc[nt]);
-                }
-                const int ip = i + PF;
-                if (ip < KS) {
-                    const int col = (s0 + ip) * 32 + kq;
-#pragma unroll
-                    for (int nt = 0; nt < NT; ++nt) {
-                        const int t = nt * 16 + r16;
-                        b[i % PF][nt] = (s0 + ip < s1 && t < T && col < D)
-                                            ? load_cached(x + (size_t)t * D + col)
-                                            : u32x4{0u, 0u, 0u, 0u};
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
+// Stage 1: gate and up projection of UB = 16*UT units for T <= 16*NT tokens,
+// as [UB x D] x [D x TP] products on MFMA tiles (see mfma_gate_pass for the
+// staging of the operands). The (unit tile, token tile) pairs are spread over the 4 waves;
+// with fewer than 4 pairs the waves also split the chunks (K groups) and the
+// partial tiles are summed in LDS. The gate reads every W1 row of the block;
+// the up projection gathers only the W3 rows of units live for some token
+// (DENSE: all units). Writes a_rm[unit][16*NT] (unit-major; 0 for dead (unit,
+// token) pairs and padded tokens), umask[unit] (tokens for which the unit is
+// live; DENSE: all tokens), live flags [T x H] when requested, and clears y
+// (T x D) for a down pass that accumulates. `zeros`: at least 16 zero bytes.
+constexpr int KM_THREADS = 256;
+constexpr int KM_KC = 128;        // columns per chunk (4 MFMA steps of 32): 256 B per row
+
+template <int NT, int UT>
+struct GateTiles {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    static_assert(UT == 1 || UT == 2 || UT == 4, "unit tiles: 1, 2 or 4");
+    static constexpr int TP = 16 * NT;
+    static constexpr int UB = 16 * UT;
+    static constexpr int TILES = UT * NT;
+    static constexpr int KG = TILES >= 4 ? 1 : 4 / TILES;  // K groups
+    static constexpr int TPW = TILES >= 4 ? TILES / 4 : 1; // tiles per wave
+    static constexpr int ROWS = UB + TP;                   // staged rows per chunk
+    static constexpr int IPW = ROWS / 16;                  // 1 KB load instructions per wave per chunk
+    static constexpr int STAGE = ROWS * 256;               // bytes per LDS stage
+    static constexpr int NS = STAGE <= 24576 ? 4 : 3;      // LDS stages (deeper rings measured slower)
+    static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
+};
+
+// s_waitcnt with only the vector-memory count limited (expcnt, lgkmcnt left
+// free); n must be a constant after inlining, 0..31. The target builtins stay
+// in plain (non-template) functions.
+#define SFFN_VMCNT(N) __builtin_amdgcn_s_waitcnt(((N) & 15) | (7 << 4) | (15 << 8) | (((N) >> 4) << 14))
+__device__ inline void wait_vmcnt(int n) {
+    switch (n) {
+        case 0: SFFN_VMCNT(0); break;   case 1: SFFN_VMCNT(1); break;
+        case 2: SFFN_VMCNT(2); break;   case 3: SFFN_VMCNT(3); break;
+        case 4: SFFN_VMCNT(4); break;   case 5: SFFN_VMCNT(5); break;
+        case 6: SFFN_VMCNT(6); break;   case 7: SFFN_VMCNT(7); break;
+        case 8: SFFN_VMCNT(8); break;   case 9: SFFN_VMCNT(9); break;
+        case 10: SFFN_VMCNT(10); break; case 11: SFFN_VMCNT(11); break;
+        case 12: SFFN_VMCNT(12); break; case 13: SFFN_VMCNT(13); break;
+        case 14: SFFN_VMCNT(14); break; case 15: SFFN_VMCNT(15); break;
+        case 16: SFFN_VMCNT(16); break; case 18: SFFN_VMCNT(18); break;
+        case 20: SFFN_VMCNT(20); break; case 24: SFFN_VMCNT(24); break;
+        default: SFFN_VMCNT(0); break;
     }
 }
+#undef SFFN_VMCNT
 
-// Stage 1: gate and up projection of 16 units for T <= 16*NT tokens.
-// The 4 waves split the K = D dimension into contiguous ranges of 32-column
-// MFMA steps (at most KS steps each). The gate reads every W1 row of the
-// block; the up projection gathers only the W3 rows of units live for some
-// token (DENSE: all units). Writes a_rm[unit][16*NT] (unit-major; 0 for dead
-// (unit, token) pairs and padded tokens), umask[unit] (tokens for which the
-// unit is live; DENSE: all tokens), live flags [T x H] when requested, and
-// clears y (T x D) for the down pass that accumulates.
-constexpr int KM_THREADS = 256;
-template <int NT, int KS, bool DENSE>
-__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
-    const uint16_t* __restrict__ W3, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
-    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act) {
-    constexpr int TP = 16 * NT;
-    __shared__ float part[4][16][TP + 1];
-    __shared__ float zf[16][TP + 1];
-    __shared__ unsigned long long tmask[16];
-    __shared__ int ulist[16];
-    __shared__ int upos[16];
-    __shared__ int nu_s;
-    __shared__ int rows_g[16];
-    __shared__ int rows_u[16];
-    __shared__ u32x4 la_all[4][16 * LA_STRIDE];
+// One 16-byte piece per lane from global memory straight into LDS at
+// lds + 16 * lane (the LDS address must be the same in every lane). Issued
+// as inline assembly so that the compiler does not treat every later LDS read
+// as waiting on it: the caller orders the pieces with wait_vmcnt. The
+// compiler's own vmcnt waits stay correct (they can only wait longer), since
+// vector-memory loads return in issue order.
+// (m0 holds no compiler value across this code: it is written here and read
+// only by the load that follows it in the same statement.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ inline void load_lds16(const void* g, void* lds) {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr)lds);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m0) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// acc[i] (tiles of this wave) = rows[] of W x tokens of x, over all of D.
+// Chunks of 128 columns of the UB weight rows and the TP token rows are
+// loaded straight into an NS-stage LDS ring (global_load_lds, 16 B per lane:
+// one wave instruction fills 4 rows of 256 B). In row r, LDS slot j holds the
+// row's 16-byte piece j ^ (r % 16), so the fragment reads of 16 rows at one
+// column hit 16 different slots (conflict-free without padding). Pieces
+// outside the operands are read from `zeros`. Every chunk issues the same
+// number of loads (also past the last chunk), so a fixed vmcnt wait marks a
+// chunk as landed; one barrier per chunk.
+template <int NT, int UT>
+__device__ inline void mfma_gate_pass(f32x4* acc, const uint16_t* __restrict__ W,
+                                      const int* rows, const uint16_t* __restrict__ x,
+                                      const uint16_t* __restrict__ zeros, int D, int T,
+                                      uint8_t* ring) {
+    using G = GateTiles<NT, UT>;
+    constexpr int NS = G::NS, IPW = G::IPW;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int u0 = blockIdx.x * 16;
-    const int S = (D + 31) / 32;
-    const int s0 = wave * S / 4, s1 = (wave + 1) * S / 4;
+    const int r16 = lane & 15, pq = lane >> 4;
+    const int kgroup = G::TILES >= 4 ? 0 : wave / G::TILES;
+    const int nchunks = (D + KM_KC - 1) / KM_KC;
+#pragma unroll
+    for (int i = 0; i < G::TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // the source row of each of this lane's pieces is the same for every chunk
+    const uint16_t* src[IPW];
+    bool rok[IPW];
+    int pcol[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int r = 4 * (wave * IPW + i) + pq;  // staged row
+        const int p = (lane & 15) ^ (r & 15);     // piece of the row this lane fetches
+        pcol[i] = 8 * p;
+        if (r < G::UB) {
+            const int row = rows[r];
+            rok[i] = row >= 0;
+            src[i] = W + (rok[i] ? (size_t)row * D + 8 * p : 0);
+        } else {
+            rok[i] = r - G::UB < T;
+            src[i] = x + (rok[i] ? (size_t)(r - G::UB) * D + 8 * p : 0);
+        }
+    }
+    auto issue = [&](int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const bool ok = rok[i] && c * KM_KC + pcol[i] < D;
+            const uint16_t* g = ok ? src[i] + (size_t)c * KM_KC : zeros;
+            load_lds16(g, ring + stage * G::STAGE + 1024 * (wave * IPW + i));
+        }
+    };
+    auto compute = [&](int stage) {
+        const uint8_t* wt = ring + stage * G::STAGE;
+        const uint8_t* xt = wt + G::UB * 256;
+#pragma unroll
+        for (int ks = 0; ks < KM_KC / 32; ++ks) {
+            const int slot = (4 * ks + pq) ^ r16;
+#pragma unroll
+            for (int i = 0; i < G::TPW; ++i) {
+                const int tile = G::TILES >= 4 ? wave * G::TPW + i : wave % G::TILES;
+                const int ut = tile / NT, nt = tile % NT;
+                const u32x4 af = *reinterpret_cast<const u32x4*>(wt + (ut * 16 + r16) * 256 + 16 * slot);
+                const u32x4 bf = *reinterpret_cast<const u32x4*>(xt + (nt * 16 + r16) * 256 + 16 * slot);
+                acc[i] = mfma_bf16(af, bf, acc[i]);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + NS - 1) / NS * NS;
+    for (int c0 = 0; c0 < niter; c0 += NS) {
+#pragma unroll
+        for (int d = 0; d < NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((NS - 2) * IPW);  // this wave's pieces of chunk c have landed
+            __syncthreads();                // ... and every wave's; chunk c - 1 is consumed
+            issue((d + NS - 1) % NS, c + NS - 1);
+            if (c < nchunks && c % G::KG == kgroup) compute(d);
+        }
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+}
+
+template <int NT, int UT, bool DENSE>
+__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, const uint16_t* __restrict__ zeros, float* __restrict__ a_rm,
+    uint64_t* __restrict__ umask, uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D,
+    int H, int T, int act) {
+    using G = GateTiles<NT, UT>;
+    constexpr int TP = G::TP, UB = G::UB;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
+    __shared__ float part[G::KG][UB][TP + 1];
+    __shared__ float zf[UB][TP + 1];
+    __shared__ unsigned long long tmask[UB];
+    __shared__ int rows_g[UB];
+    __shared__ int rows_u[UB];
+    __shared__ int upos[UB];
+    __shared__ int nu_s;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
     const int r16 = lane & 15;
+    const int u0 = blockIdx.x * UB;
+    const int kgroup = G::TILES >= 4 ? 0 : wave / G::TILES;
 
     if (y_zero) {
         for (int j = blockIdx.x * KM_THREADS + threadIdx.x; j < T * D; j += gridDim.x * KM_THREADS)
             y_zero[j] = 0.0f;
     }
-    if (threadIdx.x < 16) {
+    if (threadIdx.x < UB) {
         tmask[threadIdx.x] = 0ull;
         rows_g[threadIdx.x] = (u0 + (int)threadIdx.x < H) ? u0 + (int)threadIdx.x : -1;
     }
     __syncthreads();
 
-    // ---- gate: z[16 units][TP tokens]
+    auto store_tiles = [&](const f32x4 (&acc)[G::TPW]) {
+#pragma unroll
+        for (int i = 0; i < G::TPW; ++i) {
+            const int tile = G::TILES >= 4 ? wave * G::TPW + i : wave % G::TILES;
+            const int ut = tile / NT, nt = tile % NT;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part[kgroup][ut * 16 + 4 * (lane >> 4) + j][nt * 16 + r16] = acc[i][j];
+        }
+    };
+
+    // ---- gate: z[UB units][TP tokens]
     {
-        f32x4 acc[NT];
-        mfma_rows_x_tokens<NT, KS>(acc, W1, rows_g, la_all[wave], x, D, T, s0, s1, lane);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) part[wave][4 * (lane >> 4) + j][nt * 16 + r16] = acc[nt][j];
+        f32x4 acc[G::TPW];
+        mfma_gate_pass<NT, UT>(acc, W1, rows_g, x, zeros, D, T, ring);
+        store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 16 * TP; e += KM_THREADS) {
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
         const int i = e / TP, t = e % TP;
-        const float z = part[0][i][t] + part[1][i][t] + part[2][i][t] + part[3][i][t];
+        float z = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G::KG; ++g) z += part[g][i][t];
         zf[i][t] = z;
         const bool ok = (u0 + i < H) && t < T;
         const bool live = ok && (DENSE || z > 0.0f);
@@ -1290,38 +1366,39 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
     }
     __syncthreads();
     if (wave == 0) {
-        const bool any = lane < 16 && tmask[lane] != 0ull;
+        // compaction of the units live for some token (UB <= 64 = one wave)
+        const bool any = lane < UB && tmask[lane] != 0ull;
         const uint64_t m = __ballot(any);
         const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
                                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (any) ulist[pos] = lane;
-        if (lane < 16) upos[lane] = any ? pos : -1;
-        if (lane < 16) rows_u[lane] = -1;
+        if (lane < UB) {
+            upos[lane] = any ? pos : -1;
+            rows_u[lane] = -1;
+            if (u0 + lane < H) umask[u0 + lane] = tmask[lane];
+        }
         if (lane == 0) nu_s = __popcll(m);
-        if (lane < 16 && u0 + lane < H) umask[u0 + lane] = tmask[lane];
     }
     __syncthreads();
+    if (threadIdx.x < UB && upos[threadIdx.x] >= 0) rows_u[upos[threadIdx.x]] = u0 + threadIdx.x;
     const int nu = nu_s;
-    if (threadIdx.x < 16 && (int)threadIdx.x < nu) rows_u[threadIdx.x] = u0 + ulist[threadIdx.x];
     __syncthreads();
 
     // ---- up projection over the gathered live units: u[p][token], p < nu
     if (nu > 0) {
-        f32x4 acc[NT];
-        mfma_rows_x_tokens<NT, KS>(acc, W3, rows_u, la_all[wave], x, D, T, s0, s1, lane);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) part[wave][4 * (lane >> 4) + j][nt * 16 + r16] = acc[nt][j];
+        f32x4 acc[G::TPW];
+        mfma_gate_pass<NT, UT>(acc, W3, rows_u, x, zeros, D, T, ring);
+        store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < 16 * TP; e += KM_THREADS) {
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
         const int i = e / TP, t = e % TP;
         if (u0 + i >= H) continue;
         const int p = upos[i];
         float av = 0.0f;
         if (p >= 0 && t < T && ((tmask[i] >> t) & 1ull)) {
-            const float u = part[0][p][t] + part[1][p][t] + part[2][p][t] + part[3][p][t];
+            float u = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G::KG; ++g) u += part[g][p][t];
             av = activation(act, zf[i][t]) * u;
         }
         a_rm[(size_t)(u0 + i) * TP + t] = av;
@@ -1330,39 +1407,47 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
 
 // Stage 2: y[T x D] += sum over units of a_rm[unit][t] * W2T[unit][:], over the
 // units live for some token (y is cleared by stage 1). Grid: (column tiles of
-// 64, row splits). Each of the 4 waves takes its own 32-unit chunks of the
-// block's compacted unit list: it stages the chunk's W2T tile [32 x 64]
-// transposed in LDS and its unit products [TP x 32] in LDS, then runs MFMAs
-// with the products split into bf16 hi + lo parts (two MFMAs, close to fp32
-// accuracy). The global loads of the next two chunks are in flight while a
-// chunk is staged and multiplied. The waves' tiles are summed in LDS and each
-// block adds its tile to y with fp32 atomics (one add per split per output).
+// 128, row splits). The block compacts its split's units, then runs through them
+// in chunks of 64: the chunk's W2T rows are staged in LDS transposed
+// ([column][unit], two units packed per 32-bit write, rows padded to 144 B) and
+// its unit products as [unit][token]; the global loads of the next 3..6
+// chunks are in flight in registers. Each wave owns 2*NT of the block's NT x 8
+// output tiles (one token tile); the products are split into bf16 hi + lo
+// parts (two MFMAs, about 16 significant bits). Each wave adds its tiles to y
+// with fp32 atomics (one add per split per output), or stores them when there
+// is one split.
 constexpr int KDM_THREADS = 256;
 constexpr int KDM_LCAP = 2048;
+constexpr int KDM_KC = 64;         // units per chunk
+constexpr int KDM_NB = 128;        // columns per block
+constexpr int KDM_RS = KDM_KC + 8; // LDS row stride of the transposed W2T chunk (bf16)
 template <int NT>
 __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
     const float* __restrict__ a_rm, const uint64_t* __restrict__ umask,
     const uint16_t* __restrict__ W2T, float* __restrict__ y, int D, int H, int T, int splits) {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
     constexpr int TP = 16 * NT;
-    constexpr int CWT = 64;  // columns per block
+    constexpr int AS = TP + 4;              // LDS row stride of the product chunk (floats)
+    constexpr int APT = KDM_KC * TP / 4 / KDM_THREADS;  // float4 product pieces per thread
+    constexpr int WPT = 2;                              // (unit pair, 8 columns) pieces per thread
+    constexpr int NCW = 2 * NT;                         // column tiles per wave
+    constexpr int KDM_DEPTH = APT == 1 ? 6 : (APT == 2 ? 4 : 3);
     __shared__ int list[KDM_LCAP];
     __shared__ int wcnt[KDM_THREADS / WAVE];
     __shared__ int nlist_s;
-    __shared__ __attribute__((aligned(16))) uint16_t bt[4][CWT][32 + 8];  // W2T chunk, [col][unit]
-    __shared__ float at[4][TP][32 + 1];                                     // products, [token][unit]
-    __shared__ float ysum[TP][CWT + 1];
+    __shared__ __attribute__((aligned(16))) uint16_t bt[2][KDM_NB][KDM_RS];
+    __shared__ __attribute__((aligned(16))) float at[2][KDM_KC][AS];
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int r16 = lane & 15;
     const int kq = 8 * (lane >> 4);
-    const int col0 = blockIdx.x * CWT;
+    const int col0 = blockIdx.x * KDM_NB;
     const int hs = (H + splits - 1) / splits;
     const int h0 = blockIdx.y * hs;
     const int h1 = min(H, h0 + hs);
 
     // compaction of the units live for some token, ascending within the block
     if (threadIdx.x == 0) nlist_s = 0;
-    for (int e = threadIdx.x; e < TP * (CWT + 1); e += KDM_THREADS) (&ysum[0][0])[e] = 0.0f;
     __syncthreads();
     for (int base = h0; base < h1; base += KDM_THREADS) {
         const int row = base + threadIdx.x;
@@ -1382,112 +1467,132 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
         __syncthreads();
     }
     const int n = nlist_s;
+    const int nchunks = (n + KDM_KC - 1) / KDM_KC;
 
-    f32x4 acc[NT][4];
+    // this wave's output tiles: token tile tt, column tiles cb .. cb + NCW - 1
+    const int tt = wave / (4 / NT);
+    const int cb = (wave % (4 / NT)) * NCW;
+    f32x4 acc[NCW];
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[nt][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < NCW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    constexpr int AV = TP / 8;  // float4 loads of unit products per lane per chunk
-    constexpr int DEPTH = 3;    // chunks whose global loads are in flight
-    u32x4 wv[DEPTH][4];
-    float4 avv[DEPTH][AV];
-    auto fetch = [&](int slot, int c0) {
+    // W2T pieces: piece g = tid + 256 k -> unit pair g / 16, 8 columns at 8 * (g % 16)
+    u32x4 wv[KDM_DEPTH][WPT][2];
+    float4 av[KDM_DEPTH][APT];
+    // unconditional loads (pieces past the list read row 0 and become zeros), so the
+    // number of loads in flight is the same on every path
+    // (zeros are applied when the chunk is staged, not at the load)
+    bool wok[KDM_DEPTH][WPT][2], aok[KDM_DEPTH][APT];
+    auto fetch = [&](int slot, int c) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = c0 + q * 8 + (lane >> 3);
-            const int cc = (lane & 7) * 8;
-            wv[slot][q] = (e < n && col0 + cc < D)
-                              ? load_stream(W2T + (size_t)list[e] * D + col0 + cc)
-                              : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int k = 0; k < WPT; ++k) {
+            const int g = threadIdx.x + k * KDM_THREADS;
+            const int up = g >> 4, col = col0 + 8 * (g & 15);
 #pragma unroll
-        for (int v = 0; v < AV; ++v) {
-            const int idx = v * WAVE + lane;
-            const int uu = idx / (TP / 4), t4 = (idx % (TP / 4)) * 4;
-            const int e = c0 + uu;
-            avv[slot][v] = e < n ? *reinterpret_cast<const float4*>(a_rm + (size_t)list[e] * TP + t4)
-                                 : make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-    };
-    const int cstep = 4 * 32;  // this wave's chunks are wave*32 + j*cstep
-    const int nch = (n > wave * 32) ? (n - wave * 32 + cstep - 1) / cstep : 0;
-#pragma unroll
-    for (int d = 0; d < DEPTH - 1; ++d)
-        if (d < nch) fetch(d, wave * 32 + d * cstep);
-    for (int j0 = 0; j0 < nch; j0 += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            const int j = j0 + d;
-            if (j < nch) {
-                const int jn = j + DEPTH - 1;
-                if (jn < nch) fetch((d + DEPTH - 1) % DEPTH, wave * 32 + jn * cstep);
-                // stage chunk j: W2T transposed [col][unit], products [token][unit]
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int uu = q * 8 + (lane >> 3);
-                    const int cc = (lane & 7) * 8;
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const uint32_t w32 = wv[d][q][k >> 1];
-                        bt[wave][cc + k][uu] = (uint16_t)((k & 1) ? (w32 >> 16) : (w32 & 0xffffu));
-                    }
-                }
-#pragma unroll
-                for (int v = 0; v < AV; ++v) {
-                    const int idx = v * WAVE + lane;
-                    const int uu = idx / (TP / 4), t4 = (idx % (TP / 4)) * 4;
-                    at[wave][t4 + 0][uu] = avv[d][v].x;
-                    at[wave][t4 + 1][uu] = avv[d][v].y;
-                    at[wave][t4 + 2][uu] = avv[d][v].z;
-                    at[wave][t4 + 3][uu] = avv[d][v].w;
-                }
-                __builtin_amdgcn_wave_barrier();
-                u32x4 b[4];
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-                    b[ct] = *reinterpret_cast<const u32x4*>(&bt[wave][ct * 16 + r16][kq]);
-#pragma unroll
-                for (int nt = 0; nt < NT; ++nt) {
-                    const float* srcA = &at[wave][nt * 16 + r16][kq];
-                    uint32_t hi[8], lo[8];
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const float f = srcA[k];
-                        hi[k] = bf16_rne(f);
-                        lo[k] = bf16_rne(f - __uint_as_float(hi[k] << 16));
-                    }
-                    const u32x4 ahi = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                            hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-                    const u32x4 alo = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                            lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct) {
-                        acc[nt][ct] = mfma_bf16(ahi, b[ct], acc[nt][ct]);
-                        acc[nt][ct] = mfma_bf16(alo, b[ct], acc[nt][ct]);
-                    }
-                }
-                __builtin_amdgcn_wave_barrier();
+            for (int h = 0; h < 2; ++h) {
+                const int e = c * KDM_KC + 2 * up + h;
+                const bool ok = e < n && col < D;
+                wv[slot][k][h] = load_stream(W2T + (ok ? (size_t)list[e] * D + col : 0));
+                wok[slot][k][h] = ok;
             }
         }
-    }
-    // sum the 4 waves' tiles in LDS, then add the block's tile to y
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+        for (int q = 0; q < APT; ++q) {
+            const int idx = threadIdx.x + q * KDM_THREADS;
+            const int e = c * KDM_KC + idx / (TP / 4);
+            const bool ok = e < n;
+            av[slot][q] = *reinterpret_cast<const float4*>(
+                a_rm + (ok ? (size_t)list[e] * TP + 4 * (idx % (TP / 4)) : 0));
+            aok[slot][q] = ok;
+        }
+    };
+    auto stage_write = [&](int stage, int d) {
+        // W2T transposed, two units per 32-bit word. Write j of a lane goes to its
+        // column (j + cs) % 8, so that the lanes of one write instruction spread
+        // over the banks (rows 8 apart share banks).
+        const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int kk = 0; kk < WPT; ++kk) {
+            const int g = threadIdx.x + kk * KDM_THREADS;
+            const int up = g >> 4, cs = g & 15;
+            const u32x4 wa = wok[d][kk][0] ? wv[d][kk][0] : z4;
+            const u32x4 wb = wok[d][kk][1] ? wv[d][kk][1] : z4;
+            uint32_t pk[8];
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                atomicAdd(&ysum[nt * 16 + 4 * (lane >> 4) + j][ct * 16 + r16], acc[nt][ct][j]);
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t w0 = wa[k >> 1], w1 = wb[k >> 1];
+                pk[k] = (k & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = (j + cs) & 7;
+                uint32_t v = pk[0];
+#pragma unroll
+                for (int m = 1; m < 8; ++m) v = k == m ? pk[m] : v;
+                *reinterpret_cast<uint32_t*>(&bt[stage][8 * cs + k][2 * up]) = v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < APT; ++q) {
+            const int idx = threadIdx.x + q * KDM_THREADS;
+            *reinterpret_cast<float4*>(&at[stage][idx / (TP / 4)][4 * (idx % (TP / 4))]) =
+                aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    };
+    auto compute = [&](int stage) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const int m = tt * 16 + r16;
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const float f = at[stage][ks * 32 + kq + k][m];
+                hi[k] = bf16_rne(f);
+                lo[k] = bf16_rne(f - __uint_as_float(hi[k] << 16));
+            }
+            const u32x4 ahi = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
+                                    hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
+            const u32x4 alo = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
+                                    lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+#pragma unroll
+            for (int i = 0; i < NCW; ++i) {
+                const u32x4 b = *reinterpret_cast<const u32x4*>(&bt[stage][(cb + i) * 16 + r16][ks * 32 + kq]);
+                acc[i] = mfma_bf16(ahi, b, acc[i]);
+                acc[i] = mfma_bf16(alo, b, acc[i]);
+            }
+        }
+    };
+    // chunk c + 1 is staged into the other buffer while chunk c is multiplied
+#pragma unroll
+    for (int d = 0; d < KDM_DEPTH; ++d) fetch(d, d);
+    stage_write(0, 0);
     __syncthreads();
-    for (int e = threadIdx.x; e < T * CWT; e += KDM_THREADS) {
-        const int t = e / CWT, c = e % CWT;
-        if (col0 + c < D) {
-            if (splits > 1)
-                atomicAdd(y + (size_t)t * D + col0 + c, ysum[t][c]);
-            else
-                y[(size_t)t * D + col0 + c] = ysum[t][c];
+    fetch(0, KDM_DEPTH);
+    const int niter = (nchunks + KDM_DEPTH - 1) / KDM_DEPTH * KDM_DEPTH;
+    for (int c0 = 0; c0 < niter; c0 += KDM_DEPTH) {
+#pragma unroll
+        for (int d = 0; d < KDM_DEPTH; ++d) {
+            const int c = c0 + d;
+            const int nslot = (d + 1) % KDM_DEPTH;  // holds chunk c + 1
+            stage_write((c + 1) & 1, nslot);
+            if (c < nchunks) compute(c & 1);
+            __syncthreads();
+            fetch(nslot, c + 1 + KDM_DEPTH);
+        }
+    }
+    // C layout: row (token) 4*(lane/16) + j of the token tile, column r16 of the column tile
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+        const int col = col0 + (cb + i) * 16 + r16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = tt * 16 + 4 * (lane >> 4) + j;
+            if (t < T && col < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + col, acc[i][j]);
+                else
+                    y[(size_t)t * D + col] = acc[i][j];
+            }
         }
     }
 }
