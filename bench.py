@@ -108,6 +108,23 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command
 
 
 
+def summarize_counters(db_dir: str, out: str, command: str) -> None:
+    """Per-kernel averages of every counter in a rocprofv3 --pmc run, as markdown."""
+    q = ("select kernel_name, counter_name, avg(value), count(*) from counters_collection "
+         "group by kernel_name, counter_name order by kernel_name, counter_name")
+    rows = _rocpd_rows(db_dir, q)
+    lines = [f"# rocprofv3 counters: {os.path.basename(out)}", "", "Command (from the repo root):",
+             "", "```", command, "```", "", "| kernel | counter | mean per dispatch | dispatches |",
+             "|---|---|---|---|"]
+    for name, cn, v, c in rows:
+        short = name.split("(")[0].replace("void ", "")
+        if not short.startswith("sffn::"):
+            continue
+        lines.append(f"| `{short}` | {cn} | {v:,.1f} | {c} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def _graph_time(torch, fn, steps, warmup):
     """Capture fn once into a HIP graph; ms per replay."""
     g = torch.cuda.CUDAGraph()
@@ -135,13 +152,18 @@ def bench_batched(torch, sffn, gen, to_dev, x1, reps, D, H, act, args):
     R = len(reps)
     out = {}
     xb = to_dev(gen.tokens(D, 64 * 64, cfg=4, dtype="bf16"))
-    for T in (1, 4, 16, 64):
+    sizes = [int(v) for v in args.batched_sizes.split(",") if v]
+    modes = [v for v in args.batched_modes.split(",") if v]
+    for T in sizes:
         h = sffn.Handle(D, H, 0, T, act, sffn.SFFN_BF16)
         y = torch.zeros(64 * T, D, dtype=torch.float32, device="cuda")
         calls = 64
         res = {}
         for name, mode in (("per_token", sffn.SFFN_MODE_PER_TOKEN), ("union", sffn.SFFN_MODE_UNION),
                            ("dense", None)):
+            if name not in modes:
+                continue
+
             def fn():
                 for c in range(calls):
                     rp = reps[c % R]
@@ -153,7 +175,8 @@ def bench_batched(torch, sffn, gen, to_dev, x1, reps, D, H, act, args):
                                                  mode)
             ms = _graph_time(torch, fn, max(2, args.steps // 4), 1)
             res[name + "_tokens_per_s"] = round(calls * T / (ms * 1e-3), 1)
-        res["union_vs_dense"] = round(res["union_tokens_per_s"] / res["dense_tokens_per_s"], 3)
+        if "union_tokens_per_s" in res and "dense_tokens_per_s" in res:
+            res["union_vs_dense"] = round(res["union_tokens_per_s"] / res["dense_tokens_per_s"], 3)
         out[f"T{T}"] = res
         log(f"batched T={T}: " + ", ".join(f"{k} {v:,}" for k, v in res.items()))
         h.close()
@@ -200,6 +223,9 @@ def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4])
         return 0
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize-counters":
+        summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4])
+        return 0
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
         summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
         return 0
@@ -214,6 +240,11 @@ def main() -> int:
                     help="wall-clock budget of the CPU oracle baseline sample")
     ap.add_argument("--no-extras", action="store_true", help="skip the dense and LoPA streams")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--only-batched", action="store_true",
+                    help="run only the batched-decode lines (for counter collection)")
+    ap.add_argument("--batched-sizes", default="1,4,16,64", help="token batch sizes T")
+    ap.add_argument("--batched-modes", default="per_token,union,dense",
+                    help="batched lines to run: per_token, union, dense")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -248,6 +279,31 @@ def main() -> int:
     cnt = torch.zeros(n, dtype=torch.int32, device="cuda")
     idx = torch.zeros(n, H, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
+
+    if args.only_batched:
+        res = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
+        print(json.dumps({"batched": res}), flush=True)
+        return 0
+
+    # ---------------------------------------------------------------- streaming-read ceiling
+    # an 8 GiB read (torch's max reduction over fp32), median of 5: the bandwidth a plain
+    # streaming read reaches on this GPU in this process
+    big = torch.ones(2 * 2**30, dtype=torch.float32, device="cuda")
+    big.amax()
+    torch.cuda.synchronize()
+    st_ms = []
+    for _ in range(5):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        big.amax()
+        e1.record()
+        torch.cuda.synchronize()
+        st_ms.append(e0.elapsed_time(e1))
+    stream_gbps = big.numel() * 4 / (sorted(st_ms)[2] * 1e-3) / 1e9
+    del big
+    torch.cuda.empty_cache()
+    log(f"streaming read ceiling: {stream_gbps:,.0f} GB/s (8 GiB, max reduction)")
 
     hs = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_BF16)
 
@@ -412,12 +468,34 @@ def main() -> int:
                              act=ref.ACT_RSPLUS)
             done += 1
         dt = time.time() - t0
+        # the same oracle on one thread, over a shorter sample
+        ref.set_threads(1)
+        done1, t1 = 0, time.time()
+        while time.time() - t1 < args.cpu_seconds / 4:
+            ref.ffn_standard(x_np[done1 % n], w_np["W1"], w_np["W3"], w_np["W2T"],
+                             act=ref.ACT_RSPLUS)
+            done1 += 1
+        dt1 = time.time() - t1
+        ref.set_threads(threads)
+        cpu_model = "unknown"
+        try:
+            with open("/proc/cpuinfo") as f:
+                for line in f:
+                    if line.startswith("model name"):
+                        cpu_model = line.split(":", 1)[1].strip()
+                        break
+        except OSError:
+            pass
         cpu = {"value": round(done / dt, 2), "unit": "tokens/s", "cores": threads,
                "kind": "oracle",
                "sample": f"{done} tokens of the {n}-token decode stream (cycled from token 0) "
                          f"through the fp64 sparse oracle: {dt:.1f} s, OpenMP over {threads} "
-                         f"threads"}
-        log(f"cpu oracle: {cpu['value']} tokens/s on {threads} threads ({done} tokens)")
+                         f"threads",
+               "one_thread_value": round(done1 / dt1, 2),
+               "one_thread_sample": f"{done1} tokens on 1 thread: {dt1:.1f} s",
+               "cpu_model": cpu_model, "os_cpu_count": os.cpu_count()}
+        log(f"cpu oracle: {cpu['value']} tokens/s on {threads} threads ({done} tokens), "
+            f"{cpu['one_thread_value']} tokens/s on 1 thread; {cpu_model}")
 
     traffic = read_traffic(dom, "decode")
     out = {
@@ -440,6 +518,8 @@ def main() -> int:
                    "replicas": R, "parallelism": "single GPU"},
         "touched_GBps": round(float(touched_gbps), 1),
         "touched_frac_of_peak": round(float(touched_gbps) / HBM_PEAK_GBPS, 4),
+        "stream_read_GBps": round(float(stream_gbps), 1),
+        "touched_frac_of_stream": round(float(touched_gbps) / stream_gbps, 4),
         "measured_sparsity": round(float(meas_sparsity), 4),
         "k_mean": round(float(k.mean()), 1),
         "k_std": round(float(k.std()), 1),
