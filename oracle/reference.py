@@ -50,6 +50,10 @@ def _load(path: str | None = None):
     lib.orc_ffn_standard.argtypes = [I, I, I, I, P, P, P, P, I, P, P, P, P]
     lib.orc_ffn_lopa.restype = I
     lib.orc_ffn_lopa.argtypes = [I, I, I, I, I, P, P, P, P, P, I, P, P, P, P, P]
+    if hasattr(lib, "orc_ffn_lopa_full"):  # older builds used by mutation tests may lack it
+        lib.orc_ffn_lopa_full.restype = I
+        lib.orc_ffn_lopa_full.argtypes = [I, I, I, I, I, ctypes.c_uint, P, P, P, P, P, I, P, P, P,
+                                          P, P, P]
     _lib = lib
     return lib
 
@@ -153,3 +157,40 @@ def ffn_lopa(x, V, U, W3, W2T, act: int = ACT_RELU, dense: bool = False):
         ks[t] = k
         live.append(idx[:k].copy())
     return {"y": y, "z": z, "t": tt, "live": live, "k": ks}
+
+
+# flags of the full LoPA gate (page "Model casting: ...", section "LoPA Gating:
+# moving the ceiling"; paper card Figure 6 and Table 4)
+LOPA_G_TILED, LOPA_RMSNORM, LOPA_DOUBLE_ACT = 1, 2, 4
+RMS_EPS = 1e-6  # not on the pages: the oracle's reading (unit gain as well)
+
+
+def ffn_lopa_full(x, V, U, W3, W2T, flags: int, act: int = ACT_RELU, dense: bool = False):
+    """Full LoPA gate z = G x + U RMSNorm(V x) with double activation, each part
+    switched by `flags`. Returns y, z, t (after the norm), live, k, and k2 (units
+    that enter the W2 pass)."""
+    lib = _load()
+    x2 = np.atleast_2d(np.ascontiguousarray(x))
+    V, U, W3, W2T = (np.ascontiguousarray(w) for w in (V, U, W3, W2T))
+    code = _dtype_code(x2, V, U, W3, W2T)
+    T, D = x2.shape
+    r = V.shape[0]
+    H = U.shape[0]
+    if V.shape != (r, D) or U.shape != (H, r) or W3.shape != (H, D) or W2T.shape != (H, D):
+        raise ValueError("LoPA shapes: V [r, D], U [H, r], W3/W2T [H, D]")
+    y = np.zeros((T, D), np.float64)
+    z = np.zeros((T, H), np.float64)
+    tt = np.zeros((T, r), np.float64)
+    idx = np.zeros(max(H, 1), np.int32)
+    k2 = np.zeros(1, np.int32)
+    live, ks, k2s = [], np.zeros(T, np.int64), np.zeros(T, np.int64)
+    for t in range(T):
+        k = lib.orc_ffn_lopa_full(D, H, r, act, code, int(flags), _ptr(x2[t]), _ptr(V), _ptr(U),
+                                  _ptr(W3), _ptr(W2T), int(bool(dense)), _ptr(y[t]), _ptr(z[t]),
+                                  _ptr(tt[t]), None, _ptr(idx), _ptr(k2))
+        if k < 0:
+            raise RuntimeError(f"oracle failed ({k})")
+        ks[t] = k
+        k2s[t] = k2[0]
+        live.append(idx[:k].copy())
+    return {"y": y, "z": z, "t": tt, "live": live, "k": ks, "k2": k2s}

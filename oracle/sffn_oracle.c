@@ -22,9 +22,15 @@
  *   x >= 0 and 0 for x < 0. ReLU is max(0, x).
  *
  *   LoPA gate (section "LoPA Gating: moving the ceiling"): the gate
- *   pre-activation is U (V x) with U in R^{H' x r}, V in R^{r x D}. The
- *   fixed G term, the RMSNorm between the factors and the double activation are
- *   not part of this gate form (the workload specifies ReLU(U(Vx))).
+ *   pre-activation is U (V x) with U in R^{H' x r}, V in R^{r x D}
+ *   (orc_ffn_lopa). The full form the paper trains (same section, and the
+ *   paper card's Figure 6 and Table 4) is orc_ffn_lopa_full:
+ *       z = G x + U RMSNorm(V x),   a_i = A(z_i) * A(u_i)  (double activation)
+ *   with G the tiled identity, (G x)_i = x_{i mod D} (Figure 6 (c)), and
+ *   RMSNorm(t) = t / sqrt(mean_m t_m^2 + eps). The pages give neither eps nor
+ *   a gain: eps = 1e-6 and unit gain are this oracle's reading. With double
+ *   activation a live unit whose A(u_i) is 0 contributes nothing, and its W2
+ *   column is skipped (the s_gated skip of the paper card's Table 5).
  *
  * Arithmetic: every input is widened exactly to double (bf16 bit patterns by a
  * 16-bit shift into an fp32, fp32 directly). Every dot product is a plain
@@ -51,6 +57,8 @@
 
 enum { ORC_BF16 = 0, ORC_F32 = 1, ORC_F64 = 2 };
 enum { ORC_RELU = 0, ORC_RSPLUS = 1 };
+enum { ORC_G_TILED = 1, ORC_RMSNORM = 2, ORC_DOUBLE_ACT = 4 };
+#define ORC_RMS_EPS 1e-6
 
 static double elem(const void *p, int dtype, size_t idx) {
     if (dtype == ORC_BF16) {
@@ -98,11 +106,14 @@ static double dot_row(const void *M, int dtype, size_t row, int n, const double 
  * Back half shared by standard and LoPA gating, given the gate
  * pre-activation z[H]: h = A(z), L = {z > 0}, u_i = W3_i . x, a_i = h_i u_i,
  * y = sum_i a_i W2T_i.  dense != 0 visits every unit, else only L.
- * Returns k = |L|; writes L (ascending) into live_idx when non-null.
+ * double_act != 0: a_i = h_i * A(u_i), and in sparse mode the units with
+ * a_i == 0 are left out of the W2 pass (their terms are exact zeros).
+ * Returns k = |L|; writes L (ascending) into live_idx when non-null, and the
+ * number of units that enter the W2 pass into *k2_out when non-null.
  */
-static int back_half(int D, int H, int act, int dtype, const double *x, const double *z,
-                     const void *W3, const void *W2T, int dense, double *y,
-                     double *a_out, int32_t *live_idx) {
+static int back_half2(int D, int H, int act, int dtype, const double *x, const double *z,
+                      const void *W3, const void *W2T, int dense, int double_act, double *y,
+                      double *a_out, int32_t *live_idx, int32_t *k2_out) {
     int k = 0;
     for (int i = 0; i < H; ++i)
         if (z[i] > 0.0) {
@@ -127,10 +138,27 @@ static int back_half(int D, int H, int act, int dtype, const double *x, const do
         int i = vis[q];
         double h = orc_activation(act, z[i]);
         double u = dot_row(W3, dtype, (size_t)i, D, x);
-        a[q] = h * u;
+        a[q] = h * (double_act ? orc_activation(act, u) : u);
     }
     if (a_out)
         for (int q = 0; q < n_vis; ++q) a_out[q] = a[q];
+    /* s_gated: with double activation, sparse mode drops the units whose a_i is 0 */
+    if (double_act && !dense) {
+        int w = 0;
+        for (int q = 0; q < n_vis; ++q)
+            if (a[q] != 0.0) {
+                vis[w] = vis[q];
+                a[w] = a[q];
+                ++w;
+            }
+        n_vis = w;
+    }
+    if (k2_out) {
+        int c = 0;
+        for (int q = 0; q < n_vis; ++q)
+            if (z[vis[q]] > 0.0 && (!double_act || a[q] != 0.0)) ++c;
+        *k2_out = c;
+    }
 
     /* y_j = sum over visited i (ascending) of a_i * W2T[i][j]; columns split across threads */
 #pragma omp parallel for schedule(static)
@@ -148,6 +176,12 @@ static int back_half(int D, int H, int act, int dtype, const double *x, const do
     free(vis);
     free(a);
     return k;
+}
+
+static int back_half(int D, int H, int act, int dtype, const double *x, const double *z,
+                     const void *W3, const void *W2T, int dense, double *y, double *a_out,
+                     int32_t *live_idx) {
+    return back_half2(D, H, act, dtype, x, z, W3, W2T, dense, 0, y, a_out, live_idx, NULL);
 }
 
 static double *widen(const void *v, int dtype, size_t n) {
@@ -220,6 +254,51 @@ int orc_ffn_lopa(int D, int H, int r, int act, int dtype, const void *x, const v
  * GPU batch reads the union of the live sets once or each token's list on its
  * own changes only data movement, never these values.
  */
+/*
+ * Full LoPA gate (flags: ORC_G_TILED | ORC_RMSNORM | ORC_DOUBLE_ACT), one token,
+ * in the order of the pages: t = V x; t <- t / sqrt(mean(t^2) + eps) when
+ * RMSNORM; z_i = (G x)_i + U_i . t with (G x)_i = x_{i mod D} when G_TILED;
+ * then the back half with double activation when DOUBLE_ACT. t_out receives
+ * the (normalised) t. *k2_out: units that enter the W2 pass (sparse mode).
+ */
+int orc_ffn_lopa_full(int D, int H, int r, int act, int dtype, unsigned flags, const void *x,
+                      const void *V, const void *U, const void *W3, const void *W2T, int dense,
+                      double *y, double *z_out, double *t_out, double *a_out, int32_t *live_idx,
+                      int32_t *k2_out) {
+    if (D <= 0 || H < 0 || r <= 0) return -2;
+    if (flags & ~(unsigned)(ORC_G_TILED | ORC_RMSNORM | ORC_DOUBLE_ACT)) return -3;
+    double *xd = widen(x, dtype, (size_t)D);
+    double *t = (double *)malloc((size_t)r * sizeof(double));
+    double *z = (double *)malloc((size_t)(H > 0 ? H : 1) * sizeof(double));
+    if (!xd || !t || !z) {
+        free(xd);
+        free(t);
+        free(z);
+        return -1;
+    }
+#pragma omp parallel for schedule(static)
+    for (int m = 0; m < r; ++m) t[m] = dot_row(V, dtype, (size_t)m, D, xd);
+    if (flags & ORC_RMSNORM) {
+        double ss = 0.0;
+        for (int m = 0; m < r; ++m) ss += t[m] * t[m];
+        double inv = 1.0 / sqrt(ss / (double)r + ORC_RMS_EPS);
+        for (int m = 0; m < r; ++m) t[m] *= inv;
+    }
+#pragma omp parallel for schedule(static)
+    for (int i = 0; i < H; ++i) {
+        double g = (flags & ORC_G_TILED) ? xd[i % D] : 0.0;
+        z[i] = g + dot_row(U, dtype, (size_t)i, r, t);
+    }
+    if (t_out) memcpy(t_out, t, (size_t)r * sizeof(double));
+    if (z_out) memcpy(z_out, z, (size_t)H * sizeof(double));
+    int k = back_half2(D, H, act, dtype, xd, z, W3, W2T, dense, (flags & ORC_DOUBLE_ACT) ? 1 : 0,
+                       y, a_out, live_idx, k2_out);
+    free(xd);
+    free(t);
+    free(z);
+    return k;
+}
+
 int orc_ffn_standard_batch(int T, int D, int H, int act, int dtype, const void *x,
                            const void *W1, const void *W3, const void *W2T, int dense,
                            double *y, double *z_out, int32_t *live_idx, int32_t *live_count) {

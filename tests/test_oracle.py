@@ -14,7 +14,12 @@ ties it to a fact the pages or the mathematics fix:
 * closed-form special cases (every unit live, no unit live);
 * LoPA's gate is W1 = UV when G is absent (section "LoPA Gating: moving the
   ceiling"), so materialising UV must reproduce the standard oracle;
-* the input recipe's sparsity calibration, P(z > 0) = Phi(c).
+* the input recipe's sparsity calibration, P(z > 0) = Phi(c);
+* the full LoPA gate z = G x + U RMSNorm(V x) with double activation (same
+  section; paper card Figure 6 (c) for the tiled identity G, Table 5 for the
+  W2 skip): with G alone it is the standard FFN with W1 = T + UV materialised;
+  exact rationals pin the double activation and the count of W2 rows it keeps;
+  closed forms pin the RMSNorm (eps = 1e-6, unit gain, the oracle's reading).
 
 ``test_pins_catch_planted_mistakes`` plants plausible mistakes into copies of
 the oracle's C source and checks that at least one pin fails for each.
@@ -182,6 +187,116 @@ def check_all_and_none_live():
         assert np.all(s["y"] == 0.0) and not np.any(np.signbit(s["y"]))
 
 
+def tiled_identity(H, D):
+    """The paper card's Figure 6 (c): T[i][i mod D] = 1, every other entry 0."""
+    Tm = np.zeros((H, D))
+    for i in range(H):
+        Tm[i, i % D] = 1.0
+    return Tm
+
+
+def check_lopa_full_g_is_materialised_gate():
+    """G alone: the full LoPA oracle equals the standard oracle with W1 = T + UV."""
+    rng = np.random.default_rng(21)
+    for (D, H, r) in [(16, 40, 4), (24, 24, 8), (8, 19, 8)]:
+        x = rng.standard_normal((3, D))
+        V, U = rng.standard_normal((r, D)) * 0.3, rng.standard_normal((H, r)) * 0.3
+        W3, W2T = rng.standard_normal((H, D)), rng.standard_normal((H, D))
+        for act in (ref.ACT_RELU, ref.ACT_RSPLUS):
+            a = ref.ffn_lopa_full(x, V, U, W3, W2T, ref.LOPA_G_TILED, act=act)
+            b = ref.ffn_standard(x, tiled_identity(H, D) + U @ V, W3, W2T, act=act)
+            np.testing.assert_allclose(a["z"], b["z"], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(a["y"], b["y"], rtol=1e-11, atol=1e-11)
+            assert all(np.array_equal(p, q) for p, q in zip(a["live"], b["live"]))
+    # integers: exact, G included
+    D, H, r = 6, 14, 3
+    x = gen.small_integers((2, D), -2, 2, cfg=951, stream=0, dtype="f32").astype(np.float64)
+    V = gen.small_integers((r, D), -2, 2, cfg=951, stream=4, dtype="f32").astype(np.float64)
+    U = gen.small_integers((H, r), -2, 2, cfg=951, stream=5, dtype="f32").astype(np.float64)
+    W3 = gen.small_integers((H, D), -2, 2, cfg=951, stream=2, dtype="f32").astype(np.float64)
+    W2T = gen.small_integers((H, D), -2, 2, cfg=951, stream=3, dtype="f32").astype(np.float64)
+    a = ref.ffn_lopa_full(x, V, U, W3, W2T, ref.LOPA_G_TILED)
+    b = ref.ffn_standard(x, tiled_identity(H, D) + U @ V, W3, W2T)
+    assert np.array_equal(a["y"], b["y"]) and np.array_equal(a["z"], b["z"])
+
+
+def frac_lopa_double(x, V, U, W3, W2T, g_tiled):
+    """Exact rationals: z = [G x] + U (V x), a_i = relu(z_i) * relu(u_i), y = W2 a.
+    Returns y, the live set and the number of live units with a_i != 0."""
+    D, H, r = len(x), len(U), len(V)
+    xs = [Fraction(v) for v in x]
+    t = [sum(Fraction(V[m][j]) * xs[j] for j in range(D)) for m in range(r)]
+    z = [(xs[i % D] if g_tiled else Fraction(0)) + sum(Fraction(U[i][m]) * t[m] for m in range(r))
+         for i in range(H)]
+    u = [sum(Fraction(W3[i][j]) * xs[j] for j in range(D)) for i in range(H)]
+    a = [(z[i] if z[i] > 0 else 0) * (u[i] if u[i] > 0 else 0) for i in range(H)]
+    W2 = [[Fraction(W2T[i][j]) for i in range(H)] for j in range(D)]
+    y = [sum(W2[j][i] * a[i] for i in range(H)) for j in range(D)]
+    live = [i for i in range(H) if z[i] > 0]
+    return y, live, sum(1 for i in live if a[i] != 0)
+
+
+def check_lopa_full_double_act_exact():
+    """Double activation (ReLU) on integer inputs: y, L and the kept W2 rows, exactly."""
+    for (D, H, r, seed) in [(6, 14, 3, 1), (10, 20, 5, 2)]:
+        x = gen.small_integers((3, D), -2, 2, cfg=960 + seed, stream=0, dtype="bf16")
+        V = gen.small_integers((r, D), -2, 2, cfg=960 + seed, stream=4, dtype="bf16")
+        U = gen.small_integers((H, r), -2, 2, cfg=960 + seed, stream=5, dtype="bf16")
+        W3 = gen.small_integers((H, D), -2, 2, cfg=960 + seed, stream=2, dtype="bf16")
+        W2T = gen.small_integers((H, D), -2, 2, cfg=960 + seed, stream=3, dtype="bf16")
+        f = [gen.as_float(a).astype(np.float64) for a in (x, V, U, W3, W2T)]
+        for g in (False, True):
+            flags = ref.LOPA_DOUBLE_ACT | (ref.LOPA_G_TILED if g else 0)
+            for dense in (False, True):
+                got = ref.ffn_lopa_full(x, V, U, W3, W2T, flags, dense=dense)
+                for t in range(3):
+                    y, live, k2 = frac_lopa_double([int(v) for v in f[0][t]],
+                                                   *(m.astype(int).tolist() for m in f[1:]), g)
+                    assert [Fraction(v) for v in got["y"][t]] == y
+                    assert got["live"][t].tolist() == live
+                    if not dense:
+                        assert got["k2"][t] == k2 <= len(live)
+
+
+def check_lopa_full_double_act_reduces_to_single():
+    """When every u_i = W3_i . x > 0, A(u_i) = u_i for ReLU: double == single activation."""
+    rng = np.random.default_rng(23)
+    D, H, r = 20, 30, 5
+    x = rng.standard_normal((2, D))
+    V, U = rng.standard_normal((r, D)), rng.standard_normal((H, r))
+    W2T = rng.standard_normal((H, D))
+    for t in range(2):
+        W3 = np.abs(rng.standard_normal((H, D))) * np.sign(x[t])[None, :]   # u_i > 0 for token t
+        a = ref.ffn_lopa_full(x[t:t + 1], V, U, W3, W2T, ref.LOPA_DOUBLE_ACT)
+        b = ref.ffn_lopa_full(x[t:t + 1], V, U, W3, W2T, 0)
+        assert np.array_equal(a["y"], b["y"]) and a["k2"][0] == a["k"][0]
+
+
+def check_lopa_full_rmsnorm():
+    """RMSNorm(t) = t / sqrt(mean t^2 + eps): a constant t gives c / sqrt(c^2 + eps) in
+    every entry; for any t, mean(RMSNorm(t)^2) = ms / (ms + eps) with ms = mean t^2."""
+    eps = ref.RMS_EPS
+    D, H, r = 16, 24, 8
+    rng = np.random.default_rng(29)
+    U = rng.standard_normal((H, r))
+    W3, W2T = rng.standard_normal((H, D)), rng.standard_normal((H, D))
+    x = rng.standard_normal((1, D))
+    x[0, 0] = 1.0
+    for c in (3.0, 1e-3, -0.25):
+        V = np.zeros((r, D))
+        V[:, 0] = c                                   # t_m = c * x_0 = c for every m
+        o = ref.ffn_lopa_full(x, V, U, W3, W2T, ref.LOPA_RMSNORM)
+        tn = c / math.sqrt(c * c + eps)
+        np.testing.assert_allclose(o["t"][0], np.full(r, tn), rtol=1e-14)
+        np.testing.assert_allclose(o["z"][0], U.sum(axis=1) * tn, rtol=1e-12, atol=1e-14)
+    V = rng.standard_normal((r, D)) * 0.01
+    o = ref.ffn_lopa_full(x, V, U, W3, W2T, ref.LOPA_RMSNORM)
+    raw = ref.ffn_lopa_full(x, V, U, W3, W2T, 0)["t"][0]
+    ms = float(np.mean(raw ** 2))
+    assert float(np.mean(o["t"][0] ** 2)) == pytest.approx(ms / (ms + eps), rel=1e-12)
+    np.testing.assert_allclose(o["t"][0], raw / math.sqrt(ms + eps), rtol=1e-12)
+
+
 # --------------------------------------------------------------------------- tests
 def test_bruteforce_exact():
     check_bruteforce()
@@ -197,6 +312,22 @@ def test_rsplus_and_relu():
 
 def test_lopa_reduces_to_standard():
     check_lopa_is_standard_with_uv()
+
+
+def test_lopa_full_g_is_materialised_gate():
+    check_lopa_full_g_is_materialised_gate()
+
+
+def test_lopa_full_double_act_exact():
+    check_lopa_full_double_act_exact()
+
+
+def test_lopa_full_double_act_reduces_to_single():
+    check_lopa_full_double_act_reduces_to_single()
+
+
+def test_lopa_full_rmsnorm():
+    check_lopa_full_rmsnorm()
 
 
 def test_dense_equals_sparse_bitwise():
@@ -275,7 +406,15 @@ def test_lopa_sparsity_calibration():
 
 
 MUTATIONS = {
-    "drop_up_projection": ("a[q] = h * u;", "a[q] = h;"),
+    "drop_up_projection": ("a[q] = h * (double_act ? orc_activation(act, u) : u);",
+                           "a[q] = h * (double_act ? orc_activation(act, u) : 1.0);"),
+    "double_act_ignored": ("a[q] = h * (double_act ? orc_activation(act, u) : u);", "a[q] = h * u;"),
+    "g_not_tiled": ("double g = (flags & ORC_G_TILED) ? xd[i % D] : 0.0;",
+                    "double g = (flags & ORC_G_TILED) ? xd[(i + 1) % D] : 0.0;"),
+    "rms_sum_not_mean": ("double inv = 1.0 / sqrt(ss / (double)r + ORC_RMS_EPS);",
+                         "double inv = 1.0 / sqrt(ss + ORC_RMS_EPS);"),
+    "rms_no_eps": ("double inv = 1.0 / sqrt(ss / (double)r + ORC_RMS_EPS);",
+                   "double inv = 1.0 / sqrt(ss / (double)r);"),
     "sigmoid_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "live_test_not_strict": ("z[i] > 0.0", "z[i] >= 0.0"),
     "leaky_relu": ("return z > 0.0 ? z : 0.0;", "return z > 0.0 ? z : 0.01 * z;"),
@@ -291,7 +430,9 @@ MUTATIONS = {
     "bf16_wrong_shift": ("(uint32_t)((const uint16_t *)p)[idx] << 16;", "(uint32_t)((const uint16_t *)p)[idx] << 15;"),
 }
 PINS = [check_bruteforce, check_numpy_float, check_rsplus, check_lopa_is_standard_with_uv,
-        check_dense_equals_sparse, check_all_and_none_live]
+        check_dense_equals_sparse, check_all_and_none_live, check_lopa_full_g_is_materialised_gate,
+        check_lopa_full_double_act_exact, check_lopa_full_double_act_reduces_to_single,
+        check_lopa_full_rmsnorm]
 
 
 def _run_pins_with(path_so):
