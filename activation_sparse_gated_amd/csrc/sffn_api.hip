@@ -481,7 +481,7 @@ sffn_status run_lopa_t1(sffn_handle* h, const void* x, const void* V, const void
         st = launch(h, KIND_GATE_UP_LOPA_T1, k_gate_up_lopa_t1<NC, NR, RW>, dim3(nb),
                     dim3(K1_THREADS), s, (const uint16_t*)x, (const float*)h->t_buf,
                     (const uint16_t*)U, (const uint16_t*)W3, h->a_buf, live, h->D, h->H, h->r,
-                    h->act))));
+                    h->act, h->flags))));
     if (st != SFFN_OK) return st;
     st = run_down_t1(h, W2T, y, splits, 0, s);
     if (st != SFFN_OK) return st;
@@ -513,7 +513,8 @@ sffn_status run_lopa(sffn_handle* h, const void* x, const void* V, const void* U
                                                       (const float*)h->t_buf, (const WT*)U,
                                                       (const WT*)W3, h->a_buf, live, h->D, h->H,
                                                       h->r, T, h->act,
-                                                      mode == SFFN_MODE_UNION ? 1 : 0, rpw)));
+                                                      mode == SFFN_MODE_UNION ? 1 : 0, rpw,
+                                                      h->flags)));
     if (st != SFFN_OK) return st;
     st = run_down<WT>(h, W2T, y, T, mode == SFFN_MODE_UNION ? 1 : 0, 0, s);
     if (st != SFFN_OK) return st;
@@ -587,7 +588,10 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
         if (dtype != SFFN_BF16 && dtype != SFFN_F32)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
-        if (flags != 0) return fail(nullptr, SFFN_UNSUPPORTED, "flags must be 0");
+        const unsigned known = SFFN_FLAG_G_TILED | SFFN_FLAG_RMSNORM | SFFN_FLAG_DOUBLE_ACT;
+        if (flags & ~known) return fail(nullptr, SFFN_UNSUPPORTED, "unknown flag bits");
+        if (flags != 0 && r == 0)
+            return fail(nullptr, SFFN_UNSUPPORTED, "the gate flags apply to LoPA handles (r > 0) only");
         const int dmax = dtype == SFFN_BF16 ? 8192 : 4096;
         if (D <= 0 || D % 8 != 0 || D > dmax)
             return fail(nullptr, SFFN_INVALID_ARGUMENT,

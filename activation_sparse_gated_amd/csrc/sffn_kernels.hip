@@ -50,6 +50,7 @@ constexpr int K2_CAP = 2048;      // live units compacted per pass of a down blo
 // bf16 weights are carried as raw uint16 bit patterns.
 template <typename WT> struct Elem;
 template <> struct Elem<uint16_t> {
+    __device__ static inline float get1(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
     static constexpr int VEC = 8;  // elements per 16-byte load
     __device__ static inline float get(const u32x4& v, int k) {
         uint32_t w = v[k >> 1];
@@ -57,6 +58,7 @@ template <> struct Elem<uint16_t> {
     }
 };
 template <> struct Elem<float> {
+    __device__ static inline float get1(float v) { return v; }
     static constexpr int VEC = 4;
     __device__ static inline float get(const u32x4& v, int k) { return __uint_as_float(v[k]); }
 };
@@ -71,6 +73,14 @@ __device__ inline float wave_sum(float v) {
     for (int o = WAVE / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, WAVE);
     return v;
 }
+
+// Full LoPA gate options (page "Model casting: compute the gate, then skip
+// most of the FFN", section "LoPA Gating: moving the ceiling"; paper card
+// Figure 6 (c) and Table 5): z = G x + U RMSNorm(V x) with (G x)_i = x_{i mod D},
+// and double activation a_i = A(z_i) A(u_i). eps and a unit gain are this
+// library's reading (the pages give neither).
+constexpr unsigned LOPA_G_TILED = 1u, LOPA_RMSNORM = 2u, LOPA_DOUBLE_ACT = 4u;
+constexpr float RMS_EPS = 1e-6f;
 
 // A(z): ReLU, or R-S+ = z * sigmoid(z) for z >= 0 and 0 below.
 __device__ inline float activation(int act, float z) {
@@ -135,7 +145,8 @@ template <typename WT, int NC>
 __device__ void compact_and_up(const float* z_lds, uint32_t* list, uint64_t* masks, int* n_list,
                                const WT* __restrict__ x, const WT* __restrict__ W3,
                                float* __restrict__ a_out, uint8_t* __restrict__ live_out,
-                               int row0, int nrows, int D, int H, int T, int act, int union_mode) {
+                               int row0, int nrows, int D, int H, int T, int act, int union_mode,
+                               int double_act) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     if (wave == 0) {
@@ -192,7 +203,7 @@ __device__ void compact_and_up(const float* z_lds, uint32_t* list, uint64_t* mas
             }
             const float u = wave_sum(xt.dot(w3));
             const float h = activation(act, z_lds[t * K1_MAX_ROWS + rloc]);
-            if (lane == 0) a_out[(size_t)t * H + row] = h * u;
+            if (lane == 0) a_out[(size_t)t * H + row] = h * (double_act ? activation(act, u) : u);
         }
     }
 }
@@ -238,7 +249,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_sparse(
     }
     __syncthreads();
     compact_and_up<WT, NC>(z_lds, list, masks, &n_list, x, W3, a_out, live_out, row0, nrows, D,
-                           H, T, act, union_mode);
+                           H, T, act, union_mode, 0);
 }
 
 // LoPA gate: z = U t with t = V x in fp32 (t_in [T x r]), then compact_and_up.
@@ -247,11 +258,12 @@ template <typename WT, int NC, int NR>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa(
     const WT* __restrict__ x, const float* __restrict__ t_in, const WT* __restrict__ U,
     const WT* __restrict__ W3, float* __restrict__ a_out, uint8_t* __restrict__ live_out, int D,
-    int H, int r, int T, int act, int union_mode, int rows_per_wave) {
+    int H, int r, int T, int act, int union_mode, int rows_per_wave, unsigned flags) {
     __shared__ float z_lds[MAXT * K1_MAX_ROWS];
     __shared__ uint32_t list[MAXT * K1_MAX_ROWS];
     __shared__ uint64_t masks[K1_MAX_ROWS];
     __shared__ int n_list;
+    __shared__ float inv_rms[MAXT];
     constexpr int VEC = Elem<WT>::VEC;
     constexpr int CW = WAVE * VEC;
     const int lane = threadIdx.x & (WAVE - 1);
@@ -259,6 +271,17 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa(
     const int rows_per_block = rows_per_wave * K1_WAVES;
     const int row0 = blockIdx.x * rows_per_block;
     const int nrows = min(rows_per_block, H - row0);
+    // RMSNorm of each token's rank vector: 1 / sqrt(mean t^2 + eps), one wave per token
+    for (int t = wave; t < T; t += K1_WAVES) {
+        float ss = 0.0f;
+        for (int m = lane; m < r; m += WAVE) {
+            const float tv = t_in[(size_t)t * r + m];
+            ss = fmaf(tv, tv, ss);
+        }
+        ss = wave_sum(ss);
+        if (lane == 0) inv_rms[t] = (flags & LOPA_RMSNORM) ? 1.0f / sqrtf(ss / (float)r + RMS_EPS) : 1.0f;
+    }
+    __syncthreads();
 
     for (int q = 0; q < rows_per_wave; q += 2) {
         const int ra = wave * rows_per_wave + q, rb = ra + 1;
@@ -282,8 +305,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa(
                     }
                 }
             }
-            sa = wave_sum(sa);
-            sb = wave_sum(sb);
+            sa = wave_sum(sa) * inv_rms[t];
+            sb = wave_sum(sb) * inv_rms[t];
+            if (flags & LOPA_G_TILED) {  // (G x)_i = x_{i mod D}
+                if (va) sa += Elem<WT>::get1(x[(size_t)t * D + (row0 + ra) % D]);
+                if (vb) sb += Elem<WT>::get1(x[(size_t)t * D + (row0 + rb) % D]);
+            }
             if (lane == 0) {
                 if (va) z_lds[t * K1_MAX_ROWS + ra] = sa;
                 if (vb) z_lds[t * K1_MAX_ROWS + rb] = sb;
@@ -292,7 +319,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa(
     }
     __syncthreads();
     compact_and_up<WT, NC>(z_lds, list, masks, &n_list, x, W3, a_out, live_out, row0, nrows, D,
-                           H, T, act, union_mode);
+                           H, T, act, union_mode, (flags & LOPA_DOUBLE_ACT) ? 1 : 0);
 }
 
 // LoPA rank projection t = V x: one V row per wave-iteration, fp32 out [T x r].
@@ -704,7 +731,7 @@ template <int NC, int NR, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
     const uint16_t* __restrict__ x, const float* __restrict__ t_in,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W3, float* __restrict__ a_out,
-    uint8_t* __restrict__ live_out, int D, int H, int r, int act) {
+    uint8_t* __restrict__ live_out, int D, int H, int r, int act, unsigned flags) {
     constexpr int RPB = K1_WAVES * RW;
     constexpr int CW = WAVE * 8;
     __shared__ float zs[RPB];
@@ -746,6 +773,21 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
         const int col = c * CW + lane * 8;
         xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
     }
+    float gx[RW];  // (G x)_i = x_{i mod D} when G is on
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        const int rl = wave * RW + q;
+        gx[q] = ((flags & LOPA_G_TILED) && rl < nrows) ? Elem<uint16_t>::get1(x[(row0 + rl) % D]) : 0.0f;
+    }
+    float inv = 1.0f;  // RMSNorm of t: every wave sees all of t
+    if (flags & LOPA_RMSNORM) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) ss = fmaf(tv[c][k], tv[c][k], ss);
+        inv = 1.0f / sqrtf(wave_sum_dpp(ss) / (float)r + RMS_EPS);
+    }
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
         float s = 0.0f;
@@ -753,7 +795,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
         for (int c = 0; c < NR; ++c)
 #pragma unroll
             for (int k = 0; k < 8; ++k) s = fmaf(Elem<uint16_t>::get(u[q][c], k), tv[c][k], s);
-        s = wave_sum_dpp(s);
+        s = wave_sum_dpp(s) * inv + gx[q];
         const int rl = wave * RW + q;
         if (lane == 0 && rl < nrows) zs[rl] = s;
     }
@@ -787,7 +829,8 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
         for (int c = 0; c < NC; ++c) s = dot2_chunk(w3[c], xv[c], s);
         const float uu = wave_sum_dpp(s);
         const int rl = list[e];
-        if (lane == 0) a_out[row0 + rl] = activation(act, zs[rl]) * uu;
+        const float g3 = (flags & LOPA_DOUBLE_ACT) ? activation(act, uu) : uu;
+        if (lane == 0) a_out[row0 + rl] = activation(act, zs[rl]) * g3;
     }
 }
 

@@ -23,6 +23,7 @@ SFFN_INTERNAL = -5
 SFFN_ACT_RELU, SFFN_ACT_RSPLUS = 0, 1
 SFFN_BF16, SFFN_F32 = 0, 1
 SFFN_MODE_PER_TOKEN, SFFN_MODE_UNION = 0, 1
+SFFN_FLAG_G_TILED, SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT = 1, 2, 4
 
 EXPORTED = (
     "sffn_create", "sffn_destroy", "sffn_forward_dense", "sffn_forward_sparse",

@@ -75,6 +75,21 @@ enum { SFFN_BF16 = 0, SFFN_F32 = 1 };
  *            the batch grows, since the union fills up). */
 enum { SFFN_MODE_PER_TOKEN = 0, SFFN_MODE_UNION = 1 };
 
+/* Gate options of LoPA handles (r > 0): the full LoPA gate of page "Model
+ * casting: compute the gate, then skip most of the FFN", section "LoPA
+ * Gating: moving the ceiling", z = G x + U RMSNorm(V x), with the double
+ * activation described there. Bits of sffn_create's `flags`.
+ *   G_TILED     add (G x)_i = x_{i mod D}: the fixed tiled-identity term
+ *               (paper card Figure 6 (c)); it reads no weight bytes.
+ *   RMSNORM     normalise the rank vector t = V x to t / sqrt(mean(t^2) + 1e-6)
+ *               before U (eps and the unit gain are this library's reading:
+ *               the pages give neither).
+ *   DOUBLE_ACT  a_i = A(z_i) * A(W3_i . x) instead of A(z_i) * (W3_i . x); a
+ *               live unit whose A(W3_i . x) is 0 contributes nothing and its
+ *               W2T row is not read (the s_gated skip of the paper card's
+ *               Table 5). The live set is still {i : z_i > 0}. */
+enum { SFFN_FLAG_G_TILED = 1u, SFFN_FLAG_RMSNORM = 2u, SFFN_FLAG_DOUBLE_ACT = 4u };
+
 /*
  * Create a handle for one FFN shape.
  *   D, H        model width and hidden width (H' for LoPA handles)
@@ -83,7 +98,9 @@ enum { SFFN_MODE_PER_TOKEN = 0, SFFN_MODE_UNION = 1 };
  *   act         SFFN_ACT_RELU or SFFN_ACT_RSPLUS
  *   dtype       SFFN_BF16 (weights and x as bf16 bit patterns; products in
  *               fp32) or SFFN_F32
- *   flags       must be 0 (bits reserved)
+ *   flags       0, or for LoPA handles any of SFFN_FLAG_G_TILED,
+ *               SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT (other bits, or any
+ *               bit on a standard handle: SFFN_UNSUPPORTED)
  * On success *out receives the handle. Allocates device scratch on the
  * current device: max_tokens * (H + r) floats plus max_tokens * H bytes.
  */

@@ -51,8 +51,12 @@ def test_create_rejects_bad_arguments(args, status, needle):
 
 
 def test_create_rejects_flags():
-    st, h = sffn.sffn_create_status(64, 64, 0, 1, 0, 0, 1)
-    assert st == sffn.SFFN_UNSUPPORTED and "flags" in sffn.sffn_last_error(None)
+    # gate flags on a standard handle
+    st, h = sffn.sffn_create_status(64, 64, 0, 1, 0, 0, sffn.SFFN_FLAG_G_TILED)
+    assert st == sffn.SFFN_UNSUPPORTED and h is None and "flags" in sffn.sffn_last_error(None)
+    # bits outside the three gate options, on a LoPA handle
+    st, h = sffn.sffn_create_status(64, 64, 8, 1, 0, 0, 8)
+    assert st == sffn.SFFN_UNSUPPORTED and h is None and "flag" in sffn.sffn_last_error(None)
 
 
 def test_forward_with_null_handle():
