@@ -93,6 +93,32 @@ def standard_weights(D: int, H: int, sparsity: float | None, cfg: int, layer: in
             "offset": c}
 
 
+def quantize_rows_int8(w64: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric per-row int8 of a float matrix: scale_i = max_j |w_ij| / 127 (as fp32;
+    1 for an all-zero row), q_ij = clip(rint(w_ij / scale_i), -127, 127). The weights
+    the FFN then uses are q_ij * scale_i (the input recipe of the int8 workloads)."""
+    amax = np.max(np.abs(w64), axis=1)
+    scale = np.where(amax > 0, amax / 127.0, 1.0).astype(np.float32)
+    q = np.clip(np.rint(w64 / scale.astype(np.float64)[:, None]), -127, 127).astype(np.int8)
+    return np.ascontiguousarray(q), scale
+
+
+def standard_weights_int8(D: int, H: int, sparsity: float | None, cfg: int, layer: int = 0,
+                          replica: int = 0, offset: float | None = None) -> dict:
+    """The fp64 draws of standard_weights (same streams, W1[:, 0] = c), quantized per
+    row to int8: W1, W3, W2T int8 [H, D] and W1_scale, W3_scale, W2T_scale fp32 [H]."""
+    std = 1.0 / np.sqrt(D)
+    W1 = normal((H, D), std, cfg, layer, replica, S_W1)
+    c = offset if offset is not None else (gate_offset(sparsity) if sparsity is not None else None)
+    if c is not None:
+        W1[:, 0] = c
+    out = {"offset": c}
+    for name, w in (("W1", W1), ("W3", normal((H, D), std, cfg, layer, replica, S_W3)),
+                    ("W2T", normal((H, D), std, cfg, layer, replica, S_W2T))):
+        out[name], out[name + "_scale"] = quantize_rows_int8(w)
+    return out
+
+
 def lopa_weights(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, layer: int = 0,
                  replica: int = 0, dtype: str = "bf16", offset: float | None = None) -> dict:
     """V [r, D], U [Hp, r], W3 [Hp, D], W2T [Hp, D] with fan-in scaled variances."""

@@ -194,3 +194,21 @@ def ffn_lopa_full(x, V, U, W3, W2T, flags: int, act: int = ACT_RELU, dense: bool
         k2s[t] = k2[0]
         live.append(idx[:k].copy())
     return {"y": y, "z": z, "t": tt, "live": live, "k": ks, "k2": k2s}
+
+
+def dequantize_rows(q, scale):
+    """Weights of a per-row int8 matrix as fp64: q_ij * scale_i (exact in fp64: an
+    8-bit integer times an fp32 scale needs 32 significant bits)."""
+    q = np.asarray(q)
+    return q.astype(np.float64) * np.asarray(scale, np.float32).astype(np.float64)[:, None]
+
+
+def ffn_standard_int8(x, w, act: int = ACT_RELU, dense: bool = False):
+    """The standard oracle on the weights an int8 workload defines (q * scale per row);
+    x is widened exactly to fp64. w: dict with W1/W3/W2T (int8) and *_scale (fp32)."""
+    xf = np.atleast_2d(np.asarray(x))
+    if xf.dtype == np.uint16:
+        xf = (xf.astype(np.uint32) << 16).view(np.float32)
+    xf = xf.astype(np.float64)
+    return ffn_standard(xf, *(dequantize_rows(w[k], w[k + "_scale"]) for k in ("W1", "W3", "W2T")),
+                        act=act, dense=dense)

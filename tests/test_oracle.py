@@ -330,6 +330,35 @@ def test_lopa_full_rmsnorm():
     check_lopa_full_rmsnorm()
 
 
+def test_int8_weights_are_rows_times_scales():
+    """An int8 workload's weights are q_ij * scale_i: exact in fp64, within half a step
+    of the fp64 draw, and the oracle on them equals exact rationals for integer q."""
+    w = gen.standard_weights_int8(64, 96, 0.9, cfg=70)
+    w64 = gen.normal((96, 64), 1.0 / 8.0, 70, 0, 0, gen.S_W3)
+    deq = ref.dequantize_rows(w["W3"], w["W3_scale"])
+    step = w["W3_scale"].astype(np.float64)[:, None]
+    assert np.all(np.abs(deq - w64) <= 0.5 * step * (1 + 1e-12))
+    assert np.abs(w["W3"]).max() == 127
+    for k in ("W1", "W3", "W2T"):
+        assert w[k].dtype == np.int8 and w[k + "_scale"].dtype == np.float32
+    # power-of-two scales: exact, and the FFN on them is exact rationals
+    D, H = 8, 12
+    q = {k: gen.small_integers((H, D), -3, 3, cfg=71, stream=s, dtype="f32").astype(np.int8)
+         for k, s in (("W1", 1), ("W3", 2), ("W2T", 3))}
+    x = gen.small_integers((2, D), -2, 2, cfg=71, stream=0, dtype="bf16")
+    sc = {k: np.full(H, 2.0 ** -e, np.float32) for k, e in (("W1", 1), ("W3", 2), ("W2T", 3))}
+    wi = {**q, **{k + "_scale": v for k, v in sc.items()}}
+    got = ref.ffn_standard_int8(x, wi)
+    xf = gen.as_float(x).astype(np.float64)
+    for t in range(2):
+        y, z, live = frac_ffn([Fraction(v) for v in xf[t]],
+                              [[Fraction(int(v)) * Fraction(1, 2) for v in row] for row in q["W1"]],
+                              [[Fraction(int(v)) * Fraction(1, 4) for v in row] for row in q["W3"]],
+                              [[Fraction(int(v)) * Fraction(1, 8) for v in row] for row in q["W2T"]])
+        assert [Fraction(v) for v in got["y"][t]] == y
+        assert got["live"][t].tolist() == live
+
+
 def test_dense_equals_sparse_bitwise():
     check_dense_equals_sparse()
 
