@@ -22,13 +22,16 @@ namespace {
 enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GATE_UP_DENSE,
             KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_GATE_UP_DENSE_T1, KIND_DOWN_T1,
             KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
-            KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_COUNT };
+            KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
+            KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
                                             "k_ffn_t1", "k_ffn_dense_t1", "k_reduce_partials",
                                             "k_rank_proj_t1", "k_gate_up_lopa_t1",
-                                            "k_gate_up_mfma", "k_down_mfma", "k_down_tb"};
+                                            "k_gate_up_mfma", "k_down_mfma", "k_down_tb",
+                                            "k_gate_up_t1_i8", "k_gate_up_dense_t1_i8",
+                                            "k_down_t1_i8"};
 
 thread_local std::string g_thread_error = "no error";
 
@@ -535,6 +538,37 @@ sffn_status run_dense(sffn_handle* h, const void* x, const void* W1, const void*
     return run_down<WT>(h, W2T, y, T, 1, 1, s);
 }
 
+// Weight-only int8, one token: gate (+ up) pass, then the int8 down pass over
+// 256-column slices and 16 row splits (atomics into y, cleared by the gate pass).
+template <bool DENSE>
+sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float* s1,
+                      const void* W3, const float* s3, const void* W2T, const float* s2,
+                      float* y, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
+    const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
+    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    int splits = h->t1_splits_sparse;
+    while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
+    uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
+    float* yz = splits > 1 ? y : nullptr;
+    sffn_status st = SFFN_OK;
+    SFFN_NCT1_SWITCH(nc, st = launch(h, DENSE ? KIND_GATE_UP_DENSE_T1_I8 : KIND_GATE_UP_T1_I8,
+                                     k_gate_up_t1_i8<NC, DENSE>, dim3(nb), dim3(K1_THREADS), s,
+                                     (const uint16_t*)x, (const int8_t*)W1, s1, (const int8_t*)W3,
+                                     s3, s2, h->a_buf, live, yz, h->D, h->H, h->act));
+    if (st != SFFN_OK) return st;
+    const int cb = 16 * 16;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I8, k_down_t1_i8<PMAX>, dim3(nbx, splits),
+                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                       (const int8_t*)W2T, y, h->D, h->H, splits, DENSE ? 1 : 0));
+    if (st != SFFN_OK) return st;
+    if (DENSE) return SFFN_OK;
+    return run_live_list(h, 1, live_count, live_idx, s);
+}
+
 sffn_status check_common(sffn_handle* h, const void* x, const void* W3, const void* W2T,
                          const float* y, int T, int32_t* live_count, int32_t* live_idx,
                          hipStream_t* stream_out, void* stream) {
@@ -586,13 +620,19 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         *out = nullptr;
         if (act != SFFN_ACT_RELU && act != SFFN_ACT_RSPLUS)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
-        if (dtype != SFFN_BF16 && dtype != SFFN_F32)
+        if (dtype != SFFN_BF16 && dtype != SFFN_F32 && dtype != SFFN_I8)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+        if (dtype == SFFN_I8 && r != 0)
+            return fail(nullptr, SFFN_UNSUPPORTED, "int8 weights: standard-gating handles (r == 0) only");
+        if (dtype == SFFN_I8 && D % 16 != 0)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "int8 weights: D must be a multiple of 16");
+        if (dtype == SFFN_I8 && (H + KD_THREADS - 1) / KD_THREADS > 32 * 16)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "int8 weights: H too large");
         const unsigned known = SFFN_FLAG_G_TILED | SFFN_FLAG_RMSNORM | SFFN_FLAG_DOUBLE_ACT;
         if (flags & ~known) return fail(nullptr, SFFN_UNSUPPORTED, "unknown flag bits");
         if (flags != 0 && r == 0)
             return fail(nullptr, SFFN_UNSUPPORTED, "the gate flags apply to LoPA handles (r > 0) only");
-        const int dmax = dtype == SFFN_BF16 ? 8192 : 4096;
+        const int dmax = dtype == SFFN_F32 ? 4096 : 8192;
         if (D <= 0 || D % 8 != 0 || D > dmax)
             return fail(nullptr, SFFN_INVALID_ARGUMENT,
                         "D must be a positive multiple of 8, at most " + std::to_string(dmax));
@@ -731,6 +771,8 @@ sffn_status sffn_forward_dense(sffn_handle* h, const void* x, const void* W1, co
         hipStream_t s;
         sffn_status st = check_common(h, x, W3, W2T, y, T, nullptr, nullptr, &s, stream);
         if (st != SFFN_OK) return st;
+        if (h->dtype == SFFN_I8)
+            return fail(h, SFFN_INVALID_ARGUMENT, "int8 handles take the _i8 forward calls");
         if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "dense forward needs a standard-gating handle (r == 0)");
         if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
@@ -751,6 +793,8 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
         hipStream_t s;
         sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
         if (st != SFFN_OK) return st;
+        if (h->dtype == SFFN_I8)
+            return fail(h, SFFN_INVALID_ARGUMENT, "int8 handles take the _i8 forward calls");
         if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "sparse forward needs a standard-gating handle (r == 0)");
         if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
             return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
@@ -779,6 +823,59 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
     }
 }
 
+static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, const float* s1,
+                       const void* W3, const float* s3, const void* W2T, const float* s2,
+                       float* y, int T, int mode, int32_t* live_count, int32_t* live_idx,
+                       void* stream, bool dense) {
+    hipStream_t s;
+    sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
+    if (st != SFFN_OK) return st;
+    if (h->dtype != SFFN_I8) return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
+    if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
+        return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
+    if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
+    if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
+    if (!s1 || !s3 || !s2) return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
+    auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+    // a batch runs token by token (both modes compute the same result)
+    for (int t = 0; t < T; ++t) {
+        const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);
+        float* yt = y + (size_t)t * h->D;
+        st = dense ? run_i8_t1<true>(h, xt, W1, s1, W3, s3, W2T, s2, yt, nullptr, nullptr, s)
+                   : run_i8_t1<false>(h, xt, W1, s1, W3, s3, W2T, s2, yt,
+                                      live_count ? live_count + t : nullptr,
+                                      live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
+        if (st != SFFN_OK) return st;
+    }
+    return SFFN_OK;
+}
+
+sffn_status sffn_forward_sparse_i8(sffn_handle* h, const void* x, const void* W1,
+                                   const float* W1_scale, const void* W3, const float* W3_scale,
+                                   const void* W2T, const float* W2T_scale, float* y, int T,
+                                   int mode, int32_t* live_count, int32_t* live_idx,
+                                   void* stream) {
+    try {
+        return forward_i8(h, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale, y, T, mode,
+                          live_count, live_idx, stream, false);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_sparse_i8");
+    }
+}
+
+sffn_status sffn_forward_dense_i8(sffn_handle* h, const void* x, const void* W1,
+                                  const float* W1_scale, const void* W3, const float* W3_scale,
+                                  const void* W2T, const float* W2T_scale, float* y, int T,
+                                  void* stream) {
+    try {
+        return forward_i8(h, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale, y, T,
+                          SFFN_MODE_PER_TOKEN, nullptr, nullptr, stream, true);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_dense_i8");
+    }
+}
+
 sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, const void* U,
                               const void* W3, const void* W2T, float* y, int T, int mode,
                               int32_t* live_count, int32_t* live_idx, void* stream) {
@@ -786,6 +883,8 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
         hipStream_t s;
         sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
         if (st != SFFN_OK) return st;
+        if (h->dtype == SFFN_I8)
+            return fail(h, SFFN_INVALID_ARGUMENT, "int8 handles take the _i8 forward calls");
         if (h->r == 0) return fail(h, SFFN_INVALID_ARGUMENT, "LoPA forward needs a handle with r > 0");
         if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
             return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));

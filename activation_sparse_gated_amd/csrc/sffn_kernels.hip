@@ -1178,6 +1178,244 @@ __global__ __launch_bounds__(KR_THREADS) void k_reduce_partials(const float* __r
 }
 
 // ---------------------------------------------------------------------------
+// Batch-1 path with weight-only int8 weights: W[i][j] = q[i][j] * scale[i]
+// (symmetric, one fp32 scale per stored row; x stays bf16, every product and
+// sum is fp32). A lane's 16-byte piece holds 16 columns; a wave covers 1024
+// columns per chunk.
+
+// 16 int8 weights against 16 fp32 inputs, accumulated in fp32
+__device__ inline float dot16_i8(const u32x4& w, const float* xv, float s) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int v = (int)(wq << (24 - 8 * b)) >> 24;  // sign-extended byte b
+            s = fmaf((float)v, xv[4 * q + b], s);
+        }
+    }
+    return s;
+}
+
+// x[col .. col + 16) (bf16) as fp32; zeros past D
+__device__ inline void load_x16(const uint16_t* __restrict__ x, int col, int D, float* xv) {
+    if (col < D) {
+        const u32x4 a = load_cached(x + col), b = load_cached(x + col + 8);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            xv[k] = Elem<uint16_t>::get(a, k);
+            xv[8 + k] = Elem<uint16_t>::get(b, k);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) xv[k] = 0.0f;
+    }
+}
+
+// Gate and gathered up projection, int8 weights: z_i = s1_i (q1_i . x); for a
+// live unit u_i = s3_i (q3_i . x) and the unit product is stored pre-multiplied
+// by the W2T row scale, a_i * s2_i, so the down pass reads only q2. DENSE
+// visits every unit. One unit per wave; all W1 loads are issued first.
+// y_zero (nullable): D floats this grid clears for a down pass that accumulates.
+template <int NC, bool DENSE>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ W1, const float* __restrict__ s1,
+    const int8_t* __restrict__ W3, const float* __restrict__ s3, const float* __restrict__ s2,
+    float* __restrict__ a_out, uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D,
+    int H, int act) {
+    constexpr int CW = WAVE * 16;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int unit = blockIdx.x * K1_WAVES + wave;
+    const bool in = unit < H;
+    u32x4 w[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 16;
+        w[c] = (in && col < D) ? load_stream(W1 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 w3[NC];
+    if (DENSE) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 16;
+            w3[c] = (in && col < D) ? load_stream(W3 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    const float sc1 = in ? s1[unit] : 0.0f;
+    const float sc3 = in ? s3[unit] : 0.0f;
+    const float sc2 = in ? s2[unit] : 0.0f;
+    float xv[NC][16];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) load_x16(x, c * CW + lane * 16, D, xv[c]);
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    float sz = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sz = dot16_i8(w[c], xv[c], sz);
+    const float z = wave_sum_dpp(sz) * sc1;
+    const bool live = in && z > 0.0f;
+    if (!in) return;
+    if (lane == 0 && live_out) live_out[unit] = live ? 1 : 0;
+    if (!DENSE && !live) {
+        if (lane == 0) a_out[unit] = 0.0f;
+        return;
+    }
+    if (!DENSE) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 16;
+            w3[c] = col < D ? load_stream(W3 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float su = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) su = dot16_i8(w3[c], xv[c], su);
+    const float u = wave_sum_dpp(su) * sc3;
+    if (lane == 0) a_out[unit] = activation(act, z) * u * sc2;
+}
+
+// Down projection, int8 W2T rows: y[slice] = sum_i a'_i q2[i, slice] with
+// a'_i = a_i s2_i from the gate pass. As k_down_t1: grid = (column slices of
+// 16 lanes x 16 columns = 256 columns, XCD-contiguous order) x (row splits);
+// each block loads its share of a' in one round, compacts the nonzero entries
+// in LDS (all units when dense) and accumulates 8 row slices in flight per
+// lane; with splits > 1 it adds its slice into y (cleared by the gate pass).
+template <int PMAX>
+__global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restrict__ a,
+                                                           const int8_t* __restrict__ W2T,
+                                                           float* __restrict__ y, int D, int H,
+                                                           int splits, int dense) {
+    constexpr int LPR = 16;
+    constexpr int CB = LPR * 16;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 8;
+    __shared__ int list[KD_LCAP];
+    __shared__ float av[KD_LCAP];
+    __shared__ int wcount[PMAX * KD_WAVES];
+    __shared__ int woff[PMAX * KD_WAVES + 1];
+    __shared__ float red[KD_WAVES][CB];
+
+    const int nslices = (D + CB - 1) / CB;
+    const int per_xcd = (nslices + 7) / 8;
+    const int bx = blockIdx.x;
+    const int slice = (bx & 7) * per_xcd + (bx >> 3);
+    if (slice >= nslices) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * 16;
+    const bool col_ok = col < D;
+    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
+
+    float ar[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        ar[p] = (p < P && row < h1) ? a[row] : 0.0f;
+    }
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
+        mk[p] = __ballot(keep);
+        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int NCNT = PMAX * KD_WAVES;
+        int carry = 0;
+        for (int base = 0; base < NCNT; base += WAVE) {
+            const int i = base + lane;
+            const int v = i < NCNT ? wcount[i] : 0;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const int t = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += t;
+            }
+            if (i < NCNT) woff[i] = carry + incl - v;
+            carry += __shfl(incl, WAVE - 1, WAVE);
+        }
+        if (lane == 0) woff[NCNT] = carry;
+    }
+    __syncthreads();
+
+    float acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    int p0 = 0;
+    while (p0 < P) {
+        int p1 = p0 + 1;
+        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
+        const int ebase = woff[p0 * KD_WAVES];
+        const int n = woff[p1 * KD_WAVES] - ebase;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
+                const int pos = woff[p * KD_WAVES + wave] - ebase +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+                av[pos] = ar[p];
+            }
+        }
+        __syncthreads();
+        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+            u32x4 wv[UF];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)list[e] * D + col)
+                                          : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const float aval = e < n ? av[e] : 0.0f;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = wv[u][q];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[4 * q + b] = fmaf(aval, (float)((int)(wq << (24 - 8 * b)) >> 24), acc[4 * q + b]);
+                }
+            }
+        }
+        __syncthreads();
+        p0 = p1;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        float v = acc[k];
+        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+        acc[k] = v;
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k) red[wave][sub * 16 + k] = acc[k];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+        float s = 0.0f;
+        for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+        if (col0 + c < D) {
+            if (splits > 1)
+                atomicAdd(y + col0 + c, s);
+            else
+                y[col0 + c] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Batched bf16 path on MFMA (v_mfma_f32_16x16x32_bf16). Lane l of a wave holds
 // A[l%16][8(l/16) .. +8], B[8(l/16) .. +8][l%16] and C[4(l/16) .. +4][l%16].
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));

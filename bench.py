@@ -493,6 +493,57 @@ def main() -> int:
         del g_full
         hf.close()
 
+    # ---------------------------------------------------------------- weight-only int8 decode
+    if not args.no_extras:
+        # the decode workload's fp64 draws quantized per row to int8 (same streams and offset)
+        wq = gen.standard_weights_int8(D, H, s, cfg=2)
+        WQ = {kk: torch.from_numpy(np.ascontiguousarray(wq[kk])).cuda()
+              for kk in ("W1", "W3", "W2T", "W1_scale", "W3_scale", "W2T_scale")}
+        repq = [{kk: (WQ[kk] if rr == 0 else WQ[kk].clone()) for kk in WQ} for rr in range(R)]
+        hq = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_I8)
+        for t in range(n):
+            rp = repq[t % R]
+            sffn.sffn_forward_sparse_i8(hq.ptr, x[t], rp["W1"], rp["W1_scale"], rp["W3"],
+                                        rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[t], 1,
+                                        sffn.SFFN_MODE_PER_TOKEN, cnt[t:t + 1], idx[t])
+        torch.cuda.synchronize()
+        kq = cnt.cpu().numpy().astype(np.int64)
+
+        def q8_stream(dense):
+            def fn():
+                for t in range(n):
+                    rp = repq[t % R]
+                    if dense:
+                        sffn.sffn_forward_dense_i8(hq.ptr, x[t], rp["W1"], rp["W1_scale"], rp["W3"],
+                                                   rp["W3_scale"], rp["W2T"], rp["W2T_scale"],
+                                                   y[t], 1)
+                    else:
+                        sffn.sffn_forward_sparse_i8(hq.ptr, x[t], rp["W1"], rp["W1_scale"],
+                                                    rp["W3"], rp["W3_scale"], rp["W2T"],
+                                                    rp["W2T_scale"], y[t], 1,
+                                                    sffn.SFFN_MODE_PER_TOKEN)
+            return fn
+
+        res_q = {}
+        for name, dense in (("sparse", False), ("dense", True)):
+            g_q = capture(q8_stream(dense))
+            ms_q = time_graph(g_q, args.steps, args.warmup)
+            del g_q
+            kk_ = H if dense else kq
+            # int8 weight bytes, the fp32 scales of the rows read, x in and y out
+            bytes_q = (H * D + 2 * kk_ * D) + 4 * (H + 2 * kk_) + 6 * D
+            if dense:
+                bytes_q = np.full(n, 3 * H * D + 12 * H + 6 * D)
+            res_q[name + "_tokens_per_s"] = round(n / (ms_q * 1e-3), 1)
+            res_q[name + "_touched_GBps"] = round(float(np.sum(bytes_q)) / (ms_q * 1e-3) / 1e9, 1)
+        res_q["measured_sparsity"] = round(float(1 - kq.mean() / H), 4)
+        res_q["sparse_vs_dense_int8"] = round(res_q["sparse_tokens_per_s"] / res_q["dense_tokens_per_s"], 3)
+        res_q["sparse_vs_dense_bf16"] = round(res_q["sparse_tokens_per_s"] / extras["dense_tokens_per_s"], 3)
+        extras["int8"] = res_q
+        log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items()))
+        hq.close()
+        del repq, WQ
+
     # ---------------------------------------------------------------- batched decode and stacks
     if not args.no_extras:
         extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)

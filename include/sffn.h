@@ -66,7 +66,12 @@ enum {
 };
 
 enum { SFFN_ACT_RELU = 0, SFFN_ACT_RSPLUS = 1 };
-enum { SFFN_BF16 = 0, SFFN_F32 = 1 };
+/* Weight storage. SFFN_I8: weight-only int8, symmetric per stored row: the
+ * weight is q[i][j] * scale[i] with q int8 and one fp32 scale per row (the
+ * pages report int8 weight-only models and kernels, paper card Table 17 and
+ * Figure 9; the scheme is this library's reading). x stays bf16 and every
+ * product and sum is fp32. Standard gating only; forward calls: the _i8 ones. */
+enum { SFFN_BF16 = 0, SFFN_F32 = 1, SFFN_I8 = 2 };
 /* How a batch of T tokens moves data; never changes the result.
  * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set.
  * UNION:     the union of the tokens' live sets is read once and each row is
@@ -97,7 +102,8 @@ enum { SFFN_FLAG_G_TILED = 1u, SFFN_FLAG_RMSNORM = 2u, SFFN_FLAG_DOUBLE_ACT = 4u
  *   max_tokens  largest T any forward call on this handle will pass (1..64)
  *   act         SFFN_ACT_RELU or SFFN_ACT_RSPLUS
  *   dtype       SFFN_BF16 (weights and x as bf16 bit patterns; products in
- *               fp32) or SFFN_F32
+ *               fp32), SFFN_F32, or SFFN_I8 (int8 weights with per-row
+ *               scales, x bf16; needs D % 16 == 0 and r == 0)
  *   flags       0, or for LoPA handles any of SFFN_FLAG_G_TILED,
  *               SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT (other bits, or any
  *               bit on a standard handle: SFFN_UNSUPPORTED)
@@ -144,6 +150,26 @@ sffn_status sffn_forward_sparse(sffn_handle *h, const void *x, const void *W1, c
 sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, const void *U,
                               const void *W3, const void *W2T, float *y, int T, int mode,
                               int32_t *live_count, int32_t *live_idx, void *stream);
+
+/*
+ * Gate-first sparse forward and the dense comparator with weight-only int8
+ * weights (SFFN_I8 handles): as sffn_forward_sparse / sffn_forward_dense, with
+ * W1, W3, W2T int8 [H x D] row-major (16-byte aligned) and W1_scale, W3_scale,
+ * W2T_scale fp32 [H] (4-byte aligned): weight (i, j) of each matrix is
+ * q[i][j] * scale[i]. x is bf16 [T x D], y fp32 [T x D]. Tokens of a batch are
+ * processed one after another (mode only selects the live-list semantics,
+ * which are the same for one token). Errors as for the other forward calls;
+ * a non-int8 handle gives SFFN_INVALID_ARGUMENT.
+ */
+sffn_status sffn_forward_sparse_i8(sffn_handle *h, const void *x, const void *W1,
+                                   const float *W1_scale, const void *W3, const float *W3_scale,
+                                   const void *W2T, const float *W2T_scale, float *y, int T,
+                                   int mode, int32_t *live_count, int32_t *live_idx,
+                                   void *stream);
+sffn_status sffn_forward_dense_i8(sffn_handle *h, const void *x, const void *W1,
+                                  const float *W1_scale, const void *W3, const float *W3_scale,
+                                  const void *W2T, const float *W2T_scale, float *y, int T,
+                                  void *stream);
 
 /* Message of the last failure on this handle; with NULL, the calling thread's
  * last failure that had no handle (e.g. in sffn_create). Never NULL. */

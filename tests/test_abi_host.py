@@ -42,12 +42,20 @@ def test_library_exports_every_declared_function():
     ((64, 64, 0, 0, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
     ((64, 64, 0, 65, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
     ((64, 64, 0, 1, 2, 0), sffn.SFFN_UNSUPPORTED, "activation"),
-    ((64, 64, 0, 1, 0, 2), sffn.SFFN_UNSUPPORTED, "dtype"),
+    ((64, 64, 0, 1, 0, 3), sffn.SFFN_UNSUPPORTED, "dtype"),
 ])
 def test_create_rejects_bad_arguments(args, status, needle):
     st, h = sffn.sffn_create_status(*args)
     assert st == status and h is None
     assert needle in sffn.sffn_last_error(None)
+
+
+def test_create_int8_checks():
+    # int8 weights: D a multiple of 16, standard gating only
+    st, h = sffn.sffn_create_status(264, 64, 0, 1, 0, sffn.SFFN_I8, 0)
+    assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "16" in sffn.sffn_last_error(None)
+    st, h = sffn.sffn_create_status(256, 64, 8, 1, 0, sffn.SFFN_I8, 0)
+    assert st == sffn.SFFN_UNSUPPORTED and h is None and "int8" in sffn.sffn_last_error(None)
 
 
 def test_create_rejects_flags():
