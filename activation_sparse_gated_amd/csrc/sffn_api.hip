@@ -23,7 +23,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_GATE_UP_DENSE_T1, KIND_DOWN_T1,
             KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
-            KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_COUNT };
+            KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
+            KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -31,7 +32,7 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_rank_proj_t1", "k_gate_up_lopa_t1",
                                             "k_gate_up_mfma", "k_down_mfma", "k_down_tb",
                                             "k_gate_up_t1_i8", "k_gate_up_dense_t1_i8",
-                                            "k_down_t1_i8"};
+                                            "k_down_t1_i8", "k_moe_gather", "k_moe_combine"};
 
 thread_local std::string g_thread_error = "no error";
 
@@ -71,6 +72,9 @@ struct sffn_handle {
     int m_splits = 16;             // row splits of the MFMA down pass
     int m_ut1 = 1, m_ut2 = 2, m_ut4 = 2;  // unit tiles per gate block for <=16, <=32, <=64 tokens
     void* m_zero = nullptr;        // 4 KB of zeros (source of the staged pieces outside the operands)
+    // mixture of experts: tokens gathered per expert, expert outputs per slot
+    uint16_t* moe_x = nullptr;     // [2 * max_tokens x D] bf16
+    float* moe_y = nullptr;        // [2 * max_tokens x D] fp32
     int tb_splits = 16;            // row splits of the small-batch down pass
     int tb_max = 8;                // batches up to this size use the small-batch down pass
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
@@ -569,6 +573,40 @@ sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
+// Launch plan of a checked sparse / dense call (no argument checks).
+sffn_status dispatch_sparse(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                            const void* W2T, float* y, int T, int mode, int32_t* live_count,
+                            int32_t* live_idx, hipStream_t s) {
+    sffn_status st = SFFN_OK;
+    if (T == 0) return SFFN_OK;
+    if (t1_ok(h, T)) return run_sparse_t1(h, x, W1, W3, W2T, y, live_count, live_idx, s);
+    if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1)) {
+        // per-token lists: every token runs the whole batch-1 pass on its own live set
+        const size_t xb = (size_t)h->D * sizeof(uint16_t);
+        for (int t = 0; t < T; ++t) {
+            st = run_sparse_t1(h, (const char*)x + t * xb, W1, W3, W2T, y + (size_t)t * h->D,
+                               live_count ? live_count + t : nullptr,
+                               live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
+            if (st != SFFN_OK) return st;
+        }
+        return SFFN_OK;
+    }
+    if (mode == SFFN_MODE_UNION && mfma_ok(h, T))
+        return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
+    return h->dtype == SFFN_BF16
+               ? run_sparse<uint16_t>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s)
+               : run_sparse<float>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
+}
+
+sffn_status dispatch_dense(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                           const void* W2T, float* y, int T, hipStream_t s) {
+    if (T == 0) return SFFN_OK;
+    if (t1_ok(h, T)) return run_dense_t1(h, x, W1, W3, W2T, y, s);
+    if (mfma_ok(h, T)) return run_mfma<true>(h, x, W1, W3, W2T, y, T, nullptr, nullptr, s);
+    return h->dtype == SFFN_BF16 ? run_dense<uint16_t>(h, x, W1, W3, W2T, y, T, s)
+                                 : run_dense<float>(h, x, W1, W3, W2T, y, T, s);
+}
+
 sffn_status check_common(sffn_handle* h, const void* x, const void* W3, const void* W2T,
                          const float* y, int T, int32_t* live_count, int32_t* live_idx,
                          hipStream_t* stream_out, void* stream) {
@@ -740,6 +778,15 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
                 return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
             }
         }
+        if (dtype == SFFN_BF16 && r == 0) {
+            const size_t rows = 2 * (size_t)max_tokens;
+            e = hipMalloc(&h->moe_x, rows * D * sizeof(uint16_t));
+            if (e == hipSuccess) e = hipMalloc(&h->moe_y, rows * D * sizeof(float));
+            if (e != hipSuccess) {
+                sffn_destroy(h);
+                return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
+            }
+        }
         *out = h;
         return SFFN_OK;
     } catch (...) {
@@ -761,6 +808,8 @@ void sffn_destroy(sffn_handle* h) {
     if (h->m_a) (void)hipFree(h->m_a);
     if (h->m_mask) (void)hipFree(h->m_mask);
     if (h->m_zero) (void)hipFree(h->m_zero);
+    if (h->moe_x) (void)hipFree(h->moe_x);
+    if (h->moe_y) (void)hipFree(h->moe_y);
 
     delete h;
 }
@@ -776,13 +825,71 @@ sffn_status sffn_forward_dense(sffn_handle* h, const void* x, const void* W1, co
         if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "dense forward needs a standard-gating handle (r == 0)");
         if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
-        if (T == 0) return SFFN_OK;
-        if (t1_ok(h, T)) return run_dense_t1(h, x, W1, W3, W2T, y, s);
-        if (mfma_ok(h, T)) return run_mfma<true>(h, x, W1, W3, W2T, y, T, nullptr, nullptr, s);
-        return h->dtype == SFFN_BF16 ? run_dense<uint16_t>(h, x, W1, W3, W2T, y, T, s)
-                                     : run_dense<float>(h, x, W1, W3, W2T, y, T, s);
+        return dispatch_dense(h, x, W1, W3, W2T, y, T, s);
     } catch (...) {
         return fail(h, SFFN_INTERNAL, "exception in sffn_forward_dense");
+    }
+}
+
+sffn_status sffn_forward_moe(sffn_handle* h, const void* x, int E, const void* const* W1,
+                             const void* const* W3, const void* const* W2T, int K,
+                             const int32_t* route, const float* gate, float* y, int T, int dense,
+                             void* stream) {
+    try {
+        if (!h) return fail(nullptr, SFFN_INVALID_ARGUMENT, "null handle");
+        if (h->dtype != SFFN_BF16 || h->r != 0 || !h->moe_x)
+            return fail(h, SFFN_INVALID_ARGUMENT, "mixture of experts needs a bf16 standard-gating handle");
+        if (E < 1 || E > 1024) return fail(h, SFFN_INVALID_ARGUMENT, "E must be in [1, 1024]");
+        if (K < 1 || K > 2) return fail(h, SFFN_INVALID_ARGUMENT, "K must be 1 or 2");
+        if (!W1 || !W3 || !W2T || !route || !gate)
+            return fail(h, SFFN_INVALID_ARGUMENT, "null expert table or routing array");
+        hipStream_t s;
+        // check_common validates x, y, T, the device; expert weights are checked below
+        sffn_status st = check_common(h, x, h->moe_x, h->moe_y, y, T, nullptr, nullptr, &s, stream);
+        if (st != SFFN_OK) return st;
+        if (T == 0) return SFFN_OK;
+        for (int i = 0; i < T * K; ++i)
+            if (route[i] < 0 || route[i] >= E)
+                return fail(h, SFFN_INVALID_ARGUMENT, "route entry outside [0, E)");
+        // slots in expert order; within an expert, tokens ascending
+        MoeGather g{};
+        MoeCombine c{};
+        std::vector<int> first(E + 1, 0);
+        for (int i = 0; i < T * K; ++i) ++first[route[i] + 1];
+        for (int e = 0; e < E; ++e) first[e + 1] += first[e];
+        std::vector<int> next(first.begin(), first.end() - 1);
+        for (int t = 0; t < T; ++t)
+            for (int k = 0; k < K; ++k) {
+                const int e = route[t * K + k];
+                const int slot = next[e]++;
+                g.src[slot] = (int16_t)t;
+                c.slot[t * K + k] = (int16_t)slot;
+                c.gate[t * K + k] = gate[t * K + k];
+            }
+        for (int e = 0; e < E; ++e) {
+            if (first[e + 1] == first[e]) continue;
+            if (!W1[e] || !W3[e] || !W2T[e])
+                return fail(h, SFFN_INVALID_ARGUMENT, "null weight pointer of a routed expert");
+            if (!aligned16(W1[e]) || !aligned16(W3[e]) || !aligned16(W2T[e]))
+                return fail(h, SFFN_INVALID_ARGUMENT, "expert weights must be 16-byte aligned");
+        }
+        st = launch(h, KIND_MOE_GATHER, k_moe_gather, dim3(T * K), dim3(256), s,
+                    (const uint16_t*)x, h->moe_x, h->D, g);
+        if (st != SFFN_OK) return st;
+        for (int e = 0; e < E; ++e) {
+            const int n = first[e + 1] - first[e];
+            if (n == 0) continue;
+            const uint16_t* xe = h->moe_x + (size_t)first[e] * h->D;
+            float* ye = h->moe_y + (size_t)first[e] * h->D;
+            st = dense ? dispatch_dense(h, xe, W1[e], W3[e], W2T[e], ye, n, s)
+                       : dispatch_sparse(h, xe, W1[e], W3[e], W2T[e], ye, n, SFFN_MODE_UNION,
+                                         nullptr, nullptr, s);
+            if (st != SFFN_OK) return st;
+        }
+        return launch(h, KIND_MOE_COMBINE, k_moe_combine, dim3(T), dim3(256), s,
+                      (const float*)h->moe_y, y, h->D, K, c);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_moe");
     }
 }
 
@@ -800,24 +907,7 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
             return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
         if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
-        if (T == 0) return SFFN_OK;
-        if (t1_ok(h, T)) return run_sparse_t1(h, x, W1, W3, W2T, y, live_count, live_idx, s);
-        if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1)) {
-            // per-token lists: every token runs the whole batch-1 pass on its own live set
-            const size_t xb = (size_t)h->D * sizeof(uint16_t);
-            for (int t = 0; t < T; ++t) {
-                st = run_sparse_t1(h, (const char*)x + t * xb, W1, W3, W2T, y + (size_t)t * h->D,
-                                   live_count ? live_count + t : nullptr,
-                                   live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
-                if (st != SFFN_OK) return st;
-            }
-            return SFFN_OK;
-        }
-        if (mode == SFFN_MODE_UNION && mfma_ok(h, T))
-            return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
-        return h->dtype == SFFN_BF16
-                   ? run_sparse<uint16_t>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s)
-                   : run_sparse<float>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
+        return dispatch_sparse(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
     } catch (...) {
         return fail(h, SFFN_INTERNAL, "exception in sffn_forward_sparse");
     }

@@ -2022,6 +2022,40 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
     }
 }
 
+// ---------------------------------------------------------------------------
+// Sparse expert FFNs in a top-K mixture of experts (page "Model casting:
+// compute the gate, then skip most of the FFN", section "Where it
+// generalizes": the same gate-first skip applied to each expert's FFN). The
+// tokens routed to one expert are gathered into a contiguous batch, the
+// expert's FFN runs on it, and y_t = sum_k gate_{t,k} * y_slot(t,k) in k order.
+// The routing tables travel by value in the kernel arguments.
+constexpr int MOE_MAX_SLOTS = 128;  // T * K <= 64 * 2
+struct MoeGather { int16_t src[MOE_MAX_SLOTS]; };                 // token of each slot
+struct MoeCombine { int16_t slot[MOE_MAX_SLOTS]; float gate[MOE_MAX_SLOTS]; };  // [t * K + k]
+
+// x_g[slot] = x[src[slot]]: one block per slot, 16-byte copies
+__global__ __launch_bounds__(256) void k_moe_gather(const uint16_t* __restrict__ x,
+                                                    uint16_t* __restrict__ x_g, int D,
+                                                    MoeGather g) {
+    const int slot = blockIdx.x;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (size_t)g.src[slot] * D);
+    u32x4* dst = reinterpret_cast<u32x4*>(x_g + (size_t)slot * D);
+    for (int i = threadIdx.x; i < D / 8; i += 256) dst[i] = src[i];
+}
+
+// y[t] = sum_k gate[t, k] * y_g[slot[t, k]], k ascending: one block per token
+__global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y_g,
+                                                     float* __restrict__ y, int D, int K,
+                                                     MoeCombine c) {
+    const int t = blockIdx.x;
+    for (int j = threadIdx.x; j < D; j += 256) {
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k)
+            acc = fmaf(c.gate[t * K + k], y_g[(size_t)c.slot[t * K + k] * D + j], acc);
+        y[(size_t)t * D + j] = acc;
+    }
+}
+
 // Ascending live lists from the live flags: one block per token.
 __global__ __launch_bounds__(1024) void k_live_list(const uint8_t* __restrict__ live, int H,
                                                     int32_t* __restrict__ count,

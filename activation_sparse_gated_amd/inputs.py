@@ -119,6 +119,19 @@ def standard_weights_int8(D: int, H: int, sparsity: float | None, cfg: int, laye
     return out
 
 
+S_ROUTE = 6
+
+
+def moe_routing(T: int, E: int, K: int, cfg: int, layer: int = 0) -> tuple[np.ndarray, np.ndarray]:
+    """Synthetic top-K routing: K distinct experts per token, uniform, and positive gate
+    weights that sum to 1 per token (fp32). Returns route int32 [T, K], gate fp32 [T, K]."""
+    g = rng(cfg, layer, 0, S_ROUTE)
+    route = np.stack([g.permutation(E)[:K] for _ in range(T)]).astype(np.int32)
+    w = g.random((T, K)) + 0.1
+    gate = (w / w.sum(axis=1, keepdims=True)).astype(np.float32)
+    return route, gate
+
+
 def lopa_weights(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, layer: int = 0,
                  replica: int = 0, dtype: str = "bf16", offset: float | None = None) -> dict:
     """V [r, D], U [Hp, r], W3 [Hp, D], W2T [Hp, D] with fan-in scaled variances."""

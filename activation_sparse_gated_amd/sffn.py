@@ -29,7 +29,7 @@ EXPORTED = (
     "sffn_create", "sffn_destroy", "sffn_forward_dense", "sffn_forward_sparse",
     "sffn_forward_lopa", "sffn_last_error", "sffn_status_string", "sffn_abi_version",
     "sffn_timing_enable", "sffn_timing_read", "sffn_kernel_kinds", "sffn_kernel_name",
-    "sffn_forward_sparse_i8", "sffn_forward_dense_i8",
+    "sffn_forward_sparse_i8", "sffn_forward_dense_i8", "sffn_forward_moe",
 )
 
 _lib = None
@@ -70,6 +70,9 @@ def load() -> ctypes.CDLL:
     lib.sffn_forward_sparse_i8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_dense_i8.restype = I
     lib.sffn_forward_dense_i8.argtypes = [P, P, P, P, P, P, P, P, P, I, P]
+    lib.sffn_forward_moe.restype = I
+    lib.sffn_forward_moe.argtypes = [P, P, I, PP, PP, PP, I, ctypes.POINTER(ctypes.c_int32),
+                                     ctypes.POINTER(ctypes.c_float), P, I, I, P]
     lib.sffn_last_error.restype = ctypes.c_char_p
     lib.sffn_last_error.argtypes = [P]
     lib.sffn_status_string.restype = ctypes.c_char_p
@@ -186,6 +189,25 @@ def sffn_forward_dense_i8(handle, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale,
     st = load().sffn_forward_dense_i8(handle, _ptr(x), _ptr(W1), _ptr(W1_scale), _ptr(W3),
                                       _ptr(W3_scale), _ptr(W2T), _ptr(W2T_scale), _ptr(y), T,
                                       _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_moe(handle, x, W1s, W3s, W2Ts, route, gate, y, T: int, dense: bool = False,
+                     stream=None, check: bool = True) -> int:
+    """W1s/W3s/W2Ts: sequences of E device tensors (or addresses); route [T, K] int32 and
+    gate [T, K] float32 are host arrays."""
+    import numpy as np
+    E = len(W1s)
+    route = np.ascontiguousarray(route, dtype=np.int32)
+    gate = np.ascontiguousarray(gate, dtype=np.float32)
+    K = route.shape[1] if route.ndim == 2 else 1
+    arr = lambda ts: (ctypes.c_void_p * E)(*[_ptr(t) for t in ts])
+    st = load().sffn_forward_moe(handle, _ptr(x), E, arr(W1s), arr(W3s), arr(W2Ts), K,
+                                 route.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                                 gate.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), _ptr(y), T,
+                                 int(bool(dense)), _stream(stream))
     if check:
         _check(st, handle)
     return st

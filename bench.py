@@ -183,6 +183,52 @@ def bench_batched(torch, sffn, gen, to_dev, x1, reps, D, H, act, args):
     return out
 
 
+def bench_moe(torch, sffn, gen, to_dev, act, args):
+    """A synthetic top-2 mixture of 8 sparse experts of the decode shape (D=2560, H=7168,
+    s=0.9; 880 MB of expert weights), 64 tokens per call, 16 routings per replay."""
+    D, H, E, K, T, calls = 2560, 7168, 8, 2, 64, 16
+    ex = [gen.standard_weights(D, H, 0.9, cfg=6, replica=e, dtype="bf16") for e in range(E)]
+    W = [{k: to_dev(w[k]) for k in ("W1", "W3", "W2T")} for w in ex]
+    del ex
+    xs = to_dev(gen.tokens(D, T * calls, cfg=6, dtype="bf16"))
+    routes = [gen.moe_routing(T, E, K, cfg=6, layer=c) for c in range(calls)]
+    h = sffn.Handle(D, H, 0, T, act, sffn.SFFN_BF16)
+    y = torch.zeros(T * calls, D, dtype=torch.float32, device="cuda")
+    # union of live sets of each (call, expert): bytes each expert's weights contribute
+    cnt = torch.zeros(T, dtype=torch.int32, device="cuda")
+    idx = torch.zeros(T, H, dtype=torch.int32, device="cuda")
+    ybuf = torch.zeros(T, D, dtype=torch.float32, device="cuda")
+    byts = 0
+    for c, (route, _) in enumerate(routes):
+        for e in range(E):
+            toks = np.flatnonzero((route == e).any(axis=1))
+            if toks.size == 0:
+                continue
+            xe = xs[c * T:(c + 1) * T][torch.from_numpy(toks).cuda()].contiguous()
+            sffn.sffn_forward_sparse(h.ptr, xe, W[e]["W1"], W[e]["W3"], W[e]["W2T"], ybuf, int(toks.size),
+                                     sffn.SFFN_MODE_UNION, cnt, idx)
+            torch.cuda.synchronize()
+            cc = cnt.cpu().numpy()
+            ii = idx.cpu().numpy()
+            u = len(set(np.concatenate([ii[t, :cc[t]] for t in range(toks.size)]).tolist()))
+            byts += 2 * (H * D + 2 * u * D)
+    out = {}
+    for name, dense in (("sparse", False), ("dense", True)):
+        def fn():
+            for c, (route, gate) in enumerate(routes):
+                sffn.sffn_forward_moe(h.ptr, xs[c * T:(c + 1) * T], [w["W1"] for w in W],
+                                      [w["W3"] for w in W], [w["W2T"] for w in W], route, gate,
+                                      y[c * T:(c + 1) * T], T, dense=dense)
+        ms = _graph_time(torch, fn, max(2, args.steps // 4), 1)
+        out[name + "_tokens_per_s"] = round(calls * T / (ms * 1e-3), 1)
+        if not dense:
+            out["sparse_touched_GBps"] = round(byts / (ms * 1e-3) / 1e9, 1)
+    out["sparse_vs_dense"] = round(out["sparse_tokens_per_s"] / out["dense_tokens_per_s"], 3)
+    log("moe: " + ", ".join(f"{k} {v:,}" for k, v in out.items()))
+    h.close()
+    return out
+
+
 def bench_stacks(torch, sffn, gen, to_dev, act, args):
     """32-layer stacks at s = 0.895, batch-1 decode of 256 tokens through all layers.
     The 32 layers are byte-identical copies of one generated layer at distinct addresses
@@ -536,6 +582,17 @@ def main() -> int:
                 bytes_q = np.full(n, 3 * H * D + 12 * H + 6 * D)
             res_q[name + "_tokens_per_s"] = round(n / (ms_q * 1e-3), 1)
             res_q[name + "_touched_GBps"] = round(float(np.sum(bytes_q)) / (ms_q * 1e-3) / 1e9, 1)
+        # per-kernel durations of the int8 sparse stream
+        sffn.sffn_timing_enable(hq.ptr, True)
+        q8_stream(False)()
+        torch.cuda.synchronize()
+        sffn.sffn_timing_enable(hq.ptr, False)
+        ktq = {}
+        for kd in range(sffn.sffn_kernel_kinds()):
+            ms, launches = sffn.sffn_timing_read(hq.ptr, kd, reset=True)
+            if launches:
+                ktq[sffn.sffn_kernel_name(kd)] = round(ms * 1e3 / launches, 3)
+        res_q["kernel_us"] = ktq
         res_q["measured_sparsity"] = round(float(1 - kq.mean() / H), 4)
         res_q["sparse_vs_dense_int8"] = round(res_q["sparse_tokens_per_s"] / res_q["dense_tokens_per_s"], 3)
         res_q["sparse_vs_dense_bf16"] = round(res_q["sparse_tokens_per_s"] / extras["dense_tokens_per_s"], 3)
@@ -548,6 +605,7 @@ def main() -> int:
     if not args.no_extras:
         extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
         extras["stacks"] = bench_stacks(torch, sffn, gen, to_dev, act, args)
+        extras["moe_top2_8x"] = bench_moe(torch, sffn, gen, to_dev, act, args)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

@@ -171,6 +171,28 @@ sffn_status sffn_forward_dense_i8(sffn_handle *h, const void *x, const void *W1,
                                   const void *W2T, const float *W2T_scale, float *y, int T,
                                   void *stream);
 
+/*
+ * Sparse expert FFNs inside a top-K mixture of experts (K = 1 or 2), the
+ * generalisation named in section "Where it generalizes" of page "Model
+ * casting: compute the gate, then skip most of the FFN": every expert is a
+ * gate-first sparse FFN of the handle's shape (bf16, standard gating), and
+ *   y[t] = sum_k gate[t*K + k] * FFN_{route[t*K + k]}(x[t])   (k ascending).
+ *   E              number of experts (1..1024)
+ *   W1, W3, W2T    HOST arrays of E device pointers: expert e's weights, each
+ *                  [H x D] bf16, 16-byte aligned (only routed experts are read)
+ *   route, gate    HOST arrays [T x K]: expert index in [0, E) and weight of
+ *                  each (token, k); read during the call only
+ *   dense          0: each expert runs the sparse forward over the tokens routed
+ *                  to it as one batch in union mode; 1: the dense comparator
+ * x bf16 [T x D], y fp32 [T x D] (overwritten); T <= max_tokens. Uses the
+ * handle's scratch, so calls on one handle must not overlap. Errors as for
+ * the other forward calls (a route entry outside [0, E): INVALID_ARGUMENT).
+ */
+sffn_status sffn_forward_moe(sffn_handle *h, const void *x, int E, const void *const *W1,
+                             const void *const *W3, const void *const *W2T, int K,
+                             const int32_t *route, const float *gate, float *y, int T, int dense,
+                             void *stream);
+
 /* Message of the last failure on this handle; with NULL, the calling thread's
  * last failure that had no handle (e.g. in sffn_create). Never NULL. */
 const char *sffn_last_error(const sffn_handle *h);

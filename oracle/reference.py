@@ -212,3 +212,20 @@ def ffn_standard_int8(x, w, act: int = ACT_RELU, dense: bool = False):
     xf = xf.astype(np.float64)
     return ffn_standard(xf, *(dequantize_rows(w[k], w[k + "_scale"]) for k in ("W1", "W3", "W2T")),
                         act=act, dense=dense)
+
+
+def ffn_moe(x, experts, route, gate, act: int = ACT_RELU):
+    """Top-K mixture of sparse FFN experts (page "Model casting: ...", section "Where it
+    generalizes"): y_t = sum_k gate[t, k] * FFN_{route[t, k]}(x_t), k ascending, in fp64.
+    experts: list of dicts with W1, W3, W2T."""
+    x2 = np.atleast_2d(np.asarray(x))
+    route = np.atleast_2d(np.asarray(route))
+    gate = np.atleast_2d(np.asarray(gate, np.float64))
+    T, D = x2.shape
+    y = np.zeros((T, D), np.float64)
+    for t in range(T):
+        for k in range(route.shape[1]):
+            w = experts[int(route[t, k])]
+            o = ffn_standard(x2[t:t + 1], w["W1"], w["W3"], w["W2T"], act=act)
+            y[t] += float(np.float32(gate[t, k])) * o["y"][0]
+    return y
