@@ -588,8 +588,9 @@ def main() -> int:
         torch.cuda.synchronize()
         sffn.sffn_timing_enable(hq.ptr, False)
         ktq = {}
-        for kd in range(sffn.sffn_kernel_kinds()):
-            ms, launches = sffn.sffn_timing_read(hq.ptr, kd, reset=True)
+        nk = sffn.sffn_kernel_kinds()
+        for kd in range(nk):
+            ms, launches = sffn.sffn_timing_read(hq.ptr, kd, reset=(kd == nk - 1))
             if launches:
                 ktq[sffn.sffn_kernel_name(kd)] = round(ms * 1e3 / launches, 3)
         res_q["kernel_us"] = ktq
@@ -597,7 +598,8 @@ def main() -> int:
         res_q["sparse_vs_dense_int8"] = round(res_q["sparse_tokens_per_s"] / res_q["dense_tokens_per_s"], 3)
         res_q["sparse_vs_dense_bf16"] = round(res_q["sparse_tokens_per_s"] / extras["dense_tokens_per_s"], 3)
         extras["int8"] = res_q
-        log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items()))
+        log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items() if not isinstance(v, dict))
+            + f", kernels (us/launch) {ktq}")
         hq.close()
         del repq, WQ
 

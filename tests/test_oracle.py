@@ -359,6 +359,63 @@ def test_int8_weights_are_rows_times_scales():
         assert got["live"][t].tolist() == live
 
 
+def test_moe_exact_on_integers():
+    """Top-K mixture (page "Model casting: ...", section "Where it generalizes"): y_t is the
+    gate-weighted sum of the routed experts' FFN outputs, checked with exact rationals on
+    small integers and dyadic gates, K = 1 and 2, with an expert no token uses."""
+    D, H, E, T = 6, 10, 4, 5
+    experts = []
+    for e in range(E):
+        _, W1, W3, W2T = int_case(D, H, 1, 40 + e)
+        experts.append({"W1": W1, "W3": W3, "W2T": W2T})
+    x = int_case(D, H, T, 50)[0]
+    xf = gen.as_float(x).astype(np.float64)
+    route2 = np.array([[0, 2], [2, 0], [1, 2], [0, 1], [2, 1]], np.int32)   # expert 3 unused
+    gate2 = np.array([[0.75, 0.25], [0.5, 0.5], [1.0, 0.125], [0.375, 0.625], [0.25, 0.0]],
+                     np.float32)
+    for route, gate in ((route2, gate2), (route2[:, :1], np.ones((T, 1), np.float32))):
+        got = ref.ffn_moe(x, experts, route, gate)
+        for t in range(T):
+            want = [Fraction(0)] * D
+            for k in range(route.shape[1]):
+                w = experts[int(route[t, k])]
+                yk, _, _ = frac_ffn([int(v) for v in xf[t]],
+                                    *(gen.as_float(w[m]).astype(int).tolist()
+                                      for m in ("W1", "W3", "W2T")))
+                want = [a + Fraction(float(gate[t, k])) * b for a, b in zip(want, yk)]
+            assert [Fraction(v) for v in got[t]] == want
+
+
+def test_moe_invariants():
+    """Relabelling the experts (and the routing with them) leaves y unchanged; with every
+    expert the same FFN and gates summing to one, y is that FFN's output."""
+    D, H, E, T, K = 32, 48, 5, 7, 2
+    experts = [gen.standard_weights(D, H, 0.8, cfg=60, replica=e, dtype="bf16") for e in range(E)]
+    x = gen.tokens(D, T, cfg=60, dtype="bf16")
+    route, gate = gen.moe_routing(T, E, K, cfg=60)
+    base = ref.ffn_moe(x, experts, route, gate)
+    perm = np.array([3, 0, 4, 1, 2])                      # new label of expert e is perm[e]
+    relabelled = [None] * E
+    for e in range(E):
+        relabelled[perm[e]] = experts[e]
+    np.testing.assert_array_equal(ref.ffn_moe(x, relabelled, perm[route], gate), base)
+    same = [experts[0]] * E
+    one = ref.ffn_standard(x, experts[0]["W1"], experts[0]["W3"], experts[0]["W2T"])["y"]
+    g = np.full((T, K), 0.5, np.float32)
+    np.testing.assert_allclose(ref.ffn_moe(x, same, route, g), one, rtol=1e-13, atol=1e-13)
+    # route order within a token only reorders the two terms of the sum
+    np.testing.assert_allclose(ref.ffn_moe(x, experts, route[:, ::-1], gate[:, ::-1]), base,
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_moe_routing_recipe():
+    route, gate = gen.moe_routing(200, 8, 2, cfg=61)
+    assert route.dtype == np.int32 and gate.dtype == np.float32 and route.shape == (200, 2)
+    assert ((route >= 0) & (route < 8)).all() and (route[:, 0] != route[:, 1]).all()
+    assert (gate > 0).all() and np.allclose(gate.sum(axis=1), 1.0, atol=1e-6)
+    assert len(np.unique(route)) == 8
+
+
 def test_dense_equals_sparse_bitwise():
     check_dense_equals_sparse()
 
