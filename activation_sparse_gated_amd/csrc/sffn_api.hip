@@ -24,7 +24,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
-            KIND_COUNT };
+            KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -32,7 +32,11 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_rank_proj_t1", "k_gate_up_lopa_t1",
                                             "k_gate_up_mfma", "k_down_mfma", "k_down_tb",
                                             "k_gate_up_t1_i8", "k_gate_up_dense_t1_i8",
-                                            "k_down_t1_i8", "k_moe_gather", "k_moe_combine"};
+                                            "k_down_t1_i8", "k_moe_gather", "k_moe_combine",
+                                            "k_gate_up_gemm", "k_union_list", "k_down_gemm"};
+
+// Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
+constexpr int MAXT_GEMM = 8192;
 
 thread_local std::string g_thread_error = "no error";
 
@@ -79,6 +83,14 @@ struct sffn_handle {
     int tb_max = 8;                // batches up to this size use the small-batch down pass
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
     uint64_t* m_mask = nullptr;    // [H] tokens for which each unit is live
+    // large batches as GEMMs on MFMA
+    int g_min_t = MAXT + 1;        // smallest batch that takes the GEMM path
+    int g_tp = 0;                  // padded token count of g_a (multiple of 256)
+    int g_splits = 0;              // unit-range splits of the down GEMM (0: chosen per call)
+    int g_wide_min = 200;          // gate tiles of 256 x 128 from this many tiles on
+    uint16_t* g_a = nullptr;       // [H x g_tp] bf16 unit products, unit-major
+    uint64_t* g_any = nullptr;     // [g_tp / 256 x 2 ceil(H / 128)] 64-unit live masks per token tile
+    int32_t* g_list = nullptr;     // [H + 32] units live for some token, then the count
 
     // instrumentation
     bool timing = false;
@@ -440,6 +452,59 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     return SFFN_OK;
 }
 
+// ---- large batches: gate/up GEMM, union list, gathered down GEMM
+bool gemm_ok(const sffn_handle* h, int T) {
+    return h->g_a != nullptr && T >= h->g_min_t && T <= h->max_tokens;
+}
+
+template <int TM, int UN, bool DENSE>
+sffn_status run_gate_gemm(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                          uint8_t* live, float* yz, int T, hipStream_t s) {
+    using G = GemmTile<TM, UN>;
+    const int ntt = (T + TM - 1) / TM;
+    const int nut = (h->H + UN - 1) / UN;
+    sffn_status st = launch(h, KIND_GATE_UP_GEMM, k_gate_up_gemm<TM, UN, DENSE>,
+                            dim3(nut * ntt), dim3(G::THREADS), s, (const uint16_t*)x,
+                            (const uint16_t*)W1, (const uint16_t*)W3, (const uint16_t*)h->m_zero,
+                            h->g_a, DENSE ? (uint64_t*)nullptr : h->g_any, live, yz, h->D, h->H,
+                            T, h->g_tp, h->act);
+    if (st != SFFN_OK || DENSE) return st;
+    int32_t* count = h->g_list + h->H + 32;
+    return launch(h, KIND_UNION_LIST, k_union_list, dim3(1), dim3(1024), s,
+                  (const uint64_t*)h->g_any, ntt, nut * (UN / 64), h->g_list, count);
+}
+
+template <bool DENSE>
+sffn_status run_gemm(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                     const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
+                     hipStream_t s) {
+    const int nmt = (T + KDG_TM - 1) / KDG_TM;
+    const int nnt = (h->D + KDG_NB - 1) / KDG_NB;
+    int splits = h->g_splits;
+    if (splits <= 0) {
+        // unit-range splits only while the output tiles alone leave CUs idle, and
+        // never below 8 chunks of units per split
+        splits = 1;
+        const int nch = (h->H + KDG_KC - 1) / KDG_KC;
+        while (nmt * nnt * splits < 256 && splits < 16 && nch / (2 * splits) >= 8) splits *= 2;
+    }
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    float* yz = splits > 1 ? y : nullptr;
+    int32_t* count = h->g_list + h->H + 32;
+    // 256 x 128 gate tiles once there are g_wide_min of them, else 256 x 64 (more blocks)
+    const bool wide = (long)((T + 255) / 256) * ((h->H + 127) / 128) >= h->g_wide_min;
+    sffn_status st = wide ? run_gate_gemm<256, 128, DENSE>(h, x, W1, W3, live, yz, T, s)
+                          : run_gate_gemm<256, 64, DENSE>(h, x, W1, W3, live, yz, T, s);
+    if (st != SFFN_OK) return st;
+    st = launch(h, KIND_DOWN_GEMM, k_down_gemm, dim3(nmt * nnt * splits), dim3(KDG_THREADS), s,
+                (const uint16_t*)h->g_a, DENSE ? (const int32_t*)nullptr : (const int32_t*)h->g_list,
+                (const int32_t*)count, (const uint16_t*)W2T, (const uint16_t*)h->m_zero, y, h->D,
+                h->H, T, h->g_tp, splits);
+    if (st != SFFN_OK) return st;
+    if (!DENSE) return run_live_list(h, T, live_count, live_idx, s);
+    return SFFN_OK;
+}
+
 template <typename WT>
 sffn_status run_sparse(sffn_handle* h, const void* x, const void* W1, const void* W3,
                        const void* W2T, float* y, int T, int mode, int32_t* live_count,
@@ -591,8 +656,12 @@ sffn_status dispatch_sparse(sffn_handle* h, const void* x, const void* W1, const
         }
         return SFFN_OK;
     }
-    if (mode == SFFN_MODE_UNION && mfma_ok(h, T))
+    if (mode == SFFN_MODE_UNION && gemm_ok(h, T))
+        return run_gemm<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
+    if (mode == SFFN_MODE_UNION && mfma_ok(h, T) && T <= MAXT)
         return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
+    if (T > MAXT)
+        return fail(h, SFFN_UNSUPPORTED, "no launch plan for this batch size and mode");
     return h->dtype == SFFN_BF16
                ? run_sparse<uint16_t>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s)
                : run_sparse<float>(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
@@ -602,7 +671,10 @@ sffn_status dispatch_dense(sffn_handle* h, const void* x, const void* W1, const 
                            const void* W2T, float* y, int T, hipStream_t s) {
     if (T == 0) return SFFN_OK;
     if (t1_ok(h, T)) return run_dense_t1(h, x, W1, W3, W2T, y, s);
-    if (mfma_ok(h, T)) return run_mfma<true>(h, x, W1, W3, W2T, y, T, nullptr, nullptr, s);
+    if (gemm_ok(h, T)) return run_gemm<true>(h, x, W1, W3, W2T, y, T, nullptr, nullptr, s);
+    if (mfma_ok(h, T) && T <= MAXT)
+        return run_mfma<true>(h, x, W1, W3, W2T, y, T, nullptr, nullptr, s);
+    if (T > MAXT) return fail(h, SFFN_UNSUPPORTED, "no launch plan for this batch size");
     return h->dtype == SFFN_BF16 ? run_dense<uint16_t>(h, x, W1, W3, W2T, y, T, s)
                                  : run_dense<float>(h, x, W1, W3, W2T, y, T, s);
 }
@@ -680,8 +752,11 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if (r != 0 && (r < 8 || r % 8 != 0 || r > rmax))
             return fail(nullptr, SFFN_INVALID_ARGUMENT,
                         "r must be 0 or a multiple of 8 in [8, 2048]");
-        if (max_tokens < 1 || max_tokens > MAXT)
-            return fail(nullptr, SFFN_INVALID_ARGUMENT, "max_tokens must be in [1, 64]");
+        const bool big_ok = dtype == SFFN_BF16 && r == 0;
+        if (max_tokens < 1 || max_tokens > (big_ok ? MAXT_GEMM : MAXT))
+            return fail(nullptr, SFFN_INVALID_ARGUMENT,
+                        big_ok ? "max_tokens must be in [1, 8192]"
+                               : "max_tokens must be in [1, 64] for this dtype and gate");
 
         sffn_handle* h = new (std::nothrow) sffn_handle();
         if (!h) return fail(nullptr, SFFN_OUT_OF_MEMORY, "host allocation failed");
@@ -693,7 +768,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             return fail(nullptr, SFFN_HIP_ERROR, std::string("hipGetDevice: ") + hipGetErrorString(e));
         }
         const size_t th = (size_t)max_tokens * (size_t)H;
-        e = hipMalloc(&h->a_buf, th * sizeof(float));
+        const size_t th_small = (size_t)std::min(max_tokens, MAXT) * (size_t)H;
+        e = hipMalloc(&h->a_buf, th_small * sizeof(float));
         if (e == hipSuccess) e = hipMalloc(&h->live_buf, th);
         if (e == hipSuccess && r > 0) e = hipMalloc(&h->t_buf, (size_t)max_tokens * r * sizeof(float));
         if (e != hipSuccess) {
@@ -778,8 +854,32 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
                 return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
             }
         }
+        if (dtype == SFFN_BF16 && r == 0 && h->m_zero) {
+            // large batches as GEMMs: bf16 unit products for up to g_tp tokens
+            int gmin = env_int("SFFN_GEMM_MIN_T", MAXT + 1);
+            if (gmin < 2) gmin = 2;
+            h->g_min_t = gmin;
+            const int gs = env_int("SFFN_GEMM_SPLITS", 0);
+            if (gs >= 1 && gs <= 64) h->g_splits = gs;
+            h->g_wide_min = env_int("SFFN_GEMM_WIDE_MIN", h->g_wide_min);
+            if (max_tokens >= gmin) {
+                h->g_tp = 256 * ((max_tokens + 255) / 256);
+                const int ntt = h->g_tp / 256;
+                e = hipMalloc(&h->g_a, (size_t)H * h->g_tp * sizeof(uint16_t));
+                // one 64-bit mask per 64 units of each gate tile (tiles of 64 or 128 units)
+                const size_t nm = 2 * (((size_t)H + 127) / 128);
+                if (e == hipSuccess) e = hipMalloc(&h->g_any, (size_t)ntt * nm * sizeof(uint64_t));
+                if (e == hipSuccess) e = hipMalloc(&h->g_list, ((size_t)H + 33) * sizeof(int32_t));
+                if (e == hipSuccess) e = hipMemset(h->g_list, 0, ((size_t)H + 33) * sizeof(int32_t));
+                if (e == hipSuccess) e = hipDeviceSynchronize();
+                if (e != hipSuccess) {
+                    sffn_destroy(h);
+                    return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
+                }
+            }
+        }
         if (dtype == SFFN_BF16 && r == 0) {
-            const size_t rows = 2 * (size_t)max_tokens;
+            const size_t rows = 2 * (size_t)std::min(max_tokens, MAXT);
             e = hipMalloc(&h->moe_x, rows * D * sizeof(uint16_t));
             if (e == hipSuccess) e = hipMalloc(&h->moe_y, rows * D * sizeof(float));
             if (e != hipSuccess) {
@@ -810,6 +910,9 @@ void sffn_destroy(sffn_handle* h) {
     if (h->m_zero) (void)hipFree(h->m_zero);
     if (h->moe_x) (void)hipFree(h->moe_x);
     if (h->moe_y) (void)hipFree(h->moe_y);
+    if (h->g_a) (void)hipFree(h->g_a);
+    if (h->g_any) (void)hipFree(h->g_any);
+    if (h->g_list) (void)hipFree(h->g_list);
 
     delete h;
 }
@@ -848,6 +951,8 @@ sffn_status sffn_forward_moe(sffn_handle* h, const void* x, int E, const void* c
         sffn_status st = check_common(h, x, h->moe_x, h->moe_y, y, T, nullptr, nullptr, &s, stream);
         if (st != SFFN_OK) return st;
         if (T == 0) return SFFN_OK;
+        if (T * K > MOE_MAX_SLOTS)
+            return fail(h, SFFN_INVALID_ARGUMENT, "T * K must be at most 128");
         for (int i = 0; i < T * K; ++i)
             if (route[i] < 0 || route[i] >= E)
                 return fail(h, SFFN_INVALID_ARGUMENT, "route entry outside [0, E)");

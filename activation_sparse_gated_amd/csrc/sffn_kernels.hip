@@ -2056,6 +2056,416 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large batches (prefill, T > 64): the FFN as three MFMA contractions. At this
+// size the union of the tokens' live sets covers nearly every unit (1 - s^T),
+// so the gate and the up projection run as one GEMM over all units, and the
+// down projection is a GEMM whose reduction runs over the gathered list of
+// units that are live for some token (the page on model casting notes in
+// "Checking the three claims" that batching erodes the skip).
+//
+//   k_gate_up_gemm  z = X W1^T and u = X W3^T for a tile of 256 tokens x 128
+//                   units (both weight rows of each unit in the tile), then
+//                   a = A(z) * u rounded to bf16, stored unit-major
+//                   a_um[unit][token], and a 64-bit mask of the tile's units
+//                   that are live for some token of the tile.
+//   k_union_list    ascending list of the units live for some token.
+//   k_down_gemm     y = a W2 over the listed units: 128 tokens x 128 columns
+//                   per block, split over unit ranges when the tiles alone do
+//                   not fill the chip (fp32 atomics then; y cleared by the gate).
+//
+// Operands go from global memory straight into LDS rings (global_load_lds,
+// 16 B per lane). The gate kernel's operands are K-contiguous rows (X, W1,
+// W3), read as MFMA fragments with 16-byte LDS reads. The down kernel stages
+// K-rows of both operands (a_um rows of 128 tokens and W2T rows of 128
+// columns, one row per listed unit) and reads the fragments with the
+// transposing LDS read ds_read_b64_tr_b16: in each group of 16 lanes, lane l
+// receives element l%4 of the 4 consecutive bf16 that lane 4j + l/4 points at,
+// as its element j (checked on the device), so two reads give a lane the 8
+// consecutive K values of one row or column of the tile.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Gate/up tile: TM tokens x UN units, one wave per 64 x 64 sub-tile (z and u).
+template <int TM, int UN>
+struct GemmTile {
+    static_assert(TM % 64 == 0 && UN % 64 == 0, "64 x 64 wave tiles");
+    static constexpr int WAVES = (TM / 64) * (UN / 64);
+    static constexpr int THREADS = WAVES * WAVE;
+    static constexpr int KC = 32;                 // columns per chunk: rows of 64 B
+    static constexpr int ROWS = TM + 2 * UN;      // staged rows: X, then W1, then W3
+    static constexpr int STAGE = ROWS * 64;
+    static constexpr int NS = 4;                  // LDS stages
+    static constexpr int IPW = STAGE / 1024 / WAVES;  // wave load instructions per wave per chunk
+    static_assert(STAGE % (1024 * WAVES) == 0, "whole wave loads per wave");
+    static_assert(NS * STAGE <= 131072, "LDS ring");
+};
+constexpr int KG_UN_MIN = 64;  // the smallest unit tile (masks of the union list are per 64 units)
+
+// Slot of 16-byte piece p in staged 64-byte row r: the 16 rows read by one
+// fragment instruction fall on 16 different (row mod 4, slot) pairs, i.e.
+// cover one 256-byte bank window once.
+__device__ inline int swz64(int r, int p) { return p ^ ((r >> 2) & 3); }
+
+// Map a linear block id to a work item so that each XCD (block id mod 8)
+// receives a contiguous range of work items.
+__device__ inline int xcd_work_item(int b, int nblocks) {
+    const int x = b & 7, j = b >> 3;
+    const int per = nblocks >> 3, rem = nblocks & 7;
+    return x * per + (x < rem ? x : rem) + j;
+}
+
+template <int TM, int UN, bool DENSE>
+__global__ __launch_bounds__((TM / 64) * (UN / 64) * WAVE) void k_gate_up_gemm(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, const uint16_t* __restrict__ zeros,
+    uint16_t* __restrict__ a_um, uint64_t* __restrict__ any_out, uint8_t* __restrict__ live_out,
+    float* __restrict__ y_zero, int D, int H, int T, int TP, int act) {
+    using G = GemmTile<TM, UN>;
+    constexpr int KG_TM = TM, KG_UN = UN, KG_KC = G::KC, KG_NS = G::NS, KG_IPW = G::IPW;
+    constexpr int KG_STAGE = G::STAGE, KG_THREADS = G::THREADS;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[KG_NS * KG_STAGE];
+    __shared__ uint32_t umask[KG_UN / 16];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int tw = wave % (TM / 64), uw = wave / (TM / 64);  // wave tile: tokens 64 tw .., units 64 uw ..
+    const int ntt = (T + KG_TM - 1) / KG_TM;
+    const int nut = (H + KG_UN - 1) / KG_UN;
+    const int wi = xcd_work_item(blockIdx.x, nut * ntt);
+    const int ut0 = wi / ntt, tt0 = wi % ntt;
+    const int u0 = ut0 * KG_UN, tok0 = tt0 * KG_TM;
+
+    if (y_zero) {
+        for (size_t j = (size_t)blockIdx.x * KG_THREADS + threadIdx.x; j < (size_t)T * D;
+             j += (size_t)gridDim.x * KG_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    if (threadIdx.x < KG_UN / 16) umask[threadIdx.x] = 0u;
+
+    // sources of this lane's pieces: row and piece are the same for every chunk
+    const uint16_t* src[KG_IPW];
+    bool rok[KG_IPW];
+    int pcol[KG_IPW];
+#pragma unroll
+    for (int i = 0; i < KG_IPW; ++i) {
+        const int r = 16 * (wave * KG_IPW + i) + (lane >> 2);
+        const int p = swz64(r, lane & 3);
+        pcol[i] = 8 * p;
+        if (r < KG_TM) {
+            const int t = tok0 + r;
+            rok[i] = t < T;
+            src[i] = x + (rok[i] ? (size_t)t * D + 8 * p : 0);
+        } else {
+            const int u = u0 + (r - KG_TM) % KG_UN;
+            const uint16_t* W = (r < KG_TM + KG_UN) ? W1 : W3;
+            rok[i] = u < H;
+            src[i] = W + (rok[i] ? (size_t)u * D + 8 * p : 0);
+        }
+    }
+    auto issue = [&](int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < KG_IPW; ++i) {
+            const bool ok = rok[i] && c * KG_KC + pcol[i] < D;
+            const uint16_t* gp = ok ? src[i] + (size_t)c * KG_KC : zeros;
+            load_lds16(gp, ring + stage * KG_STAGE + 1024 * (wave * KG_IPW + i));
+        }
+    };
+
+    f32x4 accz[4][4], accu[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            accz[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accu[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+    auto compute = [&](int stage) {
+        const uint8_t* st = ring + stage * KG_STAGE;
+        u32x4 xf[4], w1f[4], w3f[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rx = 64 * tw + 16 * i + r16;
+            const int r1 = KG_TM + 64 * uw + 16 * i + r16;
+            const int r3 = KG_TM + KG_UN + 64 * uw + 16 * i + r16;
+            xf[i] = *reinterpret_cast<const u32x4*>(st + rx * 64 + 16 * swz64(rx, g));
+            w1f[i] = *reinterpret_cast<const u32x4*>(st + r1 * 64 + 16 * swz64(r1, g));
+            w3f[i] = *reinterpret_cast<const u32x4*>(st + r3 * 64 + 16 * swz64(r3, g));
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                accz[a][b] = mfma_bf16(xf[a], w1f[b], accz[a][b]);
+                accu[a][b] = mfma_bf16(xf[a], w3f[b], accu[a][b]);
+            }
+    };
+
+    const int nchunks = (D + KG_KC - 1) / KG_KC;
+#pragma unroll
+    for (int d = 0; d < KG_NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + KG_NS - 1) / KG_NS * KG_NS;
+    for (int c0 = 0; c0 < niter; c0 += KG_NS) {
+#pragma unroll
+        for (int d = 0; d < KG_NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((KG_NS - 2) * KG_IPW);  // this wave's pieces of chunk c have landed
+            __syncthreads();                     // ... and every wave's; chunk c - 1 is consumed
+            issue((d + KG_NS - 1) % KG_NS, c + KG_NS - 1);
+            if (c < nchunks) compute(d);
+        }
+    }
+    wait_vmcnt(0);
+
+    // epilogue: lane holds tokens 4g + j of each token tile, unit r16 of each unit tile
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const int u = u0 + 64 * uw + 16 * b + r16;
+        bool any = false;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const int t0 = tok0 + 64 * tw + 16 * a + 4 * g;
+            uint32_t packed[2];
+#pragma unroll
+            for (int j = 0; j < 4; j += 2) {
+                const float z0 = accz[a][b][j], z1 = accz[a][b][j + 1];
+                const float v0 = activation(act, z0) * accu[a][b][j];
+                const float v1 = activation(act, z1) * accu[a][b][j + 1];
+                packed[j / 2] = bf16_rne(v0) | (bf16_rne(v1) << 16);
+                any |= (t0 + j < T && z0 > 0.0f) || (t0 + j + 1 < T && z1 > 0.0f);
+            }
+            if (u < H && t0 < TP)
+                *reinterpret_cast<uint2*>(a_um + (size_t)u * TP + t0) = uint2{packed[0], packed[1]};
+            if (live_out && u < H) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (t0 + j < T) live_out[(size_t)(t0 + j) * H + u] = accz[a][b][j] > 0.0f ? 1 : 0;
+            }
+        }
+        if (!DENSE) {
+            const uint64_t m = __ballot(any);
+            const uint32_t m16 = (uint32_t)((m | (m >> 16) | (m >> 32) | (m >> 48)) & 0xFFFFull);
+            if (lane == 0 && m16) atomicOr(&umask[4 * uw + b], m16);
+        }
+    }
+    if (!DENSE) {
+        // one 64-bit mask per 64 units: [token tile][64-unit tile]
+        __syncthreads();
+        constexpr int NM = KG_UN / 64;
+        if (threadIdx.x < NM)
+            any_out[((size_t)tt0 * nut + ut0) * NM + threadIdx.x] =
+                (uint64_t)umask[4 * threadIdx.x] | ((uint64_t)umask[4 * threadIdx.x + 1] << 16) |
+                ((uint64_t)umask[4 * threadIdx.x + 2] << 32) |
+                ((uint64_t)umask[4 * threadIdx.x + 3] << 48);
+    }
+}
+
+// Ascending list of the units live for some token, from the masks of every
+// (token tile, unit tile): one block; each thread ORs one unit tile's masks over
+// the token tiles, a block scan of the popcounts places its units.
+__global__ __launch_bounds__(1024) void k_union_list(const uint64_t* __restrict__ any, int ntt,
+                                                     int nut, int32_t* __restrict__ list,
+                                                     int32_t* __restrict__ count) {
+    __shared__ int wsum[16];
+    __shared__ int base_s;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    if (threadIdx.x == 0) base_s = 0;
+    __syncthreads();
+    for (int j0 = 0; j0 < nut; j0 += 1024) {
+        const int j = j0 + threadIdx.x;
+        uint64_t m = 0;
+        if (j < nut) {
+            int t = 0;
+            for (; t + 4 <= ntt; t += 4) {
+                const uint64_t a0 = any[(size_t)t * nut + j], a1 = any[(size_t)(t + 1) * nut + j];
+                const uint64_t a2 = any[(size_t)(t + 2) * nut + j], a3 = any[(size_t)(t + 3) * nut + j];
+                m |= a0 | a1 | a2 | a3;
+            }
+            for (; t < ntt; ++t) m |= any[(size_t)t * nut + j];
+        }
+        const int c = __popcll(m);
+        // inclusive scan of c within the wave
+        int incl = c;
+#pragma unroll
+        for (int d = 1; d < WAVE; d <<= 1) {
+            const int v = __shfl_up(incl, d);
+            if (lane >= d) incl += v;
+        }
+        if (lane == WAVE - 1) wsum[wave] = incl;
+        __syncthreads();
+        int off = base_s, tot = 0;
+        for (int w = 0; w < 16; ++w) {
+            if (w < wave) off += wsum[w];
+            tot += wsum[w];
+        }
+        off += incl - c;
+        while (m) {
+            const int b = __builtin_ctzll(m);
+            list[off++] = 64 * j + b;
+            m &= m - 1;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) base_s += tot;
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *count = base_s;
+}
+
+constexpr int KDG_THREADS = 256;
+constexpr int KDG_TM = 128;                 // tokens per down block
+constexpr int KDG_NB = 128;                 // columns per down block
+constexpr int KDG_KC = 32;                  // listed units per chunk
+constexpr int KDG_STAGE = 2 * KDG_KC * 256; // a_um rows, then W2T rows: 16 KB
+constexpr int KDG_NS = 4;
+constexpr int KDG_SEG = 256;                  // list entries per staged segment (one wave load)
+constexpr int KDG_SEG_CH = KDG_SEG / KDG_KC;  // chunks per segment
+constexpr int KDG_IPW = KDG_STAGE / 1024 / 4;
+
+// Slot of 16-byte piece p in staged 256-byte K-row r (r < 32): a transposing
+// read touches rows 8g + {0..3} (or + {4..7}) at two adjacent pieces, which
+// land on 8 different slots; groups g and g + 1 use disjoint slot halves.
+__device__ inline int swz256(int r, int p) { return p ^ (2 * (r & 3) + 8 * ((r >> 3) & 1)); }
+
+__device__ inline u32x4 frag_tr(const uint8_t* part, int col0, int lane) {
+    typedef __attribute__((address_space(3))) i16x4* lds_v4;
+    const int g = lane >> 4, s = lane & 15;
+    const int col = col0 + 4 * (s & 3);
+    const int p = col >> 3, half = (col >> 2) & 1;
+    const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
+    const uint8_t* a0 = part + r0 * 256 + 16 * swz256(r0, p) + 8 * half;
+    const uint8_t* a1 = part + r1 * 256 + 16 * swz256(r1, p) + 8 * half;
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a0));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a1));
+    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+    return u32x4{w0.x, w0.y, w1.x, w1.y};
+}
+
+// y[T x D] (+)= sum over listed units k of a_um[k][t] W2T[k][:]. list == nullptr:
+// every unit 0..H-1. Grid: (token tiles x column tiles) x splits, XCD-contiguous.
+__global__ __launch_bounds__(KDG_THREADS) void k_down_gemm(
+    const uint16_t* __restrict__ a_um, const int32_t* __restrict__ list,
+    const int32_t* __restrict__ count_ptr, const uint16_t* __restrict__ W2T,
+    const uint16_t* __restrict__ zeros, float* __restrict__ y, int D, int H, int T, int TP,
+    int splits) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[KDG_NS * KDG_STAGE];
+    __shared__ __attribute__((aligned(16))) int32_t lseg[2][KDG_SEG];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15, g = lane >> 4;
+    const int nmt = (T + KDG_TM - 1) / KDG_TM;
+    const int nnt = (D + KDG_NB - 1) / KDG_NB;
+    const int wi = xcd_work_item(blockIdx.x, nmt * nnt * splits);
+    const int mt = wi % nmt, rest = wi / nmt;
+    const int nt = rest % nnt, split = rest / nnt;
+    const int tok0 = mt * KDG_TM, col0 = nt * KDG_NB;
+    const int count = list ? *count_ptr : H;
+    const int nch_all = (count + KDG_KC - 1) / KDG_KC;
+    const int per = (nch_all + splits - 1) / splits;
+    const int cbeg = split * per;
+    const int cend = min(nch_all, cbeg + per);
+    const int nchunks = cend > cbeg ? cend - cbeg : 0;
+
+    // Waves 0 and 1 stage the a_um rows of the chunk (rows 0-15 and 16-31),
+    // waves 2 and 3 the W2T rows; instruction i of a wave covers rows 4i .. 4i + 3
+    // of its 16, lane l row 4i + l / 16. The unit indices come from the list in
+    // segments of 256 entries (8 chunks) that wave 0 stages into LDS through the
+    // same ordered loads, one segment ahead: segment s is issued together with
+    // the pieces of chunk 8 (s - 1), so the wait that marks chunk 8s - NS + 1 as
+    // landed (before chunk 8s is issued) also covers it.
+    static_assert(KDG_IPW == 4 && KDG_KC == 32, "staging plan: 4 waves x 4 instructions");
+    static_assert(KDG_NS <= KDG_SEG_CH + 1, "list segments must land before they are read");
+    const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool stage_a = wave_u < 2;
+    const int rhalf = 16 * (wave_u & 1);
+    int pof[KDG_IPW];
+    bool cok[KDG_IPW];
+#pragma unroll
+    for (int i = 0; i < KDG_IPW; ++i) {
+        const int r = rhalf + 4 * i + g;
+        pof[i] = 8 * swz256(r, lane & 15);
+        cok[i] = stage_a || col0 + pof[i] < D;
+    }
+    const uint16_t* base = stage_a ? a_um + tok0 : W2T + col0;
+    const size_t rstride = stage_a ? (size_t)TP : (size_t)D;
+    auto issue_seg = [&](int sg) {
+        if (!list || wave_u != 0) return;
+        const int pos = (cbeg + KDG_SEG_CH * sg) * KDG_KC + 4 * lane;
+        const bool ok = KDG_SEG_CH * sg < nchunks && pos < count;
+        load_lds16(ok ? (const void*)(list + pos) : (const void*)zeros, &lseg[sg & 1][0]);
+    };
+    auto issue = [&](int stage, int c) {
+        if (c % KDG_SEG_CH == 0) issue_seg(c / KDG_SEG_CH + 1);
+        const int k0 = (cbeg + c) * KDG_KC + rhalf;
+        const int* seg = &lseg[(c / KDG_SEG_CH) & 1][(c % KDG_SEG_CH) * KDG_KC + rhalf];
+#pragma unroll
+        for (int i = 0; i < KDG_IPW; ++i) {
+            const int k = k0 + 4 * i + g;
+            const bool ok = c < nchunks && k < count && cok[i];
+            const int unit = list ? seg[4 * i + g] : k;
+            const uint16_t* gp = ok ? base + (size_t)unit * rstride + pof[i] : zeros;
+            load_lds16(gp, ring + stage * KDG_STAGE + 1024 * (wave_u * KDG_IPW + i));
+        }
+    };
+
+    // wave tile: tokens 64 (wave / 2) .. + 64, columns 64 (wave % 2) .. + 64
+    const int wt0 = 64 * (wave >> 1), wc0 = 64 * (wave & 1);
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto compute = [&](int stage) {
+        const uint8_t* pa = ring + stage * KDG_STAGE;
+        const uint8_t* pb = pa + KDG_KC * 256;
+        u32x4 af[4], bfr[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[i] = frag_tr(pa, wt0 + 16 * i, lane);
+            bfr[i] = frag_tr(pb, wc0 + 16 * i, lane);
+        }
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = mfma_bf16(af[a], bfr[b], acc[a][b]);
+    };
+
+    issue_seg(0);
+    wait_vmcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < KDG_NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + KDG_NS - 1) / KDG_NS * KDG_NS;
+    for (int c0 = 0; c0 < niter; c0 += KDG_NS) {
+#pragma unroll
+        for (int d = 0; d < KDG_NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((KDG_NS - 2) * KDG_IPW);
+            __syncthreads();
+            issue((d + KDG_NS - 1) % KDG_NS, c + KDG_NS - 1);
+            if (c < nchunks) compute(d);
+        }
+    }
+    wait_vmcnt(0);
+    if (nchunks == 0 && splits > 1) return;  // nothing to add
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int n = col0 + wc0 + 16 * b + r16;
+            if (n >= D) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = tok0 + wt0 + 16 * a + 4 * g + j;
+                if (t >= T) continue;
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + n, acc[a][b][j]);
+                else
+                    y[(size_t)t * D + n] = acc[a][b][j];
+            }
+        }
+    }
+}
+
 // Ascending live lists from the live flags: one block per token.
 __global__ __launch_bounds__(1024) void k_live_list(const uint8_t* __restrict__ live, int H,
                                                     int32_t* __restrict__ count,

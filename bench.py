@@ -183,6 +183,88 @@ def bench_batched(torch, sffn, gen, to_dev, x1, reps, D, H, act, args):
     return out
 
 
+def bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args):
+    """Large batches (prefill) of T tokens in one call, D=2560, H=7168, s=0.9: the union
+    path and the dense comparator as MFMA GEMMs, their per-kernel durations, and the
+    same FFN as three hipBLASLt bf16 matmuls through torch for comparison."""
+    import torch.nn.functional as F
+    sizes = [int(v) for v in args.prefill_sizes.split(",") if v]
+    R = len(reps)
+    tmax = max(sizes)
+    h = sffn.Handle(D, H, 0, tmax, act, sffn.SFFN_BF16)
+    xb = to_dev(gen.tokens(D, tmax, cfg=5, dtype="bf16"))
+    y = torch.zeros(tmax, D, dtype=torch.float32, device="cuda")
+    peak = 2500.0  # TFLOP/s, dense bf16 MFMA
+    out = {}
+    for T in sizes:
+        calls = max(2, 4096 // T)
+        res = {"calls_per_replay": calls}
+        flops = 6.0 * H * D * T  # gate, up and down over every unit (the union is ~all units)
+        for name, dense in (("union", False), ("dense", True)):
+            def fn():
+                for c in range(calls):
+                    rp = reps[c % R]
+                    if dense:
+                        sffn.sffn_forward_dense(h.ptr, xb[:T], rp["W1"], rp["W3"], rp["W2T"], y[:T], T)
+                    else:
+                        sffn.sffn_forward_sparse(h.ptr, xb[:T], rp["W1"], rp["W3"], rp["W2T"], y[:T],
+                                                 T, sffn.SFFN_MODE_UNION)
+            ms = _graph_time(torch, fn, max(2, args.steps // 4), 1) / calls
+            res[name + "_tokens_per_s"] = round(T / (ms * 1e-3), 1)
+            res[name + "_TFLOPs"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        # per-kernel durations of the union path (events at kernel begin and end)
+        sffn.sffn_timing_enable(h.ptr, True)
+        for c in range(4):
+            rp = reps[c % R]
+            sffn.sffn_forward_sparse(h.ptr, xb[:T], rp["W1"], rp["W3"], rp["W2T"], y[:T], T,
+                                     sffn.SFFN_MODE_UNION)
+        torch.cuda.synchronize()
+        sffn.sffn_timing_enable(h.ptr, False)
+        kt = {}
+        nk = sffn.sffn_kernel_kinds()
+        for kd in range(nk):
+            ms_k, launches = sffn.sffn_timing_read(h.ptr, kd, reset=(kd == nk - 1))
+            if launches:
+                kt[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 2)
+        res["kernel_us"] = kt
+        if "k_gate_up_gemm" in kt:
+            res["gate_up_TFLOPs"] = round(4.0 * H * D * T / (kt["k_gate_up_gemm"] * 1e-6) / 1e12, 1)
+        if "k_down_gemm" in kt:
+            res["down_TFLOPs"] = round(2.0 * H * D * T / (kt["k_down_gemm"] * 1e-6) / 1e12, 1)
+        res["frac_of_mfma_peak"] = round(res["union_TFLOPs"] / peak, 4)
+        # the same FFN as torch bf16 matmuls (hipBLASLt), eager, same weights
+        xt = xb[:T].view(torch.bfloat16)
+        wt = [{k: rp[k].view(torch.bfloat16) for k in ("W1", "W3", "W2T")} for rp in reps[:2]]
+
+        def torch_ffn(wd):
+            z = F.linear(xt, wd["W1"])
+            u = F.linear(xt, wd["W3"])
+            a = (torch.where(z >= 0, F.silu(z), torch.zeros_like(z)) if act == sffn.SFFN_ACT_RSPLUS
+                 else torch.relu(z)) * u
+            return torch.matmul(a, wd["W2T"])
+        for i in range(3):
+            torch_ffn(wt[i % 2])
+        torch.cuda.synchronize()
+        n_t = max(4, calls)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(n_t):
+            torch_ffn(wt[i % 2])
+        e1.record()
+        torch.cuda.synchronize()
+        ms_t = e0.elapsed_time(e1) / n_t
+        res["torch_bf16_tokens_per_s"] = round(T / (ms_t * 1e-3), 1)
+        res["torch_bf16_TFLOPs"] = round(flops / (ms_t * 1e-3) / 1e12, 1)
+        res["union_vs_dense"] = round(res["union_tokens_per_s"] / res["dense_tokens_per_s"], 3)
+        res["union_vs_torch"] = round(res["union_tokens_per_s"] / res["torch_bf16_tokens_per_s"], 3)
+        out[f"T{T}"] = res
+        log(f"prefill T={T}: " + ", ".join(f"{k} {v:,}" for k, v in res.items() if not isinstance(v, dict))
+            + f", kernels (us) {kt}")
+    h.close()
+    return out
+
+
 def bench_moe(torch, sffn, gen, to_dev, act, args):
     """A synthetic top-2 mixture of 8 sparse experts of the decode shape (D=2560, H=7168,
     s=0.9; 880 MB of expert weights), 64 tokens per call, 16 routings per replay."""
@@ -291,6 +373,9 @@ def main() -> int:
     ap.add_argument("--batched-sizes", default="1,4,16,64", help="token batch sizes T")
     ap.add_argument("--batched-modes", default="per_token,union,dense",
                     help="batched lines to run: per_token, union, dense")
+    ap.add_argument("--only-prefill", action="store_true",
+                    help="run only the large-batch (prefill) lines")
+    ap.add_argument("--prefill-sizes", default="256,1024,2048", help="large batch sizes T")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -329,6 +414,10 @@ def main() -> int:
     if args.only_batched:
         res = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
         print(json.dumps({"batched": res}), flush=True)
+        return 0
+    if args.only_prefill:
+        res = bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args)
+        print(json.dumps({"prefill": res}), flush=True)
         return 0
 
     # ---------------------------------------------------------------- streaming ceiling
@@ -608,6 +697,7 @@ def main() -> int:
         extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
         extras["stacks"] = bench_stacks(torch, sffn, gen, to_dev, act, args)
         extras["moe_top2_8x"] = bench_moe(torch, sffn, gen, to_dev, act, args)
+        extras["prefill"] = bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

@@ -40,7 +40,9 @@ def test_library_exports_every_declared_function():
     ((64, 64, 12, 1, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "r must"),
     ((64, 64, 4096, 1, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "r must"),
     ((64, 64, 0, 0, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
-    ((64, 64, 0, 65, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
+    ((64, 64, 0, 65, 0, 1), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
+    ((64, 64, 8, 65, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
+    ((64, 64, 0, 8193, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
     ((64, 64, 0, 1, 2, 0), sffn.SFFN_UNSUPPORTED, "activation"),
     ((64, 64, 0, 1, 0, 3), sffn.SFFN_UNSUPPORTED, "dtype"),
 ])
