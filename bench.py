@@ -91,7 +91,9 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command
     res = {}
     for d, counter in ((fetch_dir, "FETCH_SIZE"), (write_dir, "WRITE_SIZE")):
         vals = {name: (v, c) for name, cn, v, c in _rocpd_rows(d, q) if cn == counter}
-        calib = [v for name, (v, c) in vals.items() if "elementwise" in name and v * 1024 > CALIB_BYTES / 8]
+        # the calibration is the one scalar multiply of a float tensor (torch.mul(t, 1.0))
+        calib = [v for name, (v, c) in vals.items()
+                 if "AUnaryFunctor<float, float, float" in name and "MulFunctor" in name]
         kern = [v for name, (v, c) in vals.items() if kernel + "<" in name or kernel + "(" in name]
         if not calib or not kern:
             raise SystemExit(f"{counter}: calibration copy or {kernel} not found in {d}")
