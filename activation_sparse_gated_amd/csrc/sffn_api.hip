@@ -24,7 +24,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
-            KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_COUNT };
+            KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
+            KIND_GATE_UP_LOPA_T1_I8, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -33,7 +34,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_mfma", "k_down_mfma", "k_down_tb",
                                             "k_gate_up_t1_i8", "k_gate_up_dense_t1_i8",
                                             "k_down_t1_i8", "k_moe_gather", "k_moe_combine",
-                                            "k_gate_up_gemm", "k_union_list", "k_down_gemm"};
+                                            "k_gate_up_gemm", "k_union_list", "k_down_gemm",
+                                            "k_rank_proj_t1_i8", "k_gate_up_lopa_t1_i8"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -609,6 +611,21 @@ sffn_status run_dense(sffn_handle* h, const void* x, const void* W1, const void*
 
 // Weight-only int8, one token: gate (+ up) pass, then the int8 down pass over
 // 256-column slices and 16 row splits (atomics into y, cleared by the gate pass).
+// int8 down pass over the products the gate pass stored (pre-scaled by s2)
+sffn_status run_down_t1_i8(sffn_handle* h, const void* W2T, float* y, int splits, bool dense,
+                           hipStream_t s) {
+    const int cb = 16 * 16;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    sffn_status st = SFFN_OK;
+    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I8, k_down_t1_i8<PMAX>, dim3(nbx, splits),
+                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                       (const int8_t*)W2T, y, h->D, h->H, splits, dense ? 1 : 0));
+    return st;
+}
+
 template <bool DENSE>
 sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float* s1,
                       const void* W3, const float* s3, const void* W2T, const float* s2,
@@ -625,16 +642,51 @@ sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float
                                      (const uint16_t*)x, (const int8_t*)W1, s1, (const int8_t*)W3,
                                      s3, s2, h->a_buf, live, yz, h->D, h->H, h->act));
     if (st != SFFN_OK) return st;
-    const int cb = 16 * 16;
-    const int nslices = (h->D + cb - 1) / cb;
-    const int nbx = ((nslices + 7) / 8) * 8;
-    const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
-    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I8, k_down_t1_i8<PMAX>, dim3(nbx, splits),
-                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
-                                       (const int8_t*)W2T, y, h->D, h->H, splits, DENSE ? 1 : 0));
+    st = run_down_t1_i8(h, W2T, y, splits, DENSE, s);
     if (st != SFFN_OK) return st;
     if (DENSE) return SFFN_OK;
+    return run_live_list(h, 1, live_count, live_idx, s);
+}
+
+// batch-1 LoPA with int8 V, U, W3, W2T rows
+sffn_status run_lopa_i8_t1(sffn_handle* h, const void* x, const void* V, const float* sV,
+                           const void* U, const float* sU, const void* W3, const float* s3,
+                           const void* W2T, const float* s2, float* y, int32_t* live_count,
+                           int32_t* live_idx, hipStream_t s) {
+    const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
+    int splits = h->t1_splits_sparse;
+    while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
+    float* yz = splits > 1 ? y : nullptr;
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    sffn_status st = SFFN_OK;
+    const int nbr = (h->r + K1_WAVES - 1) / K1_WAVES;
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_RANK_PROJ_T1_I8, k_rank_proj_t1_i8<NC>, dim3(nbr),
+                                     dim3(K1_THREADS), s, (const uint16_t*)x, (const int8_t*)V,
+                                     sV, h->t_buf, yz, h->D, h->r));
+    if (st != SFFN_OK) return st;
+    const int nb = (h->H + K1_WAVES * KLQ_UPW - 1) / (K1_WAVES * KLQ_UPW);
+    const int nr = (h->r + 255) / 256;
+#define SFFN_LOPA_I8(NRV)                                                                          \
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_LOPA_T1_I8, k_gate_up_lopa_t1_i8<NC, NRV>,   \
+                                     dim3(nb), dim3(K1_THREADS), s, (const uint16_t*)x,           \
+                                     (const float*)h->t_buf, (const int8_t*)U, sU,                 \
+                                     (const int8_t*)W3, s3, s2, h->a_buf, live, h->D, h->H, h->r,  \
+                                     h->act, h->flags))
+    switch (nr) {
+        case 1: SFFN_LOPA_I8(1); break;
+        case 2: SFFN_LOPA_I8(2); break;
+        case 3: SFFN_LOPA_I8(3); break;
+        case 4: SFFN_LOPA_I8(4); break;
+        case 5: SFFN_LOPA_I8(5); break;
+        case 6: SFFN_LOPA_I8(6); break;
+        case 7: SFFN_LOPA_I8(7); break;
+        case 8: SFFN_LOPA_I8(8); break;
+        default: return fail(h, SFFN_INTERNAL, "rank too large for the int8 LoPA gate");
+    }
+#undef SFFN_LOPA_I8
+    if (st != SFFN_OK) return st;
+    st = run_down_t1_i8(h, W2T, y, splits, false, s);
+    if (st != SFFN_OK) return st;
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
@@ -732,8 +784,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
         if (dtype != SFFN_BF16 && dtype != SFFN_F32 && dtype != SFFN_I8)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
-        if (dtype == SFFN_I8 && r != 0)
-            return fail(nullptr, SFFN_UNSUPPORTED, "int8 weights: standard-gating handles (r == 0) only");
+        if (dtype == SFFN_I8 && r != 0 && r % 16 != 0)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "int8 weights: r must be a multiple of 16");
         if (dtype == SFFN_I8 && D % 16 != 0)
             return fail(nullptr, SFFN_INVALID_ARGUMENT, "int8 weights: D must be a multiple of 16");
         if (dtype == SFFN_I8 && (H + KD_THREADS - 1) / KD_THREADS > 32 * 16)
@@ -1026,6 +1078,7 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
     if (st != SFFN_OK) return st;
     if (h->dtype != SFFN_I8) return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
+    if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "standard-gating forward needs a handle with r == 0");
     if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
         return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
     if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
@@ -1044,6 +1097,42 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
         if (st != SFFN_OK) return st;
     }
     return SFFN_OK;
+}
+
+sffn_status sffn_forward_lopa_i8(sffn_handle* h, const void* x, const void* V,
+                                 const float* V_scale, const void* U, const float* U_scale,
+                                 const void* W3, const float* W3_scale, const void* W2T,
+                                 const float* W2T_scale, float* y, int T, int mode,
+                                 int32_t* live_count, int32_t* live_idx, void* stream) {
+    try {
+        hipStream_t s;
+        sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
+        if (st != SFFN_OK) return st;
+        if (h->dtype != SFFN_I8)
+            return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
+        if (h->r == 0) return fail(h, SFFN_INVALID_ARGUMENT, "LoPA forward needs a handle with r > 0");
+        if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
+            return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
+        if (!V || !U) return fail(h, SFFN_INVALID_ARGUMENT, "null V or U");
+        if (!aligned16(V) || !aligned16(U))
+            return fail(h, SFFN_INVALID_ARGUMENT, "V and U must be 16-byte aligned");
+        if (!V_scale || !U_scale || !W3_scale || !W2T_scale)
+            return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
+        auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+        if (!al4(V_scale) || !al4(U_scale) || !al4(W3_scale) || !al4(W2T_scale))
+            return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+        // a batch runs token by token (both modes compute the same result)
+        for (int t = 0; t < T; ++t) {
+            const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);
+            st = run_lopa_i8_t1(h, xt, V, V_scale, U, U_scale, W3, W3_scale, W2T, W2T_scale,
+                                y + (size_t)t * h->D, live_count ? live_count + t : nullptr,
+                                live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
+            if (st != SFFN_OK) return st;
+        }
+        return SFFN_OK;
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_lopa_i8");
+    }
 }
 
 sffn_status sffn_forward_sparse_i8(sffn_handle* h, const void* x, const void* W1,

@@ -1277,6 +1277,130 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i8(
     if (lane == 0) a_out[unit] = activation(act, z) * u * sc2;
 }
 
+// LoPA rank projection, int8 V rows: t_m = sV_m (qV_m . x), one row per wave.
+// y_zero (nullable): D floats this grid clears for a down pass that accumulates.
+template <int NC>
+__global__ __launch_bounds__(K1_THREADS) void k_rank_proj_t1_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ V, const float* __restrict__ sV,
+    float* __restrict__ t_out, float* __restrict__ y_zero, int D, int r) {
+    constexpr int CW = WAVE * 16;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int m = blockIdx.x * K1_WAVES + wave;
+    u32x4 w[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 16;
+        w[c] = (m < r && col < D) ? load_stream(V + (size_t)m * D + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float xv[NC][16];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) load_x16(x, c * CW + lane * 16, D, xv[c]);
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) s = dot16_i8(w[c], xv[c], s);
+    s = wave_sum_dpp(s);
+    if (lane == 0 && m < r) t_out[m] = s * sV[m];
+}
+
+// Sum over the 16 lanes of a lane group (lanes 16g .. 16g + 15).
+__device__ inline float group16_sum(float v) {
+    v += __shfl_xor(v, 8, 16);
+    v += __shfl_xor(v, 4, 16);
+    v += __shfl_xor(v, 2, 16);
+    v += __shfl_xor(v, 1, 16);
+    return v;
+}
+
+// LoPA gate and gathered up projection, int8 U and W3 rows. Gate: four units
+// per wave, 16 lanes per unit (a U row of r int8 is NR pieces of 256 B):
+// z_i = sU_i (qU_i . t) (t through RMSNorm when asked) + (G x)_i when asked.
+// Up projection: the wave's live units one after another, 64 lanes each:
+// u_i = s3_i (q3_i . x), through A as well under double activation. The stored
+// product is pre-multiplied by the W2T row scale s2_i.
+constexpr int KLQ_UPW = 4;  // units per wave in the gate phase
+template <int NC, int NR>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
+    const uint16_t* __restrict__ x, const float* __restrict__ t_in,
+    const int8_t* __restrict__ U, const float* __restrict__ sU, const int8_t* __restrict__ W3,
+    const float* __restrict__ s3, const float* __restrict__ s2, float* __restrict__ a_out,
+    uint8_t* __restrict__ live_out, int D, int H, int r, int act, unsigned flags) {
+    constexpr int CW = WAVE * 16;  // columns of one full-wave chunk of an int8 row
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane & 15, grp = lane >> 4;
+    const int base = (blockIdx.x * K1_WAVES + wave) * KLQ_UPW;
+    const int unit = base + grp;
+    const bool in = unit < H;
+    u32x4 u[NR];
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+        const int col = c * 256 + sub * 16;
+        u[c] = (in && col < r) ? load_stream(U + (size_t)unit * r + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float tv[NR][16];
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+        const int col = c * 256 + sub * 16;
+        if (col < r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a = *reinterpret_cast<const float4*>(t_in + col + 4 * q);
+                tv[c][4 * q] = a.x; tv[c][4 * q + 1] = a.y; tv[c][4 * q + 2] = a.z; tv[c][4 * q + 3] = a.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) tv[c][k] = 0.0f;
+        }
+    }
+    float xv[NC][16];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) load_x16(x, c * CW + lane * 16, D, xv[c]);
+    const float su_ = in ? sU[unit] : 0.0f;
+    const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
+    float inv = 1.0f;  // RMSNorm of t: every lane group sees all of t
+    if (flags & LOPA_RMSNORM) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) ss = fmaf(tv[c][k], tv[c][k], ss);
+        inv = 1.0f / sqrtf(group16_sum(ss) / (float)r + RMS_EPS);
+    }
+    float sz = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NR; ++c) sz = dot16_i8(u[c], tv[c], sz);
+    const float z = group16_sum(sz) * su_ * inv + gx;
+    const bool live = in && z > 0.0f;
+    if (in && sub == 0) {
+        if (live_out) live_out[unit] = live ? 1 : 0;
+        if (!live) a_out[unit] = 0.0f;
+    }
+    uint64_t m = __ballot(live && sub == 0);
+    while (m) {
+        const int g = __builtin_ctzll(m) >> 4;
+        m &= m - 1;
+        const int ul = base + g;
+        const float zl = __shfl(z, 16 * g);
+        u32x4 w3[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 16;
+            w3[c] = col < D ? load_stream(W3 + (size_t)ul * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = dot16_i8(w3[c], xv[c], s);
+        const float uu = wave_sum_dpp(s) * s3[ul];
+        const float g3 = (flags & LOPA_DOUBLE_ACT) ? activation(act, uu) : uu;
+        if (lane == 0) a_out[ul] = activation(act, zl) * g3 * s2[ul];
+    }
+}
+
 // Down projection, int8 W2T rows: y[slice] = sum_i a'_i q2[i, slice] with
 // a'_i = a_i s2_i from the gate pass. As k_down_t1: grid = (column slices of
 // 16 lanes x 16 columns = 256 columns, XCD-contiguous order) x (row splits);

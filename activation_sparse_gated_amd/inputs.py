@@ -148,6 +148,25 @@ def lopa_weights(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, laye
             "W2T": _finish(W2T, dtype), "offset": c}
 
 
+def lopa_weights_int8(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, layer: int = 0,
+                      replica: int = 0, offset: float | None = None) -> dict:
+    """The fp64 draws of lopa_weights (same streams, V[0] = e_0, U[:, 0] = c), quantized
+    per row to int8: V, U, W3, W2T int8 and V_scale, U_scale, W3_scale, W2T_scale fp32."""
+    V = normal((r, D), 1.0 / np.sqrt(D), cfg, layer, replica, S_V)
+    U = normal((Hp, r), 1.0 / np.sqrt(r), cfg, layer, replica, S_U)
+    c = offset if offset is not None else (gate_offset(sparsity) if sparsity is not None else None)
+    if c is not None:
+        V[0, :] = 0.0
+        V[0, 0] = 1.0
+        U[:, 0] = c
+    out = {"offset": c}
+    for name, w in (("V", V), ("U", U),
+                    ("W3", normal((Hp, D), 1.0 / np.sqrt(D), cfg, layer, replica, S_W3)),
+                    ("W2T", normal((Hp, D), 1.0 / np.sqrt(Hp), cfg, layer, replica, S_W2T))):
+        out[name], out[name + "_scale"] = quantize_rows_int8(w)
+    return out
+
+
 def small_integers(shape, lo: int, hi: int, cfg: int, layer: int = 0, replica: int = 0,
                    stream: int = 0, dtype: str = "bf16") -> np.ndarray:
     """Integers uniform in [lo, hi]; exact in bf16 and fp32 for |v| <= 256."""

@@ -30,6 +30,7 @@ EXPORTED = (
     "sffn_forward_lopa", "sffn_last_error", "sffn_status_string", "sffn_abi_version",
     "sffn_timing_enable", "sffn_timing_read", "sffn_kernel_kinds", "sffn_kernel_name",
     "sffn_forward_sparse_i8", "sffn_forward_dense_i8", "sffn_forward_moe",
+    "sffn_forward_lopa_i8",
 )
 
 _lib = None
@@ -68,6 +69,8 @@ def load() -> ctypes.CDLL:
     lib.sffn_forward_lopa.argtypes = [P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_sparse_i8.restype = I
     lib.sffn_forward_sparse_i8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_forward_lopa_i8.restype = I
+    lib.sffn_forward_lopa_i8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_dense_i8.restype = I
     lib.sffn_forward_dense_i8.argtypes = [P, P, P, P, P, P, P, P, P, I, P]
     lib.sffn_forward_moe.restype = I
@@ -179,6 +182,18 @@ def sffn_forward_sparse_i8(handle, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale
     st = load().sffn_forward_sparse_i8(handle, _ptr(x), _ptr(W1), _ptr(W1_scale), _ptr(W3),
                                        _ptr(W3_scale), _ptr(W2T), _ptr(W2T_scale), _ptr(y), T,
                                        mode, _ptr(live_count), _ptr(live_idx), _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_lopa_i8(handle, x, V, V_scale, U, U_scale, W3, W3_scale, W2T, W2T_scale, y,
+                         T: int, mode: int = SFFN_MODE_PER_TOKEN, live_count=None, live_idx=None,
+                         stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_lopa_i8(handle, _ptr(x), _ptr(V), _ptr(V_scale), _ptr(U),
+                                     _ptr(U_scale), _ptr(W3), _ptr(W3_scale), _ptr(W2T),
+                                     _ptr(W2T_scale), _ptr(y), T, mode, _ptr(live_count),
+                                     _ptr(live_idx), _stream(stream))
     if check:
         _check(st, handle)
     return st

@@ -28,7 +28,9 @@
  *   V    [r x D], U [H x r]   LoPA factors
  *   y    [T x D]   fp32 output, overwritten
  * Requirements: D % 8 == 0, D <= 8192; 1 <= H <= 1<<20; LoPA: r % 8 == 0 and
- * 8 <= r <= 2048; 0 <= T <= max_tokens <= 64; every pointer 16-byte aligned
+ * 8 <= r <= 2048; 0 <= T <= max_tokens (at most 64, or 8192 for bf16
+ * standard-gating handles: union and dense calls with T > 64 run as MFMA
+ * GEMMs with the unit products rounded to bf16); every pointer 16-byte aligned
  * and a device pointer (hipMalloc or torch CUDA tensors). T == 0 is a no-op.
  *
  * Ownership: the caller owns every tensor. The library borrows them only for
@@ -70,7 +72,8 @@ enum { SFFN_ACT_RELU = 0, SFFN_ACT_RSPLUS = 1 };
  * weight is q[i][j] * scale[i] with q int8 and one fp32 scale per row (the
  * pages report int8 weight-only models and kernels, paper card Table 17 and
  * Figure 9; the scheme is this library's reading). x stays bf16 and every
- * product and sum is fp32. Standard gating only; forward calls: the _i8 ones. */
+ * product and sum is fp32. Forward calls: the _i8 ones (standard gating with
+ * r == 0, LoPA with r > 0). */
 enum { SFFN_BF16 = 0, SFFN_F32 = 1, SFFN_I8 = 2 };
 /* How a batch of T tokens moves data; never changes the result.
  * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set.
@@ -99,16 +102,19 @@ enum { SFFN_FLAG_G_TILED = 1u, SFFN_FLAG_RMSNORM = 2u, SFFN_FLAG_DOUBLE_ACT = 4u
  * Create a handle for one FFN shape.
  *   D, H        model width and hidden width (H' for LoPA handles)
  *   r           LoPA rank; 0 for a standard-gating handle
- *   max_tokens  largest T any forward call on this handle will pass (1..64)
+ *   max_tokens  largest T any forward call on this handle will pass (1..64;
+ *               1..8192 for SFFN_BF16 handles with r == 0)
  *   act         SFFN_ACT_RELU or SFFN_ACT_RSPLUS
  *   dtype       SFFN_BF16 (weights and x as bf16 bit patterns; products in
  *               fp32), SFFN_F32, or SFFN_I8 (int8 weights with per-row
- *               scales, x bf16; needs D % 16 == 0 and r == 0)
+ *               scales, x bf16; needs D % 16 == 0 and r % 16 == 0)
  *   flags       0, or for LoPA handles any of SFFN_FLAG_G_TILED,
  *               SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT (other bits, or any
  *               bit on a standard handle: SFFN_UNSUPPORTED)
  * On success *out receives the handle. Allocates device scratch on the
- * current device: max_tokens * (H + r) floats plus max_tokens * H bytes.
+ * current device: about min(max_tokens, 64) * (H + r) floats plus
+ * max_tokens * H bytes, and for max_tokens > 64 also H * 256 ceil(max_tokens /
+ * 256) bf16 unit products.
  */
 sffn_status sffn_create(sffn_handle **out, int D, int H, int r, int max_tokens, int act,
                         int dtype, unsigned flags);
@@ -161,6 +167,22 @@ sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, cons
  * which are the same for one token). Errors as for the other forward calls;
  * a non-int8 handle gives SFFN_INVALID_ARGUMENT.
  */
+/*
+ * LoPA gating with weight-only int8 weights (SFFN_I8 handles with r > 0, r a
+ * multiple of 16): as sffn_forward_lopa, with V int8 [r x D], U int8 [H x r],
+ * W3 and W2T int8 [H x D] (row-major, 16-byte aligned) and one fp32 scale per
+ * stored row of each (V_scale [r], U_scale [H], W3_scale [H], W2T_scale [H],
+ * 4-byte aligned): t = V x is exact in fp32 on the dequantised rows, the gate
+ * options of the handle (G, RMSNorm, double activation) apply as for bf16.
+ * Tokens of a batch are processed one after another. Errors as for the other
+ * forward calls; a non-int8 or r == 0 handle gives SFFN_INVALID_ARGUMENT.
+ */
+sffn_status sffn_forward_lopa_i8(sffn_handle *h, const void *x, const void *V,
+                                 const float *V_scale, const void *U, const float *U_scale,
+                                 const void *W3, const float *W3_scale, const void *W2T,
+                                 const float *W2T_scale, float *y, int T, int mode,
+                                 int32_t *live_count, int32_t *live_idx, void *stream);
+
 sffn_status sffn_forward_sparse_i8(sffn_handle *h, const void *x, const void *W1,
                                    const float *W1_scale, const void *W3, const float *W3_scale,
                                    const void *W2T, const float *W2T_scale, float *y, int T,

@@ -53,11 +53,11 @@ def test_create_rejects_bad_arguments(args, status, needle):
 
 
 def test_create_int8_checks():
-    # int8 weights: D a multiple of 16, standard gating only
+    # int8 weights: D and (LoPA) r multiples of 16
     st, h = sffn.sffn_create_status(264, 64, 0, 1, 0, sffn.SFFN_I8, 0)
     assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "16" in sffn.sffn_last_error(None)
-    st, h = sffn.sffn_create_status(256, 64, 8, 1, 0, sffn.SFFN_I8, 0)
-    assert st == sffn.SFFN_UNSUPPORTED and h is None and "int8" in sffn.sffn_last_error(None)
+    st, h = sffn.sffn_create_status(256, 64, 24, 1, 0, sffn.SFFN_I8, 0)
+    assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "r must" in sffn.sffn_last_error(None)
 
 
 def test_create_rejects_flags():

@@ -359,6 +359,45 @@ def test_int8_weights_are_rows_times_scales():
         assert got["live"][t].tolist() == live
 
 
+def test_lopa_int8_weights_and_exact_oracle():
+    """An int8 LoPA workload's V, U, W3, W2T are rows q * scale (within half a step of the
+    fp64 draws, V[0] = e_0 exactly representable), and the int8 LoPA oracle equals exact
+    rationals on small integer codes with power-of-two scales: the plain gate U (V x), and
+    G x + U (V x) with double activation."""
+    D, Hp, r = 64, 80, 16
+    w = gen.lopa_weights_int8(D, Hp, r, 0.9, cfg=72)
+    U64 = gen.normal((Hp, r), 1.0 / np.sqrt(r), 72, 0, 0, gen.S_U)
+    U64[:, 0] = w["offset"]
+    deq = ref.dequantize_rows(w["U"], w["U_scale"])
+    assert np.all(np.abs(deq - U64) <= 0.5 * w["U_scale"].astype(np.float64)[:, None] * (1 + 1e-12))
+    assert w["V"][0, 0] == 127 and not w["V"][0, 1:].any()
+    for k in ("V", "U", "W3", "W2T"):
+        assert w[k].dtype == np.int8 and w[k + "_scale"].dtype == np.float32
+    D, H, r = 6, 10, 4
+    shapes = {"V": (r, D), "U": (H, r), "W3": (H, D), "W2T": (H, D)}
+    q = {k: gen.small_integers(sh, -3, 3, cfg=73, stream=i + 1, dtype="f32").astype(np.int8)
+         for i, (k, sh) in enumerate(shapes.items())}
+    sc = {"V": 0.5, "U": 0.25, "W3": 0.5, "W2T": 0.125}
+    wi = {**q, **{k + "_scale": np.full(shapes[k][0], v, np.float32) for k, v in sc.items()}}
+    x = gen.small_integers((2, D), -2, 2, cfg=73, stream=0, dtype="bf16")
+    xf = gen.as_float(x).astype(np.float64)
+    mats = {k: [[Fraction(int(v)) * Fraction(sc[k]) for v in row] for row in q[k]] for k in q}
+    plain = ref.ffn_lopa_int8(x, wi)
+    full = ref.ffn_lopa_int8(x, wi, flags=ref.LOPA_G_TILED | ref.LOPA_DOUBLE_ACT)
+    for t in range(2):
+        xs = [Fraction(v) for v in xf[t]]
+        tt = [sum(mats["V"][m][j] * xs[j] for j in range(D)) for m in range(r)]
+        z = [sum(mats["U"][i][m] * tt[m] for m in range(r)) for i in range(H)]
+        u = [sum(mats["W3"][i][j] * xs[j] for j in range(D)) for i in range(H)]
+        a = [(z[i] if z[i] > 0 else 0) * u[i] for i in range(H)]
+        y = [sum(mats["W2T"][i][j] * a[i] for i in range(H)) for j in range(D)]
+        assert [Fraction(v) for v in plain["y"][t]] == y
+        assert plain["live"][t].tolist() == [i for i in range(H) if z[i] > 0]
+        yd, live_d, k2 = frac_lopa_double(xs, mats["V"], mats["U"], mats["W3"], mats["W2T"], True)
+        assert [Fraction(v) for v in full["y"][t]] == yd
+        assert full["live"][t].tolist() == live_d and full["k2"][t] == k2
+
+
 def test_moe_exact_on_integers():
     """Top-K mixture (page "Model casting: ...", section "Where it generalizes"): y_t is the
     gate-weighted sum of the routed experts' FFN outputs, checked with exact rationals on
