@@ -2225,10 +2225,11 @@ struct GemmTile {
 };
 constexpr int KG_UN_MIN = 64;  // the smallest unit tile (masks of the union list are per 64 units)
 
-// Slot of 16-byte piece p in staged 64-byte row r: the 16 rows read by one
-// fragment instruction fall on 16 different (row mod 4, slot) pairs, i.e.
-// cover one 256-byte bank window once.
-__device__ inline int swz64(int r, int p) { return p ^ ((r >> 2) & 3); }
+// Slot of 16-byte piece p in staged 64-byte row r. A fragment read takes one
+// piece of 16 consecutive rows; measured with the LDS bank-conflict counter on
+// gfx950, p ^ ((r >> 1) & 3) reads them without conflicts, while p ^ ((r >> 2) & 3),
+// p ^ (r & 3) and no swizzle cost 4 extra cycles per read.
+__device__ inline int swz64(int r, int p) { return p ^ ((r >> 1) & 3); }
 
 // Map a linear block id to a work item so that each XCD (block id mod 8)
 // receives a contiguous range of work items.
