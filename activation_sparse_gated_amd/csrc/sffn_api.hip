@@ -63,6 +63,7 @@ struct sffn_handle {
     int down_lpr = 8;
     // batch-1 bf16 path
     int t1_rw = 1;            // units per wave in the gate pass
+    int t1_rw_lopa = 2;       // units per wave in the LoPA gate pass (short U rows)
     int t1_lpr = 32;          // lanes per W2T row slice in the down pass (512 B per row)
     int t1_splits_sparse = 16; // row splits of the down pass (sparse)
     int t1_splits_dense = 16; // row splits of the down pass (dense, unfused)
@@ -548,7 +549,7 @@ sffn_status run_lopa_t1(sffn_handle* h, const void* x, const void* V, const void
                                      dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)V,
                                      h->t_buf, yz, h->D, h->r));
     if (st != SFFN_OK) return st;
-    const int rw = h->t1_rw;
+    const int rw = h->t1_rw_lopa;
     const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
     uint8_t* live = live_count ? h->live_buf : nullptr;
     SFFN_NCT1_SWITCH(nc, SFFN_NRT1_SWITCH(nr, SFFN_RW_SWITCH(rw,
@@ -840,6 +841,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if (env_lpr == 4 || env_lpr == 8) h->down_lpr = env_lpr;
         const int e_rw = env_int("SFFN_T1_ROWS_PER_WAVE", 0);
         if (e_rw == 1 || e_rw == 2 || e_rw == 4) h->t1_rw = e_rw;
+        const int e_rwl = env_int("SFFN_T1_LOPA_ROWS_PER_WAVE", 0);
+        if (e_rwl == 1 || e_rwl == 2 || e_rwl == 4) h->t1_rw_lopa = e_rwl;
         const int e_lpr = env_int("SFFN_T1_LANES_PER_ROW", 0);
         if (e_lpr == 4 || e_lpr == 8 || e_lpr == 16 || e_lpr == 32) h->t1_lpr = e_lpr;
         const int e_ss = env_int("SFFN_T1_SPLITS_SPARSE", 0);

@@ -551,32 +551,28 @@ __device__ inline float dot2_chunk(const u32x4& w, const u32x4& x, float s) {
 // Gate and gathered up projection for one token, bf16. Each wave owns RW
 // consecutive units and issues all of their W1 loads before any arithmetic;
 // the grid is sized so every block is resident at once, so the whole of W1 is
-// requested in one round. y_zero (nullable): D floats this grid clears for a
-// down pass that accumulates.
+// requested in one round. A wave then reads the W3 rows of its own live units
+// as soon as their z is known (no block-wide compaction or barrier, so a live
+// unit's W3 round trip never waits for another wave's W1 row). y_zero
+// (nullable): D floats this grid clears for a down pass that accumulates.
 template <int NC, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W3, float* __restrict__ a_out, uint8_t* __restrict__ live_out,
     float* __restrict__ y_zero, int D, int H, int act) {
-    constexpr int RPB = K1_WAVES * RW;
     constexpr int CW = WAVE * 8;
-    __shared__ float zs[RPB];
-    __shared__ int list[RPB];
-    __shared__ int nlist;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int row0 = blockIdx.x * RPB;
-    const int nrows = min(RPB, H - row0);
+    const int unit0 = (blockIdx.x * K1_WAVES + wave) * RW;
 
     u32x4 w[RW][NC];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        const int rl = wave * RW + r;
+    for (int q = 0; q < RW; ++q) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int col = c * CW + lane * 8;
-            w[r][c] = (rl < nrows && col < D) ? load_stream(W1 + (size_t)(row0 + rl) * D + col)
-                                              : u32x4{0u, 0u, 0u, 0u};
+            w[q][c] = (unit0 + q < H && col < D) ? load_stream(W1 + (size_t)(unit0 + q) * D + col)
+                                                 : u32x4{0u, 0u, 0u, 0u};
         }
     }
     u32x4 xv[NC];
@@ -589,59 +585,41 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
     }
+    float z[RW];
+    bool live[RW];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
+    for (int q = 0; q < RW; ++q) {
         float s = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s = dot2_chunk(w[r][c], xv[c], s);
-        s = wave_sum_dpp(s);
-        const int rl = wave * RW + r;
-        if (lane == 0 && rl < nrows) zs[rl] = s;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const bool in = lane < nrows;
-        const float z = in ? zs[lane] : 0.0f;
-        const bool live = in && z > 0.0f;
-        const uint64_t m = __ballot(live);
-        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (live) list[pos] = lane;
-        if (lane == 0) nlist = __popcll(m);
-        if (in) {
-            if (!live) a_out[row0 + lane] = 0.0f;
-            if (live_out) live_out[row0 + lane] = live ? 1 : 0;
+        for (int c = 0; c < NC; ++c) s = dot2_chunk(w[q][c], xv[c], s);
+        z[q] = wave_sum_dpp(s);
+        const bool in = unit0 + q < H;
+        live[q] = in && z[q] > 0.0f;
+        if (lane == 0 && in) {
+            if (live_out) live_out[unit0 + q] = live[q] ? 1 : 0;
+            if (!live[q]) a_out[unit0 + q] = 0.0f;
         }
     }
-    __syncthreads();
-    const int n = nlist;
-    // this block's live units, RW per wave at most; all W3 loads first
+    // the wave's live units: all W3 loads first (wave-uniform branches)
 #pragma unroll
-    for (int j = 0; j < RW; ++j) {
-        const int e = wave + j * K1_WAVES;
+    for (int q = 0; q < RW; ++q) {
+        if (!live[q]) continue;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int col = c * CW + lane * 8;
-            w[j][c] = (e < n && col < D) ? load_stream(W3 + (size_t)(row0 + list[e]) * D + col)
-                                         : u32x4{0u, 0u, 0u, 0u};
+            w[q][c] = col < D ? load_stream(W3 + (size_t)(unit0 + q) * D + col) : u32x4{0u, 0u, 0u, 0u};
         }
     }
 #pragma unroll
-    for (int j = 0; j < RW; ++j) {
-        const int e = wave + j * K1_WAVES;
-        if (e < n) {
-            float s = 0.0f;
+    for (int q = 0; q < RW; ++q) {
+        if (!live[q]) continue;
+        float s = 0.0f;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) s = dot2_chunk(w[j][c], xv[c], s);
-            const float u = wave_sum_dpp(s);
-            const int rl = list[e];
-            if (lane == 0) a_out[row0 + rl] = activation(act, zs[rl]) * u;
-        }
+        for (int c = 0; c < NC; ++c) s = dot2_chunk(w[q][c], xv[c], s);
+        const float u = wave_sum_dpp(s);
+        if (lane == 0) a_out[unit0 + q] = activation(act, z[q]) * u;
     }
 }
-
-// Dense comparator, batch-1 bf16: W1 and W3 rows of RW units per wave read
-// together (one merged pass), a_i = A(z_i) u_i for every unit.
 template <int NC, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_dense_t1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
@@ -725,32 +703,27 @@ __global__ __launch_bounds__(K1_THREADS) void k_rank_proj_t1(const uint16_t* __r
 }
 
 // LoPA batch-1 bf16 gate: z_i = U_i . t with t in fp32 (U rows widened exactly
-// from bf16), then the same compaction and live W3 rows as k_gate_up_t1.
+// from bf16), then, as in k_gate_up_t1, each wave reads the W3 rows of its own
+// live units.
 // NR = 16-byte register chunks of a U row (r <= NR * 512).
 template <int NC, int NR, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
     const uint16_t* __restrict__ x, const float* __restrict__ t_in,
     const uint16_t* __restrict__ U, const uint16_t* __restrict__ W3, float* __restrict__ a_out,
     uint8_t* __restrict__ live_out, int D, int H, int r, int act, unsigned flags) {
-    constexpr int RPB = K1_WAVES * RW;
     constexpr int CW = WAVE * 8;
-    __shared__ float zs[RPB];
-    __shared__ int list[RPB];
-    __shared__ int nlist;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int row0 = blockIdx.x * RPB;
-    const int nrows = min(RPB, H - row0);
+    const int unit0 = (blockIdx.x * K1_WAVES + wave) * RW;
 
     u32x4 u[RW][NR];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
-        const int rl = wave * RW + q;
 #pragma unroll
         for (int c = 0; c < NR; ++c) {
             const int col = c * CW + lane * 8;
-            u[q][c] = (rl < nrows && col < r) ? load_stream(U + (size_t)(row0 + rl) * r + col)
-                                              : u32x4{0u, 0u, 0u, 0u};
+            u[q][c] = (unit0 + q < H && col < r) ? load_stream(U + (size_t)(unit0 + q) * r + col)
+                                                 : u32x4{0u, 0u, 0u, 0u};
         }
     }
     float tv[NR][8];
@@ -773,12 +746,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
         const int col = c * CW + lane * 8;
         xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
     }
-    float gx[RW];  // (G x)_i = x_{i mod D} when G is on
-#pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        const int rl = wave * RW + q;
-        gx[q] = ((flags & LOPA_G_TILED) && rl < nrows) ? Elem<uint16_t>::get1(x[(row0 + rl) % D]) : 0.0f;
-    }
     float inv = 1.0f;  // RMSNorm of t: every wave sees all of t
     if (flags & LOPA_RMSNORM) {
         float ss = 0.0f;
@@ -788,49 +755,46 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
             for (int k = 0; k < 8; ++k) ss = fmaf(tv[c][k], tv[c][k], ss);
         inv = 1.0f / sqrtf(wave_sum_dpp(ss) / (float)r + RMS_EPS);
     }
+    float z[RW];
+    bool live[RW];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
+        const int unit = unit0 + q;
+        const bool in = unit < H;
         float s = 0.0f;
 #pragma unroll
         for (int c = 0; c < NR; ++c)
 #pragma unroll
             for (int k = 0; k < 8; ++k) s = fmaf(Elem<uint16_t>::get(u[q][c], k), tv[c][k], s);
-        s = wave_sum_dpp(s) * inv + gx[q];
-        const int rl = wave * RW + q;
-        if (lane == 0 && rl < nrows) zs[rl] = s;
-    }
-    __syncthreads();
-    if (wave == 0) {
-        const bool in = lane < nrows;
-        const float z = in ? zs[lane] : 0.0f;
-        const bool live = in && z > 0.0f;
-        const uint64_t m = __ballot(live);
-        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-        if (live) list[pos] = lane;
-        if (lane == 0) nlist = __popcll(m);
-        if (in) {
-            if (!live) a_out[row0 + lane] = 0.0f;
-            if (live_out) live_out[row0 + lane] = live ? 1 : 0;
+        // (G x)_i = x_{i mod D} when G is on
+        const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
+        z[q] = wave_sum_dpp(s) * inv + gx;
+        live[q] = in && z[q] > 0.0f;
+        if (lane == 0 && in) {
+            if (live_out) live_out[unit] = live[q] ? 1 : 0;
+            if (!live[q]) a_out[unit] = 0.0f;
         }
     }
-    __syncthreads();
-    const int n = nlist;
-    for (int e = wave; e < n; e += K1_WAVES) {
-        u32x4 w3[NC];
+    // the wave's live units: all W3 loads first (wave-uniform branches)
+    u32x4 w3[RW][NC];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        if (!live[q]) continue;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int col = c * CW + lane * 8;
-            w3[c] = col < D ? load_stream(W3 + (size_t)(row0 + list[e]) * D + col)
-                            : u32x4{0u, 0u, 0u, 0u};
+            w3[q][c] = col < D ? load_stream(W3 + (size_t)(unit0 + q) * D + col) : u32x4{0u, 0u, 0u, 0u};
         }
+    }
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        if (!live[q]) continue;
         float s = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s = dot2_chunk(w3[c], xv[c], s);
+        for (int c = 0; c < NC; ++c) s = dot2_chunk(w3[q][c], xv[c], s);
         const float uu = wave_sum_dpp(s);
-        const int rl = list[e];
         const float g3 = (flags & LOPA_DOUBLE_ACT) ? activation(act, uu) : uu;
-        if (lane == 0) a_out[row0 + rl] = activation(act, zs[rl]) * g3;
+        if (lane == 0) a_out[unit0 + q] = activation(act, z[q]) * g3;
     }
 }
 
