@@ -25,7 +25,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
             KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
-            KIND_GATE_UP_LOPA_T1_I8, KIND_COUNT };
+            KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -35,7 +35,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_t1_i8", "k_gate_up_dense_t1_i8",
                                             "k_down_t1_i8", "k_moe_gather", "k_moe_combine",
                                             "k_gate_up_gemm", "k_union_list", "k_down_gemm",
-                                            "k_rank_proj_t1_i8", "k_gate_up_lopa_t1_i8"};
+                                            "k_rank_proj_t1_i8", "k_gate_up_lopa_t1_i8",
+                                            "k_gate_up_tb"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -84,6 +85,8 @@ struct sffn_handle {
     float* moe_y = nullptr;        // [2 * max_tokens x D] fp32
     int tb_splits = 16;            // row splits of the small-batch down pass
     int tb_max = 8;                // batches up to this size use the small-batch down pass
+    int tbv_max = 4;               // batches up to this size use the VALU gate/up pass
+    int tbv_rw2 = 2, tbv_rw4 = 4;  // units per wave of the VALU gate/up pass (2 and 4 token slots)
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
     uint64_t* m_mask = nullptr;    // [H] tokens for which each unit is live
     // large batches as GEMMs on MFMA
@@ -413,6 +416,20 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     const bool small = T <= h->tb_max && T <= 8;
     const int splits = small ? h->tb_splits : h->m_splits;
     float* yz = splits > 1 ? y : nullptr;
+    if (small && T <= h->tbv_max && T <= 4) {
+        // gate/up on the VALU: x of the batch in registers, W1 streamed once
+        const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
+        const int tt = T <= 2 ? 2 : 4;
+        const int rw = tt == 2 ? h->tbv_rw2 : h->tbv_rw4;
+        const int nbv = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
+#define SFFN_TBV(TTV)                                                                               \
+        SFFN_NCT1_SWITCH(nc, SFFN_RW_SWITCH(rw, st = launch(h, KIND_GATE_UP_TB,                    \
+            k_gate_up_tb<NC, RW, TTV, DENSE>, dim3(nbv), dim3(K1_THREADS), s, (const uint16_t*)x,   \
+            (const uint16_t*)W1, (const uint16_t*)W3, h->m_a, h->m_mask, live, yz, h->D, h->H, T,   \
+            16 * nt, h->act)))
+        if (tt == 2) { SFFN_TBV(2); } else { SFFN_TBV(4); }
+#undef SFFN_TBV
+    } else {
 #define SFFN_GATE_MFMA(NTV, UTV)                                                               \
     st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NTV, UTV, DENSE>, dim3(nb),               \
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
@@ -424,6 +441,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
         if (ut == 4) { SFFN_GATE_MFMA(2, 4); } else if (ut == 2) { SFFN_GATE_MFMA(2, 2); } else { SFFN_GATE_MFMA(2, 1); }
     } else {
         if (ut == 4) { SFFN_GATE_MFMA(4, 4); } else if (ut == 2) { SFFN_GATE_MFMA(4, 2); } else { SFFN_GATE_MFMA(4, 1); }
+    }
     }
 #undef SFFN_GATE_MFMA
     if (st != SFFN_OK) return st;
@@ -896,6 +914,13 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             h->m_splits = sp;
             const int tbs = env_int("SFFN_TB_SPLITS", 16);
             if (tbs >= 1 && tbs <= 64) h->tb_splits = tbs;
+            h->tbv_max = env_int("SFFN_TBV_MAX", h->tbv_max);
+            auto rw_env = [](const char* name, int dflt) {
+                const int v = env_int(name, dflt);
+                return (v == 1 || v == 2 || v == 4) ? v : dflt;
+            };
+            h->tbv_rw2 = rw_env("SFFN_TBV_RW2", h->tbv_rw2);
+            h->tbv_rw4 = rw_env("SFFN_TBV_RW4", h->tbv_rw4);
             const int tbm = env_int("SFFN_TB_MAX", 8);
             if (tbm >= 0 && tbm <= 8) h->tb_max = tbm;
             while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;

@@ -1504,6 +1504,134 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Small batches (2 <= T <= TT <= 4), bf16, on the VALU.
+//
+// N partial sums per lane reduced over the wave at once: log2(N) halving
+// exchanges (each lane keeps one half of its values and adds the partner's
+// copy of that half), then a plain reduction of the one value left. Lane l ends
+// with the total of value index rev(l mod N), rev = bit reversal over log2(N)
+// bits (an involution).
+template <int N>
+__device__ inline float multi_reduce(float (&v)[N]) {
+    const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+    for (int h = N / 2, m = 1; h >= 1; h /= 2, m *= 2) {
+        const bool hi = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < h; ++i) {
+            const float keep = hi ? v[i + h] : v[i];
+            const float send = hi ? v[i] : v[i + h];
+            v[i] = keep + __shfl_xor(send, m);
+        }
+    }
+    float s = v[0];
+#pragma unroll
+    for (int m = N; m < WAVE; m *= 2) s += __shfl_xor(s, m);
+    return s;
+}
+
+template <int N>
+__device__ inline int bit_rev(int i) {
+    int r = 0;
+#pragma unroll
+    for (int b = 1; b < N; b *= 2) r = (r << 1) | ((i & b) ? 1 : 0);
+    return r;
+}
+
+// Gate and gathered up projection of a small batch, as k_gate_up_t1 for TT
+// token slots: each wave owns RW consecutive units, keeps x of the T tokens
+// for its columns in registers, streams each W1 row once against all of them,
+// then reads the W3 row of each of its units that is live for some token
+// (DENSE: every unit). Writes a_rm[unit][t] (row stride tp; 0 for dead pairs
+// and for T <= t < TT) for units live for some token, umask[unit] (tokens for
+// which the unit is live; DENSE: all T), live flags [T x H] when asked, and
+// clears y (T x D) when y_zero is set.
+template <int NC, int RW, int TT, bool DENSE>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
+    const uint16_t* __restrict__ W3, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int tp,
+    int act) {
+    constexpr int CW = WAVE * 8;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int unit0 = (blockIdx.x * K1_WAVES + wave) * RW;
+    u32x4 w[RW][NC];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            w[q][c] = (unit0 + q < H && col < D) ? load_stream(W1 + (size_t)(unit0 + q) * D + col)
+                                                 : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    u32x4 xv[TT][NC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            xv[t][c] = (t < T && col < D) ? load_cached(x + (size_t)t * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < T * D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    const int tl = bit_rev<TT>(lane & (TT - 1));  // token whose sums this lane ends with
+    float z[RW];
+    bool any[RW];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        float v[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) s = dot2_chunk(w[q][c], xv[t][c], s);
+            v[t] = s;
+        }
+        z[q] = multi_reduce<TT>(v);
+        const int unit = unit0 + q;
+        const bool lv = tl < T && z[q] > 0.0f;
+        const uint64_t b = __ballot(lv && lane < TT);
+        uint64_t m = 0;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) m |= ((b >> bit_rev<TT>(t)) & 1ull) << t;
+        any[q] = unit < H && (DENSE || m != 0);
+        if (unit < H) {
+            if (lane == 0) umask[unit] = DENSE ? ((T >= 64) ? ~0ull : ((1ull << T) - 1)) : m;
+            if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
+        }
+    }
+    // the wave's units live for some token: all W3 loads first (wave-uniform branches)
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        if (!any[q]) continue;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 8;
+            w[q][c] = col < D ? load_stream(W3 + (size_t)(unit0 + q) * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+        if (!any[q]) continue;
+        float v[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            float s = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) s = dot2_chunk(w[q][c], xv[t][c], s);
+            v[t] = s;
+        }
+        const float u = multi_reduce<TT>(v);
+        if (lane < TT) a_rm[(size_t)(unit0 + q) * tp + tl] = tl < T ? activation(act, z[q]) * u : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Batched bf16 path on MFMA (v_mfma_f32_16x16x32_bf16). Lane l of a wave holds
 // A[l%16][8(l/16) .. +8], B[8(l/16) .. +8][l%16] and C[4(l/16) .. +4][l%16].
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
