@@ -416,7 +416,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     const bool small = T <= h->tb_max && T <= 8;
     const int splits = small ? h->tb_splits : h->m_splits;
     float* yz = splits > 1 ? y : nullptr;
-    if (small && T <= h->tbv_max && T <= 4) {
+    if (small && T <= h->tbv_max && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once
         const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
         const int tt = T <= 2 ? 2 : 4;
