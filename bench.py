@@ -556,6 +556,39 @@ def main() -> int:
                        "speedup_vs_dense": round(tok_s / dense_tok_s, 3)})
         del g_dense
 
+        # the workload's other sparsities: the same draws with W1's bias column set for s
+        other = {}
+        for s_o in (0.69, 0.76, 0.896):
+            bits = gen.to_bf16_bits(np.array([gen.gate_offset(s_o)], np.float64)).view(np.int16)[0]
+            W1o = W["W1"].clone()
+            W1o[:, 0] = int(bits)
+            W1r = [W1o if rr == 0 else W1o.clone() for rr in range(R)]
+            for t in range(n):
+                rp = reps[t % R]
+                sffn.sffn_forward_sparse(hs.ptr, x[t], W1r[t % R], rp["W3"], rp["W2T"], y[t], 1,
+                                         sffn.SFFN_MODE_PER_TOKEN, cnt[t:t + 1], idx[t])
+            torch.cuda.synchronize()
+            ko = cnt.cpu().numpy().astype(np.int64)
+
+            def other_stream():
+                for t in range(n):
+                    rp = reps[t % R]
+                    sffn.sffn_forward_sparse(hs.ptr, x[t], W1r[t % R], rp["W3"], rp["W2T"], y[t], 1,
+                                             sffn.SFFN_MODE_PER_TOKEN)
+            g_o = capture(other_stream)
+            ms_o = time_graph(g_o, max(2, args.steps // 2), 1)
+            del g_o, W1r, W1o
+            tok_o = n / (ms_o * 1e-3)
+            gbps_o = (2 * (H * D + 2 * ko * D) + 6 * D).sum() / (ms_o * 1e-3) / 1e9
+            other[f"s{s_o}"] = {"tokens_per_s": round(tok_o, 1), "touched_GBps": round(float(gbps_o), 1),
+                                "touched_frac_of_peak": round(float(gbps_o) / 8000.0, 4),
+                                "measured_sparsity": round(float(1 - ko.mean() / H), 4),
+                                "k_mean": round(float(ko.mean()), 1),
+                                "speedup_vs_dense": round(tok_o / dense_tok_s, 3)}
+            log(f"sparsity {s_o}: {tok_o:,.0f} tokens/s, {gbps_o:,.0f} GB/s touched, "
+                f"measured {other[f's{s_o}']['measured_sparsity']}, {tok_o / dense_tok_s:.2f}x dense")
+        extras["other_sparsities"] = other
+
         # LoPA at constant parameter count: D = 2560, H' = 9787, r = 400
         Hp, r = 9787, 400
         wl = gen.lopa_weights(D, Hp, r, s, cfg=3, dtype="bf16")
