@@ -148,6 +148,54 @@ def lopa_weights(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, laye
             "W2T": _finish(W2T, dtype), "offset": c}
 
 
+INT4_GROUP = 128  # columns that share one int4 scale
+
+
+def quantize_groups_int4(w64: np.ndarray, group: int = INT4_GROUP) -> tuple[np.ndarray, np.ndarray]:
+    """Symmetric int4 with one scale per `group` consecutive columns of a row:
+    scale_ig = max |w| over the group / 7 (as fp32; 1 for an all-zero group),
+    q = clip(rint(w / scale), -7, 7). Returns the codes packed two per byte (column 2j
+    in the low nibble, 2j + 1 in the high nibble, two's complement), [H, D/2] uint8,
+    and the scales [H, D/group] fp32. The weights the FFN then uses are q * scale."""
+    H, D = w64.shape
+    assert D % group == 0 and group % 2 == 0
+    g = w64.reshape(H, D // group, group)
+    amax = np.max(np.abs(g), axis=2)
+    scale = np.where(amax > 0, amax / 7.0, 1.0).astype(np.float32)
+    q = np.clip(np.rint(g / scale.astype(np.float64)[:, :, None]), -7, 7).astype(np.int8).reshape(H, D)
+    packed = ((q[:, 0::2].astype(np.uint8) & 0xF) | ((q[:, 1::2].astype(np.uint8) & 0xF) << 4))
+    return np.ascontiguousarray(packed.astype(np.uint8)), np.ascontiguousarray(scale)
+
+
+def unpack_int4(packed: np.ndarray) -> np.ndarray:
+    """int4 codes [H, D] (int8) from the packed layout of quantize_groups_int4."""
+    lo = (packed & 0xF).astype(np.int8)
+    hi = (packed >> 4).astype(np.int8)
+    lo = np.where(lo > 7, lo - 16, lo).astype(np.int8)
+    hi = np.where(hi > 7, hi - 16, hi).astype(np.int8)
+    out = np.empty((packed.shape[0], packed.shape[1] * 2), np.int8)
+    out[:, 0::2] = lo
+    out[:, 1::2] = hi
+    return out
+
+
+def standard_weights_int4(D: int, H: int, sparsity: float | None, cfg: int, layer: int = 0,
+                          replica: int = 0, offset: float | None = None) -> dict:
+    """The fp64 draws of standard_weights (same streams, W1[:, 0] = c), quantized to
+    int4 with one scale per 128 columns: W1, W3, W2T packed uint8 [H, D/2] and
+    W1_scale, W3_scale, W2T_scale fp32 [H, D/128]."""
+    std = 1.0 / np.sqrt(D)
+    W1 = normal((H, D), std, cfg, layer, replica, S_W1)
+    c = offset if offset is not None else (gate_offset(sparsity) if sparsity is not None else None)
+    if c is not None:
+        W1[:, 0] = c
+    out = {"offset": c}
+    for name, w in (("W1", W1), ("W3", normal((H, D), std, cfg, layer, replica, S_W3)),
+                    ("W2T", normal((H, D), std, cfg, layer, replica, S_W2T))):
+        out[name], out[name + "_scale"] = quantize_groups_int4(w)
+    return out
+
+
 def lopa_weights_int8(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, layer: int = 0,
                       replica: int = 0, offset: float | None = None) -> dict:
     """The fp64 draws of lopa_weights (same streams, V[0] = e_0, U[:, 0] = c), quantized

@@ -214,6 +214,34 @@ def ffn_standard_int8(x, w, act: int = ACT_RELU, dense: bool = False):
                         act=act, dense=dense)
 
 
+def dequantize_groups_int4(packed, scale):
+    """Weights of a group-scaled int4 matrix as fp64: code * scale of its group (exact
+    in fp64). packed: [H, D/2] uint8, column 2j in the low nibble (two's complement);
+    scale: [H, D/G] fp32."""
+    packed = np.asarray(packed, np.uint8)
+    H = packed.shape[0]
+    D = packed.shape[1] * 2
+    q = np.empty((H, D), np.int64)
+    lo = (packed & 0xF).astype(np.int64)
+    hi = (packed >> 4).astype(np.int64)
+    q[:, 0::2] = np.where(lo >= 8, lo - 16, lo)
+    q[:, 1::2] = np.where(hi >= 8, hi - 16, hi)
+    scale = np.asarray(scale, np.float32).astype(np.float64)
+    G = D // scale.shape[1]
+    return q.astype(np.float64) * np.repeat(scale, G, axis=1)
+
+
+def ffn_standard_int4(x, w, act: int = ACT_RELU, dense: bool = False):
+    """The standard oracle on the weights a group-scaled int4 workload defines; x is
+    widened exactly to fp64. w: dict with W1/W3/W2T (packed int4) and *_scale."""
+    xf = np.atleast_2d(np.asarray(x))
+    if xf.dtype == np.uint16:
+        xf = (xf.astype(np.uint32) << 16).view(np.float32)
+    xf = xf.astype(np.float64)
+    return ffn_standard(xf, *(dequantize_groups_int4(w[k], w[k + "_scale"])
+                              for k in ("W1", "W3", "W2T")), act=act, dense=dense)
+
+
 def ffn_lopa_int8(x, w, act: int = ACT_RELU, flags: int = 0):
     """The LoPA oracle (flags as in ffn_lopa_full) on the weights an int8 LoPA workload
     defines: V, U, W3, W2T rows q * scale. x is widened exactly to fp64."""

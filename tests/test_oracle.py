@@ -398,6 +398,44 @@ def test_lopa_int8_weights_and_exact_oracle():
         assert full["live"][t].tolist() == live_d and full["k2"][t] == k2
 
 
+def test_int4_packing_scales_and_exact_oracle():
+    """A group-scaled int4 workload: the packed nibbles decode (brute force, per element)
+    to the codes both unpackers return; every weight is within half a step of its fp64
+    draw; and the int4 oracle equals exact rationals for integer codes with a different
+    power-of-two scale in each 128-column group."""
+    D, H = 256, 24
+    w = gen.standard_weights_int4(D, H, 0.9, cfg=74)
+    w64 = gen.normal((H, D), 1.0 / 16.0, 74, 0, 0, gen.S_W3)
+    codes = gen.unpack_int4(w["W3"])
+    for i in range(3):
+        for j in range(D):
+            byte = int(w["W3"][i, j // 2])
+            nib = (byte >> 4) if j % 2 else (byte & 0xF)
+            assert codes[i, j] == (nib - 16 if nib >= 8 else nib)
+    assert np.abs(codes).max() == 7 and codes.min() >= -7
+    deq = ref.dequantize_groups_int4(w["W3"], w["W3_scale"])
+    step = np.repeat(w["W3_scale"].astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(deq - w64) <= 0.5 * step * (1 + 1e-12))
+    assert np.array_equal(deq, codes.astype(np.float64) * step)
+    # integer codes, a power-of-two scale per group: exact rationals
+    D, H, T = 256, 6, 2
+    rngq = np.random.default_rng(75)
+    q = {k: rngq.integers(-8, 8, size=(H, D)).astype(np.int8) for k in ("W1", "W3", "W2T")}
+    packed = {k: ((v[:, 0::2].astype(np.uint8) & 0xF) | ((v[:, 1::2].astype(np.uint8) & 0xF) << 4))
+              for k, v in q.items()}
+    sc = {k: (2.0 ** -rngq.integers(0, 4, size=(H, D // 128))).astype(np.float32) for k in q}
+    wi = {**packed, **{k + "_scale": v for k, v in sc.items()}}
+    x = gen.small_integers((T, D), -1, 1, cfg=75, stream=0, dtype="bf16")
+    got = ref.ffn_standard_int4(x, wi)
+    xf = gen.as_float(x).astype(np.float64)
+    mats = {k: [[Fraction(int(q[k][i, j])) * Fraction(float(sc[k][i, j // 128])) for j in range(D)]
+                for i in range(H)] for k in q}
+    for t in range(T):
+        y, z, live = frac_ffn([Fraction(v) for v in xf[t]], mats["W1"], mats["W3"], mats["W2T"])
+        assert [Fraction(v) for v in got["y"][t]] == y
+        assert got["live"][t].tolist() == live
+
+
 def test_moe_exact_on_integers():
     """Top-K mixture (page "Model casting: ...", section "Where it generalizes"): y_t is the
     gate-weighted sum of the routed experts' FFN outputs, checked with exact rationals on
