@@ -25,7 +25,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
             KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
-            KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_COUNT };
+            KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_GATE_UP_T1_I4,
+            KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -36,7 +37,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_down_t1_i8", "k_moe_gather", "k_moe_combine",
                                             "k_gate_up_gemm", "k_union_list", "k_down_gemm",
                                             "k_rank_proj_t1_i8", "k_gate_up_lopa_t1_i8",
-                                            "k_gate_up_tb"};
+                                            "k_gate_up_tb", "k_gate_up_t1_i4",
+                                            "k_gate_up_dense_t1_i4", "k_down_t1_i4"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -667,6 +669,46 @@ sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
+// batch-1 int4 (group-scaled) standard gating
+template <bool DENSE>
+sffn_status run_i4_t1(sffn_handle* h, const void* x, const void* W1, const float* s1,
+                      const void* W3, const float* s3, const void* W2T, const float* s2,
+                      float* y, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
+    const int nc = (h->D + 2047) / 2048;
+    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    int splits = h->t1_splits_sparse;
+    while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
+    uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
+    float* yz = splits > 1 ? y : nullptr;
+    sffn_status st = SFFN_OK;
+#define SFFN_I4_GATE(NCV)                                                                         \
+    st = launch(h, DENSE ? KIND_GATE_UP_DENSE_T1_I4 : KIND_GATE_UP_T1_I4,                        \
+                k_gate_up_t1_i4<NCV, DENSE>, dim3(nb), dim3(K1_THREADS), s, (const uint16_t*)x,   \
+                (const uint8_t*)W1, s1, (const uint8_t*)W3, s3, h->a_buf, live, yz, h->D, h->H,   \
+                h->act)
+    switch (nc) {
+        case 1: SFFN_I4_GATE(1); break;
+        case 2: SFFN_I4_GATE(2); break;
+        case 3: SFFN_I4_GATE(3); break;
+        case 4: SFFN_I4_GATE(4); break;
+        default: return fail(h, SFFN_INTERNAL, "no int4 gate kernel for this width");
+    }
+#undef SFFN_I4_GATE
+    if (st != SFFN_OK) return st;
+    const int cb = 8 * 32;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I4, k_down_t1_i4<PMAX>, dim3(nbx, splits),
+                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                       (const uint8_t*)W2T, s2, y, h->D, h->H, splits,
+                                       DENSE ? 1 : 0));
+    if (st != SFFN_OK) return st;
+    if (DENSE) return SFFN_OK;
+    return run_live_list(h, 1, live_count, live_idx, s);
+}
+
 // batch-1 LoPA with int8 V, U, W3, W2T rows
 sffn_status run_lopa_i8_t1(sffn_handle* h, const void* x, const void* V, const float* sV,
                            const void* U, const float* sU, const void* W3, const float* s3,
@@ -801,8 +843,14 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         *out = nullptr;
         if (act != SFFN_ACT_RELU && act != SFFN_ACT_RSPLUS)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
-        if (dtype != SFFN_BF16 && dtype != SFFN_F32 && dtype != SFFN_I8)
+        if (dtype != SFFN_BF16 && dtype != SFFN_F32 && dtype != SFFN_I8 && dtype != SFFN_I4)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
+        if (dtype == SFFN_I4 && r != 0)
+            return fail(nullptr, SFFN_UNSUPPORTED, "int4 weights: standard-gating handles (r == 0) only");
+        if (dtype == SFFN_I4 && D % 128 != 0)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "int4 weights: D must be a multiple of 128");
+        if (dtype == SFFN_I4 && (H + KD_THREADS - 1) / KD_THREADS > 32 * 16)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "int4 weights: H too large");
         if (dtype == SFFN_I8 && r != 0 && r % 16 != 0)
             return fail(nullptr, SFFN_INVALID_ARGUMENT, "int8 weights: r must be a multiple of 16");
         if (dtype == SFFN_I8 && D % 16 != 0)
@@ -1003,8 +1051,8 @@ sffn_status sffn_forward_dense(sffn_handle* h, const void* x, const void* W1, co
         hipStream_t s;
         sffn_status st = check_common(h, x, W3, W2T, y, T, nullptr, nullptr, &s, stream);
         if (st != SFFN_OK) return st;
-        if (h->dtype == SFFN_I8)
-            return fail(h, SFFN_INVALID_ARGUMENT, "int8 handles take the _i8 forward calls");
+        if (h->dtype == SFFN_I8 || h->dtype == SFFN_I4)
+            return fail(h, SFFN_INVALID_ARGUMENT, "int8 and int4 handles take the _i8 / _i4 forward calls");
         if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "dense forward needs a standard-gating handle (r == 0)");
         if (!W1) return fail(h, SFFN_INVALID_ARGUMENT, "null W1");
         if (!aligned16(W1)) return fail(h, SFFN_INVALID_ARGUMENT, "W1 must be 16-byte aligned");
@@ -1085,8 +1133,8 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
         hipStream_t s;
         sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
         if (st != SFFN_OK) return st;
-        if (h->dtype == SFFN_I8)
-            return fail(h, SFFN_INVALID_ARGUMENT, "int8 handles take the _i8 forward calls");
+        if (h->dtype == SFFN_I8 || h->dtype == SFFN_I4)
+            return fail(h, SFFN_INVALID_ARGUMENT, "int8 and int4 handles take the _i8 / _i4 forward calls");
         if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "sparse forward needs a standard-gating handle (r == 0)");
         if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
             return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
@@ -1101,11 +1149,14 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
 static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, const float* s1,
                        const void* W3, const float* s3, const void* W2T, const float* s2,
                        float* y, int T, int mode, int32_t* live_count, int32_t* live_idx,
-                       void* stream, bool dense) {
+                       void* stream, bool dense, int bits = 8) {
     hipStream_t s;
     sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
     if (st != SFFN_OK) return st;
-    if (h->dtype != SFFN_I8) return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
+    if (bits == 8 && h->dtype != SFFN_I8)
+        return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
+    if (bits == 4 && h->dtype != SFFN_I4)
+        return fail(h, SFFN_INVALID_ARGUMENT, "the int4 forward needs an SFFN_I4 handle");
     if (h->r != 0) return fail(h, SFFN_INVALID_ARGUMENT, "standard-gating forward needs a handle with r == 0");
     if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
         return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
@@ -1118,13 +1169,42 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     for (int t = 0; t < T; ++t) {
         const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);
         float* yt = y + (size_t)t * h->D;
-        st = dense ? run_i8_t1<true>(h, xt, W1, s1, W3, s3, W2T, s2, yt, nullptr, nullptr, s)
-                   : run_i8_t1<false>(h, xt, W1, s1, W3, s3, W2T, s2, yt,
-                                      live_count ? live_count + t : nullptr,
-                                      live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
+        int32_t* lc = live_count ? live_count + t : nullptr;
+        int32_t* li = live_idx ? live_idx + (size_t)t * h->H : nullptr;
+        if (bits == 4)
+            st = dense ? run_i4_t1<true>(h, xt, W1, s1, W3, s3, W2T, s2, yt, nullptr, nullptr, s)
+                       : run_i4_t1<false>(h, xt, W1, s1, W3, s3, W2T, s2, yt, lc, li, s);
+        else
+            st = dense ? run_i8_t1<true>(h, xt, W1, s1, W3, s3, W2T, s2, yt, nullptr, nullptr, s)
+                       : run_i8_t1<false>(h, xt, W1, s1, W3, s3, W2T, s2, yt, lc, li, s);
         if (st != SFFN_OK) return st;
     }
     return SFFN_OK;
+}
+
+sffn_status sffn_forward_sparse_i4(sffn_handle* h, const void* x, const void* W1,
+                                   const float* W1_scale, const void* W3, const float* W3_scale,
+                                   const void* W2T, const float* W2T_scale, float* y, int T,
+                                   int mode, int32_t* live_count, int32_t* live_idx,
+                                   void* stream) {
+    try {
+        return forward_i8(h, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale, y, T, mode, live_count,
+                          live_idx, stream, false, 4);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_sparse_i4");
+    }
+}
+
+sffn_status sffn_forward_dense_i4(sffn_handle* h, const void* x, const void* W1,
+                                  const float* W1_scale, const void* W3, const float* W3_scale,
+                                  const void* W2T, const float* W2T_scale, float* y, int T,
+                                  void* stream) {
+    try {
+        return forward_i8(h, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale, y, T,
+                          SFFN_MODE_PER_TOKEN, nullptr, nullptr, stream, true, 4);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_dense_i4");
+    }
 }
 
 sffn_status sffn_forward_lopa_i8(sffn_handle* h, const void* x, const void* V,
@@ -1195,8 +1275,8 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
         hipStream_t s;
         sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
         if (st != SFFN_OK) return st;
-        if (h->dtype == SFFN_I8)
-            return fail(h, SFFN_INVALID_ARGUMENT, "int8 handles take the _i8 forward calls");
+        if (h->dtype == SFFN_I8 || h->dtype == SFFN_I4)
+            return fail(h, SFFN_INVALID_ARGUMENT, "int8 and int4 handles take the _i8 / _i4 forward calls");
         if (h->r == 0) return fail(h, SFFN_INVALID_ARGUMENT, "LoPA forward needs a handle with r > 0");
         if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
             return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));

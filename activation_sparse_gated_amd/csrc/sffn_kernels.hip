@@ -1504,6 +1504,234 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
 }
 
 // ---------------------------------------------------------------------------
+// Weight-only int4, batch 1: codes packed two per byte (column 2j in the low
+// nibble, two's complement), one fp32 scale per 128 columns of a row. A lane's
+// 16-byte load holds 32 codes of one 128-column group, so its partial dot
+// product takes one scale.
+constexpr int I4_GROUP = 128;
+
+// sum over 32 int4 codes (16 bytes) times fp32 x
+__device__ inline float dot32_i4(const u32x4& w, const float* xv) {
+    float s = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const int v = (int)(wq << (28 - 4 * b)) >> 28;  // sign-extended nibble b
+            s = fmaf((float)v, xv[8 * q + b], s);
+        }
+    }
+    return s;
+}
+
+// x[col .. col + 32) (bf16) as fp32; zeros past D
+__device__ inline void load_x32(const uint16_t* __restrict__ x, int col, int D, float* xv) {
+    load_x16(x, col, D, xv);
+    load_x16(x, col + 16, D, xv + 16);
+}
+
+// Gate and gathered up projection, int4 weights: z_i = sum_g s1_ig (q1_i,g . x_g);
+// for a live unit u_i likewise with W3, and a_i = A(z_i) u_i (the W2T scales
+// vary along D, so the down pass applies them). DENSE visits every unit. One
+// unit per wave; all W1 loads are issued first.
+template <int NC, bool DENSE>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i4(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ W1, const float* __restrict__ s1,
+    const uint8_t* __restrict__ W3, const float* __restrict__ s3, float* __restrict__ a_out,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int act) {
+    constexpr int CW = WAVE * 32;  // columns of one chunk
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int unit = blockIdx.x * K1_WAVES + wave;
+    const bool in = unit < H;
+    const int G = D / I4_GROUP;
+    const size_t rb = (size_t)D / 2;  // bytes per row
+    u32x4 w[NC], w3[NC];
+    float sc1[NC], sc3[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 32;
+        const bool ok = in && col < D;
+        w[c] = ok ? load_stream(W1 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+        sc1[c] = ok ? s1[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+        if (DENSE) w3[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+        sc3[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+    }
+    float xv[NC][32];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) load_x32(x, c * CW + lane * 32, D, xv[c]);
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    float sz = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) sz = fmaf(sc1[c], dot32_i4(w[c], xv[c]), sz);
+    const float z = wave_sum_dpp(sz);
+    const bool live = in && z > 0.0f;
+    if (!in) return;
+    if (lane == 0 && live_out) live_out[unit] = live ? 1 : 0;
+    if (!DENSE && !live) {
+        if (lane == 0) a_out[unit] = 0.0f;
+        return;
+    }
+    if (!DENSE) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 32;
+            w3[c] = col < D ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+        }
+    }
+    float su = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) su = fmaf(sc3[c], dot32_i4(w3[c], xv[c]), su);
+    const float u = wave_sum_dpp(su);
+    if (lane == 0) a_out[unit] = activation(act, z) * u;
+}
+
+// Down projection, int4 W2T rows: y[slice] = sum_i a_i s2_ig q2[i, slice] with
+// g the 128-column group of each lane's 32 columns. As k_down_t1_i8, with
+// column slices of 8 lanes x 32 columns = 256 columns (8 rows per wave load).
+template <int PMAX>
+__global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restrict__ a,
+                                                           const uint8_t* __restrict__ W2T,
+                                                           const float* __restrict__ s2,
+                                                           float* __restrict__ y, int D, int H,
+                                                           int splits, int dense) {
+    constexpr int LPR = 8;
+    constexpr int CB = LPR * 32;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 8;
+    __shared__ int list[KD_LCAP];
+    __shared__ float av[KD_LCAP];
+    __shared__ int wcount[PMAX * KD_WAVES];
+    __shared__ int woff[PMAX * KD_WAVES + 1];
+    __shared__ float red[KD_WAVES][CB];
+
+    const int nslices = (D + CB - 1) / CB;
+    const int per_xcd = (nslices + 7) / 8;
+    const int bx = blockIdx.x;
+    const int slice = (bx & 7) * per_xcd + (bx >> 3);
+    if (slice >= nslices) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * 32;
+    const bool col_ok = col < D;
+    const int G = D / I4_GROUP;
+    const size_t rb = (size_t)D / 2;
+    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
+
+    float ar[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        ar[p] = (p < P && row < h1) ? a[row] : 0.0f;
+    }
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
+        mk[p] = __ballot(keep);
+        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    if (wave == 0) {
+        constexpr int NCNT = PMAX * KD_WAVES;
+        int carry = 0;
+        for (int base = 0; base < NCNT; base += WAVE) {
+            const int i = base + lane;
+            const int v = i < NCNT ? wcount[i] : 0;
+            int incl = v;
+#pragma unroll
+            for (int o = 1; o < WAVE; o <<= 1) {
+                const int t = __shfl_up(incl, o, WAVE);
+                if (lane >= o) incl += t;
+            }
+            if (i < NCNT) woff[i] = carry + incl - v;
+            carry += __shfl(incl, WAVE - 1, WAVE);
+        }
+        if (lane == 0) woff[NCNT] = carry;
+    }
+    __syncthreads();
+
+    float acc[32];
+#pragma unroll
+    for (int k = 0; k < 32; ++k) acc[k] = 0.0f;
+    int p0 = 0;
+    while (p0 < P) {
+        int p1 = p0 + 1;
+        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
+        const int ebase = woff[p0 * KD_WAVES];
+        const int n = woff[p1 * KD_WAVES] - ebase;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
+                const int pos = woff[p * KD_WAVES + wave] - ebase +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+                av[pos] = ar[p];
+            }
+        }
+        __syncthreads();
+        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+            u32x4 wv[UF];
+            float sg[UF];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const bool ok = e < n && col_ok;
+                const int row = ok ? list[e] : 0;
+                wv[u] = ok ? load_stream(W2T + (size_t)row * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+                sg[u] = ok ? s2[(size_t)row * G + col / I4_GROUP] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const float aval = (e < n ? av[e] : 0.0f) * sg[u];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = wv[u][q];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        acc[8 * q + b] = fmaf(aval, (float)((int)(wq << (28 - 4 * b)) >> 28), acc[8 * q + b]);
+                }
+            }
+        }
+        __syncthreads();
+        p0 = p1;
+    }
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+        float v = acc[k];
+        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+        acc[k] = v;
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int k = 0; k < 32; ++k) red[wave][sub * 32 + k] = acc[k];
+    }
+    __syncthreads();
+    for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+        float s = 0.0f;
+        for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+        if (col0 + c < D) {
+            if (splits > 1)
+                atomicAdd(y + col0 + c, s);
+            else
+                y[col0 + c] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Small batches (2 <= T <= TT <= 4), bf16, on the VALU.
 //
 // N partial sums per lane reduced over the wave at once: log2(N) halving

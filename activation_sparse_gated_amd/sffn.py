@@ -21,7 +21,7 @@ SFFN_HIP_ERROR = -4
 SFFN_INTERNAL = -5
 
 SFFN_ACT_RELU, SFFN_ACT_RSPLUS = 0, 1
-SFFN_BF16, SFFN_F32, SFFN_I8 = 0, 1, 2
+SFFN_BF16, SFFN_F32, SFFN_I8, SFFN_I4 = 0, 1, 2, 3
 SFFN_MODE_PER_TOKEN, SFFN_MODE_UNION = 0, 1
 SFFN_FLAG_G_TILED, SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT = 1, 2, 4
 
@@ -30,7 +30,7 @@ EXPORTED = (
     "sffn_forward_lopa", "sffn_last_error", "sffn_status_string", "sffn_abi_version",
     "sffn_timing_enable", "sffn_timing_read", "sffn_kernel_kinds", "sffn_kernel_name",
     "sffn_forward_sparse_i8", "sffn_forward_dense_i8", "sffn_forward_moe",
-    "sffn_forward_lopa_i8",
+    "sffn_forward_lopa_i8", "sffn_forward_sparse_i4", "sffn_forward_dense_i4",
 )
 
 _lib = None
@@ -69,6 +69,10 @@ def load() -> ctypes.CDLL:
     lib.sffn_forward_lopa.argtypes = [P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_sparse_i8.restype = I
     lib.sffn_forward_sparse_i8.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_forward_sparse_i4.restype = I
+    lib.sffn_forward_sparse_i4.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_forward_dense_i4.restype = I
+    lib.sffn_forward_dense_i4.argtypes = [P, P, P, P, P, P, P, P, P, I, P]
     lib.sffn_forward_lopa_i8.restype = I
     lib.sffn_forward_lopa_i8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_dense_i8.restype = I
@@ -182,6 +186,27 @@ def sffn_forward_sparse_i8(handle, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale
     st = load().sffn_forward_sparse_i8(handle, _ptr(x), _ptr(W1), _ptr(W1_scale), _ptr(W3),
                                        _ptr(W3_scale), _ptr(W2T), _ptr(W2T_scale), _ptr(y), T,
                                        mode, _ptr(live_count), _ptr(live_idx), _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_sparse_i4(handle, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale, y, T: int,
+                           mode: int = SFFN_MODE_PER_TOKEN, live_count=None, live_idx=None,
+                           stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_sparse_i4(handle, _ptr(x), _ptr(W1), _ptr(W1_scale), _ptr(W3),
+                                       _ptr(W3_scale), _ptr(W2T), _ptr(W2T_scale), _ptr(y), T,
+                                       mode, _ptr(live_count), _ptr(live_idx), _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_dense_i4(handle, x, W1, W1_scale, W3, W3_scale, W2T, W2T_scale, y, T: int,
+                          stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_dense_i4(handle, _ptr(x), _ptr(W1), _ptr(W1_scale), _ptr(W3),
+                                      _ptr(W3_scale), _ptr(W2T), _ptr(W2T_scale), _ptr(y), T,
+                                      _stream(stream))
     if check:
         _check(st, handle)
     return st

@@ -727,6 +727,61 @@ def main() -> int:
         hq.close()
         del repq, WQ
 
+        # weight-only int4 with one scale per 128 columns: the decode workload's draws
+        w4 = gen.standard_weights_int4(D, H, s, cfg=2)
+        W4 = {kk: torch.from_numpy(np.ascontiguousarray(w4[kk])).cuda()
+              for kk in ("W1", "W3", "W2T", "W1_scale", "W3_scale", "W2T_scale")}
+        rep4 = [{kk: (W4[kk] if rr == 0 else W4[kk].clone()) for kk in W4} for rr in range(R)]
+        h4 = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_I4)
+
+        def q4_call(t, dense=False, live=False):
+            rp = rep4[t % R]
+            if dense:
+                sffn.sffn_forward_dense_i4(h4.ptr, x[t], rp["W1"], rp["W1_scale"], rp["W3"],
+                                           rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[t], 1)
+            else:
+                sffn.sffn_forward_sparse_i4(h4.ptr, x[t], rp["W1"], rp["W1_scale"], rp["W3"],
+                                            rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[t], 1,
+                                            sffn.SFFN_MODE_PER_TOKEN, cnt[t:t + 1] if live else None,
+                                            idx[t] if live else None)
+        for t in range(n):
+            q4_call(t, live=True)
+        torch.cuda.synchronize()
+        k4 = cnt.cpu().numpy().astype(np.int64)
+        res4 = {}
+        G4 = D // 128
+        for name, dense in (("sparse", False), ("dense", True)):
+            def fn4(dense=dense):
+                for t in range(n):
+                    q4_call(t, dense=dense)
+            g4 = capture(fn4)
+            ms4 = time_graph(g4, args.steps, args.warmup)
+            del g4
+            rows = np.full(n, H) if dense else k4
+            # packed int4 rows (D/2 bytes), their group scales, x in and y out
+            b4 = (H * D // 2 + 2 * rows * D // 2) + 4 * G4 * (H + 2 * rows) + 6 * D
+            res4[name + "_tokens_per_s"] = round(n / (ms4 * 1e-3), 1)
+            res4[name + "_touched_GBps"] = round(float(np.sum(b4)) / (ms4 * 1e-3) / 1e9, 1)
+        sffn.sffn_timing_enable(h4.ptr, True)
+        for t in range(n):
+            q4_call(t)
+        torch.cuda.synchronize()
+        sffn.sffn_timing_enable(h4.ptr, False)
+        kt4 = {}
+        for kd in range(nk):
+            ms_k, launches = sffn.sffn_timing_read(h4.ptr, kd, reset=(kd == nk - 1))
+            if launches:
+                kt4[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
+        res4["kernel_us"] = kt4
+        res4["measured_sparsity"] = round(float(1 - k4.mean() / H), 4)
+        res4["sparse_vs_dense_int4"] = round(res4["sparse_tokens_per_s"] / res4["dense_tokens_per_s"], 3)
+        res4["sparse_vs_dense_bf16"] = round(res4["sparse_tokens_per_s"] / extras["dense_tokens_per_s"], 3)
+        extras["int4_group128"] = res4
+        log("int4: " + ", ".join(f"{kk} {v:,}" for kk, v in res4.items() if not isinstance(v, dict))
+            + f", kernels (us/launch) {kt4}")
+        h4.close()
+        del rep4, W4
+
         # weight-only int8 LoPA: the LoPA workload's fp64 draws quantized per row
         wlq = gen.lopa_weights_int8(D, Hp, r, s, cfg=3)
         names = ("V", "U", "W3", "W2T", "V_scale", "U_scale", "W3_scale", "W2T_scale")

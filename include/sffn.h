@@ -74,7 +74,12 @@ enum { SFFN_ACT_RELU = 0, SFFN_ACT_RSPLUS = 1 };
  * Figure 9; the scheme is this library's reading). x stays bf16 and every
  * product and sum is fp32. Forward calls: the _i8 ones (standard gating with
  * r == 0, LoPA with r > 0). */
-enum { SFFN_BF16 = 0, SFFN_F32 = 1, SFFN_I8 = 2 };
+/* SFFN_I4: weight-only int4 with one fp32 scale per 128 columns of a row
+ * (one scale per row would round nearly every weight of a row with a large
+ * bias-like entry to zero); codes in [-8, 7], packed two per byte, column 2j
+ * in the low nibble. D % 128 == 0; standard gating only; forward calls: the
+ * _i4 ones. */
+enum { SFFN_BF16 = 0, SFFN_F32 = 1, SFFN_I8 = 2, SFFN_I4 = 3 };
 /* How a batch of T tokens moves data; never changes the result.
  * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set.
  * UNION:     the union of the tokens' live sets is read once and each row is
@@ -106,8 +111,10 @@ enum { SFFN_FLAG_G_TILED = 1u, SFFN_FLAG_RMSNORM = 2u, SFFN_FLAG_DOUBLE_ACT = 4u
  *               1..8192 for SFFN_BF16 handles with r == 0)
  *   act         SFFN_ACT_RELU or SFFN_ACT_RSPLUS
  *   dtype       SFFN_BF16 (weights and x as bf16 bit patterns; products in
- *               fp32), SFFN_F32, or SFFN_I8 (int8 weights with per-row
- *               scales, x bf16; needs D % 16 == 0 and r % 16 == 0)
+ *               fp32), SFFN_F32, SFFN_I8 (int8 weights with per-row
+ *               scales, x bf16; needs D % 16 == 0 and r % 16 == 0), or
+ *               SFFN_I4 (int4 weights with per-128-column scales, x bf16;
+ *               needs D % 128 == 0 and r == 0)
  *   flags       0, or for LoPA handles any of SFFN_FLAG_G_TILED,
  *               SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT (other bits, or any
  *               bit on a standard handle: SFFN_UNSUPPORTED)
@@ -167,6 +174,25 @@ sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, cons
  * which are the same for one token). Errors as for the other forward calls;
  * a non-int8 handle gives SFFN_INVALID_ARGUMENT.
  */
+/*
+ * Gate-first sparse forward and the dense comparator with weight-only int4
+ * weights (SFFN_I4 handles): as the _i8 calls, with W1, W3, W2T packed int4
+ * [H x D/2] bytes (16-byte aligned) and W1_scale, W3_scale, W2T_scale fp32
+ * [H x D/128] (4-byte aligned): weight (i, j) is code(i, j) * scale[i][j / 128].
+ * x bf16 [T x D], y fp32 [T x D]; tokens of a batch run one after another.
+ * Errors as for the other forward calls; a non-int4 handle gives
+ * SFFN_INVALID_ARGUMENT.
+ */
+sffn_status sffn_forward_sparse_i4(sffn_handle *h, const void *x, const void *W1,
+                                   const float *W1_scale, const void *W3, const float *W3_scale,
+                                   const void *W2T, const float *W2T_scale, float *y, int T,
+                                   int mode, int32_t *live_count, int32_t *live_idx,
+                                   void *stream);
+sffn_status sffn_forward_dense_i4(sffn_handle *h, const void *x, const void *W1,
+                                  const float *W1_scale, const void *W3, const float *W3_scale,
+                                  const void *W2T, const float *W2T_scale, float *y, int T,
+                                  void *stream);
+
 /*
  * LoPA gating with weight-only int8 weights (SFFN_I8 handles with r > 0, r a
  * multiple of 16): as sffn_forward_lopa, with V int8 [r x D], U int8 [H x r],

@@ -122,3 +122,22 @@ def run_lopa_i8(h, x, w, T, mode=sffn.SFFN_MODE_PER_TOKEN, want_live=True):
                               cnt, idx)
     torch.cuda.synchronize()
     return y, cnt, idx
+
+
+def run_i4(h, x, w, T, mode=sffn.SFFN_MODE_PER_TOKEN, dense=False, want_live=True):
+    """group-scaled int4 weights (W1/W3/W2T packed, *_scale fp32 [H, D/128])."""
+    D, H = h.D, h.H
+    dv = {k: torch.from_numpy(np.ascontiguousarray(w[k])).cuda()
+          for k in ("W1", "W3", "W2T", "W1_scale", "W3_scale", "W2T_scale")}
+    y = torch.full((T, D), float("nan"), dtype=torch.float32, device="cuda")
+    if dense:
+        sffn.sffn_forward_dense_i4(h.ptr, dev(x), dv["W1"], dv["W1_scale"], dv["W3"],
+                                   dv["W3_scale"], dv["W2T"], dv["W2T_scale"], y, T)
+        torch.cuda.synchronize()
+        return y, None, None
+    cnt = torch.full((T,), -1, dtype=torch.int32, device="cuda") if want_live else None
+    idx = torch.full((T, H), -1, dtype=torch.int32, device="cuda") if want_live else None
+    sffn.sffn_forward_sparse_i4(h.ptr, dev(x), dv["W1"], dv["W1_scale"], dv["W3"], dv["W3_scale"],
+                                dv["W2T"], dv["W2T_scale"], y, T, mode, cnt, idx)
+    torch.cuda.synchronize()
+    return y, cnt, idx

@@ -44,7 +44,7 @@ def test_library_exports_every_declared_function():
     ((64, 64, 8, 65, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
     ((64, 64, 0, 8193, 0, 0), sffn.SFFN_INVALID_ARGUMENT, "max_tokens"),
     ((64, 64, 0, 1, 2, 0), sffn.SFFN_UNSUPPORTED, "activation"),
-    ((64, 64, 0, 1, 0, 3), sffn.SFFN_UNSUPPORTED, "dtype"),
+    ((64, 64, 0, 1, 0, 4), sffn.SFFN_UNSUPPORTED, "dtype"),
 ])
 def test_create_rejects_bad_arguments(args, status, needle):
     st, h = sffn.sffn_create_status(*args)
@@ -58,6 +58,14 @@ def test_create_int8_checks():
     assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "16" in sffn.sffn_last_error(None)
     st, h = sffn.sffn_create_status(256, 64, 24, 1, 0, sffn.SFFN_I8, 0)
     assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "r must" in sffn.sffn_last_error(None)
+
+
+def test_create_int4_checks():
+    # int4 weights: D a multiple of 128, standard gating only
+    st, h = sffn.sffn_create_status(192, 64, 0, 1, 0, sffn.SFFN_I4, 0)
+    assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "128" in sffn.sffn_last_error(None)
+    st, h = sffn.sffn_create_status(256, 64, 16, 1, 0, sffn.SFFN_I4, 0)
+    assert st == sffn.SFFN_UNSUPPORTED and h is None and "int4" in sffn.sffn_last_error(None)
 
 
 def test_create_rejects_flags():
