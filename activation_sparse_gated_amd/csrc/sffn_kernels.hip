@@ -2130,68 +2130,126 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
     }
 }
 
-// Stage 2: y[T x D] += sum over units of a_rm[unit][t] * W2T[unit][:], over the
-// units live for some token (y is cleared by stage 1). Grid: (column tiles of
-// 128, row splits). The block compacts its split's units, then runs through them
-// in chunks of 64: the chunk's W2T rows are staged in LDS transposed
-// ([column][unit], two units packed per 32-bit write, rows padded to 144 B) and
-// its unit products as [unit][token]; the global loads of the next 3..6
-// chunks are in flight in registers. Each wave owns 2*NT of the block's NT x 8
-// output tiles (one token tile); the products are split into bf16 hi + lo
-// parts (two MFMAs, about 16 significant bits). Each wave adds its tiles to y
-// with fp32 atomics (one add per split per output), or stores them when there
-// is one split.
+// The transposing LDS read ds_read_b64_tr_b16: in each group of 16 lanes, lane l
+// receives element l%4 of the 4 consecutive bf16 that lane 4j + l/4 points at,
+// as its element j (checked on the device), so two reads give a lane the 8
+// consecutive K values of one column of a tile staged as K-rows.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Slot of 16-byte piece p in staged 256-byte K-row r (r < 32): a transposing
+// read touches rows 8g + {0..3} (or + {4..7}) at two adjacent pieces, which
+// land on 8 different slots; groups g and g + 1 use disjoint slot halves.
+__device__ inline int swz256(int r, int p) { return p ^ (2 * (r & 3) + 8 * ((r >> 3) & 1)); }
+
+__device__ inline u32x4 frag_tr(const uint8_t* part, int col0, int lane) {
+    typedef __attribute__((address_space(3))) i16x4* lds_v4;
+    const int g = lane >> 4, s = lane & 15;
+    const int col = col0 + 4 * (s & 3);
+    const int p = col >> 3, half = (col >> 2) & 1;
+    const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
+    const uint8_t* a0 = part + r0 * 256 + 16 * swz256(r0, p) + 8 * half;
+    const uint8_t* a1 = part + r1 * 256 + 16 * swz256(r1, p) + 8 * half;
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a0));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a1));
+    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+    return u32x4{w0.x, w0.y, w1.x, w1.y};
+}
+
+// Slot of 16-byte piece p in a staged 128-byte K-row r (r < 32). A transposing
+// read (frag_tr128) touches rows 8g + {0..3} (or + {4..7}) at two adjacent
+// pieces; rows of the same parity share a half of the banks, and bits 1 and 3
+// of the row put the four rows of each parity that one half-wave reads on four
+// different 32-byte slot pairs.
+__device__ inline int swz128(int r, int p) { return p ^ (2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1)); }
+
+// frag_tr over a part of 32 K-rows of 128 bytes (up to 64 bf16 columns).
+__device__ inline u32x4 frag_tr128(const uint8_t* part, int col0, int lane) {
+    typedef __attribute__((address_space(3))) i16x4* lds_v4;
+    const int g = lane >> 4, s = lane & 15;
+    const int col = col0 + 4 * (s & 3);
+    const int p = col >> 3, half = (col >> 2) & 1;
+    const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
+    const uint8_t* a0 = part + r0 * 128 + 16 * swz128(r0, p) + 8 * half;
+    const uint8_t* a1 = part + r1 * 128 + 16 * swz128(r1, p) + 8 * half;
+    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a0));
+    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a1));
+    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+    return u32x4{w0.x, w0.y, w1.x, w1.y};
+}
+
+// Stage 2: y[T x D] (+)= sum over the units live for some token of
+// a_rm[unit][t] W2T[unit][:] (y is cleared by stage 1 when splits > 1). Grid:
+// (column tiles of 128, unit-range splits). The block loads the umask words of
+// its split in one round and compacts the live units into an ascending list in
+// LDS, then runs through them in chunks of 64 with the global loads of the next
+// 4..6 chunks in flight in registers. A chunk is staged without reshaping: each
+// W2T row slice goes to LDS as it is (256-byte K-rows), the unit products as
+// bf16 hi and lo parts (about 16 significant bits together, rounded once per
+// block) in 128-byte K-rows [unit][token]. Both MFMA operands are read with the
+// transposing LDS read, which hands a lane the 8 consecutive units of one token
+// or one column. Each wave owns 2*NT of the block's NT x 8 output tiles (one
+// token tile) and adds them to y with fp32 atomics (one add per split per
+// output), or stores them when there is one split.
 constexpr int KDM_THREADS = 256;
 constexpr int KDM_LCAP = 2048;
 constexpr int KDM_KC = 64;         // units per chunk
 constexpr int KDM_NB = 128;        // columns per block
-constexpr int KDM_RS = KDM_KC + 8; // LDS row stride of the transposed W2T chunk (bf16)
 template <int NT>
 __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
     const float* __restrict__ a_rm, const uint64_t* __restrict__ umask,
     const uint16_t* __restrict__ W2T, float* __restrict__ y, int D, int H, int T, int splits) {
     static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
     constexpr int TP = 16 * NT;
-    constexpr int AS = TP + 4;              // LDS row stride of the product chunk (floats)
-    constexpr int APT = KDM_KC * TP / 4 / KDM_THREADS;  // float4 product pieces per thread
-    constexpr int WPT = 2;                              // (unit pair, 8 columns) pieces per thread
-    constexpr int NCW = 2 * NT;                         // column tiles per wave
-    constexpr int KDM_DEPTH = APT == 1 ? 6 : (APT == 2 ? 4 : 3);
+    constexpr int APT = KDM_KC * TP / 4 / KDM_THREADS;            // float4 product pieces per thread
+    constexpr int WPT = KDM_KC * KDM_NB * 2 / 16 / KDM_THREADS;   // 16-byte W2T pieces per thread
+    constexpr int NCW = 2 * NT;                                   // column tiles per wave
+    constexpr int DEPTH = NT == 1 ? 6 : (NT == 2 ? 5 : 4);        // chunks in flight
+    constexpr int WPART = 32 * 256;                               // 32 W2T K-rows of 128 columns
+    constexpr int APART = 32 * 128;                               // 32 product K-rows of <= 64 tokens
+    constexpr int STAGE = 2 * WPART + 4 * APART;                  // W (ks 0, 1), hi (ks 0, 1), lo (ks 0, 1)
+    constexpr int PM = KDM_LCAP / KDM_THREADS;                    // umask words per thread
+    static_assert(WPT == 4 && KDM_KC == 64, "staging plan: 64 units x 128 columns");
     __shared__ int list[KDM_LCAP];
-    __shared__ int wcnt[KDM_THREADS / WAVE];
-    __shared__ int nlist_s;
-    __shared__ __attribute__((aligned(16))) uint16_t bt[2][KDM_NB][KDM_RS];
-    __shared__ __attribute__((aligned(16))) float at[2][KDM_KC][AS];
+    __shared__ int wcnt[PM][KDM_THREADS / WAVE];
+    __shared__ __attribute__((aligned(256))) uint8_t stg[2][STAGE];
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int r16 = lane & 15;
-    const int kq = 8 * (lane >> 4);
     const int col0 = blockIdx.x * KDM_NB;
-    const int hs = (H + splits - 1) / splits;
+    const int hs = (H + splits - 1) / splits;  // <= KDM_LCAP (host-checked)
     const int h0 = blockIdx.y * hs;
     const int h1 = min(H, h0 + hs);
 
-    // compaction of the units live for some token, ascending within the block
-    if (threadIdx.x == 0) nlist_s = 0;
-    __syncthreads();
-    for (int base = h0; base < h1; base += KDM_THREADS) {
-        const int row = base + threadIdx.x;
-        const bool keep = row < h1 && umask[row] != 0ull;
-        const uint64_t m = __ballot(keep);
-        if (lane == 0) wcnt[wave] = __popcll(m);
-        __syncthreads();
-        int off = nlist_s;
-        for (int w = 0; w < wave; ++w) off += wcnt[w];
-        if (keep) {
-            const int pos = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            list[pos] = row;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) nlist_s += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-        __syncthreads();
+    // compaction of the units live for some token, ascending: every umask word of
+    // the split is requested before the first is used
+    bool keep[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        const int row = h0 + p * KDM_THREADS + threadIdx.x;
+        keep[p] = row < h1 && umask[row] != 0ull;
     }
-    const int n = nlist_s;
+    uint64_t mk[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        mk[p] = __ballot(keep[p]);
+        if (lane == 0) wcnt[p][wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    int n = 0;
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        int off = n;
+        for (int w = 0; w < KDM_THREADS / WAVE; ++w) {
+            const int c = wcnt[p][w];
+            if (w < wave) off += c;
+            n += c;
+        }
+        if (keep[p]) {
+            const int pos = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+            list[pos] = h0 + p * KDM_THREADS + threadIdx.x;
+        }
+    }
+    __syncthreads();
     const int nchunks = (n + KDM_KC - 1) / KDM_KC;
 
     // this wave's output tiles: token tile tt, column tiles cb .. cb + NCW - 1
@@ -2201,25 +2259,18 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
 #pragma unroll
     for (int i = 0; i < NCW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // W2T pieces: piece g = tid + 256 k -> unit pair g / 16, 8 columns at 8 * (g % 16)
-    u32x4 wv[KDM_DEPTH][WPT][2];
-    float4 av[KDM_DEPTH][APT];
-    // unconditional loads (pieces past the list read row 0 and become zeros), so the
-    // number of loads in flight is the same on every path
-    // (zeros are applied when the chunk is staged, not at the load)
-    bool wok[KDM_DEPTH][WPT][2], aok[KDM_DEPTH][APT];
+    // W2T piece g = tid + 256 k: unit row g / 16 of the chunk, 8 columns at 8 (g % 16)
+    u32x4 wv[DEPTH][WPT];
+    float4 av[DEPTH][APT];
+    bool wok[DEPTH][WPT], aok[DEPTH][APT];
     auto fetch = [&](int slot, int c) {
 #pragma unroll
         for (int k = 0; k < WPT; ++k) {
             const int g = threadIdx.x + k * KDM_THREADS;
-            const int up = g >> 4, col = col0 + 8 * (g & 15);
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int e = c * KDM_KC + 2 * up + h;
-                const bool ok = e < n && col < D;
-                wv[slot][k][h] = load_stream(W2T + (ok ? (size_t)list[e] * D + col : 0));
-                wok[slot][k][h] = ok;
-            }
+            const int e = c * KDM_KC + (g >> 4), col = col0 + 8 * (g & 15);
+            const bool ok = e < n && col < D;
+            wv[slot][k] = load_stream(W2T + (ok ? (size_t)list[e] * D + col : 0));
+            wok[slot][k] = ok;
         }
 #pragma unroll
         for (int q = 0; q < APT; ++q) {
@@ -2232,80 +2283,67 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
         }
     };
     auto stage_write = [&](int stage, int d) {
-        // W2T transposed, two units per 32-bit word. Write j of a lane goes to its
-        // column (j + cs) % 8, so that the lanes of one write instruction spread
-        // over the banks (rows 8 apart share banks).
-        const u32x4 z4 = u32x4{0u, 0u, 0u, 0u};
+        uint8_t* st = stg[stage];
 #pragma unroll
-        for (int kk = 0; kk < WPT; ++kk) {
-            const int g = threadIdx.x + kk * KDM_THREADS;
-            const int up = g >> 4, cs = g & 15;
-            const u32x4 wa = wok[d][kk][0] ? wv[d][kk][0] : z4;
-            const u32x4 wb = wok[d][kk][1] ? wv[d][kk][1] : z4;
-            uint32_t pk[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const uint32_t w0 = wa[k >> 1], w1 = wb[k >> 1];
-                pk[k] = (k & 1) ? ((w0 >> 16) | (w1 & 0xffff0000u)) : ((w0 & 0xffffu) | (w1 << 16));
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int k = (j + cs) & 7;
-                uint32_t v = pk[0];
-#pragma unroll
-                for (int m = 1; m < 8; ++m) v = k == m ? pk[m] : v;
-                *reinterpret_cast<uint32_t*>(&bt[stage][8 * cs + k][2 * up]) = v;
-            }
+        for (int k = 0; k < WPT; ++k) {
+            const int g = threadIdx.x + k * KDM_THREADS;
+            const int row = g >> 4, r = row & 31;
+            *reinterpret_cast<u32x4*>(st + (row >> 5) * WPART + r * 256 + 16 * swz256(r, g & 15)) =
+                wok[d][k] ? wv[d][k] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int q = 0; q < APT; ++q) {
             const int idx = threadIdx.x + q * KDM_THREADS;
-            *reinterpret_cast<float4*>(&at[stage][idx / (TP / 4)][4 * (idx % (TP / 4))]) =
-                aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const int row = idx / (TP / 4), r = row & 31, t0 = 4 * (idx % (TP / 4));
+            const float4 f = aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float fv[4] = {f.x, f.y, f.z, f.w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hi[j] = bf16_rne(fv[j]);
+                lo[j] = bf16_rne(fv[j] - __uint_as_float(hi[j] << 16));
+            }
+            const int off = 2 * WPART + (row >> 5) * APART + r * 128 + 16 * swz128(r, t0 >> 3) + 8 * ((t0 >> 2) & 1);
+            *reinterpret_cast<uint2*>(st + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+            *reinterpret_cast<uint2*>(st + off + 2 * APART) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
         }
     };
     auto compute = [&](int stage) {
+        const uint8_t* st = stg[stage];
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-            const int m = tt * 16 + r16;
-            uint32_t hi[8], lo[8];
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const float f = at[stage][ks * 32 + kq + k][m];
-                hi[k] = bf16_rne(f);
-                lo[k] = bf16_rne(f - __uint_as_float(hi[k] << 16));
-            }
-            const u32x4 ahi = u32x4{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16),
-                                    hi[4] | (hi[5] << 16), hi[6] | (hi[7] << 16)};
-            const u32x4 alo = u32x4{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16),
-                                    lo[4] | (lo[5] << 16), lo[6] | (lo[7] << 16)};
+            const uint8_t* ah = st + 2 * WPART + ks * APART;
+            const u32x4 fh = frag_tr128(ah, tt * 16, lane);
+            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane);
 #pragma unroll
             for (int i = 0; i < NCW; ++i) {
-                const u32x4 b = *reinterpret_cast<const u32x4*>(&bt[stage][(cb + i) * 16 + r16][ks * 32 + kq]);
-                acc[i] = mfma_bf16(ahi, b, acc[i]);
-                acc[i] = mfma_bf16(alo, b, acc[i]);
+                const u32x4 b = frag_tr(st + ks * WPART, (cb + i) * 16, lane);
+                acc[i] = mfma_bf16(fh, b, acc[i]);
+                acc[i] = mfma_bf16(fl, b, acc[i]);
             }
         }
     };
     // chunk c + 1 is staged into the other buffer while chunk c is multiplied
 #pragma unroll
-    for (int d = 0; d < KDM_DEPTH; ++d) fetch(d, d);
+    for (int d = 0; d < DEPTH; ++d) fetch(d, d);
     stage_write(0, 0);
     __syncthreads();
-    fetch(0, KDM_DEPTH);
-    const int niter = (nchunks + KDM_DEPTH - 1) / KDM_DEPTH * KDM_DEPTH;
-    for (int c0 = 0; c0 < niter; c0 += KDM_DEPTH) {
+    fetch(0, DEPTH);
+    const int niter = (nchunks + DEPTH - 1) / DEPTH * DEPTH;
+    for (int c0 = 0; c0 < niter; c0 += DEPTH) {
 #pragma unroll
-        for (int d = 0; d < KDM_DEPTH; ++d) {
+        for (int d = 0; d < DEPTH; ++d) {
             const int c = c0 + d;
-            const int nslot = (d + 1) % KDM_DEPTH;  // holds chunk c + 1
+            const int nslot = (d + 1) % DEPTH;  // holds chunk c + 1
             stage_write((c + 1) & 1, nslot);
             if (c < nchunks) compute(c & 1);
             __syncthreads();
-            fetch(nslot, c + 1 + KDM_DEPTH);
+            fetch(nslot, c + 1 + DEPTH);
         }
     }
-    // C layout: row (token) 4*(lane/16) + j of the token tile, column r16 of the column tile
+    if (n == 0 && splits > 1) return;  // nothing to add
+    // C layout: row (token) 4*(lane/16) + j of the token tile, column lane%16 of the column tile
+    const int r16 = lane & 15;
 #pragma unroll
     for (int i = 0; i < NCW; ++i) {
         const int col = col0 + (cb + i) * 16 + r16;
@@ -2523,11 +2561,7 @@ __global__ __launch_bounds__(256) void k_moe_combine(const float* __restrict__ y
 // W3), read as MFMA fragments with 16-byte LDS reads. The down kernel stages
 // K-rows of both operands (a_um rows of 128 tokens and W2T rows of 128
 // columns, one row per listed unit) and reads the fragments with the
-// transposing LDS read ds_read_b64_tr_b16: in each group of 16 lanes, lane l
-// receives element l%4 of the 4 consecutive bf16 that lane 4j + l/4 points at,
-// as its element j (checked on the device), so two reads give a lane the 8
-// consecutive K values of one row or column of the tile.
-typedef short i16x4 __attribute__((ext_vector_type(4)));
+// transposing LDS read (frag_tr, as the batched down kernel).
 
 // Gate/up tile: TM tokens x UN units, one wave per 64 x 64 sub-tile (z and u).
 template <int TM, int UN>
@@ -2765,25 +2799,6 @@ constexpr int KDG_NS = 4;
 constexpr int KDG_SEG = 256;                  // list entries per staged segment (one wave load)
 constexpr int KDG_SEG_CH = KDG_SEG / KDG_KC;  // chunks per segment
 constexpr int KDG_IPW = KDG_STAGE / 1024 / 4;
-
-// Slot of 16-byte piece p in staged 256-byte K-row r (r < 32): a transposing
-// read touches rows 8g + {0..3} (or + {4..7}) at two adjacent pieces, which
-// land on 8 different slots; groups g and g + 1 use disjoint slot halves.
-__device__ inline int swz256(int r, int p) { return p ^ (2 * (r & 3) + 8 * ((r >> 3) & 1)); }
-
-__device__ inline u32x4 frag_tr(const uint8_t* part, int col0, int lane) {
-    typedef __attribute__((address_space(3))) i16x4* lds_v4;
-    const int g = lane >> 4, s = lane & 15;
-    const int col = col0 + 4 * (s & 3);
-    const int p = col >> 3, half = (col >> 2) & 1;
-    const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
-    const uint8_t* a0 = part + r0 * 256 + 16 * swz256(r0, p) + 8 * half;
-    const uint8_t* a1 = part + r1 * 256 + 16 * swz256(r1, p) + 8 * half;
-    const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a0));
-    const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a1));
-    const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
-    return u32x4{w0.x, w0.y, w1.x, w1.y};
-}
 
 // y[T x D] (+)= sum over listed units k of a_um[k][t] W2T[k][:]. list == nullptr:
 // every unit 0..H-1. Grid: (token tiles x column tiles) x splits, XCD-contiguous.

@@ -236,7 +236,9 @@ def bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args):
         res["frac_of_mfma_peak"] = round(res["union_TFLOPs"] / peak, 4)
         # the same FFN as torch bf16 matmuls (hipBLASLt), eager, same weights
         xt = xb[:T].view(torch.bfloat16)
-        wt = [{k: rp[k].view(torch.bfloat16) for k in ("W1", "W3", "W2T")} for rp in reps[:2]]
+        # every replica, as the library calls rotate through them (two would stay in the
+        # memory-side cache at small T)
+        wt = [{k: rp[k].view(torch.bfloat16) for k in ("W1", "W3", "W2T")} for rp in reps]
 
         def torch_ffn(wd):
             z = F.linear(xt, wd["W1"])
@@ -245,14 +247,14 @@ def bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args):
                  else torch.relu(z)) * u
             return torch.matmul(a, wd["W2T"])
         for i in range(3):
-            torch_ffn(wt[i % 2])
+            torch_ffn(wt[i % R])
         torch.cuda.synchronize()
         n_t = max(4, calls)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(n_t):
-            torch_ffn(wt[i % 2])
+            torch_ffn(wt[i % R])
         e1.record()
         torch.cuda.synchronize()
         ms_t = e0.elapsed_time(e1) / n_t

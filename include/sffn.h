@@ -257,10 +257,13 @@ int sffn_abi_version(void);
  * pair recorded at the kernel's own begin and end. sffn_timing_read
  * synchronises with those events and returns, for kernel kind `kind`, the
  * summed duration in milliseconds and the number of launches since the last
- * reset (reset != 0 clears the totals after reading). Kinds are numbered
- * 0 .. sffn_kernel_kinds()-1 and named by sffn_kernel_name. Timing adds
- * events between launches, so it is off by default and must stay off during
- * stream capture.
+ * reset (reset != 0 clears the totals of every kind after reading). Kinds are
+ * numbered 0 .. sffn_kernel_kinds()-1 and named by sffn_kernel_name. Each timed
+ * launch holds two events until the next sffn_timing_read folds them into the
+ * totals and returns them to the handle's pool, so a long timed run should be
+ * read now and then. Timing adds events between launches, so it is off by
+ * default and must stay off during stream capture. Like the forward calls,
+ * these two must not run on one handle from two threads at once.
  */
 sffn_status sffn_timing_enable(sffn_handle *h, int enable);
 sffn_status sffn_timing_read(sffn_handle *h, int kind, double *total_ms, int64_t *launches,
