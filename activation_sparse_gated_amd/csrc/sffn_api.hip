@@ -86,7 +86,7 @@ struct sffn_handle {
     uint16_t* moe_x = nullptr;     // [2 * max_tokens x D] bf16
     float* moe_y = nullptr;        // [2 * max_tokens x D] fp32
     int tb_splits = 16;            // row splits of the small-batch down pass
-    int tb_max = 8;                // batches up to this size use the small-batch down pass
+    int tb_max = 4;                // batches up to this size use the small-batch down pass
     int tbv_max = 4;               // batches up to this size use the VALU gate/up pass
     int tbv_rw2 = 2, tbv_rw4 = 4;  // units per wave of the VALU gate/up pass (2 and 4 token slots)
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
@@ -415,10 +415,10 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     sffn_status st = SFFN_OK;
     const int ut = nt == 4 ? h->m_ut4 : (nt == 2 ? h->m_ut2 : h->m_ut1);  // unit tiles per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
-    const bool small = T <= h->tb_max && T <= 8;
-    const int splits = small ? h->tb_splits : h->m_splits;
+    const bool small_down = T <= h->tb_max && T <= 8;
+    const int splits = small_down ? h->tb_splits : h->m_splits;
     float* yz = splits > 1 ? y : nullptr;
-    if (small && T <= h->tbv_max && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
+    if (T <= h->tbv_max && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once
         const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
         const int tt = T <= 2 ? 2 : 4;
@@ -447,7 +447,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     }
 #undef SFFN_GATE_MFMA
     if (st != SFFN_OK) return st;
-    if (small) {
+    if (small_down) {
         // 512-byte row slices (32 lanes x 16 B), XCD-contiguous slice order
         const int cb = 32 * 8;
         const int nslices = (h->D + cb - 1) / cb;
@@ -969,7 +969,7 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             };
             h->tbv_rw2 = rw_env("SFFN_TBV_RW2", h->tbv_rw2);
             h->tbv_rw4 = rw_env("SFFN_TBV_RW4", h->tbv_rw4);
-            const int tbm = env_int("SFFN_TB_MAX", 8);
+            const int tbm = env_int("SFFN_TB_MAX", h->tb_max);
             if (tbm >= 0 && tbm <= 8) h->tb_max = tbm;
             while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;
             e = hipMalloc(&h->m_a, (size_t)H * h->m_tp * sizeof(float));
