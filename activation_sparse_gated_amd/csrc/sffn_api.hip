@@ -26,7 +26,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
             KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
             KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_GATE_UP_T1_I4,
-            KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_COUNT };
+            KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -38,7 +38,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_gemm", "k_union_list", "k_down_gemm",
                                             "k_rank_proj_t1_i8", "k_gate_up_lopa_t1_i8",
                                             "k_gate_up_tb", "k_gate_up_t1_i4",
-                                            "k_gate_up_dense_t1_i4", "k_down_t1_i4"};
+                                            "k_gate_up_dense_t1_i4", "k_down_t1_i4",
+                                            "k_gate_up_lopa_t1_i4"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -669,6 +670,22 @@ sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
+// int4 down pass over a_buf (group scales applied per 32-column piece)
+sffn_status run_down_t1_i4(sffn_handle* h, const void* W2T, const float* s2, float* y, int splits,
+                           bool dense, hipStream_t s) {
+    const int cb = 8 * 32;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    sffn_status st = SFFN_OK;
+    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I4, k_down_t1_i4<PMAX>, dim3(nbx, splits),
+                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                       (const uint8_t*)W2T, s2, y, h->D, h->H, splits,
+                                       dense ? 1 : 0));
+    return st;
+}
+
 // batch-1 int4 (group-scaled) standard gating
 template <bool DENSE>
 sffn_status run_i4_t1(sffn_handle* h, const void* x, const void* W1, const float* s1,
@@ -695,17 +712,59 @@ sffn_status run_i4_t1(sffn_handle* h, const void* x, const void* W1, const float
     }
 #undef SFFN_I4_GATE
     if (st != SFFN_OK) return st;
-    const int cb = 8 * 32;
-    const int nslices = (h->D + cb - 1) / cb;
-    const int nbx = ((nslices + 7) / 8) * 8;
-    const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
-    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I4, k_down_t1_i4<PMAX>, dim3(nbx, splits),
-                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
-                                       (const uint8_t*)W2T, s2, y, h->D, h->H, splits,
-                                       DENSE ? 1 : 0));
+    st = run_down_t1_i4(h, W2T, s2, y, splits, DENSE, s);
     if (st != SFFN_OK) return st;
     if (DENSE) return SFFN_OK;
+    return run_live_list(h, 1, live_count, live_idx, s);
+}
+
+// batch-1 LoPA with int8 V and U rows and group-scaled int4 W3 and W2T rows
+sffn_status run_lopa_i4_t1(sffn_handle* h, const void* x, const void* V, const float* sV,
+                           const void* U, const float* sU, const void* W3, const float* s3,
+                           const void* W2T, const float* s2, float* y, int32_t* live_count,
+                           int32_t* live_idx, hipStream_t s) {
+    int splits = h->t1_splits_sparse;
+    while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
+    float* yz = splits > 1 ? y : nullptr;
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    sffn_status st = SFFN_OK;
+    const int nc8 = pick(kNC_T1, 7, (h->D + 1023) / 1024);
+    const int nbr = (h->r + K1_WAVES - 1) / K1_WAVES;
+    SFFN_NCT1_SWITCH(nc8, st = launch(h, KIND_RANK_PROJ_T1_I8, k_rank_proj_t1_i8<NC>, dim3(nbr),
+                                      dim3(K1_THREADS), s, (const uint16_t*)x, (const int8_t*)V,
+                                      sV, h->t_buf, yz, h->D, h->r));
+    if (st != SFFN_OK) return st;
+    const int nb = (h->H + K1_WAVES * KLQ_UPW - 1) / (K1_WAVES * KLQ_UPW);
+    const int nr = (h->r + 255) / 256;
+    const int nc = (h->D + 2047) / 2048;
+#define SFFN_LOPA_I4(NCV, NRV)                                                                    \
+    st = launch(h, KIND_GATE_UP_LOPA_T1_I4, k_gate_up_lopa_t1_i4<NCV, NRV>, dim3(nb),             \
+                dim3(K1_THREADS), s, (const uint16_t*)x, (const float*)h->t_buf, (const int8_t*)U, \
+                sU, (const uint8_t*)W3, s3, h->a_buf, live, h->D, h->H, h->r, h->act, h->flags)
+#define SFFN_LOPA_I4_NR(NCV)                                                                      \
+    switch (nr) {                                                                                 \
+        case 1: SFFN_LOPA_I4(NCV, 1); break;                                                      \
+        case 2: SFFN_LOPA_I4(NCV, 2); break;                                                      \
+        case 3: SFFN_LOPA_I4(NCV, 3); break;                                                      \
+        case 4: SFFN_LOPA_I4(NCV, 4); break;                                                      \
+        case 5: SFFN_LOPA_I4(NCV, 5); break;                                                      \
+        case 6: SFFN_LOPA_I4(NCV, 6); break;                                                      \
+        case 7: SFFN_LOPA_I4(NCV, 7); break;                                                      \
+        case 8: SFFN_LOPA_I4(NCV, 8); break;                                                      \
+        default: return fail(h, SFFN_INTERNAL, "rank too large for the int4 LoPA gate");          \
+    }
+    switch (nc) {
+        case 1: SFFN_LOPA_I4_NR(1); break;
+        case 2: SFFN_LOPA_I4_NR(2); break;
+        case 3: SFFN_LOPA_I4_NR(3); break;
+        case 4: SFFN_LOPA_I4_NR(4); break;
+        default: return fail(h, SFFN_INTERNAL, "no int4 LoPA gate kernel for this width");
+    }
+#undef SFFN_LOPA_I4_NR
+#undef SFFN_LOPA_I4
+    if (st != SFFN_OK) return st;
+    st = run_down_t1_i4(h, W2T, s2, y, splits, false, s);
+    if (st != SFFN_OK) return st;
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
@@ -845,8 +904,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
         if (dtype != SFFN_BF16 && dtype != SFFN_F32 && dtype != SFFN_I8 && dtype != SFFN_I4)
             return fail(nullptr, SFFN_UNSUPPORTED, "unknown dtype " + std::to_string(dtype));
-        if (dtype == SFFN_I4 && r != 0)
-            return fail(nullptr, SFFN_UNSUPPORTED, "int4 weights: standard-gating handles (r == 0) only");
+        if (dtype == SFFN_I4 && r != 0 && r % 16 != 0)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "int4 LoPA weights: r must be a multiple of 16");
         if (dtype == SFFN_I4 && D % 128 != 0)
             return fail(nullptr, SFFN_INVALID_ARGUMENT, "int4 weights: D must be a multiple of 128");
         if (dtype == SFFN_I4 && (H + KD_THREADS - 1) / KD_THREADS > 32 * 16)
@@ -1207,39 +1266,65 @@ sffn_status sffn_forward_dense_i4(sffn_handle* h, const void* x, const void* W1,
     }
 }
 
+// LoPA with quantised weights: int8 rows everywhere (bits 8), or int8 V and U
+// rows with group-scaled int4 W3 and W2T rows (bits 4)
+static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, const float* sV,
+                                  const void* U, const float* sU, const void* W3, const float* s3,
+                                  const void* W2T, const float* s2, float* y, int T, int mode,
+                                  int32_t* live_count, int32_t* live_idx, void* stream, int bits) {
+    hipStream_t s;
+    sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
+    if (st != SFFN_OK) return st;
+    if (bits == 8 && h->dtype != SFFN_I8)
+        return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
+    if (bits == 4 && h->dtype != SFFN_I4)
+        return fail(h, SFFN_INVALID_ARGUMENT, "the int4 forward needs an SFFN_I4 handle");
+    if (h->r == 0) return fail(h, SFFN_INVALID_ARGUMENT, "LoPA forward needs a handle with r > 0");
+    if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
+        return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
+    if (!V || !U) return fail(h, SFFN_INVALID_ARGUMENT, "null V or U");
+    if (!aligned16(V) || !aligned16(U))
+        return fail(h, SFFN_INVALID_ARGUMENT, "V and U must be 16-byte aligned");
+    if (!sV || !sU || !s3 || !s2) return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
+    auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
+    if (!al4(sV) || !al4(sU) || !al4(s3) || !al4(s2))
+        return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
+    // a batch runs token by token (both modes compute the same result)
+    for (int t = 0; t < T; ++t) {
+        const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);
+        float* yt = y + (size_t)t * h->D;
+        int32_t* lc = live_count ? live_count + t : nullptr;
+        int32_t* li = live_idx ? live_idx + (size_t)t * h->H : nullptr;
+        st = bits == 4 ? run_lopa_i4_t1(h, xt, V, sV, U, sU, W3, s3, W2T, s2, yt, lc, li, s)
+                       : run_lopa_i8_t1(h, xt, V, sV, U, sU, W3, s3, W2T, s2, yt, lc, li, s);
+        if (st != SFFN_OK) return st;
+    }
+    return SFFN_OK;
+}
+
 sffn_status sffn_forward_lopa_i8(sffn_handle* h, const void* x, const void* V,
                                  const float* V_scale, const void* U, const float* U_scale,
                                  const void* W3, const float* W3_scale, const void* W2T,
                                  const float* W2T_scale, float* y, int T, int mode,
                                  int32_t* live_count, int32_t* live_idx, void* stream) {
     try {
-        hipStream_t s;
-        sffn_status st = check_common(h, x, W3, W2T, y, T, live_count, live_idx, &s, stream);
-        if (st != SFFN_OK) return st;
-        if (h->dtype != SFFN_I8)
-            return fail(h, SFFN_INVALID_ARGUMENT, "the int8 forward needs an SFFN_I8 handle");
-        if (h->r == 0) return fail(h, SFFN_INVALID_ARGUMENT, "LoPA forward needs a handle with r > 0");
-        if (mode != SFFN_MODE_PER_TOKEN && mode != SFFN_MODE_UNION)
-            return fail(h, SFFN_UNSUPPORTED, "unknown mode " + std::to_string(mode));
-        if (!V || !U) return fail(h, SFFN_INVALID_ARGUMENT, "null V or U");
-        if (!aligned16(V) || !aligned16(U))
-            return fail(h, SFFN_INVALID_ARGUMENT, "V and U must be 16-byte aligned");
-        if (!V_scale || !U_scale || !W3_scale || !W2T_scale)
-            return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
-        auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
-        if (!al4(V_scale) || !al4(U_scale) || !al4(W3_scale) || !al4(W2T_scale))
-            return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-        // a batch runs token by token (both modes compute the same result)
-        for (int t = 0; t < T; ++t) {
-            const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);
-            st = run_lopa_i8_t1(h, xt, V, V_scale, U, U_scale, W3, W3_scale, W2T, W2T_scale,
-                                y + (size_t)t * h->D, live_count ? live_count + t : nullptr,
-                                live_idx ? live_idx + (size_t)t * h->H : nullptr, s);
-            if (st != SFFN_OK) return st;
-        }
-        return SFFN_OK;
+        return forward_lopa_q(h, x, V, V_scale, U, U_scale, W3, W3_scale, W2T, W2T_scale, y, T,
+                              mode, live_count, live_idx, stream, 8);
     } catch (...) {
         return fail(h, SFFN_INTERNAL, "exception in sffn_forward_lopa_i8");
+    }
+}
+
+sffn_status sffn_forward_lopa_i4(sffn_handle* h, const void* x, const void* V,
+                                 const float* V_scale, const void* U, const float* U_scale,
+                                 const void* W3, const float* W3_scale, const void* W2T,
+                                 const float* W2T_scale, float* y, int T, int mode,
+                                 int32_t* live_count, int32_t* live_idx, void* stream) {
+    try {
+        return forward_lopa_q(h, x, V, V_scale, U, U_scale, W3, W3_scale, W2T, W2T_scale, y, T,
+                              mode, live_count, live_idx, stream, 4);
+    } catch (...) {
+        return fail(h, SFFN_INTERNAL, "exception in sffn_forward_lopa_i4");
     }
 }
 

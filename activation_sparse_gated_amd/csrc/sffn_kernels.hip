@@ -1590,6 +1590,96 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i4(
     if (lane == 0) a_out[unit] = activation(act, z) * u;
 }
 
+// LoPA gate with int8 U rows and gathered up projection with group-scaled int4
+// W3 rows. The gate is that of k_gate_up_lopa_t1_i8 (four units per wave, 16
+// lanes per unit: z_i = sU_i (qU_i . t), t through RMSNorm when asked, plus
+// (G x)_i when asked); each live unit of the wave then takes the whole wave for
+// its W3 row: u_i = sum_g s3_ig (q3_i,g . x_g), through A as well under double
+// activation, and a_i = A(z_i) g(u_i) (the down pass applies the W2T group
+// scales). NC chunks of 2048 columns, NR pieces of 256 int8 of a U row.
+template <int NC, int NR>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i4(
+    const uint16_t* __restrict__ x, const float* __restrict__ t_in,
+    const int8_t* __restrict__ U, const float* __restrict__ sU, const uint8_t* __restrict__ W3,
+    const float* __restrict__ s3, float* __restrict__ a_out, uint8_t* __restrict__ live_out,
+    int D, int H, int r, int act, unsigned flags) {
+    constexpr int CW = WAVE * 32;  // columns of one full-wave chunk of an int4 row
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane & 15, grp = lane >> 4;
+    const int base = (blockIdx.x * K1_WAVES + wave) * KLQ_UPW;
+    const int unit = base + grp;
+    const bool in = unit < H;
+    const int G = D / I4_GROUP;
+    const size_t rb = (size_t)D / 2;  // bytes per int4 row
+    u32x4 u[NR];
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+        const int col = c * 256 + sub * 16;
+        u[c] = (in && col < r) ? load_stream(U + (size_t)unit * r + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float tv[NR][16];
+#pragma unroll
+    for (int c = 0; c < NR; ++c) {
+        const int col = c * 256 + sub * 16;
+        if (col < r) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a = *reinterpret_cast<const float4*>(t_in + col + 4 * q);
+                tv[c][4 * q] = a.x; tv[c][4 * q + 1] = a.y; tv[c][4 * q + 2] = a.z; tv[c][4 * q + 3] = a.w;
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 16; ++k) tv[c][k] = 0.0f;
+        }
+    }
+    float xv[NC][32];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) load_x32(x, c * CW + lane * 32, D, xv[c]);
+    const float su_ = in ? sU[unit] : 0.0f;
+    const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
+    float inv = 1.0f;  // RMSNorm of t: every lane group sees all of t
+    if (flags & LOPA_RMSNORM) {
+        float ss = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NR; ++c)
+#pragma unroll
+            for (int k = 0; k < 16; ++k) ss = fmaf(tv[c][k], tv[c][k], ss);
+        inv = 1.0f / sqrtf(group16_sum(ss) / (float)r + RMS_EPS);
+    }
+    float sz = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NR; ++c) sz = dot16_i8(u[c], tv[c], sz);
+    const float z = group16_sum(sz) * su_ * inv + gx;
+    const bool live = in && z > 0.0f;
+    if (in && sub == 0) {
+        if (live_out) live_out[unit] = live ? 1 : 0;
+        if (!live) a_out[unit] = 0.0f;
+    }
+    uint64_t m = __ballot(live && sub == 0);
+    while (m) {
+        const int g = __builtin_ctzll(m) >> 4;
+        m &= m - 1;
+        const int ul = base + g;
+        const float zl = __shfl(z, 16 * g);
+        u32x4 w3[NC];
+        float sc3[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 32;
+            const bool ok = col < D;
+            w3[c] = ok ? load_stream(W3 + (size_t)ul * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+            sc3[c] = ok ? s3[(size_t)ul * G + col / I4_GROUP] : 0.0f;
+        }
+        float s = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) s = fmaf(sc3[c], dot32_i4(w3[c], xv[c]), s);
+        const float uu = wave_sum_dpp(s);
+        const float g3 = (flags & LOPA_DOUBLE_ACT) ? activation(act, uu) : uu;
+        if (lane == 0) a_out[ul] = activation(act, zl) * g3;
+    }
+}
+
 // Down projection, int4 W2T rows: y[slice] = sum_i a_i s2_ig q2[i, slice] with
 // g the 128-column group of each lane's 32 columns. As k_down_t1_i8, with
 // column slices of 8 lanes x 32 columns = 256 columns (8 rows per wave load).

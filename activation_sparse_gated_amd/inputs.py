@@ -215,6 +215,28 @@ def lopa_weights_int8(D: int, Hp: int, r: int, sparsity: float | None, cfg: int,
     return out
 
 
+def lopa_weights_int4(D: int, Hp: int, r: int, sparsity: float | None, cfg: int, layer: int = 0,
+                      replica: int = 0, offset: float | None = None) -> dict:
+    """The fp64 draws of lopa_weights (same streams, V[0] = e_0, U[:, 0] = c): V and U
+    quantized per row to int8 (V, U int8 and V_scale, U_scale fp32), W3 and W2T to int4
+    with one scale per 128 columns (packed uint8 [Hp, D/2], scales fp32 [Hp, D/128])."""
+    V = normal((r, D), 1.0 / np.sqrt(D), cfg, layer, replica, S_V)
+    U = normal((Hp, r), 1.0 / np.sqrt(r), cfg, layer, replica, S_U)
+    c = offset if offset is not None else (gate_offset(sparsity) if sparsity is not None else None)
+    if c is not None:
+        V[0, :] = 0.0
+        V[0, 0] = 1.0
+        U[:, 0] = c
+    out = {"offset": c}
+    out["V"], out["V_scale"] = quantize_rows_int8(V)
+    out["U"], out["U_scale"] = quantize_rows_int8(U)
+    out["W3"], out["W3_scale"] = quantize_groups_int4(normal((Hp, D), 1.0 / np.sqrt(D), cfg, layer,
+                                                             replica, S_W3))
+    out["W2T"], out["W2T_scale"] = quantize_groups_int4(normal((Hp, D), 1.0 / np.sqrt(Hp), cfg,
+                                                               layer, replica, S_W2T))
+    return out
+
+
 def small_integers(shape, lo: int, hi: int, cfg: int, layer: int = 0, replica: int = 0,
                    stream: int = 0, dtype: str = "bf16") -> np.ndarray:
     """Integers uniform in [lo, hi]; exact in bf16 and fp32 for |v| <= 256."""

@@ -31,6 +31,7 @@ EXPORTED = (
     "sffn_timing_enable", "sffn_timing_read", "sffn_kernel_kinds", "sffn_kernel_name",
     "sffn_forward_sparse_i8", "sffn_forward_dense_i8", "sffn_forward_moe",
     "sffn_forward_lopa_i8", "sffn_forward_sparse_i4", "sffn_forward_dense_i4",
+    "sffn_forward_lopa_i4",
 )
 
 _lib = None
@@ -75,6 +76,8 @@ def load() -> ctypes.CDLL:
     lib.sffn_forward_dense_i4.argtypes = [P, P, P, P, P, P, P, P, P, I, P]
     lib.sffn_forward_lopa_i8.restype = I
     lib.sffn_forward_lopa_i8.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_forward_lopa_i4.restype = I
+    lib.sffn_forward_lopa_i4.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_dense_i8.restype = I
     lib.sffn_forward_dense_i8.argtypes = [P, P, P, P, P, P, P, P, P, I, P]
     lib.sffn_forward_moe.restype = I
@@ -216,6 +219,18 @@ def sffn_forward_lopa_i8(handle, x, V, V_scale, U, U_scale, W3, W3_scale, W2T, W
                          T: int, mode: int = SFFN_MODE_PER_TOKEN, live_count=None, live_idx=None,
                          stream=None, check: bool = True) -> int:
     st = load().sffn_forward_lopa_i8(handle, _ptr(x), _ptr(V), _ptr(V_scale), _ptr(U),
+                                     _ptr(U_scale), _ptr(W3), _ptr(W3_scale), _ptr(W2T),
+                                     _ptr(W2T_scale), _ptr(y), T, mode, _ptr(live_count),
+                                     _ptr(live_idx), _stream(stream))
+    if check:
+        _check(st, handle)
+    return st
+
+
+def sffn_forward_lopa_i4(handle, x, V, V_scale, U, U_scale, W3, W3_scale, W2T, W2T_scale, y,
+                         T: int, mode: int = SFFN_MODE_PER_TOKEN, live_count=None, live_idx=None,
+                         stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_lopa_i4(handle, _ptr(x), _ptr(V), _ptr(V_scale), _ptr(U),
                                      _ptr(U_scale), _ptr(W3), _ptr(W3_scale), _ptr(W2T),
                                      _ptr(W2T_scale), _ptr(y), T, mode, _ptr(live_count),
                                      _ptr(live_idx), _stream(stream))

@@ -784,52 +784,60 @@ def main() -> int:
         h4.close()
         del rep4, W4
 
-        # weight-only int8 LoPA: the LoPA workload's fp64 draws quantized per row
-        wlq = gen.lopa_weights_int8(D, Hp, r, s, cfg=3)
+        # quantised LoPA: the LoPA workload's fp64 draws with V, U, W3, W2T in int8 rows, and
+        # with V, U in int8 rows and W3, W2T in int4 (one scale per 128 columns)
         names = ("V", "U", "W3", "W2T", "V_scale", "U_scale", "W3_scale", "W2T_scale")
-        WLQ = {kk: torch.from_numpy(np.ascontiguousarray(wlq[kk])).cuda() for kk in names}
-        replq = [{kk: (WLQ[kk] if rr == 0 else WLQ[kk].clone()) for kk in WLQ} for rr in range(R)]
-        hlq = sffn.Handle(D, Hp, r, 1, act, sffn.SFFN_I8)
+        for bits in (8, 4):
+            wlq = (gen.lopa_weights_int8 if bits == 8 else gen.lopa_weights_int4)(D, Hp, r, s, cfg=3)
+            WLQ = {kk: torch.from_numpy(np.ascontiguousarray(wlq[kk])).cuda() for kk in names}
+            replq = [{kk: (WLQ[kk] if rr == 0 else WLQ[kk].clone()) for kk in WLQ} for rr in range(R)]
+            hlq = sffn.Handle(D, Hp, r, 1, act, sffn.SFFN_I8 if bits == 8 else sffn.SFFN_I4)
+            fwd = sffn.sffn_forward_lopa_i8 if bits == 8 else sffn.sffn_forward_lopa_i4
 
-        def lq_call(t, live=False):
-            rp = replq[t % R]
-            sffn.sffn_forward_lopa_i8(hlq.ptr, xl[t], rp["V"], rp["V_scale"], rp["U"], rp["U_scale"],
-                                      rp["W3"], rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[t], 1,
-                                      sffn.SFFN_MODE_PER_TOKEN, cl[t:t + 1] if live else None,
-                                      il[t] if live else None)
-        for t in range(n):
-            lq_call(t, live=True)
-        torch.cuda.synchronize()
-        klq = cl.cpu().numpy().astype(np.int64)
-
-        def lq_stream():
+            def lq_call(t, live=False):
+                rp = replq[t % R]
+                fwd(hlq.ptr, xl[t], rp["V"], rp["V_scale"], rp["U"], rp["U_scale"], rp["W3"],
+                    rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[t], 1, sffn.SFFN_MODE_PER_TOKEN,
+                    cl[t:t + 1] if live else None, il[t] if live else None)
             for t in range(n):
-                lq_call(t)
-        g_lq = capture(lq_stream)
-        ms_lq = time_graph(g_lq, args.steps, args.warmup)
-        del g_lq
-        lq_tok_s = n / (ms_lq * 1e-3)
-        # int8 V, U, live W3 and W2T rows, their fp32 scales, x in and y out
-        lq_bytes = (r * (D + Hp) + 2 * klq * D) + 4 * (r + Hp + 2 * klq) + 6 * D
-        sffn.sffn_timing_enable(hlq.ptr, True)
-        lq_stream()
-        torch.cuda.synchronize()
-        sffn.sffn_timing_enable(hlq.ptr, False)
-        ktl = {}
-        for kd in range(nk):
-            ms_k, launches = sffn.sffn_timing_read(hlq.ptr, kd, reset=(kd == nk - 1))
-            if launches:
-                ktl[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
-        extras["lopa_int8"] = {
-            "tokens_per_s": round(lq_tok_s, 1),
-            "touched_GBps": round(float(np.sum(lq_bytes)) / (ms_lq * 1e-3) / 1e9, 1),
-            "measured_sparsity": round(float(1 - klq.mean() / Hp), 4),
-            "speedup_vs_lopa_bf16": round(lq_tok_s / extras["lopa_tokens_per_s"], 3),
-            "speedup_vs_dense_bf16": round(lq_tok_s / extras["dense_tokens_per_s"], 3),
-            "kernel_us": ktl}
-        log(f"lopa int8: {ms_lq:.3f} ms/step, {lq_tok_s:,.0f} tokens/s, kernels (us/launch) {ktl}")
-        hlq.close()
-        del replq, WLQ
+                lq_call(t, live=True)
+            torch.cuda.synchronize()
+            klq = cl.cpu().numpy().astype(np.int64)
+
+            def lq_stream():
+                for t in range(n):
+                    lq_call(t)
+            g_lq = capture(lq_stream)
+            ms_lq = time_graph(g_lq, args.steps, args.warmup)
+            del g_lq
+            lq_tok_s = n / (ms_lq * 1e-3)
+            # int8 V and U rows and their row scales; the live W3 and W2T rows (int8 with a
+            # row scale, or int4 with a scale per 128 columns); x in and y out
+            if bits == 8:
+                lq_bytes = (r * (D + Hp) + 2 * klq * D) + 4 * (r + Hp + 2 * klq) + 6 * D
+            else:
+                lq_bytes = (r * (D + Hp) + klq * D) + 4 * (r + Hp) + 2 * klq * 4 * (D // 128) + 6 * D
+            sffn.sffn_timing_enable(hlq.ptr, True)
+            lq_stream()
+            torch.cuda.synchronize()
+            sffn.sffn_timing_enable(hlq.ptr, False)
+            ktl = {}
+            for kd in range(nk):
+                ms_k, launches = sffn.sffn_timing_read(hlq.ptr, kd, reset=(kd == nk - 1))
+                if launches:
+                    ktl[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
+            extras["lopa_int8" if bits == 8 else "lopa_int4_up_down"] = {
+                "tokens_per_s": round(lq_tok_s, 1),
+                "touched_GBps": round(float(np.sum(lq_bytes)) / (ms_lq * 1e-3) / 1e9, 1),
+                "touched_MB_per_token": round(float(np.mean(lq_bytes)) / 1e6, 3),
+                "measured_sparsity": round(float(1 - klq.mean() / Hp), 4),
+                "speedup_vs_lopa_bf16": round(lq_tok_s / extras["lopa_tokens_per_s"], 3),
+                "speedup_vs_dense_bf16": round(lq_tok_s / extras["dense_tokens_per_s"], 3),
+                "kernel_us": ktl}
+            log(f"lopa int{bits}: {ms_lq:.3f} ms/step, {lq_tok_s:,.0f} tokens/s, "
+                f"kernels (us/launch) {ktl}")
+            hlq.close()
+            del replq, WLQ
 
     # ---------------------------------------------------------------- batched decode and stacks
     if not args.no_extras:

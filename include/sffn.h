@@ -77,8 +77,11 @@ enum { SFFN_ACT_RELU = 0, SFFN_ACT_RSPLUS = 1 };
 /* SFFN_I4: weight-only int4 with one fp32 scale per 128 columns of a row
  * (one scale per row would round nearly every weight of a row with a large
  * bias-like entry to zero); codes in [-8, 7], packed two per byte, column 2j
- * in the low nibble. D % 128 == 0; standard gating only; forward calls: the
- * _i4 ones. */
+ * in the low nibble. D % 128 == 0. Standard gating: W1, W3, W2T in int4.
+ * LoPA (r > 0, r % 16 == 0): W3 and W2T in int4, the low-rank gate V, U in
+ * int8 rows as for SFFN_I8 (a U row's bias-like first column rules out one
+ * scale per row in int4, and r need not be a multiple of 128). Forward calls:
+ * the _i4 ones. */
 enum { SFFN_BF16 = 0, SFFN_F32 = 1, SFFN_I8 = 2, SFFN_I4 = 3 };
 /* How a batch of T tokens moves data; never changes the result.
  * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set.
@@ -114,7 +117,7 @@ enum { SFFN_FLAG_G_TILED = 1u, SFFN_FLAG_RMSNORM = 2u, SFFN_FLAG_DOUBLE_ACT = 4u
  *               fp32), SFFN_F32, SFFN_I8 (int8 weights with per-row
  *               scales, x bf16; needs D % 16 == 0 and r % 16 == 0), or
  *               SFFN_I4 (int4 weights with per-128-column scales, x bf16;
- *               needs D % 128 == 0 and r == 0)
+ *               needs D % 128 == 0, and r % 16 == 0 for LoPA)
  *   flags       0, or for LoPA handles any of SFFN_FLAG_G_TILED,
  *               SFFN_FLAG_RMSNORM, SFFN_FLAG_DOUBLE_ACT (other bits, or any
  *               bit on a standard handle: SFFN_UNSUPPORTED)
@@ -204,6 +207,22 @@ sffn_status sffn_forward_dense_i4(sffn_handle *h, const void *x, const void *W1,
  * forward calls; a non-int8 or r == 0 handle gives SFFN_INVALID_ARGUMENT.
  */
 sffn_status sffn_forward_lopa_i8(sffn_handle *h, const void *x, const void *V,
+                                 const float *V_scale, const void *U, const float *U_scale,
+                                 const void *W3, const float *W3_scale, const void *W2T,
+                                 const float *W2T_scale, float *y, int T, int mode,
+                                 int32_t *live_count, int32_t *live_idx, void *stream);
+
+/*
+ * LoPA gating with int4 up and down weights (SFFN_I4 handles with r > 0, r a
+ * multiple of 16): as sffn_forward_lopa_i8 for V int8 [r x D] and U int8
+ * [H x r] with one fp32 scale per stored row (V_scale [r], U_scale [H]), and
+ * W3, W2T packed int4 [H x D/2] bytes with W3_scale, W2T_scale fp32
+ * [H x D/128] as for sffn_forward_sparse_i4. The gate options of the handle
+ * apply as for bf16; tokens of a batch run one after another. Errors as for
+ * the other forward calls; a non-int4 or r == 0 handle gives
+ * SFFN_INVALID_ARGUMENT.
+ */
+sffn_status sffn_forward_lopa_i4(sffn_handle *h, const void *x, const void *V,
                                  const float *V_scale, const void *U, const float *U_scale,
                                  const void *W3, const float *W3_scale, const void *W2T,
                                  const float *W2T_scale, float *y, int T, int mode,

@@ -255,6 +255,21 @@ def ffn_lopa_int8(x, w, act: int = ACT_RELU, flags: int = 0):
     return ffn_lopa(xf, V, U, W3, W2T, act=act)
 
 
+def ffn_lopa_int4(x, w, act: int = ACT_RELU, flags: int = 0):
+    """The LoPA oracle (flags as in ffn_lopa_full) on the weights an int4 LoPA workload
+    defines: V, U rows q * scale (int8), W3, W2T codes * their group's scale (int4). x is
+    widened exactly to fp64."""
+    xf = np.atleast_2d(np.asarray(x))
+    if xf.dtype == np.uint16:
+        xf = (xf.astype(np.uint32) << 16).view(np.float32)
+    xf = xf.astype(np.float64)
+    V, U = (dequantize_rows(w[k], w[k + "_scale"]) for k in ("V", "U"))
+    W3, W2T = (dequantize_groups_int4(w[k], w[k + "_scale"]) for k in ("W3", "W2T"))
+    if flags:
+        return ffn_lopa_full(xf, V, U, W3, W2T, flags, act=act)
+    return ffn_lopa(xf, V, U, W3, W2T, act=act)
+
+
 def ffn_moe(x, experts, route, gate, act: int = ACT_RELU):
     """Top-K mixture of sparse FFN experts (page "Model casting: ...", section "Where it
     generalizes"): y_t = sum_k gate[t, k] * FFN_{route[t, k]}(x_t), k ascending, in fp64.

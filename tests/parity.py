@@ -124,6 +124,22 @@ def run_lopa_i8(h, x, w, T, mode=sffn.SFFN_MODE_PER_TOKEN, want_live=True):
     return y, cnt, idx
 
 
+def run_lopa_i4(h, x, w, T, mode=sffn.SFFN_MODE_PER_TOKEN, want_live=True):
+    """int4 LoPA weights (V/U int8 rows, W3/W2T packed int4 with group scales) through
+    sffn_forward_lopa_i4."""
+    D, H = h.D, h.H
+    dv = {k: torch.from_numpy(np.ascontiguousarray(w[k])).cuda()
+          for k in ("V", "U", "W3", "W2T", "V_scale", "U_scale", "W3_scale", "W2T_scale")}
+    y = torch.full((T, D), float("nan"), dtype=torch.float32, device="cuda")
+    cnt = torch.full((T,), -1, dtype=torch.int32, device="cuda") if want_live else None
+    idx = torch.full((T, H), -1, dtype=torch.int32, device="cuda") if want_live else None
+    sffn.sffn_forward_lopa_i4(h.ptr, dev(x), dv["V"], dv["V_scale"], dv["U"], dv["U_scale"],
+                              dv["W3"], dv["W3_scale"], dv["W2T"], dv["W2T_scale"], y, T, mode,
+                              cnt, idx)
+    torch.cuda.synchronize()
+    return y, cnt, idx
+
+
 def run_i4(h, x, w, T, mode=sffn.SFFN_MODE_PER_TOKEN, dense=False, want_live=True):
     """group-scaled int4 weights (W1/W3/W2T packed, *_scale fp32 [H, D/128])."""
     D, H = h.D, h.H

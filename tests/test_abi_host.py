@@ -61,11 +61,11 @@ def test_create_int8_checks():
 
 
 def test_create_int4_checks():
-    # int4 weights: D a multiple of 128, standard gating only
+    # int4 weights: D a multiple of 128; LoPA ranks a multiple of 16 (int8 U rows)
     st, h = sffn.sffn_create_status(192, 64, 0, 1, 0, sffn.SFFN_I4, 0)
     assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "128" in sffn.sffn_last_error(None)
-    st, h = sffn.sffn_create_status(256, 64, 16, 1, 0, sffn.SFFN_I4, 0)
-    assert st == sffn.SFFN_UNSUPPORTED and h is None and "int4" in sffn.sffn_last_error(None)
+    st, h = sffn.sffn_create_status(256, 64, 24, 1, 0, sffn.SFFN_I4, 0)
+    assert st == sffn.SFFN_INVALID_ARGUMENT and h is None and "r must" in sffn.sffn_last_error(None)
 
 
 def test_create_rejects_flags():

@@ -436,6 +436,58 @@ def test_int4_packing_scales_and_exact_oracle():
         assert got["live"][t].tolist() == live
 
 
+def test_lopa_int4_weights_and_exact_oracle():
+    """An int4 LoPA workload: V and U are int8 rows q * scale (V[0] = e_0 exactly), W3 and
+    W2T int4 codes times their 128-column group's scale, each within half a step of the
+    fp64 draws; and the int4 LoPA oracle equals exact rationals on integer codes with
+    power-of-two scales (a different one per group of W3 and W2T): the plain gate
+    U (V x), and G x + U (V x) with double activation."""
+    D, Hp, r = 256, 40, 16
+    w = gen.lopa_weights_int4(D, Hp, r, 0.9, cfg=76)
+    assert w["V"][0, 0] == 127 and not w["V"][0, 1:].any()
+    for k in ("V", "U"):
+        assert w[k].dtype == np.int8 and w[k + "_scale"].shape == (w[k].shape[0],)
+    for k in ("W3", "W2T"):
+        assert w[k].dtype == np.uint8 and w[k].shape == (Hp, D // 2)
+        assert w[k + "_scale"].shape == (Hp, D // 128)
+    W2T64 = gen.normal((Hp, D), 1.0 / np.sqrt(Hp), 76, 0, 0, gen.S_W2T)
+    deq = ref.dequantize_groups_int4(w["W2T"], w["W2T_scale"])
+    step = np.repeat(w["W2T_scale"].astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(deq - W2T64) <= 0.5 * step * (1 + 1e-12))
+    D, H, r, T = 256, 6, 4, 2
+    rngq = np.random.default_rng(77)
+    qV = rngq.integers(-3, 4, size=(r, D)).astype(np.int8)
+    qU = rngq.integers(-3, 4, size=(H, r)).astype(np.int8)
+    q4 = {k: rngq.integers(-8, 8, size=(H, D)).astype(np.int8) for k in ("W3", "W2T")}
+    sc4 = {k: (2.0 ** -rngq.integers(0, 4, size=(H, D // 128))).astype(np.float32) for k in q4}
+    wi = {"V": qV, "V_scale": np.full(r, 0.5, np.float32), "U": qU,
+          "U_scale": np.full(H, 0.25, np.float32)}
+    for k, v in q4.items():
+        wi[k] = ((v[:, 0::2].astype(np.uint8) & 0xF) | ((v[:, 1::2].astype(np.uint8) & 0xF) << 4))
+        wi[k + "_scale"] = sc4[k]
+    x = gen.small_integers((T, D), -1, 1, cfg=77, stream=0, dtype="bf16")
+    xf = gen.as_float(x).astype(np.float64)
+    mats = {"V": [[Fraction(int(v)) * Fraction(1, 2) for v in row] for row in qV],
+            "U": [[Fraction(int(v)) * Fraction(1, 4) for v in row] for row in qU]}
+    for k in q4:
+        mats[k] = [[Fraction(int(q4[k][i, j])) * Fraction(float(sc4[k][i, j // 128])) for j in range(D)]
+                   for i in range(H)]
+    plain = ref.ffn_lopa_int4(x, wi)
+    full = ref.ffn_lopa_int4(x, wi, flags=ref.LOPA_G_TILED | ref.LOPA_DOUBLE_ACT)
+    for t in range(T):
+        xs = [Fraction(v) for v in xf[t]]
+        tt = [sum(mats["V"][m][j] * xs[j] for j in range(D)) for m in range(r)]
+        z = [sum(mats["U"][i][m] * tt[m] for m in range(r)) for i in range(H)]
+        u = [sum(mats["W3"][i][j] * xs[j] for j in range(D)) for i in range(H)]
+        a = [(z[i] if z[i] > 0 else 0) * u[i] for i in range(H)]
+        y = [sum(mats["W2T"][i][j] * a[i] for i in range(H)) for j in range(D)]
+        assert [Fraction(v) for v in plain["y"][t]] == y
+        assert plain["live"][t].tolist() == [i for i in range(H) if z[i] > 0]
+        yd, live_d, k2 = frac_lopa_double(xs, mats["V"], mats["U"], mats["W3"], mats["W2T"], True)
+        assert [Fraction(v) for v in full["y"][t]] == yd
+        assert full["live"][t].tolist() == live_d and full["k2"][t] == k2
+
+
 def test_moe_exact_on_integers():
     """Top-K mixture (page "Model casting: ...", section "Where it generalizes"): y_t is the
     gate-weighted sum of the routed experts' FFN outputs, checked with exact rationals on
