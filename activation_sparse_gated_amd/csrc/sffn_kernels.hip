@@ -1480,16 +1480,23 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
         __syncthreads();
         p0 = p1;
     }
+    // sum over the 4 row groups of a wave as a reduce-scatter (lanes 32 and 16
+    // apart): each lane ends with 4 whole columns of its 16 (12 shuffles, not 32)
+    static_assert(LPR == 16, "two halving exchanges over 4 row groups");
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-        float v = acc[k];
-        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-        acc[k] = v;
-    }
-    if (grp == 0) {
+    for (int st = 0; st < 2; ++st) {
+        const int o = 32 >> st, half = 8 >> st;
+        const bool upper = (lane & o) != 0;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) red[wave][sub * 16 + k] = acc[k];
+        for (int k = 0; k < half; ++k) {
+            const float lo = acc[k], hi = acc[k + half];
+            const float keep = upper ? hi : lo;
+            acc[k] = keep + __shfl_xor(upper ? lo : hi, o, WAVE);
+        }
     }
+    const int cpart = 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[wave][sub * 16 + cpart + k] = acc[k];
     __syncthreads();
     for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
         float s = 0.0f;
@@ -1510,25 +1517,46 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
 // product takes one scale.
 constexpr int I4_GROUP = 128;
 
-// sum over 32 int4 codes (16 bytes) times fp32 x
-__device__ inline float dot32_i4(const u32x4& w, const float* xv) {
+// 32 bf16 of x (64 bytes at col) as 16 bf16 pairs, and their fp32 sum; zeros past D
+struct X32 {
+    u32x4 v[4];
+    float sum;
+};
+__device__ inline X32 load_x32(const uint16_t* __restrict__ x, int col, int D) {
+    X32 r;
+    r.sum = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        r.v[q] = col < D ? load_cached(x + col + 8 * q) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) r.sum += Elem<uint16_t>::get(r.v[q], k);
+    }
+    return r;
+}
+
+// sum over 32 int4 codes (16 bytes) times x. A code n (two's complement
+// nibble u) becomes the bf16 128 + (u ^ 8) = n + 136 exactly: the nibble goes
+// into the low mantissa bits of 128.0 (0x4300). One byte permute places the
+// codes of columns 2b and 2b + 1 side by side, so a bf16 dot2 takes two
+// codes against two x values; the 136 * sum(x) this adds is taken off once.
+__device__ inline float dot32_i4(const u32x4& w, const X32& xv) {
     float s = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        const uint32_t wq = w[q];
+        const uint32_t wq = w[q] ^ 0x88888888u;
+        const uint32_t lo = wq & 0x0F0F0F0Fu;         // byte b: column 2b (offset binary)
+        const uint32_t hi = (wq >> 4) & 0x0F0F0F0Fu;  // byte b: column 2b + 1
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const int v = (int)(wq << (28 - 4 * b)) >> 28;  // sign-extended nibble b
-            s = fmaf((float)v, xv[8 * q + b], s);
+        for (int b = 0; b < 4; ++b) {
+            // bytes: lo.b, 0, hi.b, 0 (selector 0x0c gives a zero byte)
+            const uint32_t sel = (uint32_t)b | (0x0cu << 8) | ((4u + b) << 16) | (0x0cu << 24);
+            const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+            const uint32_t xp = xv.v[q][b];  // x of columns 8q + 2b, 8q + 2b + 1
+            s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                                __builtin_bit_cast(bf16x2, xp), s, false);
         }
     }
-    return s;
-}
-
-// x[col .. col + 32) (bf16) as fp32; zeros past D
-__device__ inline void load_x32(const uint16_t* __restrict__ x, int col, int D, float* xv) {
-    load_x16(x, col, D, xv);
-    load_x16(x, col + 16, D, xv + 16);
+    return fmaf(-136.0f, xv.sum, s);
 }
 
 // Gate and gathered up projection, int4 weights: z_i = sum_g s1_ig (q1_i,g . x_g);
@@ -1558,9 +1586,9 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i4(
         if (DENSE) w3[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
         sc3[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
     }
-    float xv[NC][32];
+    X32 xv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) load_x32(x, c * CW + lane * 32, D, xv[c]);
+    for (int c = 0; c < NC; ++c) xv[c] = load_x32(x, c * CW + lane * 32, D);
     if (y_zero) {
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
@@ -1633,9 +1661,9 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i4(
             for (int k = 0; k < 16; ++k) tv[c][k] = 0.0f;
         }
     }
-    float xv[NC][32];
+    X32 xv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) load_x32(x, c * CW + lane * 32, D, xv[c]);
+    for (int c = 0; c < NC; ++c) xv[c] = load_x32(x, c * CW + lane * 32, D);
     const float su_ = in ? sU[unit] : 0.0f;
     const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
     float inv = 1.0f;  // RMSNorm of t: every lane group sees all of t
@@ -1798,16 +1826,25 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
         __syncthreads();
         p0 = p1;
     }
+    // sum over the 8 row groups of a wave as a reduce-scatter: at the exchange with
+    // the lane 32, 16, 8 apart each lane sends the half of its columns that its
+    // partner keeps, so a lane ends with 4 whole columns (28 shuffles, not 96)
+    static_assert(LPR == 8, "three halving exchanges over 8 row groups");
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-        float v = acc[k];
-        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-        acc[k] = v;
-    }
-    if (grp == 0) {
+    for (int st = 0; st < 3; ++st) {
+        const int o = 32 >> st, half = 16 >> st;
+        const bool upper = (lane & o) != 0;
 #pragma unroll
-        for (int k = 0; k < 32; ++k) red[wave][sub * 32 + k] = acc[k];
+        for (int k = 0; k < half; ++k) {
+            const float lo = acc[k], hi = acc[k + half];
+            const float keep = upper ? hi : lo;
+            acc[k] = keep + __shfl_xor(upper ? lo : hi, o, WAVE);
+        }
     }
+    // columns 16 b5 + 8 b4 + 4 b3 + k of this lane's 32 (b: bits of the lane)
+    const int cpart = 16 * ((lane >> 5) & 1) + 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) red[wave][sub * 32 + cpart + k] = acc[k];
     __syncthreads();
     for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
         float s = 0.0f;
