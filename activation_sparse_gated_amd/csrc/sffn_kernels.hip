@@ -798,6 +798,27 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
     }
 }
 
+// Exclusive prefix of N per-(row group, wave) counts, by one wave: woff[i] =
+// sum of counts[0 .. i), woff[N] = the total. One LDS read per lane and count,
+// then a wave-wide scan (shuffles) carried across groups of 64.
+template <int N>
+__device__ inline void counts_exclusive_prefix(const int* counts, int* woff, int lane) {
+    int carry = 0;
+    for (int base = 0; base < N; base += WAVE) {
+        const int i = base + lane;
+        const int v = i < N ? counts[i] : 0;
+        int incl = v;
+#pragma unroll
+        for (int o = 1; o < WAVE; o <<= 1) {
+            const int t = __shfl_up(incl, o, WAVE);
+            if (lane >= o) incl += t;
+        }
+        if (i < N) woff[i] = carry + incl - v;
+        carry += __shfl(incl, WAVE - 1, WAVE);
+    }
+    if (lane == 0) woff[N] = carry;
+}
+
 // Down projection for one token: y[slice] = sum_i a_i W2T[i, slice].
 // Grid = (column slices, remapped XCD-contiguous) x (row splits S). Every
 // thread first loads its share of a (one round trip for the whole vector),
@@ -854,25 +875,8 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
         if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
     }
     __syncthreads();
-    // exclusive prefix over the (p, wave) counts by wave 0: one independent LDS
-    // read per lane, then a wave-wide scan with DPP-free shuffles
-    if (wave == 0) {
-        constexpr int NCNT = PMAX * KD_WAVES;
-        int carry = 0;
-        for (int base = 0; base < NCNT; base += WAVE) {
-            const int i = base + lane;
-            const int v = i < NCNT ? wcount[i] : 0;
-            int incl = v;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const int t = __shfl_up(incl, o, WAVE);
-                if (lane >= o) incl += t;
-            }
-            if (i < NCNT) woff[i] = carry + incl - v;
-            carry += __shfl(incl, WAVE - 1, WAVE);
-        }
-        if (lane == 0) woff[NCNT] = carry;
-    }
+    // exclusive prefix of the (p, wave) counts, by wave 0
+    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
     __syncthreads();
 
     float acc[VEC];
@@ -1417,23 +1421,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
         if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
     }
     __syncthreads();
-    if (wave == 0) {
-        constexpr int NCNT = PMAX * KD_WAVES;
-        int carry = 0;
-        for (int base = 0; base < NCNT; base += WAVE) {
-            const int i = base + lane;
-            const int v = i < NCNT ? wcount[i] : 0;
-            int incl = v;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const int t = __shfl_up(incl, o, WAVE);
-                if (lane >= o) incl += t;
-            }
-            if (i < NCNT) woff[i] = carry + incl - v;
-            carry += __shfl(incl, WAVE - 1, WAVE);
-        }
-        if (lane == 0) woff[NCNT] = carry;
-    }
+    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
     __syncthreads();
 
     float acc[16];
@@ -1760,23 +1748,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
         if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
     }
     __syncthreads();
-    if (wave == 0) {
-        constexpr int NCNT = PMAX * KD_WAVES;
-        int carry = 0;
-        for (int base = 0; base < NCNT; base += WAVE) {
-            const int i = base + lane;
-            const int v = i < NCNT ? wcount[i] : 0;
-            int incl = v;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const int t = __shfl_up(incl, o, WAVE);
-                if (lane >= o) incl += t;
-            }
-            if (i < NCNT) woff[i] = carry + incl - v;
-            carry += __shfl(incl, WAVE - 1, WAVE);
-        }
-        if (lane == 0) woff[NCNT] = carry;
-    }
+    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
     __syncthreads();
 
     float acc[32];
@@ -2531,23 +2503,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
         if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
     }
     __syncthreads();
-    if (wave == 0) {
-        constexpr int NCNT = PMAX * KD_WAVES;
-        int carry = 0;
-        for (int base = 0; base < NCNT; base += WAVE) {
-            const int i = base + lane;
-            const int v = i < NCNT ? wcount[i] : 0;
-            int incl = v;
-#pragma unroll
-            for (int o = 1; o < WAVE; o <<= 1) {
-                const int t = __shfl_up(incl, o, WAVE);
-                if (lane >= o) incl += t;
-            }
-            if (i < NCNT) woff[i] = carry + incl - v;
-            carry += __shfl(incl, WAVE - 1, WAVE);
-        }
-        if (lane == 0) woff[NCNT] = carry;
-    }
+    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
     __syncthreads();
 
     float acc[TT][VEC];
