@@ -885,6 +885,25 @@ def main() -> int:
                "cpu_model": cpu_model, "os_cpu_count": os.cpu_count()}
         log(f"cpu oracle: {cpu['value']} tokens/s on {threads} threads ({done} tokens), "
             f"{cpu['one_thread_value']} tokens/s on 1 thread; {cpu_model}")
+        if not args.no_extras:
+            # the 32-layer stacks: the first 8 stack tokens through all 32 layers (the
+            # layers are copies of one generated layer, as on the GPU), extrapolated
+            stk = {}
+            for (Ds, Hs) in ((2048, 6144), (4096, 12288)):
+                ws = gen.standard_weights(Ds, Hs, 0.895, cfg=5, dtype="bf16")
+                xs_np = gen.tokens(Ds, 8 * 32, cfg=5, dtype="bf16")
+                t2 = time.time()
+                ref.ffn_standard(xs_np, ws["W1"], ws["W3"], ws["W2T"], act=ref.ACT_RSPLUS)
+                dts = time.time() - t2
+                stk[f"D{Ds}_H{Hs}"] = {
+                    "stack_tokens_per_s": round(8 / dts, 3),
+                    "layer_tokens_per_s": round(8 * 32 / dts, 1),
+                    "sample": f"extrapolated: 8 stack tokens x 32 layers through the fp64 sparse "
+                              f"oracle on {threads} threads, {dts:.2f} s"}
+                del ws
+            cpu["stacks_extrapolated"] = stk
+            log("cpu oracle stacks (extrapolated from 8 tokens): " + ", ".join(
+                f"{k} {v['stack_tokens_per_s']} stack tokens/s" for k, v in stk.items()))
 
     traffic = read_traffic(dom, "decode")
     out = {
