@@ -26,7 +26,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
             KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
             KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_GATE_UP_T1_I4,
-            KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4, KIND_COUNT };
+            KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4,
+            KIND_RANK_PROJ_MFMA, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -39,7 +40,7 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_rank_proj_t1_i8", "k_gate_up_lopa_t1_i8",
                                             "k_gate_up_tb", "k_gate_up_t1_i4",
                                             "k_gate_up_dense_t1_i4", "k_down_t1_i4",
-                                            "k_gate_up_lopa_t1_i4"};
+                                            "k_gate_up_lopa_t1_i4", "k_rank_proj_mfma"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -92,6 +93,7 @@ struct sffn_handle {
     int tbv_rw2 = 2, tbv_rw4 = 4;  // units per wave of the VALU gate/up pass (2 and 4 token slots)
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
     uint64_t* m_mask = nullptr;    // [H] tokens for which each unit is live
+    uint16_t* m_t = nullptr;       // LoPA: [2 x m_tp x r] bf16 rank vectors, hi then lo parts
     // large batches as GEMMs on MFMA
     int g_min_t = MAXT + 1;        // smallest batch that takes the GEMM path
     int g_tp = 0;                  // padded token count of g_a (multiple of 256)
@@ -407,19 +409,30 @@ bool mfma_ok(const sffn_handle* h, int T) {
 // token tiles of 16 for a batch of T tokens: 1, 2 or 4
 inline int token_tiles(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
-template <bool DENSE>
+// LOPA: W1 is U, V the rank factor; the batch's rank vectors go through m_t
+// (bf16 hi and lo parts) into the MFMA gate, the rest is the standard plan.
+template <bool DENSE, bool LOPA = false>
 sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* W3,
                      const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
-                     hipStream_t s) {
+                     hipStream_t s, const void* V = nullptr) {
     const int nt = token_tiles(T);
     uint8_t* live = live_count ? h->live_buf : nullptr;
     sffn_status st = SFFN_OK;
+    uint16_t* t_hi = h->m_t;
+    uint16_t* t_lo = h->m_t ? h->m_t + (size_t)h->m_tp * h->r : nullptr;
+    if (LOPA) {
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA, k_rank_proj_mfma<NT>,
+                                       dim3((h->r + 15) / 16), dim3(KM_THREADS), s,
+                                       (const uint16_t*)x, (const uint16_t*)V,
+                                       (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
+        if (st != SFFN_OK) return st;
+    }
     const int ut = nt == 4 ? h->m_ut4 : (nt == 2 ? h->m_ut2 : h->m_ut1);  // unit tiles per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const bool small_down = T <= h->tb_max && T <= 8;
     const int splits = small_down ? h->tb_splits : h->m_splits;
     float* yz = splits > 1 ? y : nullptr;
-    if (T <= h->tbv_max && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
+    if (!LOPA && T <= h->tbv_max && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once
         const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
         const int tt = T <= 2 ? 2 : 4;
@@ -434,10 +447,11 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
 #undef SFFN_TBV
     } else {
 #define SFFN_GATE_MFMA(NTV, UTV)                                                               \
-    st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NTV, UTV, DENSE>, dim3(nb),               \
+    st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NTV, UTV, DENSE, LOPA>, dim3(nb),         \
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
                 (const uint16_t*)W3, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, yz,   \
-                h->D, h->H, T, h->act)
+                h->D, h->H, T, h->act, (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r,      \
+                h->flags)
     if (nt == 1) {
         if (ut == 4) { SFFN_GATE_MFMA(1, 4); } else if (ut == 2) { SFFN_GATE_MFMA(1, 2); } else { SFFN_GATE_MFMA(1, 1); }
     } else if (nt == 2) {
@@ -1033,6 +1047,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;
             e = hipMalloc(&h->m_a, (size_t)H * h->m_tp * sizeof(float));
             if (e == hipSuccess) e = hipMalloc(&h->m_mask, (size_t)H * sizeof(uint64_t));
+            if (e == hipSuccess && r > 0)
+                e = hipMalloc(&h->m_t, 2 * (size_t)h->m_tp * r * sizeof(uint16_t));
             if (e == hipSuccess) e = hipMalloc(&h->m_zero, 4096);
             if (e == hipSuccess) e = hipMemset(h->m_zero, 0, 4096);
             if (e == hipSuccess) e = hipDeviceSynchronize();
@@ -1095,6 +1111,7 @@ void sffn_destroy(sffn_handle* h) {
     if (h->m_a) (void)hipFree(h->m_a);
     if (h->m_mask) (void)hipFree(h->m_mask);
     if (h->m_zero) (void)hipFree(h->m_zero);
+    if (h->m_t) (void)hipFree(h->m_t);
     if (h->moe_x) (void)hipFree(h->moe_x);
     if (h->moe_y) (void)hipFree(h->moe_y);
     if (h->g_a) (void)hipFree(h->g_a);
@@ -1371,7 +1388,13 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
         if (T == 0) return SFFN_OK;
         if (t1_ok(h, T) && h->r <= 4 * WAVE * 8)
             return run_lopa_t1(h, x, V, U, W3, W2T, y, live_count, live_idx, s);
-        if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1) && h->r <= 4 * WAVE * 8) {
+        // bf16 union batches: rank projection, U gate and W3 gather on MFMA (RMSNorm of
+        // the rank vectors excepted: it needs each token's whole t before the gate)
+        if (mode == SFFN_MODE_UNION && mfma_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
+            return run_mfma<false, true>(h, x, U, W3, W2T, y, T, live_count, live_idx, s, V);
+        // other bf16 batches: each token runs the batch-1 pass on its own live set (the
+        // general kernels measured slower than this at every T)
+        if (t1_ok(h, 1) && h->r <= 4 * WAVE * 8) {
             const size_t xb = (size_t)h->D * sizeof(uint16_t);
             for (int t = 0; t < T; ++t) {
                 st = run_lopa_t1(h, (const char*)x + t * xb, V, U, W3, W2T, y + (size_t)t * h->D,

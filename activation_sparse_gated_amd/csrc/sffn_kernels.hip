@@ -2127,12 +2127,13 @@ __device__ inline void mfma_gate_pass(f32x4* acc, const uint16_t* __restrict__ W
     __syncthreads();
 }
 
-template <int NT, int UT, bool DENSE>
+template <int NT, int UT, bool DENSE, bool LOPA>
 __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W3, const uint16_t* __restrict__ zeros, float* __restrict__ a_rm,
     uint64_t* __restrict__ umask, uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D,
-    int H, int T, int act) {
+    int H, int T, int act, const uint16_t* __restrict__ t_hi, const uint16_t* __restrict__ t_lo,
+    int r, unsigned flags) {
     using G = GateTiles<NT, UT>;
     constexpr int TP = G::TP, UB = G::UB;
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
@@ -2170,10 +2171,19 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
         }
     };
 
-    // ---- gate: z[UB units][TP tokens]
+    // ---- gate: z[UB units][TP tokens]; LoPA: z = U t with t = t_hi + t_lo (two
+    // bf16 parts of the fp32 rank vectors, K = r), plus (G x)_i when asked
     {
         f32x4 acc[G::TPW];
-        mfma_gate_pass<NT, UT>(acc, W1, rows_g, x, zeros, D, T, ring);
+        if (LOPA) {
+            f32x4 acc2[G::TPW];
+            mfma_gate_pass<NT, UT>(acc, W1, rows_g, t_hi, zeros, r, T, ring);
+            mfma_gate_pass<NT, UT>(acc2, W1, rows_g, t_lo, zeros, r, T, ring);
+#pragma unroll
+            for (int i = 0; i < G::TPW; ++i) acc[i] += acc2[i];
+        } else {
+            mfma_gate_pass<NT, UT>(acc, W1, rows_g, x, zeros, D, T, ring);
+        }
         store_tiles(acc);
     }
     __syncthreads();
@@ -2182,6 +2192,8 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
         float z = 0.0f;
 #pragma unroll
         for (int g = 0; g < G::KG; ++g) z += part[g][i][t];
+        if (LOPA && (flags & LOPA_G_TILED) && t < T && u0 + i < H)
+            z += Elem<uint16_t>::get1(x[(size_t)t * D + (u0 + i) % D]);
         zf[i][t] = z;
         const bool ok = (u0 + i < H) && t < T;
         const bool live = ok && (DENSE || z > 0.0f);
@@ -2223,6 +2235,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
             float u = 0.0f;
 #pragma unroll
             for (int g = 0; g < G::KG; ++g) u += part[g][p][t];
+            if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
             av = activation(act, zf[i][t]) * u;
         }
         a_rm[(size_t)(u0 + i) * TP + t] = av;
@@ -2274,6 +2287,50 @@ __device__ inline u32x4 frag_tr128(const uint8_t* part, int col0, int lane) {
     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a1));
     const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
     return u32x4{w0.x, w0.y, w1.x, w1.y};
+}
+
+// LoPA rank projection for a batch: t[token][m] = V_m . x_token for 16 rank
+// rows per block (the gate pass above with V for W1 and all D columns), stored
+// token-major as two bf16 parts, t_hi = bf16(t) and t_lo = bf16(t - t_hi)
+// (about 16 significant bits together), rows of r; tokens past T get zeros.
+template <int NT>
+__global__ __launch_bounds__(KM_THREADS) void k_rank_proj_mfma(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ zeros, uint16_t* __restrict__ t_hi, uint16_t* __restrict__ t_lo,
+    int D, int r, int T) {
+    using G = GateTiles<NT, 1>;
+    constexpr int TP = G::TP;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
+    __shared__ float part[G::KG][16][TP + 1];
+    __shared__ int rows[16];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int m0 = blockIdx.x * 16;
+    const int kgroup = G::TILES >= 4 ? 0 : wave / G::TILES;
+    if (threadIdx.x < 16) rows[threadIdx.x] = m0 + (int)threadIdx.x < r ? m0 + (int)threadIdx.x : -1;
+    __syncthreads();
+    f32x4 acc[G::TPW];
+    mfma_gate_pass<NT, 1>(acc, V, rows, x, zeros, D, T, ring);
+#pragma unroll
+    for (int i = 0; i < G::TPW; ++i) {
+        const int tile = G::TILES >= 4 ? wave * G::TPW + i : wave % G::TILES;
+        const int nt = tile % NT;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[kgroup][4 * (lane >> 4) + j][nt * 16 + (lane & 15)] = acc[i][j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * TP; e += KM_THREADS) {
+        const int m = e % 16, t = e / 16;
+        if (m0 + m >= r) continue;
+        float v = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G::KG; ++g) v += part[g][m][t];
+        if (t >= T) v = 0.0f;
+        const uint32_t hi = bf16_rne(v);
+        const uint32_t lo = bf16_rne(v - __uint_as_float(hi << 16));
+        t_hi[(size_t)t * r + m0 + m] = (uint16_t)hi;
+        t_lo[(size_t)t * r + m0 + m] = (uint16_t)lo;
+    }
 }
 
 // Stage 2: y[T x D] (+)= sum over the units live for some token of
