@@ -148,6 +148,36 @@ def _graph_time(torch, fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
+def bench_lopa_batched(torch, sffn, gen, to_dev, act, args):
+    """LoPA token batches (D=2560, H'=9787, r=400, s=0.9; 8 weight replicas, 32 calls
+    per replay): per-token lists and the union of live sets, T = 4, 16, 64."""
+    D, Hp, r, R = 2560, 9787, 400, 8
+    w = gen.lopa_weights(D, Hp, r, 0.9, cfg=3, dtype="bf16")
+    W = {k: to_dev(w[k]) for k in ("V", "U", "W3", "W2T")}
+    reps = [{k: (W[k] if i == 0 else W[k].clone()) for k in W} for i in range(R)]
+    xb = to_dev(gen.tokens(D, 64 * 32, cfg=3, dtype="bf16"))
+    h = sffn.Handle(D, Hp, r, 64, act, sffn.SFFN_BF16)
+    y = torch.zeros(64 * 32, D, dtype=torch.float32, device="cuda")
+    out = {}
+    for T in (4, 16, 64):
+        res = {}
+        for name, mode in (("per_token", sffn.SFFN_MODE_PER_TOKEN), ("union", sffn.SFFN_MODE_UNION)):
+            def fn():
+                for c in range(32):
+                    rp = reps[c % R]
+                    sffn.sffn_forward_lopa(h.ptr, xb[c * T:(c + 1) * T], rp["V"], rp["U"], rp["W3"],
+                                           rp["W2T"], y[c * T:(c + 1) * T], T, mode)
+            ms = _graph_time(torch, fn, max(2, args.steps // 4), 1) / 32
+            res[name + "_tokens_per_s"] = round(T / (ms * 1e-3), 1)
+        res["union_vs_per_token"] = round(res["union_tokens_per_s"] / res["per_token_tokens_per_s"], 3)
+        out[f"T{T}"] = res
+        log(f"lopa batched T={T}: " + ", ".join(f"{k} {v:,}" for k, v in res.items()))
+    h.close()
+    del reps, W
+    torch.cuda.empty_cache()
+    return out
+
+
 def bench_batched(torch, sffn, gen, to_dev, x1, reps, D, H, act, args):
     """Token batches of T = 1, 4, 16, 64 at s = 0.9 (i.i.d. tokens, independent live sets):
     per-token lists, union of live sets, and the dense comparator. 64 calls per replay."""
@@ -842,6 +872,7 @@ def main() -> int:
     # ---------------------------------------------------------------- batched decode and stacks
     if not args.no_extras:
         extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
+        extras["lopa_batched"] = bench_lopa_batched(torch, sffn, gen, to_dev, act, args)
         extras["stacks"] = bench_stacks(torch, sffn, gen, to_dev, act, args)
         extras["moe_top2_8x"] = bench_moe(torch, sffn, gen, to_dev, act, args)
         extras["prefill"] = bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args)
