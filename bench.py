@@ -414,7 +414,7 @@ def main() -> int:
 
     if args.gpus != 1:
         log(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-            "(the FFN path has no cross-GPU step in this build).")
+            "(the library's FFN path runs on one GPU and has no cross-GPU step).")
         return 2
 
     import torch
