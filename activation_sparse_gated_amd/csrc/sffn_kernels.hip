@@ -2644,6 +2644,225 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
     }
 }
 
+// Small batches (T <= TT <= 4) with weight-only int8 weights, union of the
+// tokens' live sets. Gate/up: one unit per wave; every int8 weight of the W1
+// row (and of the W3 row when the unit is live for some token) is converted
+// once and multiplied with the TT tokens' x (bf16, unpacked per use); the TT
+// per-lane sums are reduced together (multi_reduce: lane l ends with token
+// bitrev(l mod TT)). Writes a'[unit][tp] = A(z) u s2 (the W2T row scale folded
+// in; 0 for dead pairs and padded slots), the token mask umask[unit] (DENSE:
+// all tokens), live flags [T x H] when asked, and clears y for the down pass.
+template <int NC, int TT, bool DENSE>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ W1, const float* __restrict__ s1,
+    const int8_t* __restrict__ W3, const float* __restrict__ s3, const float* __restrict__ s2,
+    float* __restrict__ a_rm, uint64_t* __restrict__ umask, uint8_t* __restrict__ live_out,
+    float* __restrict__ y_zero, int D, int H, int T, int tp, int act) {
+    constexpr int CW = WAVE * 16;  // columns of one chunk: 16 int8 per lane
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int unit = blockIdx.x * K1_WAVES + wave;
+    const bool in = unit < H;
+    u32x4 w[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 16;
+        w[c] = (in && col < D) ? load_stream(W1 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    u32x4 xb[TT][NC][2];  // the lane's 16 columns of each token: two pieces of 8 bf16
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 16;
+            const bool ok = t < T && col < D;
+            xb[t][c][0] = ok ? load_cached(x + (size_t)t * D + col) : u32x4{0u, 0u, 0u, 0u};
+            xb[t][c][1] = ok ? load_cached(x + (size_t)t * D + col + 8) : u32x4{0u, 0u, 0u, 0u};
+        }
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < T * D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    const float sc1 = in ? s1[unit] : 0.0f;
+    const float sc3 = in ? s3[unit] : 0.0f;
+    const float sc2 = in ? s2[unit] : 0.0f;
+    auto dot_tokens = [&](const u32x4 (&wr)[NC], float (&v)[TT]) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) v[t] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wq = wr[c][q];
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const float wf = (float)((int)(wq << (24 - 8 * b)) >> 24);  // byte b, signed
+                    const int k = 4 * q + b;                                     // column of the lane
+#pragma unroll
+                    for (int t = 0; t < TT; ++t)
+                        v[t] = fmaf(wf, Elem<uint16_t>::get(xb[t][c][k >> 3], k & 7), v[t]);
+                }
+            }
+    };
+    const int tl = bit_rev<TT>(lane & (TT - 1));  // token whose sums this lane ends with
+    float v[TT];
+    dot_tokens(w, v);
+    const float z = multi_reduce<TT>(v) * sc1;
+    const bool lv = in && tl < T && z > 0.0f;
+    const uint64_t bl = __ballot(lv && lane < TT);
+    uint64_t m = 0;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) m |= ((bl >> bit_rev<TT>(t)) & 1ull) << t;
+    if (!in) return;  // wave-uniform: one unit per wave
+    if (lane == 0) umask[unit] = DENSE ? ((1ull << T) - 1) : m;
+    if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
+    if (!DENSE && m == 0) {
+        if (lane < TT) a_rm[(size_t)unit * tp + tl] = 0.0f;
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 16;
+        w[c] = col < D ? load_stream(W3 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    dot_tokens(w, v);
+    const float u = multi_reduce<TT>(v) * sc3;
+    if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u * sc2 : 0.0f;
+}
+
+// Down pass of the int8 small batches: as k_down_t1_i8 (16 lanes x 16 int8
+// columns per 256-column slice, 16 unit-range splits, fp32 atomics into y)
+// over the units live for some token (umask != 0), with TT accumulators per
+// column per lane; a unit's TT products a' come from a_rm[unit][tp].
+template <int PMAX, int TT>
+__global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restrict__ a_rm,
+                                                           const uint64_t* __restrict__ umask,
+                                                           const int8_t* __restrict__ W2T,
+                                                           float* __restrict__ y, int D, int H,
+                                                           int T, int tp, int splits) {
+    constexpr int LPR = 16;
+    constexpr int VEC = 16;
+    constexpr int CB = LPR * VEC;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 4;
+    __shared__ int list[KD_LCAP];
+    __shared__ int wcount[PMAX * KD_WAVES];
+    __shared__ int woff[PMAX * KD_WAVES + 1];
+    __shared__ float red[KD_WAVES][CB];
+
+    const int nslices = (D + CB - 1) / CB;
+    const int per_xcd = (nslices + 7) / 8;
+    const int bx = blockIdx.x;
+    const int slice = (bx & 7) * per_xcd + (bx >> 3);
+    if (slice >= nslices) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * VEC;
+    const bool col_ok = col < D;
+    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
+
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        const bool keep = p < P && row < h1 && umask[row] != 0ull;
+        mk[p] = __ballot(keep);
+        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
+    __syncthreads();
+
+    float acc[TT][VEC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[t][k] = 0.0f;
+
+    int p0 = 0;
+    while (p0 < P) {
+        int p1 = p0 + 1;
+        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
+        const int ebase = woff[p0 * KD_WAVES];
+        const int n = woff[p1 * KD_WAVES] - ebase;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
+                const int pos = woff[p * KD_WAVES + wave] - ebase +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+            }
+        }
+        __syncthreads();
+        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+            u32x4 wv[UF];
+            float av[UF][TT];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const int row = e < n ? list[e] : 0;
+                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)row * D + col)
+                                          : u32x4{0u, 0u, 0u, 0u};
+                // TT <= 16 <= tp, and padded token slots of a_rm hold 0
+                const float* ar = a_rm + (size_t)row * tp;
+#pragma unroll
+                for (int t = 0; t < TT; t += 2) {
+                    const float2 v2 = e < n ? *reinterpret_cast<const float2*>(ar + t)
+                                            : make_float2(0.0f, 0.0f);
+                    av[u][t] = v2.x;
+                    av[u][t + 1] = v2.y;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u)
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = wv[u][q];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) {
+                        const float wf = (float)((int)(wq << (24 - 8 * b)) >> 24);
+#pragma unroll
+                        for (int t = 0; t < TT; ++t) acc[t][4 * q + b] = fmaf(av[u][t], wf, acc[t][4 * q + b]);
+                    }
+                }
+        }
+        __syncthreads();
+        p0 = p1;
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            float v = acc[t][k];
+            for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+            acc[t][k] = v;
+        }
+        if (grp == 0) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[t][k];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+            float s = 0.0f;
+            for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+            if (col0 + c < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + col0 + c, s);
+                else
+                    y[(size_t)t * D + col0 + c] = s;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Sparse expert FFNs in a top-K mixture of experts (page "Model casting:
 // compute the gate, then skip most of the FFN", section "Where it

@@ -753,9 +753,30 @@ def main() -> int:
         res_q["measured_sparsity"] = round(float(1 - kq.mean() / H), 4)
         res_q["sparse_vs_dense_int8"] = round(res_q["sparse_tokens_per_s"] / res_q["dense_tokens_per_s"], 3)
         res_q["sparse_vs_dense_bf16"] = round(res_q["sparse_tokens_per_s"] / extras["dense_tokens_per_s"], 3)
+        # batches of 4 tokens: per-token lists, the union of live sets, the dense comparator
+        hq4 = sffn.Handle(D, H, 0, 4, act, sffn.SFFN_I8)
+        b4 = {}
+        for name, mode, dense in (("per_token", sffn.SFFN_MODE_PER_TOKEN, False),
+                                  ("union", sffn.SFFN_MODE_UNION, False), ("dense", 0, True)):
+            def fn4():
+                for c in range(n // 4):
+                    rp = repq[c % R]
+                    args_q = (hq4.ptr, x[4 * c:4 * c + 4], rp["W1"], rp["W1_scale"], rp["W3"],
+                              rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[4 * c:4 * c + 4], 4)
+                    if dense:
+                        sffn.sffn_forward_dense_i8(*args_q)
+                    else:
+                        sffn.sffn_forward_sparse_i8(*args_q, mode)
+            g4 = capture(fn4)
+            ms4 = time_graph(g4, args.steps, args.warmup)
+            del g4
+            b4[name + "_tokens_per_s"] = round(n / (ms4 * 1e-3), 1)
+        b4["union_vs_dense"] = round(b4["union_tokens_per_s"] / b4["dense_tokens_per_s"], 3)
+        res_q["batch4"] = b4
+        hq4.close()
         extras["int8"] = res_q
         log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items() if not isinstance(v, dict))
-            + f", kernels (us/launch) {ktq}")
+            + f", kernels (us/launch) {ktq}, batch of 4 {b4}")
         hq.close()
         del repq, WQ
 

@@ -204,10 +204,11 @@ sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, cons
  * weights (SFFN_I8 handles): as sffn_forward_sparse / sffn_forward_dense, with
  * W1, W3, W2T int8 [H x D] row-major (16-byte aligned) and W1_scale, W3_scale,
  * W2T_scale fp32 [H] (4-byte aligned): weight (i, j) of each matrix is
- * q[i][j] * scale[i]. x is bf16 [T x D], y fp32 [T x D]. Tokens of a batch are
- * processed one after another (mode only selects the live-list semantics,
- * which are the same for one token). Errors as for the other forward calls;
- * a non-int8 handle gives SFFN_INVALID_ARGUMENT.
+ * q[i][j] * scale[i]. x is bf16 [T x D], y fp32 [T x D]. Union and dense calls
+ * with 2..4 tokens read the weights once for the batch (the union of the
+ * tokens' live sets); other batches, and per-token lists, are processed token
+ * by token. Errors as for the other forward calls; a non-int8 handle gives
+ * SFFN_INVALID_ARGUMENT.
  */
 /*
  * Gate-first sparse forward and the dense comparator with weight-only int4
