@@ -27,7 +27,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
             KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_GATE_UP_T1_I4,
             KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4,
-            KIND_RANK_PROJ_MFMA, KIND_GATE_UP_TB_I8, KIND_DOWN_TB_I8, KIND_COUNT };
+            KIND_RANK_PROJ_MFMA, KIND_GATE_UP_TB_I8, KIND_DOWN_TB_I8, KIND_GATE_UP_TB_I4,
+            KIND_DOWN_TB_I4, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -41,7 +42,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_tb", "k_gate_up_t1_i4",
                                             "k_gate_up_dense_t1_i4", "k_down_t1_i4",
                                             "k_gate_up_lopa_t1_i4", "k_rank_proj_mfma",
-                                            "k_gate_up_tb_i8", "k_down_tb_i8"};
+                                            "k_gate_up_tb_i8", "k_down_tb_i8", "k_gate_up_tb_i4",
+                                            "k_down_tb_i4"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -725,6 +727,53 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
     return run_live_list(h, T, live_count, live_idx, s);
 }
 
+// int4 union of a batch of 2..4 tokens (and its dense comparator)
+template <bool DENSE>
+sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float* s1,
+                      const void* W3, const float* s3, const void* W2T, const float* s2,
+                      float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
+    const int nc = (h->D + 2047) / 2048;
+    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    const int tp = 16 * token_tiles(T);
+    const int tt = T <= 2 ? 2 : 4;
+    int splits = h->tb_splits;
+    while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
+    uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
+    float* yz = splits > 1 ? y : nullptr;
+    sffn_status st = SFFN_OK;
+#define SFFN_TB4_GATE(NCV, TTV)                                                                   \
+    st = launch(h, KIND_GATE_UP_TB_I4, k_gate_up_tb_i4<NCV, TTV, DENSE>, dim3(nb),               \
+                dim3(K1_THREADS), s, (const uint16_t*)x, (const uint8_t*)W1, s1,                 \
+                (const uint8_t*)W3, s3, h->m_a, h->m_mask, live, yz, h->D, h->H, T, tp, h->act)
+#define SFFN_TB4_NC(TTV)                                                                          \
+    switch (nc) {                                                                                 \
+        case 1: SFFN_TB4_GATE(1, TTV); break;                                                     \
+        case 2: SFFN_TB4_GATE(2, TTV); break;                                                     \
+        case 3: SFFN_TB4_GATE(3, TTV); break;                                                     \
+        case 4: SFFN_TB4_GATE(4, TTV); break;                                                     \
+        default: return fail(h, SFFN_INTERNAL, "no int4 batch gate kernel for this width");      \
+    }
+    if (tt == 2) { SFFN_TB4_NC(2); } else { SFFN_TB4_NC(4); }
+#undef SFFN_TB4_NC
+#undef SFFN_TB4_GATE
+    if (st != SFFN_OK) return st;
+    const int cb = 16 * 16;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+#define SFFN_TB4_DOWN(TTV)                                                                        \
+    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB_I4, k_down_tb_i4<PMAX, TTV>,                \
+                                       dim3(nbx, splits), dim3(KD_THREADS), s,                    \
+                                       (const float*)h->m_a, (const uint64_t*)h->m_mask,          \
+                                       (const uint8_t*)W2T, s2, y, h->D, h->H, T, tp, splits))
+    if (tt == 2) { SFFN_TB4_DOWN(2); } else { SFFN_TB4_DOWN(4); }
+#undef SFFN_TB4_DOWN
+    if (st != SFFN_OK) return st;
+    if (DENSE) return SFFN_OK;
+    return run_live_list(h, T, live_count, live_idx, s);
+}
+
 // int4 down pass over a_buf (group scales applied per 32-column piece)
 sffn_status run_down_t1_i4(sffn_handle* h, const void* W2T, const float* s2, float* y, int splits,
                            bool dense, hipStream_t s) {
@@ -1061,8 +1110,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             h->t1_fused = 0;
         }
         // batch plans: unit-major products for up to 16*ceil(max_tokens/16) tokens (bf16
-        // MFMA and VALU batches, int8 VALU batches)
-        if ((dtype == SFFN_BF16 || dtype == SFFN_I8) && max_tokens >= 2) {
+        // MFMA and VALU batches, int8 and int4 VALU batches)
+        if ((dtype == SFFN_BF16 || dtype == SFFN_I8 || dtype == SFFN_I4) && max_tokens >= 2) {
             h->m_tp = 16 * token_tiles(max_tokens);
             auto ut_env = [](const char* name, int dflt) {
                 const int v = env_int(name, dflt);
@@ -1283,10 +1332,14 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     if (!s1 || !s3 || !s2) return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // int8 union (and dense) batches of 2..4 tokens read the weights once for the batch
-    if (bits == 8 && T >= 2 && T <= 4 && h->m_a && (dense || mode == SFFN_MODE_UNION))
+    // union (and dense) batches of 2..4 tokens read the weights once for the batch
+    if (T >= 2 && T <= 4 && h->m_a && (dense || mode == SFFN_MODE_UNION)) {
+        if (bits == 4)
+            return dense ? run_i4_tb<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
+                         : run_i4_tb<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
         return dense ? run_i8_tb<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
                      : run_i8_tb<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
+    }
     // other batches run token by token (both modes compute the same result)
     for (int t = 0; t < T; ++t) {
         const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);

@@ -2863,6 +2863,240 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
     }
 }
 
+// Small batches (T <= TT <= 4) with group-scaled int4 weights, union of the
+// tokens' live sets: as k_gate_up_tb_i8, with each pair of codes turned into a
+// bf16 pair once (the byte permute of dot32_i4) and met with every token's x
+// pair by a bf16 dot2; 136 * sum(x) per token and 32 codes is taken off before
+// the group scale. Stores a[unit][tp] = A(z) u (the down pass applies the W2T
+// group scales).
+template <int NC, int TT, bool DENSE>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i4(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ W1, const float* __restrict__ s1,
+    const uint8_t* __restrict__ W3, const float* __restrict__ s3, float* __restrict__ a_rm,
+    uint64_t* __restrict__ umask, uint8_t* __restrict__ live_out, float* __restrict__ y_zero,
+    int D, int H, int T, int tp, int act) {
+    constexpr int CW = WAVE * 32;  // columns of one chunk: 32 codes per lane
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int unit = blockIdx.x * K1_WAVES + wave;
+    const bool in = unit < H;
+    const int G = D / I4_GROUP;
+    const size_t rb = (size_t)D / 2;
+    u32x4 w[NC];
+    float sc[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 32;
+        const bool ok = in && col < D;
+        w[c] = ok ? load_stream(W1 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+        sc[c] = ok ? s1[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+    }
+    X32 xv[TT][NC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            xv[t][c] = load_x32(x + (size_t)(t < T ? t : 0) * D, t < T ? c * CW + lane * 32 : D, D);
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < T * D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    auto dot_tokens = [&](const u32x4 (&wr)[NC], const float (&scl)[NC], float (&v)[TT]) {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) v[t] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float sp[TT];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) sp[t] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wq = wr[c][q] ^ 0x88888888u;
+                const uint32_t lo = wq & 0x0F0F0F0Fu;
+                const uint32_t hi = (wq >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+                for (int b = 0; b < 4; ++b) {
+                    const uint32_t sel = (uint32_t)b | (0x0cu << 8) | ((4u + b) << 16) | (0x0cu << 24);
+                    const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+#pragma unroll
+                    for (int t = 0; t < TT; ++t) {
+                        const uint32_t xp = xv[t][c].v[q][b];
+                        sp[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                                                __builtin_bit_cast(bf16x2, xp), sp[t], false);
+                    }
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < TT; ++t) v[t] = fmaf(scl[c], fmaf(-136.0f, xv[t][c].sum, sp[t]), v[t]);
+        }
+    };
+    const int tl = bit_rev<TT>(lane & (TT - 1));  // token whose sums this lane ends with
+    float v[TT];
+    dot_tokens(w, sc, v);
+    const float z = multi_reduce<TT>(v);
+    const bool lv = in && tl < T && z > 0.0f;
+    const uint64_t bl = __ballot(lv && lane < TT);
+    uint64_t m = 0;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) m |= ((bl >> bit_rev<TT>(t)) & 1ull) << t;
+    if (!in) return;  // wave-uniform: one unit per wave
+    if (lane == 0) umask[unit] = DENSE ? ((1ull << T) - 1) : m;
+    if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
+    if (!DENSE && m == 0) {
+        if (lane < TT) a_rm[(size_t)unit * tp + tl] = 0.0f;
+        return;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 32;
+        const bool ok = col < D;
+        w[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+        sc[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+    }
+    dot_tokens(w, sc, v);
+    const float u = multi_reduce<TT>(v);
+    if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u : 0.0f;
+}
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Down pass of the int4 small batches: 16 lanes x 16 codes (8 bytes) per
+// 256-column slice, the group scale of each lane's 16 columns applied to the
+// unit's products; otherwise as k_down_tb_i8.
+template <int PMAX, int TT>
+__global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restrict__ a_rm,
+                                                           const uint64_t* __restrict__ umask,
+                                                           const uint8_t* __restrict__ W2T,
+                                                           const float* __restrict__ s2,
+                                                           float* __restrict__ y, int D, int H,
+                                                           int T, int tp, int splits) {
+    constexpr int LPR = 16;
+    constexpr int VEC = 16;
+    constexpr int CB = LPR * VEC;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 4;
+    __shared__ int list[KD_LCAP];
+    __shared__ int wcount[PMAX * KD_WAVES];
+    __shared__ int woff[PMAX * KD_WAVES + 1];
+    __shared__ float red[KD_WAVES][CB];
+
+    const int nslices = (D + CB - 1) / CB;
+    const int per_xcd = (nslices + 7) / 8;
+    const int bx = blockIdx.x;
+    const int slice = (bx & 7) * per_xcd + (bx >> 3);
+    if (slice >= nslices) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * VEC;
+    const bool col_ok = col < D;
+    const int G = D / I4_GROUP;
+    const size_t rb = (size_t)D / 2;
+    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
+
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + p * KD_THREADS + threadIdx.x;
+        const bool keep = p < P && row < h1 && umask[row] != 0ull;
+        mk[p] = __ballot(keep);
+        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
+    __syncthreads();
+
+    float acc[TT][VEC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) acc[t][k] = 0.0f;
+
+    int p0 = 0;
+    while (p0 < P) {
+        int p1 = p0 + 1;
+        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
+        const int ebase = woff[p0 * KD_WAVES];
+        const int n = woff[p1 * KD_WAVES] - ebase;
+#pragma unroll
+        for (int p = 0; p < PMAX; ++p) {
+            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
+                const int pos = woff[p * KD_WAVES + wave] - ebase +
+                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
+            }
+        }
+        __syncthreads();
+        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+            u32x2 wv[UF];
+            float av[UF][TT];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const int e = e0 + u * KD_WAVES * RPI;
+                const bool ok = e < n && col_ok;
+                const int row = e < n ? list[e] : 0;
+                wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + (size_t)row * rb + col / 2))
+                           : u32x2{0u, 0u};
+                const float sg = ok ? s2[(size_t)row * G + col / I4_GROUP] : 0.0f;
+                // TT <= 16 <= tp, and padded token slots of a_rm hold 0
+                const float* ar = a_rm + (size_t)row * tp;
+#pragma unroll
+                for (int t = 0; t < TT; t += 2) {
+                    const float2 v2 = e < n ? *reinterpret_cast<const float2*>(ar + t)
+                                            : make_float2(0.0f, 0.0f);
+                    av[u][t] = v2.x * sg;
+                    av[u][t + 1] = v2.y * sg;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u)
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const uint32_t wq = wv[u][q];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b) {
+                        const float wf = (float)((int)(wq << (28 - 4 * b)) >> 28);  // nibble b, signed
+#pragma unroll
+                        for (int t = 0; t < TT; ++t) acc[t][8 * q + b] = fmaf(av[u][t], wf, acc[t][8 * q + b]);
+                    }
+                }
+        }
+        __syncthreads();
+        p0 = p1;
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+            float v = acc[t][k];
+            for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+            acc[t][k] = v;
+        }
+        if (grp == 0) {
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[t][k];
+        }
+        __syncthreads();
+        for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+            float s = 0.0f;
+            for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+            if (col0 + c < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + col0 + c, s);
+                else
+                    y[(size_t)t * D + col0 + c] = s;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Sparse expert FFNs in a top-K mixture of experts (page "Model casting:
 // compute the gate, then skip most of the FFN", section "Where it

@@ -829,9 +829,30 @@ def main() -> int:
         res4["measured_sparsity"] = round(float(1 - k4.mean() / H), 4)
         res4["sparse_vs_dense_int4"] = round(res4["sparse_tokens_per_s"] / res4["dense_tokens_per_s"], 3)
         res4["sparse_vs_dense_bf16"] = round(res4["sparse_tokens_per_s"] / extras["dense_tokens_per_s"], 3)
+        # batches of 4 tokens: per-token lists, the union of live sets, the dense comparator
+        h44 = sffn.Handle(D, H, 0, 4, act, sffn.SFFN_I4)
+        b44 = {}
+        for name, mode, dense in (("per_token", sffn.SFFN_MODE_PER_TOKEN, False),
+                                  ("union", sffn.SFFN_MODE_UNION, False), ("dense", 0, True)):
+            def fn44():
+                for c in range(n // 4):
+                    rp = rep4[c % R]
+                    args_4 = (h44.ptr, x[4 * c:4 * c + 4], rp["W1"], rp["W1_scale"], rp["W3"],
+                              rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[4 * c:4 * c + 4], 4)
+                    if dense:
+                        sffn.sffn_forward_dense_i4(*args_4)
+                    else:
+                        sffn.sffn_forward_sparse_i4(*args_4, mode)
+            g44 = capture(fn44)
+            ms44 = time_graph(g44, args.steps, args.warmup)
+            del g44
+            b44[name + "_tokens_per_s"] = round(n / (ms44 * 1e-3), 1)
+        b44["union_vs_dense"] = round(b44["union_tokens_per_s"] / b44["dense_tokens_per_s"], 3)
+        res4["batch4"] = b44
+        h44.close()
         extras["int4_group128"] = res4
         log("int4: " + ", ".join(f"{kk} {v:,}" for kk, v in res4.items() if not isinstance(v, dict))
-            + f", kernels (us/launch) {kt4}")
+            + f", kernels (us/launch) {kt4}, batch of 4 {b44}")
         h4.close()
         del rep4, W4
 

@@ -215,7 +215,8 @@ sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, cons
  * weights (SFFN_I4 handles): as the _i8 calls, with W1, W3, W2T packed int4
  * [H x D/2] bytes (16-byte aligned) and W1_scale, W3_scale, W2T_scale fp32
  * [H x D/128] (4-byte aligned): weight (i, j) is code(i, j) * scale[i][j / 128].
- * x bf16 [T x D], y fp32 [T x D]; tokens of a batch run one after another.
+ * x bf16 [T x D], y fp32 [T x D]; union and dense calls with 2..4 tokens read
+ * the weights once for the batch, other batches run token by token.
  * Errors as for the other forward calls; a non-int4 handle gives
  * SFFN_INVALID_ARGUMENT.
  */
