@@ -1165,19 +1165,44 @@ __device__ inline float dot16_i8(const u32x4& w, const float* xv, float s) {
     return s;
 }
 
-// x[col .. col + 16) (bf16) as fp32; zeros past D
-__device__ inline void load_x16(const uint16_t* __restrict__ x, int col, int D, float* xv) {
-    if (col < D) {
-        const u32x4 a = load_cached(x + col), b = load_cached(x + col + 8);
+// 16 bf16 of x (32 bytes at col) as 8 bf16 pairs, and their fp32 sum; zeros past D
+struct X16 {
+    u32x4 v[2];
+    float sum;
+};
+__device__ inline X16 load_x16(const uint16_t* __restrict__ x, int col, int D) {
+    X16 r;
+    r.v[0] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    r.v[1] = col < D ? load_cached(x + col + 8) : u32x4{0u, 0u, 0u, 0u};
+    r.sum = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            xv[k] = Elem<uint16_t>::get(a, k);
-            xv[8 + k] = Elem<uint16_t>::get(b, k);
-        }
-    } else {
+    for (int k = 0; k < 8; ++k) r.sum += Elem<uint16_t>::get(r.v[0], k) + Elem<uint16_t>::get(r.v[1], k);
+    return r;
+}
+
+// 16 int8 weights against 16 bf16 x values, fp32 sum. A weight q becomes q + 128
+// (byte ^ 0x80), converted exactly to fp32 and packed two at a time as bf16 (its
+// 8 significant bits hold 0..255), so one bf16 dot2 takes two weights; the
+// 128 * sum(x) this adds is taken off at the end.
+__device__ inline float dot16_i8x(const u32x4& w, const X16& xv, float s) {
+    float sp = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) xv[k] = 0.0f;
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q] ^ 0x80808080u;
+        const uint32_t f0 = __float_as_uint((float)(wq & 0xffu));
+        const uint32_t f1 = __float_as_uint((float)((wq >> 8) & 0xffu));
+        const uint32_t f2 = __float_as_uint((float)((wq >> 16) & 0xffu));
+        const uint32_t f3 = __float_as_uint((float)(wq >> 24));
+        const uint32_t p01 = __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // bf16 of f0, f1
+        const uint32_t p23 = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+        const u32x4 xq = xv.v[q >> 1];
+        const uint32_t x01 = xq[2 * (q & 1)], x23 = xq[2 * (q & 1) + 1];
+        sp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01),
+                                             __builtin_bit_cast(bf16x2, x01), sp, false);
+        sp = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23),
+                                             __builtin_bit_cast(bf16x2, x23), sp, false);
     }
+    return s + fmaf(-128.0f, xv.sum, sp);
 }
 
 // Gate and gathered up projection, int8 weights: z_i = s1_i (q1_i . x); for a
@@ -1213,16 +1238,16 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i8(
     const float sc1 = in ? s1[unit] : 0.0f;
     const float sc3 = in ? s3[unit] : 0.0f;
     const float sc2 = in ? s2[unit] : 0.0f;
-    float xv[NC][16];
+    X16 xv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) load_x16(x, c * CW + lane * 16, D, xv[c]);
+    for (int c = 0; c < NC; ++c) xv[c] = load_x16(x, c * CW + lane * 16, D);
     if (y_zero) {
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
     }
     float sz = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) sz = dot16_i8(w[c], xv[c], sz);
+    for (int c = 0; c < NC; ++c) sz = dot16_i8x(w[c], xv[c], sz);
     const float z = wave_sum_dpp(sz) * sc1;
     const bool live = in && z > 0.0f;
     if (!in) return;
@@ -1240,7 +1265,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i8(
     }
     float su = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) su = dot16_i8(w3[c], xv[c], su);
+    for (int c = 0; c < NC; ++c) su = dot16_i8x(w3[c], xv[c], su);
     const float u = wave_sum_dpp(su) * sc3;
     if (lane == 0) a_out[unit] = activation(act, z) * u * sc2;
 }
@@ -1261,16 +1286,16 @@ __global__ __launch_bounds__(K1_THREADS) void k_rank_proj_t1_i8(
         const int col = c * CW + lane * 16;
         w[c] = (m < r && col < D) ? load_stream(V + (size_t)m * D + col) : u32x4{0u, 0u, 0u, 0u};
     }
-    float xv[NC][16];
+    X16 xv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) load_x16(x, c * CW + lane * 16, D, xv[c]);
+    for (int c = 0; c < NC; ++c) xv[c] = load_x16(x, c * CW + lane * 16, D);
     if (y_zero) {
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
     }
     float s = 0.0f;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) s = dot16_i8(w[c], xv[c], s);
+    for (int c = 0; c < NC; ++c) s = dot16_i8x(w[c], xv[c], s);
     s = wave_sum_dpp(s);
     if (lane == 0 && m < r) t_out[m] = s * sV[m];
 }
@@ -1325,9 +1350,9 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
             for (int k = 0; k < 16; ++k) tv[c][k] = 0.0f;
         }
     }
-    float xv[NC][16];
+    X16 xv[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) load_x16(x, c * CW + lane * 16, D, xv[c]);
+    for (int c = 0; c < NC; ++c) xv[c] = load_x16(x, c * CW + lane * 16, D);
     const float su_ = in ? sU[unit] : 0.0f;
     const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
     float inv = 1.0f;  // RMSNorm of t: every lane group sees all of t
@@ -1362,7 +1387,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
         }
         float s = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) s = dot16_i8(w3[c], xv[c], s);
+        for (int c = 0; c < NC; ++c) s = dot16_i8x(w3[c], xv[c], s);
         const float uu = wave_sum_dpp(s) * s3[ul];
         const float g3 = (flags & LOPA_DOUBLE_ACT) ? activation(act, uu) : uu;
         if (lane == 0) a_out[ul] = activation(act, zl) * g3 * s2[ul];
@@ -2686,23 +2711,51 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
     const float sc1 = in ? s1[unit] : 0.0f;
     const float sc3 = in ? s3[unit] : 0.0f;
     const float sc2 = in ? s2[unit] : 0.0f;
+    // sum of each token's 16 x values of the lane per chunk (for the code offset)
+    float xs[TT][NC];
+#pragma unroll
+    for (int t = 0; t < TT; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float a = 0.0f;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) a += Elem<uint16_t>::get(xb[t][c][k >> 3], k & 7);
+            xs[t][c] = a;
+        }
+    // A weight q becomes q + 128 (byte ^ 0x80), converted exactly to fp32 and packed
+    // two at a time as bf16 (8 significant bits hold 0..255); one bf16 dot2 per token
+    // then takes two weights, and 128 * sum(x) comes off once per chunk.
     auto dot_tokens = [&](const u32x4 (&wr)[NC], float (&v)[TT]) {
 #pragma unroll
         for (int t = 0; t < TT; ++t) v[t] = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c)
+        for (int c = 0; c < NC; ++c) {
+            float sp[TT];
+#pragma unroll
+            for (int t = 0; t < TT; ++t) sp[t] = 0.0f;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const uint32_t wq = wr[c][q];
+                const uint32_t wq = wr[c][q] ^ 0x80808080u;
+                const uint32_t f0 = __float_as_uint((float)(wq & 0xffu));
+                const uint32_t f1 = __float_as_uint((float)((wq >> 8) & 0xffu));
+                const uint32_t f2 = __float_as_uint((float)((wq >> 16) & 0xffu));
+                const uint32_t f3 = __float_as_uint((float)(wq >> 24));
+                // high halves (the bf16 values): f0 | f1 << 16, f2 | f3 << 16
+                const uint32_t p01 = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+                const uint32_t p23 = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
 #pragma unroll
-                for (int b = 0; b < 4; ++b) {
-                    const float wf = (float)((int)(wq << (24 - 8 * b)) >> 24);  // byte b, signed
-                    const int k = 4 * q + b;                                     // column of the lane
-#pragma unroll
-                    for (int t = 0; t < TT; ++t)
-                        v[t] = fmaf(wf, Elem<uint16_t>::get(xb[t][c][k >> 3], k & 7), v[t]);
+                for (int t = 0; t < TT; ++t) {
+                    const u32x4 xq = xb[t][c][q >> 1];
+                    const uint32_t x01 = xq[2 * (q & 1)], x23 = xq[2 * (q & 1) + 1];
+                    sp[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01),
+                                                            __builtin_bit_cast(bf16x2, x01), sp[t], false);
+                    sp[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23),
+                                                            __builtin_bit_cast(bf16x2, x23), sp[t], false);
                 }
             }
+#pragma unroll
+            for (int t = 0; t < TT; ++t) v[t] += fmaf(-128.0f, xs[t][c], sp[t]);
+        }
     };
     const int tl = bit_rev<TT>(lane & (TT - 1));  // token whose sums this lane ends with
     float v[TT];
