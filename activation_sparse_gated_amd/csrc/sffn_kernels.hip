@@ -1174,9 +1174,15 @@ __device__ inline X16 load_x16(const uint16_t* __restrict__ x, int col, int D) {
     X16 r;
     r.v[0] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
     r.v[1] = col < D ? load_cached(x + col + 8) : u32x4{0u, 0u, 0u, 0u};
-    r.sum = 0.0f;
+    r.sum = 0.0f;  // one bf16 dot2 against (1, 1) per pair
 #pragma unroll
-    for (int k = 0; k < 8; ++k) r.sum += Elem<uint16_t>::get(r.v[0], k) + Elem<uint16_t>::get(r.v[1], k);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t xq = r.v[h][q];
+            r.sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq),
+                                                    __builtin_bit_cast(bf16x2, 0x3F803F80u), r.sum, false);
+        }
     return r;
 }
 
@@ -1537,12 +1543,16 @@ struct X32 {
 };
 __device__ inline X32 load_x32(const uint16_t* __restrict__ x, int col, int D) {
     X32 r;
-    r.sum = 0.0f;
+    r.sum = 0.0f;  // one bf16 dot2 against (1, 1) per pair
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         r.v[q] = col < D ? load_cached(x + col + 8 * q) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) r.sum += Elem<uint16_t>::get(r.v[q], k);
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t xq = r.v[q][k];
+            r.sum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq),
+                                                    __builtin_bit_cast(bf16x2, 0x3F803F80u), r.sum, false);
+        }
     }
     return r;
 }
@@ -2717,9 +2727,13 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
     for (int t = 0; t < TT; ++t)
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-            float a = 0.0f;
+            float a = 0.0f;  // one bf16 dot2 against (1, 1) per pair
 #pragma unroll
-            for (int k = 0; k < 16; ++k) a += Elem<uint16_t>::get(xb[t][c][k >> 3], k & 7);
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t xq = xb[t][c][k >> 2][k & 3];
+                a = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, xq),
+                                                    __builtin_bit_cast(bf16x2, 0x3F803F80u), a, false);
+            }
             xs[t][c] = a;
         }
     // A weight q becomes q + 128 (byte ^ 0x80), converted exactly to fp32 and packed
