@@ -1535,6 +1535,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
 // 16-byte load holds 32 codes of one 128-column group, so its partial dot
 // product takes one scale.
 constexpr int I4_GROUP = 128;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // 32 bf16 of x (64 bytes at col) as 16 bf16 pairs, and their fp32 sum; zeros past D
 struct X32 {
@@ -1732,16 +1733,16 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i4(
 }
 
 // Down projection, int4 W2T rows: y[slice] = sum_i a_i s2_ig q2[i, slice] with
-// g the 128-column group of each lane's 32 columns. As k_down_t1_i8, with
-// column slices of 8 lanes x 32 columns = 256 columns (8 rows per wave load).
+// g the 128-column group of each lane's 16 columns. As k_down_t1_i8, with
+// column slices of 16 lanes x 16 codes (8-byte loads) = 256 columns.
 template <int PMAX>
 __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restrict__ a,
                                                            const uint8_t* __restrict__ W2T,
                                                            const float* __restrict__ s2,
                                                            float* __restrict__ y, int D, int H,
                                                            int splits, int dense) {
-    constexpr int LPR = 8;
-    constexpr int CB = LPR * 32;
+    constexpr int LPR = 16;
+    constexpr int CB = LPR * 16;
     constexpr int RPI = WAVE / LPR;
     constexpr int UF = 8;
     __shared__ int list[KD_LCAP];
@@ -1762,7 +1763,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int sub = lane % LPR, grp = lane / LPR;
-    const int col = col0 + sub * 32;
+    const int col = col0 + sub * 16;
     const bool col_ok = col < D;
     const int G = D / I4_GROUP;
     const size_t rb = (size_t)D / 2;
@@ -1786,9 +1787,9 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
     if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
     __syncthreads();
 
-    float acc[32];
+    float acc[16];
 #pragma unroll
-    for (int k = 0; k < 32; ++k) acc[k] = 0.0f;
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
     int p0 = 0;
     while (p0 < P) {
         int p1 = p0 + 1;
@@ -1807,14 +1808,15 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
         }
         __syncthreads();
         for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
-            u32x4 wv[UF];
+            u32x2 wv[UF];
             float sg[UF];
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
                 const int e = e0 + u * KD_WAVES * RPI;
                 const bool ok = e < n && col_ok;
                 const int row = ok ? list[e] : 0;
-                wv[u] = ok ? load_stream(W2T + (size_t)row * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+                wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + (size_t)row * rb + col / 2))
+                           : u32x2{0u, 0u};
                 sg[u] = ok ? s2[(size_t)row * G + col / I4_GROUP] : 0.0f;
             }
 #pragma unroll
@@ -1822,7 +1824,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
                 const int e = e0 + u * KD_WAVES * RPI;
                 const float aval = (e < n ? av[e] : 0.0f) * sg[u];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
+                for (int q = 0; q < 2; ++q) {
                     const uint32_t wq = wv[u][q];
 #pragma unroll
                     for (int b = 0; b < 8; ++b)
@@ -1833,13 +1835,12 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
         __syncthreads();
         p0 = p1;
     }
-    // sum over the 8 row groups of a wave as a reduce-scatter: at the exchange with
-    // the lane 32, 16, 8 apart each lane sends the half of its columns that its
-    // partner keeps, so a lane ends with 4 whole columns (28 shuffles, not 96)
-    static_assert(LPR == 8, "three halving exchanges over 8 row groups");
+    // sum over the 4 row groups of a wave as a reduce-scatter (lanes 32 and 16
+    // apart): each lane ends with 4 whole columns of its 16 (12 shuffles)
+    static_assert(LPR == 16, "two halving exchanges over 4 row groups");
 #pragma unroll
-    for (int st = 0; st < 3; ++st) {
-        const int o = 32 >> st, half = 16 >> st;
+    for (int st = 0; st < 2; ++st) {
+        const int o = 32 >> st, half = 8 >> st;
         const bool upper = (lane & o) != 0;
 #pragma unroll
         for (int k = 0; k < half; ++k) {
@@ -1848,10 +1849,9 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
             acc[k] = keep + __shfl_xor(upper ? lo : hi, o, WAVE);
         }
     }
-    // columns 16 b5 + 8 b4 + 4 b3 + k of this lane's 32 (b: bits of the lane)
-    const int cpart = 16 * ((lane >> 5) & 1) + 8 * ((lane >> 4) & 1) + 4 * ((lane >> 3) & 1);
+    const int cpart = 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) red[wave][sub * 32 + cpart + k] = acc[k];
+    for (int k = 0; k < 4; ++k) red[wave][sub * 16 + cpart + k] = acc[k];
     __syncthreads();
     for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
         float s = 0.0f;
@@ -3024,8 +3024,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i4(
     const float u = multi_reduce<TT>(v);
     if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u : 0.0f;
 }
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Down pass of the int4 small batches: 16 lanes x 16 codes (8 bytes) per
 // 256-column slice, the group scale of each lane's 16 columns applied to the
