@@ -1607,8 +1607,10 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i4(
         const bool ok = in && col < D;
         w[c] = ok ? load_stream(W1 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
         sc1[c] = ok ? s1[(size_t)unit * G + col / I4_GROUP] : 0.0f;
-        if (DENSE) w3[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
-        sc3[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+        if (DENSE) {
+            w3[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+            sc3[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+        }
     }
     X32 xv[NC];
 #pragma unroll
@@ -1628,11 +1630,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1_i4(
         if (lane == 0) a_out[unit] = 0.0f;
         return;
     }
-    if (!DENSE) {
+    if (!DENSE) {  // the live unit's W3 row and its group scales
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const int col = c * CW + lane * 32;
             w3[c] = col < D ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+            sc3[c] = col < D ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
         }
     }
     float su = 0.0f;
