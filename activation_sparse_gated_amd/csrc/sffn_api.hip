@@ -28,7 +28,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_GATE_UP_T1_I4,
             KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4,
             KIND_RANK_PROJ_MFMA, KIND_GATE_UP_TB_I8, KIND_DOWN_TB_I8, KIND_GATE_UP_TB_I4,
-            KIND_DOWN_TB_I4, KIND_COUNT };
+            KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -43,7 +43,7 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_dense_t1_i4", "k_down_t1_i4",
                                             "k_gate_up_lopa_t1_i4", "k_rank_proj_mfma",
                                             "k_gate_up_tb_i8", "k_down_tb_i8", "k_gate_up_tb_i4",
-                                            "k_down_tb_i4"};
+                                            "k_down_tb_i4", "k_rank_proj_tb_i8", "k_gate_up_lopa_tb_q"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -1382,6 +1382,90 @@ sffn_status sffn_forward_dense_i4(sffn_handle* h, const void* x, const void* W1,
     }
 }
 
+// quantised LoPA, union of 2..4 tokens: batched rank projection (int8 V), the
+// LoPA gate and the W3 gather over the union (int8 or int4 W3), the down pass
+// of the small batches. Widths up to 4 chunks of W3 (else false: token by token).
+bool lopa_q_tb_ok(const sffn_handle* h, int T, int bits) {
+    const int nc = bits == 8 ? (h->D + 1023) / 1024 : (h->D + 2047) / 2048;
+    return T >= 2 && T <= 4 && h->m_a && nc <= 4 && (h->D + 1023) / 1024 <= 4;
+}
+
+sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const float* sV,
+                          const void* U, const float* sU, const void* W3, const float* s3,
+                          const void* W2T, const float* s2, float* y, int T, int32_t* live_count,
+                          int32_t* live_idx, hipStream_t s, int bits) {
+    const int tt = T <= 2 ? 2 : 4;
+    const int tp = 16 * token_tiles(T);
+    int splits = h->tb_splits;
+    while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
+    float* yz = splits > 1 ? y : nullptr;
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    sffn_status st = SFFN_OK;
+    const int nc8 = (h->D + 1023) / 1024;
+    const int nbr = (h->r + K1_WAVES - 1) / K1_WAVES;
+#define SFFN_RPTB(NCV, TTV)                                                                       \
+    st = launch(h, KIND_RANK_PROJ_TB_I8, k_rank_proj_tb_i8<NCV, TTV>, dim3(nbr), dim3(K1_THREADS),\
+                s, (const uint16_t*)x, (const int8_t*)V, sV, h->t_buf, yz, h->D, h->r, T)
+#define SFFN_RPTB_NC(TTV)                                                                         \
+    switch (nc8) {                                                                                \
+        case 1: SFFN_RPTB(1, TTV); break;                                                         \
+        case 2: SFFN_RPTB(2, TTV); break;                                                         \
+        case 3: SFFN_RPTB(3, TTV); break;                                                         \
+        case 4: SFFN_RPTB(4, TTV); break;                                                         \
+        default: return fail(h, SFFN_INTERNAL, "no batched rank projection for this width");     \
+    }
+    if (tt == 2) { SFFN_RPTB_NC(2); } else { SFFN_RPTB_NC(4); }
+#undef SFFN_RPTB_NC
+#undef SFFN_RPTB
+    if (st != SFFN_OK) return st;
+    const int nb = (h->H + K1_WAVES * KLQ_UPW - 1) / (K1_WAVES * KLQ_UPW);
+    const int nc = bits == 8 ? nc8 : (h->D + 2047) / 2048;
+#define SFFN_LQTB(NCV, TTV, BV)                                                                   \
+    st = launch_shm(h, KIND_GATE_UP_LOPA_TB_Q, k_gate_up_lopa_tb_q<NCV, TTV, BV>, dim3(nb),       \
+                dim3(K1_THREADS), (size_t)T * h->r * sizeof(float), s, (const uint16_t*)x,         \
+                (const float*)h->t_buf, (const int8_t*)U,                                         \
+                sU, (const uint8_t*)W3, s3, s2, h->m_a, h->m_mask, live, h->D, h->H, h->r, T, tp, \
+                h->act, h->flags)
+#define SFFN_LQTB_NC(TTV, BV)                                                                     \
+    switch (nc) {                                                                                 \
+        case 1: SFFN_LQTB(1, TTV, BV); break;                                                     \
+        case 2: SFFN_LQTB(2, TTV, BV); break;                                                     \
+        case 3: SFFN_LQTB(3, TTV, BV); break;                                                     \
+        case 4: SFFN_LQTB(4, TTV, BV); break;                                                     \
+        default: return fail(h, SFFN_INTERNAL, "no batched LoPA gate for this width");           \
+    }
+    if (bits == 8) {
+        if (tt == 2) { SFFN_LQTB_NC(2, 8); } else { SFFN_LQTB_NC(4, 8); }
+    } else {
+        if (tt == 2) { SFFN_LQTB_NC(2, 4); } else { SFFN_LQTB_NC(4, 4); }
+    }
+#undef SFFN_LQTB_NC
+#undef SFFN_LQTB
+    if (st != SFFN_OK) return st;
+    const int cb = 16 * 16;
+    const int nslices = (h->D + cb - 1) / cb;
+    const int nbx = ((nslices + 7) / 8) * 8;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+#define SFFN_LQ_DOWN(TTV)                                                                         \
+    if (bits == 8) {                                                                              \
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB_I8, k_down_tb_i8<PMAX, TTV>,            \
+                                           dim3(nbx, splits), dim3(KD_THREADS), s,                \
+                                           (const float*)h->m_a, (const uint64_t*)h->m_mask,      \
+                                           (const int8_t*)W2T, y, h->D, h->H, T, tp, splits));    \
+    } else {                                                                                      \
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB_I4, k_down_tb_i4<PMAX, TTV>,            \
+                                           dim3(nbx, splits), dim3(KD_THREADS), s,                \
+                                           (const float*)h->m_a, (const uint64_t*)h->m_mask,      \
+                                           (const uint8_t*)W2T, s2, y, h->D, h->H, T, tp,         \
+                                           splits));                                              \
+    }
+    if (tt == 2) { SFFN_LQ_DOWN(2); } else { SFFN_LQ_DOWN(4); }
+#undef SFFN_LQ_DOWN
+    if (st != SFFN_OK) return st;
+    return run_live_list(h, T, live_count, live_idx, s);
+}
+
 // LoPA with quantised weights: int8 rows everywhere (bits 8), or int8 V and U
 // rows with group-scaled int4 W3 and W2T rows (bits 4)
 static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, const float* sV,
@@ -1405,7 +1489,11 @@ static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, 
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(sV) || !al4(sU) || !al4(s3) || !al4(s2))
         return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // a batch runs token by token (both modes compute the same result)
+    // union batches of 2..4 tokens read the weights once for the batch
+    if (mode == SFFN_MODE_UNION && lopa_q_tb_ok(h, T, bits))
+        return run_lopa_q_tb(h, x, V, sV, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx, s,
+                             bits);
+    // other batches run token by token (both modes compute the same result)
     for (int t = 0; t < T; ++t) {
         const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);
         float* yt = y + (size_t)t * h->D;

@@ -32,6 +32,7 @@
 // Weights are streamed with nontemporal 16-byte loads; every product is
 // accumulated in fp32.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace sffn {
@@ -3162,6 +3163,253 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
             }
         }
         __syncthreads();
+    }
+}
+
+// Quantised LoPA, union of 2..4 tokens. Helpers: one decode of a weight piece
+// against the TT tokens' x (as dot16_i8x and dot32_i4 for one token).
+template <int TT>
+__device__ inline void dot16_i8x_tt(const u32x4& w, const X16 (&xv)[TT], float (&v)[TT]) {
+    float sp[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) sp[t] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q] ^ 0x80808080u;
+        const uint32_t f0 = __float_as_uint((float)(wq & 0xffu));
+        const uint32_t f1 = __float_as_uint((float)((wq >> 8) & 0xffu));
+        const uint32_t f2 = __float_as_uint((float)((wq >> 16) & 0xffu));
+        const uint32_t f3 = __float_as_uint((float)(wq >> 24));
+        const uint32_t p01 = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        const uint32_t p23 = __builtin_amdgcn_perm(f3, f2, 0x07060302u);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const u32x4 xq = xv[t].v[q >> 1];
+            const uint32_t x01 = xq[2 * (q & 1)], x23 = xq[2 * (q & 1) + 1];
+            sp[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p01),
+                                                    __builtin_bit_cast(bf16x2, x01), sp[t], false);
+            sp[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p23),
+                                                    __builtin_bit_cast(bf16x2, x23), sp[t], false);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) v[t] += fmaf(-128.0f, xv[t].sum, sp[t]);
+}
+
+template <int TT>
+__device__ inline void dot32_i4_tt(const u32x4& w, const X32 (&xv)[TT], float scale, float (&v)[TT]) {
+    float sp[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) sp[t] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t wq = w[q] ^ 0x88888888u;
+        const uint32_t lo = wq & 0x0F0F0F0Fu;
+        const uint32_t hi = (wq >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const uint32_t sel = (uint32_t)b | (0x0cu << 8) | ((4u + b) << 16) | (0x0cu << 24);
+            const uint32_t pair = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+#pragma unroll
+            for (int t = 0; t < TT; ++t) {
+                const uint32_t xp = xv[t].v[q][b];
+                sp[t] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                                        __builtin_bit_cast(bf16x2, xp), sp[t], false);
+            }
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) v[t] = fmaf(scale, fmaf(-136.0f, xv[t].sum, sp[t]), v[t]);
+}
+
+// Rank projection of the quantised LoPA batches: t[token][m] = sV_m (qV_m . x),
+// one int8 V row per wave, each weight decoded once for the TT tokens. Writes
+// t_out [T x r]; y_zero (nullable): T x D floats cleared for the down pass.
+template <int NC, int TT>
+__global__ __launch_bounds__(K1_THREADS) void k_rank_proj_tb_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ V, const float* __restrict__ sV,
+    float* __restrict__ t_out, float* __restrict__ y_zero, int D, int r, int T) {
+    constexpr int CW = WAVE * 16;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int m = blockIdx.x * K1_WAVES + wave;
+    const bool in = m < r;
+    u32x4 w[NC];
+    X16 xv[NC][TT];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 16;
+        w[c] = (in && col < D) ? load_stream(V + (size_t)m * D + col) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int t = 0; t < TT; ++t)
+            xv[c][t] = load_x16(x + (size_t)(t < T ? t : 0) * D, t < T ? col : D, D);
+    }
+    if (y_zero) {
+        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < T * D; j += gridDim.x * K1_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    float v[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) v[t] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) dot16_i8x_tt<TT>(w[c], xv[c], v);
+    const float tm = multi_reduce<TT>(v) * (in ? sV[m] : 0.0f);
+    const int tl = bit_rev<TT>(lane & (TT - 1));
+    if (in && lane < TT && tl < T) t_out[(size_t)tl * r + m] = tm;
+}
+
+// LoPA gate of the quantised batches and the up projection over the union:
+// four units per wave, 16 lanes per int8 U row (pieces of 256 B: the first
+// KLQ_NRU issued with the x loads at the start, any further ones in a loop);
+// the T rank vectors t (fp32) are staged in LDS by the block (dynamic LDS of
+// T r floats). z for each token against its t, through RMSNorm when asked, plus
+// (G x)_i when asked. Then each unit of the wave live for some token takes the
+// whole wave for its W3 row (int8 with a row scale, BITS = 8, or int4 with group
+// scales, BITS = 4), every weight decoded once for the TT tokens; the next live
+// unit's row is loaded while the current one is reduced. Stores
+// a[unit][tp] = A(z_t) g(u_t) (times the W2T row scale for int8), 0 for dead
+// pairs and padded slots, the token mask and live flags when asked.
+constexpr int KLQ_NRU = 2;  // U pieces of 256 B loaded up front (r <= 512)
+template <int NC, int TT, int BITS>
+__global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_tb_q(
+    const uint16_t* __restrict__ x, const float* __restrict__ t_in, const int8_t* __restrict__ U,
+    const float* __restrict__ sU, const uint8_t* __restrict__ W3, const float* __restrict__ s3,
+    const float* __restrict__ s2, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, int D, int H, int r, int T, int tp, int act, unsigned flags) {
+    static_assert(BITS == 8 || BITS == 4, "int8 or int4 W3 rows");
+    constexpr int VPL = BITS == 8 ? 16 : 32;  // W3 columns per lane and chunk
+    constexpr int CW = WAVE * VPL;
+    extern __shared__ float ts[];  // [T][r]
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane & 15, grp = lane >> 4;
+    const int base = (blockIdx.x * K1_WAVES + wave) * KLQ_UPW;
+    const int unit = base + grp;
+    const bool in = unit < H;
+    const int nr = (r + 255) / 256;
+    u32x4 u[KLQ_NRU];
+#pragma unroll
+    for (int c = 0; c < KLQ_NRU; ++c) {
+        const int col = c * 256 + sub * 16;
+        u[c] = (in && col < r) ? load_stream(U + (size_t)unit * r + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    using XT = typename std::conditional<BITS == 8, X16, X32>::type;
+    XT xv[NC][TT];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * VPL;
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const uint16_t* xr = x + (size_t)(t < T ? t : 0) * D;
+            if constexpr (BITS == 8) xv[c][t] = load_x16(xr, t < T ? col : D, D);
+            else xv[c][t] = load_x32(xr, t < T ? col : D, D);
+        }
+    }
+    for (int j = threadIdx.x; j < T * r / 4; j += K1_THREADS)
+        reinterpret_cast<float4*>(ts)[j] = reinterpret_cast<const float4*>(t_in)[j];
+    __syncthreads();
+    const float su_ = in ? sU[unit] : 0.0f;
+    float sz[TT], ss[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) sz[t] = ss[t] = 0.0f;
+    auto piece = [&](const u32x4& uw, int col) {  // one U piece against every token's t
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            if (t >= T) continue;
+            float tv[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 a = *reinterpret_cast<const float4*>(ts + t * r + col + 4 * q);
+                tv[4 * q] = a.x; tv[4 * q + 1] = a.y; tv[4 * q + 2] = a.z; tv[4 * q + 3] = a.w;
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) ss[t] = fmaf(tv[k], tv[k], ss[t]);
+            sz[t] = dot16_i8(uw, tv, sz[t]);
+        }
+    };
+#pragma unroll
+    for (int c = 0; c < KLQ_NRU; ++c) {
+        const int col = c * 256 + sub * 16;
+        if (col < r) piece(u[c], col);
+    }
+    for (int c = KLQ_NRU; c < nr; ++c) {
+        const int col = c * 256 + sub * 16;
+        if (col < r) piece(in ? load_stream(U + (size_t)unit * r + col) : u32x4{0u, 0u, 0u, 0u}, col);
+    }
+    float z[TT];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+        float inv = 1.0f;  // RMSNorm of the token's t: every lane group sees all of it
+        if (flags & LOPA_RMSNORM) inv = 1.0f / sqrtf(group16_sum(ss[t]) / (float)r + RMS_EPS);
+        const float gx = ((flags & LOPA_G_TILED) && in && t < T)
+                             ? Elem<uint16_t>::get1(x[(size_t)t * D + unit % D]) : 0.0f;
+        z[t] = group16_sum(sz[t]) * su_ * inv + gx;
+    }
+    uint32_t mb = 0;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) mb |= (in && t < T && z[t] > 0.0f) ? (1u << t) : 0u;
+    if (in && sub == 0) {
+        umask[unit] = mb;
+        if (live_out) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t)
+                if (t < T) live_out[(size_t)t * H + unit] = (mb >> t) & 1u;
+        }
+        if (mb == 0) {
+#pragma unroll
+            for (int t = 0; t < TT; ++t) a_rm[(size_t)unit * tp + t] = 0.0f;
+        }
+    }
+    uint64_t m = __ballot(in && sub == 0 && mb != 0);
+    if (m == 0) return;  // wave-uniform
+    const int tl = bit_rev<TT>(lane & (TT - 1));
+    const int G = D / I4_GROUP;
+    const size_t rb = BITS == 8 ? (size_t)D : (size_t)D / 2;  // bytes per W3 row
+    auto load_row = [&](int ul, u32x4 (&w3)[NC], float (&sc)[NC]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * VPL;
+            const bool ok = col < D;
+            w3[c] = ok ? load_stream(W3 + (size_t)ul * rb + (BITS == 8 ? col : col / 2)) : u32x4{0u, 0u, 0u, 0u};
+            sc[c] = (BITS == 4 && ok) ? s3[(size_t)ul * G + col / I4_GROUP] : 0.0f;
+        }
+    };
+    int g = __builtin_ctzll(m) >> 4;
+    m &= m - 1;
+    u32x4 w3[NC];
+    float sc[NC];
+    load_row(base + g, w3, sc);
+    while (true) {
+        const bool more = m != 0;  // wave-uniform
+        const int gn = more ? (__builtin_ctzll(m) >> 4) : g;
+        u32x4 w3n[NC];
+        float scn[NC];
+        if (more) load_row(base + gn, w3n, scn);
+        const int ul = base + g;
+        float zt = 0.0f;  // z of unit ul for this lane's token tl
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+            const float zv = __shfl(z[t], 16 * g);
+            if (t == tl) zt = zv;
+        }
+        float v[TT];
+#pragma unroll
+        for (int t = 0; t < TT; ++t) v[t] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if constexpr (BITS == 8) dot16_i8x_tt<TT>(w3[c], xv[c], v);
+            else dot32_i4_tt<TT>(w3[c], xv[c], sc[c], v);
+        }
+        float uu = multi_reduce<TT>(v);
+        if (BITS == 8) uu *= s3[ul];
+        const float g3 = (flags & LOPA_DOUBLE_ACT) ? activation(act, uu) : uu;
+        const float post = BITS == 8 ? s2[ul] : 1.0f;
+        if (lane < TT) a_rm[(size_t)ul * tp + tl] = tl < T ? activation(act, zt) * g3 * post : 0.0f;
+        if (!more) break;
+        m &= m - 1;
+        g = gn;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) { w3[c] = w3n[c]; sc[c] = scn[c]; }
     }
 }
 

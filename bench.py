@@ -906,8 +906,37 @@ def main() -> int:
                 "speedup_vs_lopa_bf16": round(lq_tok_s / extras["lopa_tokens_per_s"], 3),
                 "speedup_vs_dense_bf16": round(lq_tok_s / extras["dense_tokens_per_s"], 3),
                 "kernel_us": ktl}
+            # batches of 4 tokens: token by token, and the union of the four live sets
+            hlq4 = sffn.Handle(D, Hp, r, 4, act, sffn.SFFN_I8 if bits == 8 else sffn.SFFN_I4)
+            bq4 = {}
+            for name, mode in (("per_token", sffn.SFFN_MODE_PER_TOKEN),
+                               ("union", sffn.SFFN_MODE_UNION)):
+                def fnq4():
+                    for c in range(n // 4):
+                        rp = replq[c % R]
+                        fwd(hlq4.ptr, xl[4 * c:4 * c + 4], rp["V"], rp["V_scale"], rp["U"],
+                            rp["U_scale"], rp["W3"], rp["W3_scale"], rp["W2T"], rp["W2T_scale"],
+                            y[4 * c:4 * c + 4], 4, mode)
+                gq4 = capture(fnq4)
+                msq4 = time_graph(gq4, args.steps, args.warmup)
+                del gq4
+                bq4[name + "_tokens_per_s"] = round(4 * (n // 4) / (msq4 * 1e-3), 1)
+                if mode == sffn.SFFN_MODE_UNION:
+                    sffn.sffn_timing_enable(hlq4.ptr, True)
+                    fnq4()
+                    torch.cuda.synchronize()
+                    sffn.sffn_timing_enable(hlq4.ptr, False)
+                    ktq4 = {}
+                    for kd in range(nk):
+                        ms_k, launches = sffn.sffn_timing_read(hlq4.ptr, kd, reset=(kd == nk - 1))
+                        if launches:
+                            ktq4[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
+                    bq4["union_kernel_us"] = ktq4
+            bq4["union_vs_per_token"] = round(bq4["union_tokens_per_s"] / bq4["per_token_tokens_per_s"], 3)
+            extras["lopa_int8" if bits == 8 else "lopa_int4_up_down"]["batch4"] = bq4
+            hlq4.close()
             log(f"lopa int{bits}: {ms_lq:.3f} ms/step, {lq_tok_s:,.0f} tokens/s, "
-                f"kernels (us/launch) {ktl}")
+                f"kernels (us/launch) {ktl}, batch of 4 {bq4}")
             hlq.close()
             del replq, WLQ
 
