@@ -1404,8 +1404,9 @@ sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const fl
     const int nc8 = (h->D + 1023) / 1024;
     const int nbr = (h->r + K1_WAVES - 1) / K1_WAVES;
 #define SFFN_RPTB(NCV, TTV)                                                                       \
-    st = launch(h, KIND_RANK_PROJ_TB_I8, k_rank_proj_tb_i8<NCV, TTV>, dim3(nbr), dim3(K1_THREADS),\
-                s, (const uint16_t*)x, (const int8_t*)V, sV, h->t_buf, yz, h->D, h->r, T)
+    st = launch_shm(h, KIND_RANK_PROJ_TB_I8, k_rank_proj_tb_i8<NCV, TTV>, dim3(nbr),              \
+                    dim3(K1_THREADS), (size_t)T * h->D * sizeof(uint16_t), s, (const uint16_t*)x,  \
+                    (const int8_t*)V, sV, h->t_buf, yz, h->D, h->r, T)
 #define SFFN_RPTB_NC(TTV)                                                                         \
     switch (nc8) {                                                                                \
         case 1: SFFN_RPTB(1, TTV); break;                                                         \
@@ -1422,7 +1423,8 @@ sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const fl
     const int nc = bits == 8 ? nc8 : (h->D + 2047) / 2048;
 #define SFFN_LQTB(NCV, TTV, BV)                                                                   \
     st = launch_shm(h, KIND_GATE_UP_LOPA_TB_Q, k_gate_up_lopa_tb_q<NCV, TTV, BV>, dim3(nb),       \
-                dim3(K1_THREADS), (size_t)T * h->r * sizeof(float), s, (const uint16_t*)x,         \
+                dim3(K1_THREADS), (size_t)T * (h->r * sizeof(float) + h->D * sizeof(uint16_t)), s, \
+                (const uint16_t*)x,                                                               \
                 (const float*)h->t_buf, (const int8_t*)U,                                         \
                 sU, (const uint8_t*)W3, s3, s2, h->m_a, h->m_mask, live, h->D, h->H, h->r, T, tp, \
                 h->act, h->flags)

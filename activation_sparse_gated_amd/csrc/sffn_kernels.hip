@@ -3223,8 +3223,10 @@ __device__ inline void dot32_i4_tt(const u32x4& w, const X32 (&xv)[TT], float sc
 }
 
 // Rank projection of the quantised LoPA batches: t[token][m] = sV_m (qV_m . x),
-// one int8 V row per wave, each weight decoded once for the TT tokens. Writes
-// t_out [T x r]; y_zero (nullable): T x D floats cleared for the down pass.
+// one int8 V row per wave, each weight decoded once for the TT tokens; the
+// block stages x of the batch in LDS (dynamic, T D bf16) once for its four
+// waves. Writes t_out [T x r]; y_zero (nullable): T x D floats cleared for the
+// down pass.
 template <int NC, int TT>
 __global__ __launch_bounds__(K1_THREADS) void k_rank_proj_tb_i8(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ V, const float* __restrict__ sV,
@@ -3234,15 +3236,23 @@ __global__ __launch_bounds__(K1_THREADS) void k_rank_proj_tb_i8(
     const int wave = threadIdx.x / WAVE;
     const int m = blockIdx.x * K1_WAVES + wave;
     const bool in = m < r;
+    extern __shared__ uint16_t xrk[];  // [T][D]
     u32x4 w[NC];
-    X16 xv[NC][TT];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int col = c * CW + lane * 16;
         w[c] = (in && col < D) ? load_stream(V + (size_t)m * D + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int j = threadIdx.x; j < T * D / 8; j += K1_THREADS)
+        reinterpret_cast<u32x4*>(xrk)[j] = load_cached(x + 8 * (size_t)j);
+    __syncthreads();
+    X16 xv[NC][TT];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 16;
 #pragma unroll
         for (int t = 0; t < TT; ++t)
-            xv[c][t] = load_x16(x + (size_t)(t < T ? t : 0) * D, t < T ? col : D, D);
+            xv[c][t] = load_x16(xrk + (t < T ? t : 0) * D, t < T ? col : D, D);
     }
     if (y_zero) {
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < T * D; j += gridDim.x * K1_THREADS)
@@ -3261,8 +3271,8 @@ __global__ __launch_bounds__(K1_THREADS) void k_rank_proj_tb_i8(
 // LoPA gate of the quantised batches and the up projection over the union:
 // four units per wave, 16 lanes per int8 U row (pieces of 256 B: the first
 // KLQ_NRU issued with the x loads at the start, any further ones in a loop);
-// the T rank vectors t (fp32) are staged in LDS by the block (dynamic LDS of
-// T r floats). z for each token against its t, through RMSNorm when asked, plus
+// the T rank vectors t (fp32) and x of the batch (bf16) are staged in LDS by
+// the block (dynamic LDS of T r floats, then T D bf16). z for each token against its t, through RMSNorm when asked, plus
 // (G x)_i when asked. Then each unit of the wave live for some token takes the
 // whole wave for its W3 row (int8 with a row scale, BITS = 8, or int4 with group
 // scales, BITS = 4), every weight decoded once for the TT tokens; the next live
@@ -3293,6 +3303,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_tb_q(
         const int col = c * 256 + sub * 16;
         u[c] = (in && col < r) ? load_stream(U + (size_t)unit * r + col) : u32x4{0u, 0u, 0u, 0u};
     }
+    uint16_t* xq = reinterpret_cast<uint16_t*>(ts + T * r);  // [T][D]
+    for (int j = threadIdx.x; j < T * r / 4; j += K1_THREADS)
+        reinterpret_cast<float4*>(ts)[j] = reinterpret_cast<const float4*>(t_in)[j];
+    for (int j = threadIdx.x; j < T * D / 8; j += K1_THREADS)
+        reinterpret_cast<u32x4*>(xq)[j] = load_cached(x + 8 * (size_t)j);
+    __syncthreads();
     using XT = typename std::conditional<BITS == 8, X16, X32>::type;
     XT xv[NC][TT];
 #pragma unroll
@@ -3300,19 +3316,22 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_tb_q(
         const int col = c * CW + lane * VPL;
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-            const uint16_t* xr = x + (size_t)(t < T ? t : 0) * D;
+            const uint16_t* xr = xq + (t < T ? t : 0) * D;
             if constexpr (BITS == 8) xv[c][t] = load_x16(xr, t < T ? col : D, D);
             else xv[c][t] = load_x32(xr, t < T ? col : D, D);
         }
     }
-    for (int j = threadIdx.x; j < T * r / 4; j += K1_THREADS)
-        reinterpret_cast<float4*>(ts)[j] = reinterpret_cast<const float4*>(t_in)[j];
-    __syncthreads();
     const float su_ = in ? sU[unit] : 0.0f;
     float sz[TT], ss[TT];
 #pragma unroll
     for (int t = 0; t < TT; ++t) sz[t] = ss[t] = 0.0f;
-    auto piece = [&](const u32x4& uw, int col) {  // one U piece against every token's t
+    const bool rms = (flags & LOPA_RMSNORM) != 0;
+    auto piece = [&](const u32x4& uw, int col) {  // one U piece, decoded once, against every token's t
+        float uf[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) uf[4 * q + b] = (float)((int)(uw[q] << (24 - 8 * b)) >> 24);
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
             if (t >= T) continue;
@@ -3322,9 +3341,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_tb_q(
                 const float4 a = *reinterpret_cast<const float4*>(ts + t * r + col + 4 * q);
                 tv[4 * q] = a.x; tv[4 * q + 1] = a.y; tv[4 * q + 2] = a.z; tv[4 * q + 3] = a.w;
             }
+            if (rms) {
 #pragma unroll
-            for (int k = 0; k < 16; ++k) ss[t] = fmaf(tv[k], tv[k], ss[t]);
-            sz[t] = dot16_i8(uw, tv, sz[t]);
+                for (int k = 0; k < 16; ++k) ss[t] = fmaf(tv[k], tv[k], ss[t]);
+            }
+#pragma unroll
+            for (int k = 0; k < 16; ++k) sz[t] = fmaf(uf[k], tv[k], sz[t]);
         }
     };
 #pragma unroll
@@ -3340,7 +3362,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_tb_q(
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
         float inv = 1.0f;  // RMSNorm of the token's t: every lane group sees all of it
-        if (flags & LOPA_RMSNORM) inv = 1.0f / sqrtf(group16_sum(ss[t]) / (float)r + RMS_EPS);
+        if (rms) inv = 1.0f / sqrtf(group16_sum(ss[t]) / (float)r + RMS_EPS);
         const float gx = ((flags & LOPA_G_TILED) && in && t < T)
                              ? Elem<uint16_t>::get1(x[(size_t)t * D + unit % D]) : 0.0f;
         z[t] = group16_sum(sz[t]) * su_ * inv + gx;
