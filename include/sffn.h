@@ -237,7 +237,8 @@ sffn_status sffn_forward_dense_i4(sffn_handle *h, const void *x, const void *W1,
  * stored row of each (V_scale [r], U_scale [H], W3_scale [H], W2T_scale [H],
  * 4-byte aligned): t = V x is exact in fp32 on the dequantised rows, the gate
  * options of the handle (G, RMSNorm, double activation) apply as for bf16.
- * Tokens of a batch are processed one after another. Errors as for the other
+ * Union calls with 2..4 tokens (D <= 4096) read the weights once for the
+ * batch; other batches run token by token. Errors as for the other
  * forward calls; a non-int8 or r == 0 handle gives SFFN_INVALID_ARGUMENT.
  */
 sffn_status sffn_forward_lopa_i8(sffn_handle *h, const void *x, const void *V,
@@ -252,7 +253,8 @@ sffn_status sffn_forward_lopa_i8(sffn_handle *h, const void *x, const void *V,
  * [H x r] with one fp32 scale per stored row (V_scale [r], U_scale [H]), and
  * W3, W2T packed int4 [H x D/2] bytes with W3_scale, W2T_scale fp32
  * [H x D/128] as for sffn_forward_sparse_i4. The gate options of the handle
- * apply as for bf16; tokens of a batch run one after another. Errors as for
+ * apply as for bf16; union calls with 2..4 tokens (D <= 4096) read the
+ * weights once for the batch, other batches run token by token. Errors as for
  * the other forward calls; a non-int4 or r == 0 handle gives
  * SFFN_INVALID_ARGUMENT.
  */
