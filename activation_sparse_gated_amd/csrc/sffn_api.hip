@@ -1332,13 +1332,26 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     if (!s1 || !s3 || !s2) return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // union (and dense) batches of 2..4 tokens read the weights once for the batch
-    if (T >= 2 && T <= 4 && h->m_a && (dense || mode == SFFN_MODE_UNION)) {
-        if (bits == 4)
-            return dense ? run_i4_tb<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
-                         : run_i4_tb<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
-        return dense ? run_i8_tb<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
-                     : run_i8_tb<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
+    // union (and dense) batches of 2..4 tokens read the weights once for the batch;
+    // larger ones go as groups of 2..4 consecutive tokens (sizes as equal as can be)
+    if (T >= 2 && h->m_a && (dense || mode == SFFN_MODE_UNION)) {
+        const int ng = (T + 3) / 4;
+        for (int g = 0, t0 = 0; g < ng; ++g) {
+            const int tg = T / ng + (g < T % ng ? 1 : 0);
+            const void* xg = (const char*)x + (size_t)t0 * h->D * sizeof(uint16_t);
+            float* yg = y + (size_t)t0 * h->D;
+            int32_t* lc = live_count ? live_count + t0 : nullptr;
+            int32_t* li = live_idx ? live_idx + (size_t)t0 * h->H : nullptr;
+            if (bits == 4)
+                st = dense ? run_i4_tb<true>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, nullptr, nullptr, s)
+                           : run_i4_tb<false>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, lc, li, s);
+            else
+                st = dense ? run_i8_tb<true>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, nullptr, nullptr, s)
+                           : run_i8_tb<false>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, lc, li, s);
+            if (st != SFFN_OK) return st;
+            t0 += tg;
+        }
+        return SFFN_OK;
     }
     // other batches run token by token (both modes compute the same result)
     for (int t = 0; t < T; ++t) {
@@ -1491,10 +1504,21 @@ static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, 
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(sV) || !al4(sU) || !al4(s3) || !al4(s2))
         return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // union batches of 2..4 tokens read the weights once for the batch
-    if (mode == SFFN_MODE_UNION && lopa_q_tb_ok(h, T, bits))
-        return run_lopa_q_tb(h, x, V, sV, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx, s,
-                             bits);
+    // union batches of 2..4 tokens read the weights once for the batch; larger ones
+    // go as groups of 2..4 consecutive tokens (sizes as equal as can be)
+    if (mode == SFFN_MODE_UNION && T >= 2 && lopa_q_tb_ok(h, 2, bits)) {
+        const int ng = (T + 3) / 4;
+        for (int g = 0, t0 = 0; g < ng; ++g) {
+            const int tg = T / ng + (g < T % ng ? 1 : 0);
+            st = run_lopa_q_tb(h, (const char*)x + (size_t)t0 * h->D * sizeof(uint16_t), V, sV, U,
+                               sU, W3, s3, W2T, s2, y + (size_t)t0 * h->D, tg,
+                               live_count ? live_count + t0 : nullptr,
+                               live_idx ? live_idx + (size_t)t0 * h->H : nullptr, s, bits);
+            if (st != SFFN_OK) return st;
+            t0 += tg;
+        }
+        return SFFN_OK;
+    }
     // other batches run token by token (both modes compute the same result)
     for (int t = 0; t < T; ++t) {
         const void* xt = (const char*)x + (size_t)t * h->D * sizeof(uint16_t);

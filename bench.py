@@ -774,6 +774,20 @@ def main() -> int:
         b4["union_vs_dense"] = round(b4["union_tokens_per_s"] / b4["dense_tokens_per_s"], 3)
         res_q["batch4"] = b4
         hq4.close()
+        # union batches of 16 tokens (four groups of 4 through the same kernels)
+        hq16 = sffn.Handle(D, H, 0, 16, act, sffn.SFFN_I8)
+
+        def fn16():
+            for c in range(n // 16):
+                rp = repq[c % R]
+                sffn.sffn_forward_sparse_i8(hq16.ptr, x[16 * c:16 * c + 16], rp["W1"], rp["W1_scale"],
+                                            rp["W3"], rp["W3_scale"], rp["W2T"], rp["W2T_scale"],
+                                            y[16 * c:16 * c + 16], 16, sffn.SFFN_MODE_UNION)
+        g16 = capture(fn16)
+        ms16 = time_graph(g16, args.steps, args.warmup)
+        del g16
+        res_q["batch16_union_tokens_per_s"] = round(16 * (n // 16) / (ms16 * 1e-3), 1)
+        hq16.close()
         extras["int8"] = res_q
         log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items() if not isinstance(v, dict))
             + f", kernels (us/launch) {ktq}, batch of 4 {b4}")
