@@ -2555,6 +2555,50 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
     }
 }
 
+// Epilogue of the small-batch down passes: each lane's TT x VEC column sums are
+// reduced over the wave's lane groups (shuffles), the wave sums of up to TR
+// tokens at a time are staged in LDS (red[TR][KD_WAVES][CB]), and after one
+// barrier per round the block adds the sums over its waves into y (fp32 atomics
+// when the unit range is split, else a plain store).
+template <int TT, int TR, int VEC, int LPR, int CB>
+__device__ inline void tb_down_epilogue(float (&acc)[TT][VEC], float (*red)[KD_WAVES][CB],
+                                        float* __restrict__ y, int D, int T, int col0,
+                                        int splits, int wave, int sub, int grp) {
+#pragma unroll
+    for (int t0 = 0; t0 < TT; t0 += TR) {
+        if (t0 >= T) break;  // uniform
+        if (t0 > 0) __syncthreads();  // the previous round has read red
+#pragma unroll
+        for (int j = 0; j < TR; ++j) {
+            const int t = t0 + j;
+            if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
+#pragma unroll
+            for (int k = 0; k < VEC; ++k) {
+                float v = acc[t][k];
+                for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+                acc[t][k] = v;
+            }
+            if (grp == 0) {
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) red[j][wave][sub * VEC + k] = acc[t][k];
+            }
+        }
+        __syncthreads();
+        const int nt = min(TR, T - t0);
+        for (int i = threadIdx.x; i < nt * CB; i += KD_THREADS) {
+            const int j = i / CB, c = i % CB;
+            float s = 0.0f;
+            for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[j][w2][c];
+            if (col0 + c < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)(t0 + j) * D + col0 + c, s);
+                else
+                    y[(size_t)(t0 + j) * D + col0 + c] = s;
+            }
+        }
+    }
+}
+
 // Down projection for small batches (T <= TT <= 8), bf16: like k_down_t1, but
 // the units kept are those live for some token (umask != 0; DENSE: all), each
 // lane keeps TT x 8 accumulators, and a unit's TT products come from the
@@ -2572,7 +2616,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
     __shared__ int list[KD_LCAP];
     __shared__ int wcount[PMAX * KD_WAVES];
     __shared__ int woff[PMAX * KD_WAVES + 1];
-    __shared__ float red[KD_WAVES][CB];
+    __shared__ float red[TT < 4 ? TT : 4][KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
     const int per_xcd = (nslices + 7) / 8;
@@ -2655,32 +2699,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
         __syncthreads();
         p0 = p1;
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            float v = acc[t][k];
-            for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-            acc[t][k] = v;
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[t][k];
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
-            float s2 = 0.0f;
-            for (int w2 = 0; w2 < KD_WAVES; ++w2) s2 += red[w2][c];
-            if (col0 + c < D) {
-                if (splits > 1)
-                    atomicAdd(y + (size_t)t * D + col0 + c, s2);
-                else
-                    y[(size_t)t * D + col0 + c] = s2;
-            }
-        }
-        __syncthreads();
-    }
+    tb_down_epilogue<TT, (TT < 4 ? TT : 4), VEC, LPR, CB>(acc, red, y, D, T, col0, splits, wave, sub, grp);
 }
 
 // Small batches (T <= TT <= 4) with weight-only int8 weights, union of the
@@ -2819,7 +2838,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
     __shared__ int list[KD_LCAP];
     __shared__ int wcount[PMAX * KD_WAVES];
     __shared__ int woff[PMAX * KD_WAVES + 1];
-    __shared__ float red[KD_WAVES][CB];
+    __shared__ float red[TT < 4 ? TT : 4][KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
     const int per_xcd = (nslices + 7) / 8;
@@ -2906,32 +2925,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
         __syncthreads();
         p0 = p1;
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            float v = acc[t][k];
-            for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-            acc[t][k] = v;
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[t][k];
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
-            float s = 0.0f;
-            for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
-            if (col0 + c < D) {
-                if (splits > 1)
-                    atomicAdd(y + (size_t)t * D + col0 + c, s);
-                else
-                    y[(size_t)t * D + col0 + c] = s;
-            }
-        }
-        __syncthreads();
-    }
+    tb_down_epilogue<TT, (TT < 4 ? TT : 4), VEC, LPR, CB>(acc, red, y, D, T, col0, splits, wave, sub, grp);
 }
 
 // Small batches (T <= TT <= 4) with group-scaled int4 weights, union of the
@@ -3047,7 +3041,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
     __shared__ int list[KD_LCAP];
     __shared__ int wcount[PMAX * KD_WAVES];
     __shared__ int woff[PMAX * KD_WAVES + 1];
-    __shared__ float red[KD_WAVES][CB];
+    __shared__ float red[TT < 4 ? TT : 4][KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
     const int per_xcd = (nslices + 7) / 8;
@@ -3138,32 +3132,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
         __syncthreads();
         p0 = p1;
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-        if (t >= T) continue;  // uniform; the loop stays unrolled so acc stays in registers
-#pragma unroll
-        for (int k = 0; k < VEC; ++k) {
-            float v = acc[t][k];
-            for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
-            acc[t][k] = v;
-        }
-        if (grp == 0) {
-#pragma unroll
-            for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[t][k];
-        }
-        __syncthreads();
-        for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
-            float s = 0.0f;
-            for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
-            if (col0 + c < D) {
-                if (splits > 1)
-                    atomicAdd(y + (size_t)t * D + col0 + c, s);
-                else
-                    y[(size_t)t * D + col0 + c] = s;
-            }
-        }
-        __syncthreads();
-    }
+    tb_down_epilogue<TT, (TT < 4 ? TT : 4), VEC, LPR, CB>(acc, red, y, D, T, col0, splits, wave, sub, grp);
 }
 
 // Quantised LoPA, union of 2..4 tokens. Helpers: one decode of a weight piece
