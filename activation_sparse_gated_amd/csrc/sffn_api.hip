@@ -1400,7 +1400,9 @@ sffn_status sffn_forward_dense_i4(sffn_handle* h, const void* x, const void* W1,
 // of the small batches. Widths up to 4 chunks of W3 (else false: token by token).
 bool lopa_q_tb_ok(const sffn_handle* h, int T, int bits) {
     const int nc = bits == 8 ? (h->D + 1023) / 1024 : (h->D + 2047) / 2048;
-    return T >= 2 && T <= 4 && h->m_a && nc <= 4 && (h->D + 1023) / 1024 <= 4;
+    // the gate's dynamic LDS for a group of 4: t (4 r fp32) and x (4 D bf16), <= 64 KiB
+    const bool lds_ok = 4 * ((size_t)h->r * sizeof(float) + (size_t)h->D * sizeof(uint16_t)) <= 65536;
+    return T >= 2 && T <= 4 && h->m_a && nc <= 4 && (h->D + 1023) / 1024 <= 4 && lds_ok;
 }
 
 sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const float* sV,
