@@ -91,6 +91,7 @@ struct sffn_handle {
     uint16_t* moe_x = nullptr;     // [2 * max_tokens x D] bf16
     float* moe_y = nullptr;        // [2 * max_tokens x D] fp32
     int tb_splits = 16;            // row splits of the small-batch down pass
+    int tb_rw_i8 = 2;              // units per wave of the int8 small-batch gate (1, 2, 4)
     int tb_max = 4;                // batches up to this size use the small-batch down pass
     int tbv_max = 4;               // batches up to this size use the VALU gate/up pass
     int tbv_rw2 = 2, tbv_rw4 = 4;  // units per wave of the VALU gate/up pass (2 and 4 token slots)
@@ -694,7 +695,8 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
                       const void* W3, const float* s3, const void* W2T, const float* s2,
                       float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
     const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
-    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    const int rw = DENSE ? 1 : h->tb_rw_i8;  // the dense comparator measured best at 1
+    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
     const int tp = 16 * token_tiles(T);
     const int tt = T <= 2 ? 2 : 4;
     int splits = h->tb_splits;
@@ -702,12 +704,17 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
     uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
     float* yz = splits > 1 ? y : nullptr;
     sffn_status st = SFFN_OK;
-#define SFFN_TBQ_GATE(TTV)                                                                        \
-    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_TB_I8, k_gate_up_tb_i8<NC, TTV, DENSE>,       \
+#define SFFN_TBQ_GATE(TTV, RWV)                                                                   \
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_TB_I8, k_gate_up_tb_i8<NC, TTV, DENSE, RWV>,  \
                                      dim3(nb), dim3(K1_THREADS), s, (const uint16_t*)x,           \
                                      (const int8_t*)W1, s1, (const int8_t*)W3, s3, s2, h->m_a,     \
                                      h->m_mask, live, yz, h->D, h->H, T, tp, h->act))
-    if (tt == 2) { SFFN_TBQ_GATE(2); } else { SFFN_TBQ_GATE(4); }
+#define SFFN_TBQ_RW(TTV)                                                                          \
+    if (rw == 4) { SFFN_TBQ_GATE(TTV, 4); }                                                       \
+    else if (rw == 2) { SFFN_TBQ_GATE(TTV, 2); }                                                  \
+    else { SFFN_TBQ_GATE(TTV, 1); }
+    if (tt == 2) { SFFN_TBQ_RW(2); } else { SFFN_TBQ_RW(4); }
+#undef SFFN_TBQ_RW
 #undef SFFN_TBQ_GATE
     if (st != SFFN_OK) return st;
     const int cb = 16 * 16;
@@ -1126,6 +1133,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             h->m_splits = sp;
             const int tbs = env_int("SFFN_TB_SPLITS", 16);
             if (tbs >= 1 && tbs <= 64) h->tb_splits = tbs;
+            const int trw = env_int("SFFN_TB_RW_I8", h->tb_rw_i8);
+            if (trw == 1 || trw == 2 || trw == 4) h->tb_rw_i8 = trw;
             h->tbv_max = env_int("SFFN_TBV_MAX", h->tbv_max);
             auto rw_env = [](const char* name, int dflt) {
                 const int v = env_int(name, dflt);

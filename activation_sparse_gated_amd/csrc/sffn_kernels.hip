@@ -2703,14 +2703,16 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
 }
 
 // Small batches (T <= TT <= 4) with weight-only int8 weights, union of the
-// tokens' live sets. Gate/up: one unit per wave; every int8 weight of the W1
-// row (and of the W3 row when the unit is live for some token) is converted
-// once and multiplied with the TT tokens' x (bf16, unpacked per use); the TT
+// tokens' live sets. Gate/up: RW consecutive units per wave, their W1 rows
+// issued first, x of the tokens and its sums taken once for all of them; every
+// int8 weight of a W1 row (and of the W3 row when the unit is live for some
+// token) is converted once and multiplied with the TT tokens' x (bf16, unpacked
+// per use); the TT
 // per-lane sums are reduced together (multi_reduce: lane l ends with token
 // bitrev(l mod TT)). Writes a'[unit][tp] = A(z) u s2 (the W2T row scale folded
 // in; 0 for dead pairs and padded slots), the token mask umask[unit] (DENSE:
 // all tokens), live flags [T x H] when asked, and clears y for the down pass.
-template <int NC, int TT, bool DENSE>
+template <int NC, int TT, bool DENSE, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ W1, const float* __restrict__ s1,
     const int8_t* __restrict__ W3, const float* __restrict__ s3, const float* __restrict__ s2,
@@ -2719,14 +2721,16 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
     constexpr int CW = WAVE * 16;  // columns of one chunk: 16 int8 per lane
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int unit = blockIdx.x * K1_WAVES + wave;
-    const bool in = unit < H;
-    u32x4 w[NC];
+    const int unit0 = (blockIdx.x * K1_WAVES + wave) * RW;  // RW consecutive units per wave
+    u32x4 wr[RW][NC];  // every W1 row of the wave, issued first
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 16;
-        w[c] = (in && col < D) ? load_stream(W1 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int q = 0; q < RW; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 16;
+            wr[q][c] = (unit0 + q < H && col < D) ? load_stream(W1 + (size_t)(unit0 + q) * D + col)
+                                                  : u32x4{0u, 0u, 0u, 0u};
+        }
     u32x4 xb[TT][NC][2];  // the lane's 16 columns of each token: two pieces of 8 bf16
 #pragma unroll
     for (int t = 0; t < TT; ++t)
@@ -2741,9 +2745,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < T * D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
     }
-    const float sc1 = in ? s1[unit] : 0.0f;
-    const float sc3 = in ? s3[unit] : 0.0f;
-    const float sc2 = in ? s2[unit] : 0.0f;
     // sum of each token's 16 x values of the lane per chunk (for the code offset)
     float xs[TT][NC];
 #pragma unroll
@@ -2795,29 +2796,35 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i8(
         }
     };
     const int tl = bit_rev<TT>(lane & (TT - 1));  // token whose sums this lane ends with
-    float v[TT];
-    dot_tokens(w, v);
-    const float z = multi_reduce<TT>(v) * sc1;
-    const bool lv = in && tl < T && z > 0.0f;
-    const uint64_t bl = __ballot(lv && lane < TT);
-    uint64_t m = 0;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) m |= ((bl >> bit_rev<TT>(t)) & 1ull) << t;
-    if (!in) return;  // wave-uniform: one unit per wave
-    if (lane == 0) umask[unit] = DENSE ? ((1ull << T) - 1) : m;
-    if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
-    if (!DENSE && m == 0) {
-        if (lane < TT) a_rm[(size_t)unit * tp + tl] = 0.0f;
-        return;
-    }
+    for (int q = 0; q < RW; ++q) {
+        const int unit = unit0 + q;
+        if (unit >= H) break;  // wave-uniform
+        const float sc1 = s1[unit];
+        float v[TT];
+        dot_tokens(wr[q], v);
+        const float z = multi_reduce<TT>(v) * sc1;
+        const bool lv = tl < T && z > 0.0f;
+        const uint64_t bl = __ballot(lv && lane < TT);
+        uint64_t m = 0;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 16;
-        w[c] = col < D ? load_stream(W3 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+        for (int t = 0; t < TT; ++t) m |= ((bl >> bit_rev<TT>(t)) & 1ull) << t;
+        if (lane == 0) umask[unit] = DENSE ? ((1ull << T) - 1) : m;
+        if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
+        if (!DENSE && m == 0) {
+            if (lane < TT) a_rm[(size_t)unit * tp + tl] = 0.0f;
+            continue;
+        }
+        u32x4 w[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 16;
+            w[c] = col < D ? load_stream(W3 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
+        }
+        dot_tokens(w, v);
+        const float u = multi_reduce<TT>(v) * s3[unit];
+        if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u * s2[unit] : 0.0f;
     }
-    dot_tokens(w, v);
-    const float u = multi_reduce<TT>(v) * sc3;
-    if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u * sc2 : 0.0f;
 }
 
 // Down pass of the int8 small batches: as k_down_t1_i8 (16 lanes x 16 int8
