@@ -92,6 +92,7 @@ struct sffn_handle {
     float* moe_y = nullptr;        // [2 * max_tokens x D] fp32
     int tb_splits = 16;            // row splits of the small-batch down pass
     int tb_rw_i8 = 2;              // units per wave of the int8 small-batch gate (1, 2, 4)
+    int t1_lopa_i8_upw = 2;        // units per wave of the int8 LoPA batch-1 gate (2 or 4)
     int tb_max = 4;                // batches up to this size use the small-batch down pass
     int tbv_max = 4;               // batches up to this size use the VALU gate/up pass
     int tbv_rw2 = 2, tbv_rw4 = 4;  // units per wave of the VALU gate/up pass (2 and 4 token slots)
@@ -895,24 +896,33 @@ sffn_status run_lopa_i8_t1(sffn_handle* h, const void* x, const void* V, const f
                                      dim3(K1_THREADS), s, (const uint16_t*)x, (const int8_t*)V,
                                      sV, h->t_buf, yz, h->D, h->r));
     if (st != SFFN_OK) return st;
-    const int nb = (h->H + K1_WAVES * KLQ_UPW - 1) / (K1_WAVES * KLQ_UPW);
-    const int nr = (h->r + 255) / 256;
-#define SFFN_LOPA_I8(NRV)                                                                          \
-    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_LOPA_T1_I8, k_gate_up_lopa_t1_i8<NC, NRV>,   \
+    const int upw = (h->t1_lopa_i8_upw == 2 && h->r <= 1024) ? 2 : 4;
+    const int nb = (h->H + K1_WAVES * upw - 1) / (K1_WAVES * upw);
+    const int nr = (h->r + 16 * (64 / upw) - 1) / (16 * (64 / upw));
+#define SFFN_LOPA_I8(NRV, UPWV)                                                                    \
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_LOPA_T1_I8, k_gate_up_lopa_t1_i8<NC, NRV, UPWV>,\
                                      dim3(nb), dim3(K1_THREADS), s, (const uint16_t*)x,           \
                                      (const float*)h->t_buf, (const int8_t*)U, sU,                 \
                                      (const int8_t*)W3, s3, s2, h->a_buf, live, h->D, h->H, h->r,  \
                                      h->act, h->flags))
-    switch (nr) {
-        case 1: SFFN_LOPA_I8(1); break;
-        case 2: SFFN_LOPA_I8(2); break;
-        case 3: SFFN_LOPA_I8(3); break;
-        case 4: SFFN_LOPA_I8(4); break;
-        case 5: SFFN_LOPA_I8(5); break;
-        case 6: SFFN_LOPA_I8(6); break;
-        case 7: SFFN_LOPA_I8(7); break;
-        case 8: SFFN_LOPA_I8(8); break;
-        default: return fail(h, SFFN_INTERNAL, "rank too large for the int8 LoPA gate");
+    if (upw == 2) {
+        switch (nr) {
+            case 1: SFFN_LOPA_I8(1, 2); break;
+            case 2: SFFN_LOPA_I8(2, 2); break;
+            default: return fail(h, SFFN_INTERNAL, "rank too large for the int8 LoPA gate");
+        }
+    } else {
+        switch (nr) {
+            case 1: SFFN_LOPA_I8(1, 4); break;
+            case 2: SFFN_LOPA_I8(2, 4); break;
+            case 3: SFFN_LOPA_I8(3, 4); break;
+            case 4: SFFN_LOPA_I8(4, 4); break;
+            case 5: SFFN_LOPA_I8(5, 4); break;
+            case 6: SFFN_LOPA_I8(6, 4); break;
+            case 7: SFFN_LOPA_I8(7, 4); break;
+            case 8: SFFN_LOPA_I8(8, 4); break;
+            default: return fail(h, SFFN_INTERNAL, "rank too large for the int8 LoPA gate");
+        }
     }
 #undef SFFN_LOPA_I8
     if (st != SFFN_OK) return st;
@@ -1081,6 +1091,8 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if (e_rwl == 1 || e_rwl == 2 || e_rwl == 4) h->t1_rw_lopa = e_rwl;
         const int e_lpr = env_int("SFFN_T1_LANES_PER_ROW", 0);
         if (e_lpr == 4 || e_lpr == 8 || e_lpr == 16 || e_lpr == 32) h->t1_lpr = e_lpr;
+        const int e_lupw = env_int("SFFN_T1_LOPA_I8_UPW", h->t1_lopa_i8_upw);
+        if (e_lupw == 2 || e_lupw == 4) h->t1_lopa_i8_upw = e_lupw;
         const int e_ss = env_int("SFFN_T1_SPLITS_SPARSE", 0);
         if (e_ss >= 1 && e_ss <= 64) h->t1_splits_sparse = e_ss;
         const int e_sd = env_int("SFFN_T1_SPLITS_DENSE", 0);

@@ -1316,36 +1316,47 @@ __device__ inline float group16_sum(float v) {
     return v;
 }
 
-// LoPA gate and gathered up projection, int8 U and W3 rows. Gate: four units
-// per wave, 16 lanes per unit (a U row of r int8 is NR pieces of 256 B):
+// LoPA gate and gathered up projection, int8 U and W3 rows. Gate: UPW units
+// per wave, 64 / UPW lanes per unit (a U row of r int8 is NR pieces of 16
+// bytes per lane of the group):
 // z_i = sU_i (qU_i . t) (t through RMSNorm when asked) + (G x)_i when asked.
 // Up projection: the wave's live units one after another, 64 lanes each:
 // u_i = s3_i (q3_i . x), through A as well under double activation. The stored
 // product is pre-multiplied by the W2T row scale s2_i.
+// Sum over the N lanes of a lane group (lanes N g .. N g + N - 1), N a power of two.
+template <int N>
+__device__ inline float group_sum(float v) {
+#pragma unroll
+    for (int o = N / 2; o >= 1; o /= 2) v += __shfl_xor(v, o, N);
+    return v;
+}
+
 constexpr int KLQ_UPW = 4;  // units per wave in the gate phase
-template <int NC, int NR>
+template <int NC, int NR, int UPW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
     const uint16_t* __restrict__ x, const float* __restrict__ t_in,
     const int8_t* __restrict__ U, const float* __restrict__ sU, const int8_t* __restrict__ W3,
     const float* __restrict__ s3, const float* __restrict__ s2, float* __restrict__ a_out,
     uint8_t* __restrict__ live_out, int D, int H, int r, int act, unsigned flags) {
     constexpr int CW = WAVE * 16;  // columns of one full-wave chunk of an int8 row
+    constexpr int LPU = WAVE / UPW;  // lanes per unit in the gate phase
+    constexpr int PB = LPU * 16;     // bytes of U row per piece
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int sub = lane & 15, grp = lane >> 4;
-    const int base = (blockIdx.x * K1_WAVES + wave) * KLQ_UPW;
+    const int sub = lane % LPU, grp = lane / LPU;
+    const int base = (blockIdx.x * K1_WAVES + wave) * UPW;
     const int unit = base + grp;
     const bool in = unit < H;
     u32x4 u[NR];
 #pragma unroll
     for (int c = 0; c < NR; ++c) {
-        const int col = c * 256 + sub * 16;
+        const int col = c * PB + sub * 16;
         u[c] = (in && col < r) ? load_stream(U + (size_t)unit * r + col) : u32x4{0u, 0u, 0u, 0u};
     }
     float tv[NR][16];
 #pragma unroll
     for (int c = 0; c < NR; ++c) {
-        const int col = c * 256 + sub * 16;
+        const int col = c * PB + sub * 16;
         if (col < r) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -1369,12 +1380,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
         for (int c = 0; c < NR; ++c)
 #pragma unroll
             for (int k = 0; k < 16; ++k) ss = fmaf(tv[c][k], tv[c][k], ss);
-        inv = 1.0f / sqrtf(group16_sum(ss) / (float)r + RMS_EPS);
+        inv = 1.0f / sqrtf(group_sum<LPU>(ss) / (float)r + RMS_EPS);
     }
     float sz = 0.0f;
 #pragma unroll
     for (int c = 0; c < NR; ++c) sz = dot16_i8(u[c], tv[c], sz);
-    const float z = group16_sum(sz) * su_ * inv + gx;
+    const float z = group_sum<LPU>(sz) * su_ * inv + gx;
     const bool live = in && z > 0.0f;
     if (in && sub == 0) {
         if (live_out) live_out[unit] = live ? 1 : 0;
@@ -1382,10 +1393,10 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
     }
     uint64_t m = __ballot(live && sub == 0);
     while (m) {
-        const int g = __builtin_ctzll(m) >> 4;
+        const int g = __builtin_ctzll(m) / LPU;
         m &= m - 1;
         const int ul = base + g;
-        const float zl = __shfl(z, 16 * g);
+        const float zl = __shfl(z, LPU * g);
         u32x4 w3[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) {

@@ -139,7 +139,9 @@ sffn_status sffn_create(sffn_handle **out, int D, int H, int r, int max_tokens, 
  * result changes only by rounding (summation order, and where a path rounds
  * the unit products for its MFMA operands, as described under Requirements).
  *   batch 1:  SFFN_T1_ROWS_PER_WAVE [1] and SFFN_T1_LOPA_ROWS_PER_WAVE [2]
- *             (units per wave of the gate pass: 1, 2, 4), SFFN_T1_LANES_PER_ROW
+ *             (units per wave of the gate pass: 1, 2, 4), SFFN_T1_LOPA_I8_UPW [2]
+ *             (units per wave of the int8 LoPA gate: 2 for r <= 1024, or 4),
+ *             SFFN_T1_LANES_PER_ROW
  *             [32] (lanes per W2T row slice of the down pass: 4, 8, 16, 32),
  *             SFFN_T1_SPLITS_SPARSE [16] and SFFN_T1_SPLITS_DENSE [16] (unit
  *             ranges of the down pass), SFFN_T1_FUSED_SPARSE [0] and
