@@ -741,7 +741,8 @@ sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float
                       const void* W3, const float* s3, const void* W2T, const float* s2,
                       float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
     const int nc = (h->D + 2047) / 2048;
-    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    const int rw = (!DENSE && h->tb_rw_i8 == 2) ? 2 : 1;  // union calls as for int8 (1 or 2)
+    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
     const int tp = 16 * token_tiles(T);
     const int tt = T <= 2 ? 2 : 4;
     int splits = h->tb_splits;
@@ -750,9 +751,14 @@ sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float
     float* yz = splits > 1 ? y : nullptr;
     sffn_status st = SFFN_OK;
 #define SFFN_TB4_GATE(NCV, TTV)                                                                   \
-    st = launch(h, KIND_GATE_UP_TB_I4, k_gate_up_tb_i4<NCV, TTV, DENSE>, dim3(nb),               \
-                dim3(K1_THREADS), s, (const uint16_t*)x, (const uint8_t*)W1, s1,                 \
-                (const uint8_t*)W3, s3, h->m_a, h->m_mask, live, yz, h->D, h->H, T, tp, h->act)
+    if (rw == 2)                                                                                  \
+        st = launch(h, KIND_GATE_UP_TB_I4, k_gate_up_tb_i4<NCV, TTV, DENSE, 2>, dim3(nb),         \
+                    dim3(K1_THREADS), s, (const uint16_t*)x, (const uint8_t*)W1, s1,             \
+                    (const uint8_t*)W3, s3, h->m_a, h->m_mask, live, yz, h->D, h->H, T, tp, h->act);\
+    else                                                                                          \
+        st = launch(h, KIND_GATE_UP_TB_I4, k_gate_up_tb_i4<NCV, TTV, DENSE, 1>, dim3(nb),         \
+                    dim3(K1_THREADS), s, (const uint16_t*)x, (const uint8_t*)W1, s1,             \
+                    (const uint8_t*)W3, s3, h->m_a, h->m_mask, live, yz, h->D, h->H, T, tp, h->act)
 #define SFFN_TB4_NC(TTV)                                                                          \
     switch (nc) {                                                                                 \
         case 1: SFFN_TB4_GATE(1, TTV); break;                                                     \

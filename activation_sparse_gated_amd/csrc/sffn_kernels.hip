@@ -2947,12 +2947,12 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
 }
 
 // Small batches (T <= TT <= 4) with group-scaled int4 weights, union of the
-// tokens' live sets: as k_gate_up_tb_i8, with each pair of codes turned into a
+// tokens' live sets: as k_gate_up_tb_i8 (RW units per wave), with each pair of codes turned into a
 // bf16 pair once (the byte permute of dot32_i4) and met with every token's x
 // pair by a bf16 dot2; 136 * sum(x) per token and 32 codes is taken off before
 // the group scale. Stores a[unit][tp] = A(z) u (the down pass applies the W2T
 // group scales).
-template <int NC, int TT, bool DENSE>
+template <int NC, int TT, bool DENSE, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i4(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ W1, const float* __restrict__ s1,
     const uint8_t* __restrict__ W3, const float* __restrict__ s3, float* __restrict__ a_rm,
@@ -2961,19 +2961,20 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i4(
     constexpr int CW = WAVE * 32;  // columns of one chunk: 32 codes per lane
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int unit = blockIdx.x * K1_WAVES + wave;
-    const bool in = unit < H;
+    const int unit0 = (blockIdx.x * K1_WAVES + wave) * RW;  // RW consecutive units per wave
     const int G = D / I4_GROUP;
     const size_t rb = (size_t)D / 2;
-    u32x4 w[NC];
-    float sc[NC];
+    u32x4 wr[RW][NC];  // every W1 row of the wave, issued first
+    float scr[RW][NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 32;
-        const bool ok = in && col < D;
-        w[c] = ok ? load_stream(W1 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
-        sc[c] = ok ? s1[(size_t)unit * G + col / I4_GROUP] : 0.0f;
-    }
+    for (int q = 0; q < RW; ++q)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 32;
+            const bool ok = unit0 + q < H && col < D;
+            wr[q][c] = ok ? load_stream(W1 + (size_t)(unit0 + q) * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+            scr[q][c] = ok ? s1[(size_t)(unit0 + q) * G + col / I4_GROUP] : 0.0f;
+        }
     X32 xv[TT][NC];
 #pragma unroll
     for (int t = 0; t < TT; ++t)
@@ -3014,31 +3015,37 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_tb_i4(
         }
     };
     const int tl = bit_rev<TT>(lane & (TT - 1));  // token whose sums this lane ends with
-    float v[TT];
-    dot_tokens(w, sc, v);
-    const float z = multi_reduce<TT>(v);
-    const bool lv = in && tl < T && z > 0.0f;
-    const uint64_t bl = __ballot(lv && lane < TT);
-    uint64_t m = 0;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) m |= ((bl >> bit_rev<TT>(t)) & 1ull) << t;
-    if (!in) return;  // wave-uniform: one unit per wave
-    if (lane == 0) umask[unit] = DENSE ? ((1ull << T) - 1) : m;
-    if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
-    if (!DENSE && m == 0) {
-        if (lane < TT) a_rm[(size_t)unit * tp + tl] = 0.0f;
-        return;
-    }
+    for (int q = 0; q < RW; ++q) {
+        const int unit = unit0 + q;
+        if (unit >= H) break;  // wave-uniform
+        float v[TT];
+        dot_tokens(wr[q], scr[q], v);
+        const float z = multi_reduce<TT>(v);
+        const bool lv = tl < T && z > 0.0f;
+        const uint64_t bl = __ballot(lv && lane < TT);
+        uint64_t m = 0;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 32;
-        const bool ok = col < D;
-        w[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
-        sc[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+        for (int t = 0; t < TT; ++t) m |= ((bl >> bit_rev<TT>(t)) & 1ull) << t;
+        if (lane == 0) umask[unit] = DENSE ? ((1ull << T) - 1) : m;
+        if (live_out && lane < TT && tl < T) live_out[(size_t)tl * H + unit] = lv ? 1 : 0;
+        if (!DENSE && m == 0) {
+            if (lane < TT) a_rm[(size_t)unit * tp + tl] = 0.0f;
+            continue;
+        }
+        u32x4 w[NC];
+        float sc[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const int col = c * CW + lane * 32;
+            const bool ok = col < D;
+            w[c] = ok ? load_stream(W3 + (size_t)unit * rb + col / 2) : u32x4{0u, 0u, 0u, 0u};
+            sc[c] = ok ? s3[(size_t)unit * G + col / I4_GROUP] : 0.0f;
+        }
+        dot_tokens(w, sc, v);
+        const float u = multi_reduce<TT>(v);
+        if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u : 0.0f;
     }
-    dot_tokens(w, sc, v);
-    const float u = multi_reduce<TT>(v);
-    if (lane < TT) a_rm[(size_t)unit * tp + tl] = tl < T ? activation(act, z) * u : 0.0f;
 }
 
 // Down pass of the int4 small batches: 16 lanes x 16 codes (8 bytes) per

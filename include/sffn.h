@@ -155,9 +155,9 @@ sffn_status sffn_create(sffn_handle **out, int D, int H, int r, int max_tokens, 
  *             VALU and MFMA down passes), SFFN_MFMA_UT1 [1], SFFN_MFMA_UT2 [2],
  *             SFFN_MFMA_UT4 [2] (16-unit tiles per MFMA gate block for up to
  *             16, 32 and 64 tokens).
- *   int8 groups of 2..4 tokens: SFFN_TB_RW_I8 [2] (units per wave of the
- *             union gate pass: 1, 2, 4); SFFN_TB_SPLITS also sets the unit
- *             ranges of the int8 and int4 down passes.
+ *   int8 and int4 groups of 2..4 tokens: SFFN_TB_RW_I8 [2] (units per wave
+ *             of the union gate pass: 1, 2, 4 for int8; 1 or 2 for int4);
+ *             SFFN_TB_SPLITS also sets the unit ranges of their down passes.
  *   above 64 tokens (bf16, r == 0): SFFN_GEMM_MIN_T [65] (smallest batch on the
  *             GEMM path), SFFN_GEMM_SPLITS [chosen per call] (unit ranges of the
  *             down GEMM), SFFN_GEMM_WIDE_MIN [200] (256 x 128 gate tiles from
