@@ -21,7 +21,7 @@ namespace {
 
 enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GATE_UP_DENSE,
             KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_GATE_UP_DENSE_T1, KIND_DOWN_T1,
-            KIND_FFN_T1, KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
+            KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
             KIND_GATE_UP_GEMM, KIND_UNION_LIST, KIND_DOWN_GEMM, KIND_RANK_PROJ_T1_I8,
@@ -32,7 +32,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
-                                            "k_ffn_t1", "k_ffn_dense_t1", "k_reduce_partials",
+                                            "k_ffn_dense_t1", "k_reduce_partials",
                                             "k_rank_proj_t1", "k_gate_up_lopa_t1",
                                             "k_gate_up_mfma", "k_down_mfma", "k_down_tb",
                                             "k_gate_up_t1_i8", "k_gate_up_dense_t1_i8",
@@ -50,12 +50,6 @@ constexpr int MAXT_GEMM = 8192;
 
 thread_local std::string g_thread_error = "no error";
 
-int env_int(const char* name, int dflt) {
-    const char* v = std::getenv(name);
-    if (!v || !*v) return dflt;
-    return std::atoi(v);
-}
-
 }  // namespace
 
 struct sffn_handle {
@@ -66,44 +60,27 @@ struct sffn_handle {
     uint8_t* live_buf = nullptr; // [max_tokens x H] live flags
     float* t_buf = nullptr;      // [max_tokens x r] LoPA rank vectors
     std::string err = "no error";
-    // launch plan
-    int gate_rows_per_wave = 4;
-    int down_lpr = 8;
-    // batch-1 bf16 path
-    int t1_rw = 1;            // units per wave in the gate pass
-    int t1_rw_lopa = 2;       // units per wave in the LoPA gate pass (short U rows)
-    int t1_lpr = 32;          // lanes per W2T row slice in the down pass (512 B per row)
-    int t1_splits_sparse = 16; // row splits of the down pass (sparse)
-    int t1_splits_dense = 16; // row splits of the down pass (dense, unfused)
-    int t1_fused_sparse = 0;  // sparse: fused gate/up/down pass + partial reduction
-    int t1_fused_dense = 1;   // dense: fused one-pass W1/W3/W2T + partial reduction
-    int t1_fused = 1;         // a fused plan exists for this shape
-    int f_rows_per_block = 0; // units per fused block
-    int f_rw = 0;             // units per wave in the fused pass
-    int f_blocks = 0;         // fused blocks (= partials)
-    float* part_buf = nullptr; // [f_blocks x D] partial outputs
+    // launch plan (fixed per shape at create; the constants come from measured sweeps)
+    int gate_rows_per_wave = 4;    // units per wave of the general (fp32) gate kernels
+    int t1_splits = 16;            // unit-range splits of the batch-1 down passes
+    int t1_fused = 1;              // the batch-1 dense comparator runs as one fused pass
+    int f_rows_per_block = 0;      // units per block of that pass
+    int f_rw = 0;                  // units per wave of that pass
+    int f_blocks = 0;              // its blocks (= partial outputs)
+    float* part_buf = nullptr;     // [f_blocks x D] partial outputs of the dense comparator
     // batched bf16 path on MFMA (union of live sets, dense)
     int m_tp = 0;                  // padded token count (16 * token tiles) the buffers hold
     int m_splits = 16;             // row splits of the MFMA down pass
-    int m_ut1 = 1, m_ut2 = 2, m_ut4 = 2;  // unit tiles per gate block for <=16, <=32, <=64 tokens
     void* m_zero = nullptr;        // 4 KB of zeros (source of the staged pieces outside the operands)
     // mixture of experts: tokens gathered per expert, expert outputs per slot
     uint16_t* moe_x = nullptr;     // [2 * max_tokens x D] bf16
     float* moe_y = nullptr;        // [2 * max_tokens x D] fp32
-    int tb_splits = 16;            // row splits of the small-batch down pass
-    int tb_rw_i8 = 2;              // units per wave of the int8 small-batch gate (1, 2, 4)
-    int t1_lopa_i8_upw = 2;        // units per wave of the int8 LoPA batch-1 gate (2 or 4)
-    int tb_max = 4;                // batches up to this size use the small-batch down pass
-    int tbv_max = 4;               // batches up to this size use the VALU gate/up pass
-    int tbv_rw2 = 2, tbv_rw4 = 4;  // units per wave of the VALU gate/up pass (2 and 4 token slots)
+    int tb_splits = 16;            // row splits of the small-batch down passes
     float* m_a = nullptr;          // [H x m_tp] unit products, unit-major
     uint64_t* m_mask = nullptr;    // [H] tokens for which each unit is live
     uint16_t* m_t = nullptr;       // LoPA: [2 x m_tp x r] bf16 rank vectors, hi then lo parts
-    // large batches as GEMMs on MFMA
-    int g_min_t = MAXT + 1;        // smallest batch that takes the GEMM path
+    // large batches as GEMMs on MFMA (T > MAXT)
     int g_tp = 0;                  // padded token count of g_a (multiple of 256)
-    int g_splits = 0;              // unit-range splits of the down GEMM (0: chosen per call)
-    int g_wide_min = 200;          // gate tiles of 256 x 128 from this many tiles on
     uint16_t* g_a = nullptr;       // [H x g_tp] bf16 unit products, unit-major
     uint64_t* g_any = nullptr;     // [g_tp / 256 x 2 ceil(H / 128)] 64-unit live masks per token tile
     int32_t* g_list = nullptr;     // [H + 32] units live for some token, then the count
@@ -223,13 +200,6 @@ template <typename WT>
 sffn_status run_down(sffn_handle* h, const void* W2T, float* y, int T, int union_mode, int dense,
                      hipStream_t s) {
     const int vec = Elem<WT>::VEC;
-    if (h->down_lpr == 4) {
-        const int cb = 4 * vec;
-        const int nslices = (h->D + cb - 1) / cb;
-        const int nb = ((nslices + 7) / 8) * 8;
-        return launch(h, KIND_DOWN, k_down<WT, 4, 4>, dim3(nb), dim3(K2_THREADS), s, h->a_buf,
-                      (const WT*)W2T, y, h->D, h->H, T, union_mode, dense);
-    }
     const int cb = 8 * vec;
     const int nslices = (h->D + cb - 1) / cb;
     const int nb = ((nslices + 7) / 8) * 8;
@@ -245,7 +215,7 @@ sffn_status run_live_list(sffn_handle* h, int T, int32_t* live_count, int32_t* l
 }
 
 constexpr int kNC_T1[] = {1, 2, 3, 4, 5, 6, 8};
-constexpr int kPMAX[] = {4, 8, 16, 32};
+constexpr int kPMAX[] = {1, 2, 4, 8, 16, 32};
 
 bool t1_ok(const sffn_handle* h, int T) {
     return T == 1 && h->dtype == SFFN_BF16 &&
@@ -264,15 +234,10 @@ bool t1_ok(const sffn_handle* h, int T) {
         case 8: { constexpr int NC = 8; BODY; } break;    \
         default: return fail(h, SFFN_INTERNAL, "no batch-1 kernel for this width"); \
     }
-#define SFFN_RW_SWITCH(RWV, BODY)                         \
-    switch (RWV) {                                        \
-        case 1: { constexpr int RW = 1; BODY; } break;    \
-        case 2: { constexpr int RW = 2; BODY; } break;    \
-        case 4: { constexpr int RW = 4; BODY; } break;    \
-        default: return fail(h, SFFN_INTERNAL, "bad units per wave"); \
-    }
 #define SFFN_PMAX_SWITCH(PV, BODY)                        \
     switch (PV) {                                         \
+        case 1: { constexpr int PMAX = 1; BODY; } break;  \
+        case 2: { constexpr int PMAX = 2; BODY; } break;  \
         case 4: { constexpr int PMAX = 4; BODY; } break;  \
         case 8: { constexpr int PMAX = 8; BODY; } break;  \
         case 16: { constexpr int PMAX = 16; BODY; } break; \
@@ -280,32 +245,19 @@ bool t1_ok(const sffn_handle* h, int T) {
         default: return fail(h, SFFN_INTERNAL, "hidden width too large for the down pass"); \
     }
 
-// down pass, batch 1, bf16
+// down pass, batch 1, bf16: 256-column slices (32 lanes x 16 B per W2T row
+// slice), XCD-contiguous slice order, `splits` unit ranges
 sffn_status run_down_t1(sffn_handle* h, const void* W2T, float* y, int splits, int dense,
                         hipStream_t s) {
-    const int cb = h->t1_lpr * 8;
+    const int cb = 32 * 8;
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
     const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
     sffn_status st = SFFN_OK;
-    if (h->t1_lpr == 4) {
-        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<4, PMAX>, dim3(nbx, splits),
-                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
-                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
-    } else if (h->t1_lpr == 16) {
-        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<16, PMAX>, dim3(nbx, splits),
-                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
-                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
-    } else if (h->t1_lpr == 32) {
-        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<32, PMAX>, dim3(nbx, splits),
-                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
-                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
-    } else {
-        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<8, PMAX>, dim3(nbx, splits),
-                                           dim3(KD_THREADS), s, (const float*)h->a_buf,
-                                           (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
-    }
+    SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1, k_down_t1<PMAX>, dim3(nbx, splits),
+                                       dim3(KD_THREADS), s, (const float*)h->a_buf,
+                                       (const uint16_t*)W2T, y, h->D, h->H, splits, dense));
     return st;
 }
 
@@ -318,82 +270,69 @@ sffn_status run_down_t1(sffn_handle* h, const void* W2T, float* y, int splits, i
         default: return fail(h, SFFN_INTERNAL, "bad units per wave"); \
     }
 
-// Fused batch-1 pass (gate, live W3 and W2T rows) + partial reduction.
-template <bool DENSE>
-sffn_status run_fused_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
-                         const void* W2T, float* y, int32_t* live_count, int32_t* live_idx,
-                         hipStream_t s) {
+// Batch-1 dense comparator as one fused pass (W1, W3 and W2T rows of every unit
+// read together, one partial output per block) + the partial reduction.
+sffn_status run_fused_dense_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
+                               const void* W2T, float* y, hipStream_t s) {
     const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
     const size_t shm = (size_t)KF_WAVES * h->D * sizeof(float);
-    uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
-    const int kind = DENSE ? KIND_FFN_DENSE_T1 : KIND_FFN_T1;
     sffn_status st = SFFN_OK;
     SFFN_NCT1_SWITCH(nc, SFFN_FRW_SWITCH(h->f_rw,
-        st = launch_shm(h, kind, k_ffn_t1<NC, RW, DENSE>, dim3(h->f_blocks), dim3(KF_THREADS),
-                        shm, s, (const uint16_t*)x, (const uint16_t*)W1, (const uint16_t*)W3,
-                        (const uint16_t*)W2T, h->part_buf, live, h->D, h->H,
+        st = launch_shm(h, KIND_FFN_DENSE_T1, k_ffn_dense_t1<NC, RW>, dim3(h->f_blocks),
+                        dim3(KF_THREADS), shm, s, (const uint16_t*)x, (const uint16_t*)W1,
+                        (const uint16_t*)W3, (const uint16_t*)W2T, h->part_buf, h->D, h->H,
                         h->f_rows_per_block, h->act)));
     if (st != SFFN_OK) return st;
-    st = launch(h, KIND_REDUCE, k_reduce_partials, dim3((h->D + 63) / 64), dim3(KR_THREADS), s,
-                (const float*)h->part_buf, y, h->D, h->f_blocks);
-    if (st != SFFN_OK) return st;
-    if (!DENSE) return run_live_list(h, 1, live_count, live_idx, s);
-    return SFFN_OK;
+    return launch(h, KIND_REDUCE, k_reduce_partials, dim3((h->D + 63) / 64), dim3(KR_THREADS), s,
+                  (const float*)h->part_buf, y, h->D, h->f_blocks);
 }
 
-// Allow the fused kernels their dynamic LDS (one y slice per wave).
+// Allow the fused dense kernel its dynamic LDS (one y slice per wave).
 sffn_status prepare_fused(sffn_handle* h) {
     const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
     const int shm = KF_WAVES * h->D * (int)sizeof(float);
     hipError_t e = hipSuccess;
     SFFN_NCT1_SWITCH(nc, SFFN_FRW_SWITCH(h->f_rw,
-        e = hipFuncSetAttribute((const void*)k_ffn_t1<NC, RW, false>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, shm);
-        if (e == hipSuccess)
-            e = hipFuncSetAttribute((const void*)k_ffn_t1<NC, RW, true>,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, shm)));
+        e = hipFuncSetAttribute((const void*)k_ffn_dense_t1<NC, RW>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, shm)));
     if (e != hipSuccess) return hip_fail(h, e, "hipFuncSetAttribute");
     return SFFN_OK;
 }
 
+// Batch-1 sparse pass: the gate kernel (one unit per wave, each wave reads the
+// W3 row of its unit when it is live) and the down kernel.
 sffn_status run_sparse_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
                           const void* W2T, float* y, int32_t* live_count, int32_t* live_idx,
                           hipStream_t s) {
-    if (h->t1_fused && h->t1_fused_sparse)
-        return run_fused_t1<false>(h, x, W1, W3, W2T, y, live_count, live_idx, s);
     const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
-    const int rw = h->t1_rw;
-    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
-    const int splits = h->t1_splits_sparse;
+    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    const int splits = h->t1_splits;
     uint8_t* live = live_count ? h->live_buf : nullptr;
     float* yz = splits > 1 ? y : nullptr;
     sffn_status st = SFFN_OK;
-    SFFN_NCT1_SWITCH(nc, SFFN_RW_SWITCH(rw, st = launch(h, KIND_GATE_UP_T1, k_gate_up_t1<NC, RW>,
-                                                        dim3(nb), dim3(K1_THREADS), s,
-                                                        (const uint16_t*)x, (const uint16_t*)W1,
-                                                        (const uint16_t*)W3, h->a_buf, live, yz,
-                                                        h->D, h->H, h->act)));
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_T1, k_gate_up_t1<NC>, dim3(nb),
+                                     dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,
+                                     (const uint16_t*)W3, h->a_buf, live, yz, h->D, h->H,
+                                     h->act));
     if (st != SFFN_OK) return st;
     st = run_down_t1(h, W2T, y, splits, 0, s);
     if (st != SFFN_OK) return st;
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
+// Batch-1 dense comparator: the fused pass where its per-wave LDS slices fit
+// (D <= KF_DMAX), else a dense gate/up pass and the down kernel over every unit.
 sffn_status run_dense_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
                          const void* W2T, float* y, hipStream_t s) {
-    if (h->t1_fused && h->t1_fused_dense)
-        return run_fused_t1<true>(h, x, W1, W3, W2T, y, nullptr, nullptr, s);
+    if (h->t1_fused) return run_fused_dense_t1(h, x, W1, W3, W2T, y, s);
     const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
-    const int rw = h->t1_rw;
-    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
-    const int splits = h->t1_splits_dense;
+    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
+    const int splits = h->t1_splits;
     float* yz = splits > 1 ? y : nullptr;
     sffn_status st = SFFN_OK;
-    SFFN_NCT1_SWITCH(nc, SFFN_RW_SWITCH(rw, st = launch(h, KIND_GATE_UP_DENSE_T1,
-                                                        k_gate_up_dense_t1<NC, RW>, dim3(nb),
-                                                        dim3(K1_THREADS), s, (const uint16_t*)x,
-                                                        (const uint16_t*)W1, (const uint16_t*)W3,
-                                                        h->a_buf, yz, h->D, h->H, h->act)));
+    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_DENSE_T1, k_gate_up_dense_t1<NC>, dim3(nb),
+                                     dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,
+                                     (const uint16_t*)W3, h->a_buf, yz, h->D, h->H, h->act));
     if (st != SFFN_OK) return st;
     return run_down_t1(h, W2T, y, splits, 1, s);
 }
@@ -432,22 +371,22 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
                                        (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
         if (st != SFFN_OK) return st;
     }
-    const int ut = nt == 4 ? h->m_ut4 : (nt == 2 ? h->m_ut2 : h->m_ut1);  // unit tiles per gate block
+    const int ut = nt == 1 ? 1 : 2;  // unit tiles per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
-    const bool small_down = T <= h->tb_max && T <= 8;
+    const bool small_down = T <= 4;
     const int splits = small_down ? h->tb_splits : h->m_splits;
     float* yz = splits > 1 ? y : nullptr;
-    if (!LOPA && T <= h->tbv_max && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
-        // gate/up on the VALU: x of the batch in registers, W1 streamed once
+    if (!LOPA && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
+        // gate/up on the VALU: x of the batch in registers, W1 streamed once; units
+        // per wave = token slots (2 or 4)
         const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
         const int tt = T <= 2 ? 2 : 4;
-        const int rw = tt == 2 ? h->tbv_rw2 : h->tbv_rw4;
-        const int nbv = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
+        const int nbv = (h->H + K1_WAVES * tt - 1) / (K1_WAVES * tt);
 #define SFFN_TBV(TTV)                                                                               \
-        SFFN_NCT1_SWITCH(nc, SFFN_RW_SWITCH(rw, st = launch(h, KIND_GATE_UP_TB,                    \
-            k_gate_up_tb<NC, RW, TTV, DENSE>, dim3(nbv), dim3(K1_THREADS), s, (const uint16_t*)x,   \
+        SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_TB,                                        \
+            k_gate_up_tb<NC, TTV, TTV, DENSE>, dim3(nbv), dim3(K1_THREADS), s, (const uint16_t*)x,  \
             (const uint16_t*)W1, (const uint16_t*)W3, h->m_a, h->m_mask, live, yz, h->D, h->H, T,   \
-            16 * nt, h->act)))
+            16 * nt, h->act))
         if (tt == 2) { SFFN_TBV(2); } else { SFFN_TBV(4); }
 #undef SFFN_TBV
     } else {
@@ -458,11 +397,11 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
                 h->D, h->H, T, h->act, (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r,      \
                 h->flags)
     if (nt == 1) {
-        if (ut == 4) { SFFN_GATE_MFMA(1, 4); } else if (ut == 2) { SFFN_GATE_MFMA(1, 2); } else { SFFN_GATE_MFMA(1, 1); }
+        SFFN_GATE_MFMA(1, 1);
     } else if (nt == 2) {
-        if (ut == 4) { SFFN_GATE_MFMA(2, 4); } else if (ut == 2) { SFFN_GATE_MFMA(2, 2); } else { SFFN_GATE_MFMA(2, 1); }
+        SFFN_GATE_MFMA(2, 2);
     } else {
-        if (ut == 4) { SFFN_GATE_MFMA(4, 4); } else if (ut == 2) { SFFN_GATE_MFMA(4, 2); } else { SFFN_GATE_MFMA(4, 1); }
+        SFFN_GATE_MFMA(4, 2);
     }
     }
 #undef SFFN_GATE_MFMA
@@ -473,15 +412,15 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
         const int nslices = (h->D + cb - 1) / cb;
         const int nbx = ((nslices + 7) / 8) * 8;
         const int hs = (h->H + splits - 1) / splits;
-        const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
-        const int tt = T <= 2 ? 2 : (T <= 4 ? 4 : 8);
+        const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
+        const int tt = T <= 2 ? 2 : 4;
 #define SFFN_TB_LAUNCH(TTV)                                                                      \
         SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB, k_down_tb<32, PMAX, TTV>,            \
                                            dim3(nbx, splits), dim3(KD_THREADS), s,               \
                                            (const float*)h->m_a, (const uint64_t*)h->m_mask,     \
                                            (const uint16_t*)W2T, y, h->D, h->H, T, 16 * nt,      \
                                            splits))
-        if (tt == 2) { SFFN_TB_LAUNCH(2); } else if (tt == 4) { SFFN_TB_LAUNCH(4); } else { SFFN_TB_LAUNCH(8); }
+        if (tt == 2) { SFFN_TB_LAUNCH(2); } else { SFFN_TB_LAUNCH(4); }
 #undef SFFN_TB_LAUNCH
     } else {
         const int ntile = (h->D + KDM_NB - 1) / KDM_NB;
@@ -497,7 +436,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
 
 // ---- large batches: gate/up GEMM, union list, gathered down GEMM
 bool gemm_ok(const sffn_handle* h, int T) {
-    return h->g_a != nullptr && T >= h->g_min_t && T <= h->max_tokens;
+    return h->g_a != nullptr && T > MAXT && T <= h->max_tokens;
 }
 
 template <int TM, int UN, bool DENSE>
@@ -523,19 +462,16 @@ sffn_status run_gemm(sffn_handle* h, const void* x, const void* W1, const void* 
                      hipStream_t s) {
     const int nmt = (T + KDG_TM - 1) / KDG_TM;
     const int nnt = (h->D + KDG_NB - 1) / KDG_NB;
-    int splits = h->g_splits;
-    if (splits <= 0) {
-        // unit-range splits only while the output tiles alone leave CUs idle, and
-        // never below 8 chunks of units per split
-        splits = 1;
-        const int nch = (h->H + KDG_KC - 1) / KDG_KC;
-        while (nmt * nnt * splits < 256 && splits < 16 && nch / (2 * splits) >= 8) splits *= 2;
-    }
+    // unit-range splits only while the output tiles alone leave CUs idle, and
+    // never below 8 chunks of units per split
+    int splits = 1;
+    const int nch = (h->H + KDG_KC - 1) / KDG_KC;
+    while (nmt * nnt * splits < 256 && splits < 16 && nch / (2 * splits) >= 8) splits *= 2;
     uint8_t* live = live_count ? h->live_buf : nullptr;
     float* yz = splits > 1 ? y : nullptr;
     int32_t* count = h->g_list + h->H + 32;
-    // 256 x 128 gate tiles once there are g_wide_min of them, else 256 x 64 (more blocks)
-    const bool wide = (long)((T + 255) / 256) * ((h->H + 127) / 128) >= h->g_wide_min;
+    // 256 x 128 gate tiles once there are 200 of them, else 256 x 64 (more blocks)
+    const bool wide = (long)((T + 255) / 256) * ((h->H + 127) / 128) >= 200;
     sffn_status st = wide ? run_gate_gemm<256, 128, DENSE>(h, x, W1, W3, live, yz, T, s)
                           : run_gate_gemm<256, 64, DENSE>(h, x, W1, W3, live, yz, T, s);
     if (st != SFFN_OK) return st;
@@ -581,7 +517,7 @@ sffn_status run_lopa_t1(sffn_handle* h, const void* x, const void* V, const void
                         int32_t* live_idx, hipStream_t s) {
     const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
     const int nr = pick(kNR, 3, chunks_needed(h->r, h->dtype));
-    const int splits = h->t1_splits_sparse;
+    const int splits = h->t1_splits;
     float* yz = splits > 1 ? y : nullptr;
     sffn_status st = SFFN_OK;
     const int nbr = (h->r + K1_WAVES - 1) / K1_WAVES;
@@ -589,14 +525,14 @@ sffn_status run_lopa_t1(sffn_handle* h, const void* x, const void* V, const void
                                      dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)V,
                                      h->t_buf, yz, h->D, h->r));
     if (st != SFFN_OK) return st;
-    const int rw = h->t1_rw_lopa;
-    const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
+    // two units per wave: a U row of r <= 512 bf16 fills at most 64 lanes once
+    const int nb = (h->H + K1_WAVES * 2 - 1) / (K1_WAVES * 2);
     uint8_t* live = live_count ? h->live_buf : nullptr;
-    SFFN_NCT1_SWITCH(nc, SFFN_NRT1_SWITCH(nr, SFFN_RW_SWITCH(rw,
-        st = launch(h, KIND_GATE_UP_LOPA_T1, k_gate_up_lopa_t1<NC, NR, RW>, dim3(nb),
+    SFFN_NCT1_SWITCH(nc, SFFN_NRT1_SWITCH(nr,
+        st = launch(h, KIND_GATE_UP_LOPA_T1, k_gate_up_lopa_t1<NC, NR, 2>, dim3(nb),
                     dim3(K1_THREADS), s, (const uint16_t*)x, (const float*)h->t_buf,
                     (const uint16_t*)U, (const uint16_t*)W3, h->a_buf, live, h->D, h->H, h->r,
-                    h->act, h->flags))));
+                    h->act, h->flags)));
     if (st != SFFN_OK) return st;
     st = run_down_t1(h, W2T, y, splits, 0, s);
     if (st != SFFN_OK) return st;
@@ -659,7 +595,7 @@ sffn_status run_down_t1_i8(sffn_handle* h, const void* W2T, float* y, int splits
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
     const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
     sffn_status st = SFFN_OK;
     SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I8, k_down_t1_i8<PMAX>, dim3(nbx, splits),
                                        dim3(KD_THREADS), s, (const float*)h->a_buf,
@@ -673,7 +609,7 @@ sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float
                       float* y, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
     const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
     const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
-    int splits = h->t1_splits_sparse;
+    int splits = h->t1_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
     uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
     float* yz = splits > 1 ? y : nullptr;
@@ -696,7 +632,7 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
                       const void* W3, const float* s3, const void* W2T, const float* s2,
                       float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
     const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
-    const int rw = DENSE ? 1 : h->tb_rw_i8;  // the dense comparator measured best at 1
+    const int rw = DENSE ? 1 : 2;  // units per wave: union calls 2, the dense comparator 1 (measured)
     const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
     const int tp = 16 * token_tiles(T);
     const int tt = T <= 2 ? 2 : 4;
@@ -711,8 +647,7 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
                                      (const int8_t*)W1, s1, (const int8_t*)W3, s3, s2, h->m_a,     \
                                      h->m_mask, live, yz, h->D, h->H, T, tp, h->act))
 #define SFFN_TBQ_RW(TTV)                                                                          \
-    if (rw == 4) { SFFN_TBQ_GATE(TTV, 4); }                                                       \
-    else if (rw == 2) { SFFN_TBQ_GATE(TTV, 2); }                                                  \
+    if (rw == 2) { SFFN_TBQ_GATE(TTV, 2); }                                                       \
     else { SFFN_TBQ_GATE(TTV, 1); }
     if (tt == 2) { SFFN_TBQ_RW(2); } else { SFFN_TBQ_RW(4); }
 #undef SFFN_TBQ_RW
@@ -722,7 +657,7 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
     const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
 #define SFFN_TBQ_DOWN(TTV)                                                                        \
     SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB_I8, k_down_tb_i8<PMAX, TTV>,                \
                                        dim3(nbx, splits), dim3(KD_THREADS), s,                    \
@@ -741,7 +676,7 @@ sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float
                       const void* W3, const float* s3, const void* W2T, const float* s2,
                       float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
     const int nc = (h->D + 2047) / 2048;
-    const int rw = (!DENSE && h->tb_rw_i8 == 2) ? 2 : 1;  // union calls as for int8 (1 or 2)
+    const int rw = DENSE ? 1 : 2;  // as for int8
     const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
     const int tp = 16 * token_tiles(T);
     const int tt = T <= 2 ? 2 : 4;
@@ -775,7 +710,7 @@ sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
     const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
 #define SFFN_TB4_DOWN(TTV)                                                                        \
     SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB_I4, k_down_tb_i4<PMAX, TTV>,                \
                                        dim3(nbx, splits), dim3(KD_THREADS), s,                    \
@@ -795,7 +730,7 @@ sffn_status run_down_t1_i4(sffn_handle* h, const void* W2T, const float* s2, flo
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
     const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
     sffn_status st = SFFN_OK;
     SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_T1_I4, k_down_t1_i4<PMAX>, dim3(nbx, splits),
                                        dim3(KD_THREADS), s, (const float*)h->a_buf,
@@ -811,7 +746,7 @@ sffn_status run_i4_t1(sffn_handle* h, const void* x, const void* W1, const float
                       float* y, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
     const int nc = (h->D + 2047) / 2048;
     const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
-    int splits = h->t1_splits_sparse;
+    int splits = h->t1_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
     uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
     float* yz = splits > 1 ? y : nullptr;
@@ -841,7 +776,7 @@ sffn_status run_lopa_i4_t1(sffn_handle* h, const void* x, const void* V, const f
                            const void* U, const float* sU, const void* W3, const float* s3,
                            const void* W2T, const float* s2, float* y, int32_t* live_count,
                            int32_t* live_idx, hipStream_t s) {
-    int splits = h->t1_splits_sparse;
+    int splits = h->t1_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
     float* yz = splits > 1 ? y : nullptr;
     uint8_t* live = live_count ? h->live_buf : nullptr;
@@ -892,7 +827,7 @@ sffn_status run_lopa_i8_t1(sffn_handle* h, const void* x, const void* V, const f
                            const void* W2T, const float* s2, float* y, int32_t* live_count,
                            int32_t* live_idx, hipStream_t s) {
     const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
-    int splits = h->t1_splits_sparse;
+    int splits = h->t1_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
     float* yz = splits > 1 ? y : nullptr;
     uint8_t* live = live_count ? h->live_buf : nullptr;
@@ -902,7 +837,8 @@ sffn_status run_lopa_i8_t1(sffn_handle* h, const void* x, const void* V, const f
                                      dim3(K1_THREADS), s, (const uint16_t*)x, (const int8_t*)V,
                                      sV, h->t_buf, yz, h->D, h->r));
     if (st != SFFN_OK) return st;
-    const int upw = (h->t1_lopa_i8_upw == 2 && h->r <= 1024) ? 2 : 4;
+    // two units per wave (32 lanes per U row) up to r = 1024, four (16 lanes) above
+    const int upw = h->r <= 1024 ? 2 : 4;
     const int nb = (h->H + K1_WAVES * upw - 1) / (K1_WAVES * upw);
     const int nr = (h->r + 16 * (64 / upw) - 1) / (16 * (64 / upw));
 #define SFFN_LOPA_I8(NRV, UPWV)                                                                    \
@@ -1053,8 +989,7 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
                         "D must be a positive multiple of 8, at most " + std::to_string(dmax));
         if (H <= 0 || H > (1 << 20))
             return fail(nullptr, SFFN_INVALID_ARGUMENT, "H must be in [1, 2^20]");
-        const int rmax = dtype == SFFN_BF16 ? 2048 : 2048;
-        if (r != 0 && (r < 8 || r % 8 != 0 || r > rmax))
+        if (r != 0 && (r < 8 || r % 8 != 0 || r > 2048))
             return fail(nullptr, SFFN_INVALID_ARGUMENT,
                         "r must be 0 or a multiple of 8 in [8, 2048]");
         const bool big_ok = dtype == SFFN_BF16 && r == 0;
@@ -1082,35 +1017,18 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             return fail(nullptr, e == hipErrorOutOfMemory ? SFFN_OUT_OF_MEMORY : SFFN_HIP_ERROR,
                         std::string("scratch allocation: ") + hipGetErrorString(e));
         }
-        // launch plan: enough gate/up blocks to cover the 256 CUs several times over
+        // launch plan: enough gate/up blocks of the general kernels to cover the 256
+        // CUs several times over
         int rpw = 4;
         while (rpw > 1 && (H + rpw * K1_WAVES - 1) / (rpw * K1_WAVES) < 1024) rpw /= 2;
         h->gate_rows_per_wave = rpw;
-        h->down_lpr = 8;
-        const int env_rpw = env_int("SFFN_GATE_ROWS_PER_WAVE", 0);
-        if (env_rpw >= 1 && env_rpw <= K1_MAX_ROWS / K1_WAVES) h->gate_rows_per_wave = env_rpw;
-        const int env_lpr = env_int("SFFN_DOWN_LANES_PER_ROW", 0);
-        if (env_lpr == 4 || env_lpr == 8) h->down_lpr = env_lpr;
-        const int e_rw = env_int("SFFN_T1_ROWS_PER_WAVE", 0);
-        if (e_rw == 1 || e_rw == 2 || e_rw == 4) h->t1_rw = e_rw;
-        const int e_rwl = env_int("SFFN_T1_LOPA_ROWS_PER_WAVE", 0);
-        if (e_rwl == 1 || e_rwl == 2 || e_rwl == 4) h->t1_rw_lopa = e_rwl;
-        const int e_lpr = env_int("SFFN_T1_LANES_PER_ROW", 0);
-        if (e_lpr == 4 || e_lpr == 8 || e_lpr == 16 || e_lpr == 32) h->t1_lpr = e_lpr;
-        const int e_lupw = env_int("SFFN_T1_LOPA_I8_UPW", h->t1_lopa_i8_upw);
-        if (e_lupw == 2 || e_lupw == 4) h->t1_lopa_i8_upw = e_lupw;
-        const int e_ss = env_int("SFFN_T1_SPLITS_SPARSE", 0);
-        if (e_ss >= 1 && e_ss <= 64) h->t1_splits_sparse = e_ss;
-        const int e_sd = env_int("SFFN_T1_SPLITS_DENSE", 0);
-        if (e_sd >= 1 && e_sd <= 16) h->t1_splits_dense = e_sd;
-        h->t1_fused = 1;
-        h->t1_fused_sparse = env_int("SFFN_T1_FUSED_SPARSE", h->t1_fused_sparse) != 0;
-        h->t1_fused_dense = env_int("SFFN_T1_FUSED_DENSE", h->t1_fused_dense) != 0;
-        // fused batch-1 plan: about one block per CU, at most 64 units per block
+        // batch-1 down passes: 16 unit ranges, more when a range would exceed what
+        // one block's waves hold (32 x 512 units)
+        while ((H + h->t1_splits - 1) / h->t1_splits > 32 * KD_THREADS) ++h->t1_splits;
+        // fused batch-1 dense comparator: about one block per two CUs (128 blocks),
+        // at most 8 units per wave
         if (dtype == SFFN_BF16 && D <= KF_DMAX) {
-            int target = env_int("SFFN_T1_BLOCKS", 128);
-            if (target < 1) target = 256;
-            int rpb = (H + target - 1) / target;
+            int rpb = (H + 127) / 128;
             // keep the W1 tiles of a wave (units x register chunks) within 32 x 16 bytes per lane
             const int ncf = pick(kNC_T1, 7, chunks_needed(D, dtype));
             int rw_max = 1;
@@ -1134,70 +1052,57 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         } else {
             h->t1_fused = 0;
         }
+        // scratch that must start zeroed is cleared on a private stream of the
+        // handle's own, which create waits for (no device-wide synchronisation)
+        hipStream_t init = nullptr;
+        e = hipStreamCreateWithFlags(&init, hipStreamNonBlocking);
+        if (e != hipSuccess) {
+            sffn_destroy(h);
+            return fail(nullptr, SFFN_HIP_ERROR, std::string("hipStreamCreateWithFlags: ") + hipGetErrorString(e));
+        }
+        auto finish_init = [&](hipError_t err) {
+            hipError_t e2 = hipStreamSynchronize(init);
+            (void)hipStreamDestroy(init);
+            return err != hipSuccess ? err : e2;
+        };
         // batch plans: unit-major products for up to 16*ceil(max_tokens/16) tokens (bf16
         // MFMA and VALU batches, int8 and int4 VALU batches)
         if ((dtype == SFFN_BF16 || dtype == SFFN_I8 || dtype == SFFN_I4) && max_tokens >= 2) {
             h->m_tp = 16 * token_tiles(max_tokens);
-            auto ut_env = [](const char* name, int dflt) {
-                const int v = env_int(name, dflt);
-                return (v == 1 || v == 2 || v == 4) ? v : dflt;
-            };
-            h->m_ut1 = ut_env("SFFN_MFMA_UT1", 1);
-            h->m_ut2 = ut_env("SFFN_MFMA_UT2", 2);
-            h->m_ut4 = ut_env("SFFN_MFMA_UT4", 2);
-            int sp = env_int("SFFN_MFMA_SPLITS", 16);
-            if (sp < 1) sp = 16;
-            while ((H + sp - 1) / sp > KDM_LCAP) ++sp;
-            h->m_splits = sp;
-            const int tbs = env_int("SFFN_TB_SPLITS", 16);
-            if (tbs >= 1 && tbs <= 64) h->tb_splits = tbs;
-            const int trw = env_int("SFFN_TB_RW_I8", h->tb_rw_i8);
-            if (trw == 1 || trw == 2 || trw == 4) h->tb_rw_i8 = trw;
-            h->tbv_max = env_int("SFFN_TBV_MAX", h->tbv_max);
-            auto rw_env = [](const char* name, int dflt) {
-                const int v = env_int(name, dflt);
-                return (v == 1 || v == 2 || v == 4) ? v : dflt;
-            };
-            h->tbv_rw2 = rw_env("SFFN_TBV_RW2", h->tbv_rw2);
-            h->tbv_rw4 = rw_env("SFFN_TBV_RW4", h->tbv_rw4);
-            const int tbm = env_int("SFFN_TB_MAX", h->tb_max);
-            if (tbm >= 0 && tbm <= 8) h->tb_max = tbm;
+            while ((H + h->m_splits - 1) / h->m_splits > KDM_LCAP) ++h->m_splits;
             while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;
             e = hipMalloc(&h->m_a, (size_t)H * h->m_tp * sizeof(float));
             if (e == hipSuccess) e = hipMalloc(&h->m_mask, (size_t)H * sizeof(uint64_t));
             if (e == hipSuccess && r > 0)
                 e = hipMalloc(&h->m_t, 2 * (size_t)h->m_tp * r * sizeof(uint16_t));
             if (e == hipSuccess) e = hipMalloc(&h->m_zero, 4096);
-            if (e == hipSuccess) e = hipMemset(h->m_zero, 0, 4096);
-            if (e == hipSuccess) e = hipDeviceSynchronize();
+            if (e == hipSuccess) e = hipMemsetAsync(h->m_zero, 0, 4096, init);
             if (e != hipSuccess) {
+                (void)finish_init(e);
                 sffn_destroy(h);
                 return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
             }
         }
-        if (dtype == SFFN_BF16 && r == 0 && h->m_zero) {
+        if (dtype == SFFN_BF16 && r == 0 && h->m_zero && max_tokens > MAXT) {
             // large batches as GEMMs: bf16 unit products for up to g_tp tokens
-            int gmin = env_int("SFFN_GEMM_MIN_T", MAXT + 1);
-            if (gmin < 2) gmin = 2;
-            h->g_min_t = gmin;
-            const int gs = env_int("SFFN_GEMM_SPLITS", 0);
-            if (gs >= 1 && gs <= 64) h->g_splits = gs;
-            h->g_wide_min = env_int("SFFN_GEMM_WIDE_MIN", h->g_wide_min);
-            if (max_tokens >= gmin) {
-                h->g_tp = 256 * ((max_tokens + 255) / 256);
-                const int ntt = h->g_tp / 256;
-                e = hipMalloc(&h->g_a, (size_t)H * h->g_tp * sizeof(uint16_t));
-                // one 64-bit mask per 64 units of each gate tile (tiles of 64 or 128 units)
-                const size_t nm = 2 * (((size_t)H + 127) / 128);
-                if (e == hipSuccess) e = hipMalloc(&h->g_any, (size_t)ntt * nm * sizeof(uint64_t));
-                if (e == hipSuccess) e = hipMalloc(&h->g_list, ((size_t)H + 33) * sizeof(int32_t));
-                if (e == hipSuccess) e = hipMemset(h->g_list, 0, ((size_t)H + 33) * sizeof(int32_t));
-                if (e == hipSuccess) e = hipDeviceSynchronize();
-                if (e != hipSuccess) {
-                    sffn_destroy(h);
-                    return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
-                }
+            h->g_tp = 256 * ((max_tokens + 255) / 256);
+            const int ntt = h->g_tp / 256;
+            e = hipMalloc(&h->g_a, (size_t)H * h->g_tp * sizeof(uint16_t));
+            // one 64-bit mask per 64 units of each gate tile (tiles of 64 or 128 units)
+            const size_t nm = 2 * (((size_t)H + 127) / 128);
+            if (e == hipSuccess) e = hipMalloc(&h->g_any, (size_t)ntt * nm * sizeof(uint64_t));
+            if (e == hipSuccess) e = hipMalloc(&h->g_list, ((size_t)H + 33) * sizeof(int32_t));
+            if (e == hipSuccess) e = hipMemsetAsync(h->g_list, 0, ((size_t)H + 33) * sizeof(int32_t), init);
+            if (e != hipSuccess) {
+                (void)finish_init(e);
+                sffn_destroy(h);
+                return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
             }
+        }
+        e = finish_init(hipSuccess);
+        if (e != hipSuccess) {
+            sffn_destroy(h);
+            return fail(nullptr, SFFN_HIP_ERROR, std::string("scratch initialisation: ") + hipGetErrorString(e));
         }
         if (dtype == SFFN_BF16 && r == 0) {
             const size_t rows = 2 * (size_t)std::min(max_tokens, MAXT);
@@ -1490,7 +1395,7 @@ sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const fl
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
     const int hs = (h->H + splits - 1) / splits;
-    const int pmax = pick(kPMAX, 4, (hs + KD_THREADS - 1) / KD_THREADS);
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
 #define SFFN_LQ_DOWN(TTV)                                                                         \
     if (bits == 8) {                                                                              \
         SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_TB_I8, k_down_tb_i8<PMAX, TTV>,            \

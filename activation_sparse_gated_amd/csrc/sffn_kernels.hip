@@ -549,14 +549,16 @@ __device__ inline float dot2_chunk(const u32x4& w, const u32x4& x, float s) {
     return s;
 }
 
-// Gate and gathered up projection for one token, bf16. Each wave owns RW
-// consecutive units and issues all of their W1 loads before any arithmetic;
-// the grid is sized so every block is resident at once, so the whole of W1 is
-// requested in one round. A wave then reads the W3 rows of its own live units
-// as soon as their z is known (no block-wide compaction or barrier, so a live
-// unit's W3 round trip never waits for another wave's W1 row). y_zero
-// (nullable): D floats this grid clears for a down pass that accumulates.
-template <int NC, int RW>
+// Gate and gathered up projection for one token, bf16. Each wave owns one
+// unit and issues all of its W1 loads before any arithmetic; the grid is sized
+// so every block is resident at once, so the whole of W1 is requested in one
+// round. A wave reads the W3 row of its unit as soon as the unit's z is known
+// to be live (no block-wide compaction or barrier, so a live unit's W3 round
+// trip never waits for another wave's W1 row; with one 5 KB row per wave the
+// first z values are known early, and the W3 reads of those units overlap the
+// rest of the W1 stream). y_zero (nullable): D floats this grid clears for a
+// down pass that accumulates.
+template <int NC>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W3, float* __restrict__ a_out, uint8_t* __restrict__ live_out,
@@ -564,17 +566,14 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
     constexpr int CW = WAVE * 8;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int unit0 = (blockIdx.x * K1_WAVES + wave) * RW;
+    const int unit = blockIdx.x * K1_WAVES + wave;
+    const bool in = unit < H;
 
-    u32x4 w[RW][NC];
+    u32x4 w[NC];
 #pragma unroll
-    for (int q = 0; q < RW; ++q) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int col = c * CW + lane * 8;
-            w[q][c] = (unit0 + q < H && col < D) ? load_stream(W1 + (size_t)(unit0 + q) * D + col)
-                                                 : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        w[c] = (in && col < D) ? load_stream(W1 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
     }
     u32x4 xv[NC];
 #pragma unroll
@@ -586,62 +585,45 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
     }
-    float z[RW];
-    bool live[RW];
+    float s = 0.0f;
 #pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        float s = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) s = dot2_chunk(w[q][c], xv[c], s);
-        z[q] = wave_sum_dpp(s);
-        const bool in = unit0 + q < H;
-        live[q] = in && z[q] > 0.0f;
-        if (lane == 0 && in) {
-            if (live_out) live_out[unit0 + q] = live[q] ? 1 : 0;
-            if (!live[q]) a_out[unit0 + q] = 0.0f;
-        }
+    for (int c = 0; c < NC; ++c) s = dot2_chunk(w[c], xv[c], s);
+    const float z = wave_sum_dpp(s);
+    const bool live = in && z > 0.0f;
+    if (lane == 0 && in) {
+        if (live_out) live_out[unit] = live ? 1 : 0;
+        if (!live) a_out[unit] = 0.0f;
     }
-    // the wave's live units: all W3 loads first (wave-uniform branches)
+    if (!live) return;  // wave-uniform
 #pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        if (!live[q]) continue;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int col = c * CW + lane * 8;
-            w[q][c] = col < D ? load_stream(W3 + (size_t)(unit0 + q) * D + col) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        w[c] = col < D ? load_stream(W3 + (size_t)unit * D + col) : u32x4{0u, 0u, 0u, 0u};
     }
+    float su = 0.0f;
 #pragma unroll
-    for (int q = 0; q < RW; ++q) {
-        if (!live[q]) continue;
-        float s = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) s = dot2_chunk(w[q][c], xv[c], s);
-        const float u = wave_sum_dpp(s);
-        if (lane == 0) a_out[unit0 + q] = activation(act, z[q]) * u;
-    }
+    for (int c = 0; c < NC; ++c) su = dot2_chunk(w[c], xv[c], su);
+    const float u = wave_sum_dpp(su);
+    if (lane == 0) a_out[unit] = activation(act, z) * u;
 }
-template <int NC, int RW>
+// Dense gate and up projection for one token (the unfused batch-1 dense
+// comparator): the W1 and W3 rows of the wave's unit read together.
+template <int NC>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_dense_t1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W3, float* __restrict__ a_out, float* __restrict__ y_zero,
     int D, int H, int act) {
-    constexpr int RPB = K1_WAVES * RW;
     constexpr int CW = WAVE * 8;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
-    const int row0 = blockIdx.x * RPB;
-    u32x4 w1[RW][NC], w3[RW][NC];
+    const int row = blockIdx.x * K1_WAVES + wave;
+    u32x4 w1[NC], w3[NC];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        const int row = row0 + wave * RW + r;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int col = c * CW + lane * 8;
-            const bool ok = row < H && col < D;
-            w1[r][c] = ok ? load_stream(W1 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
-            w3[r][c] = ok ? load_stream(W3 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        const bool ok = row < H && col < D;
+        w1[c] = ok ? load_stream(W1 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
+        w3[c] = ok ? load_stream(W3 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
     }
     u32x4 xv[NC];
 #pragma unroll
@@ -653,19 +635,15 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_dense_t1(
         for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
             y_zero[j] = 0.0f;
     }
+    float sz = 0.0f, su = 0.0f;
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-        float sz = 0.0f, su = 0.0f;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            sz = dot2_chunk(w1[r][c], xv[c], sz);
-            su = dot2_chunk(w3[r][c], xv[c], su);
-        }
-        sz = wave_sum_dpp(sz);
-        su = wave_sum_dpp(su);
-        const int row = row0 + wave * RW + r;
-        if (lane == 0 && row < H) a_out[row] = activation(act, sz) * su;
+    for (int c = 0; c < NC; ++c) {
+        sz = dot2_chunk(w1[c], xv[c], sz);
+        su = dot2_chunk(w3[c], xv[c], su);
     }
+    sz = wave_sum_dpp(sz);
+    su = wave_sum_dpp(su);
+    if (lane == 0 && row < H) a_out[row] = activation(act, sz) * su;
 }
 
 // LoPA batch-1 bf16: rank projection t = V x (fp32 out), one V row per wave,
@@ -799,57 +777,87 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
     }
 }
 
-// Exclusive prefix of N per-(row group, wave) counts, by one wave: woff[i] =
-// sum of counts[0 .. i), woff[N] = the total. One LDS read per lane and count,
-// then a wave-wide scan (shuffles) carried across groups of 64.
-template <int N>
-__device__ inline void counts_exclusive_prefix(const int* counts, int* woff, int lane) {
-    int carry = 0;
-    for (int base = 0; base < N; base += WAVE) {
-        const int i = base + lane;
-        const int v = i < N ? counts[i] : 0;
-        int incl = v;
+// Wave-local compaction of the units a down pass visits: `m` marks the ones
+// still to visit among 64 consecutive units (bit b = unit b). One round takes
+// the next RPI * UF of them in ascending order, the g-th of every RPI going to
+// lane group g; bit[u] = -1 once they run out. Every step is wave-uniform
+// (scalar bit scans), so no LDS list, prefix sum or barrier is needed.
+template <int RPI, int UF>
+__device__ inline void next_live_bits(uint64_t& m, int grp, int (&bit)[UF]) {
 #pragma unroll
-        for (int o = 1; o < WAVE; o <<= 1) {
-            const int t = __shfl_up(incl, o, WAVE);
-            if (lane >= o) incl += t;
+    for (int u = 0; u < UF; ++u) {
+        int b = -1;
+#pragma unroll
+        for (int g = 0; g < RPI; ++g) {
+            const int bg = m ? (int)__builtin_ctzll(m) : -1;
+            m &= m - 1;  // stays 0 once empty
+            if (g == grp) b = bg;
         }
-        if (i < N) woff[i] = carry + incl - v;
-        carry += __shfl(incl, WAVE - 1, WAVE);
+        bit[u] = b;
     }
-    if (lane == 0) woff[N] = carry;
+}
+
+// Wave-local compaction for the batch-1 down passes. A wave holds the products
+// of 64 consecutive units, one per lane; `m` marks the ones still to visit
+// (bit b = the unit of lane b). One round takes the next RPI * UF of them in
+// ascending order, the g-th of every RPI going to lane group g, so all row
+// loads of a round are issued together. A unit's product is read from its own
+// lane with a wave-uniform lane index: no LDS list, prefix sum or barrier sits
+// between the products and the row loads. bit[u] = -1 once the units run out.
+template <int RPI, int UF>
+__device__ inline void next_live_round(uint64_t& m, float ar, int grp, int (&bit)[UF],
+                                       float (&av)[UF]) {
+#pragma unroll
+    for (int u = 0; u < UF; ++u) {
+        int b = -1;
+        float v = 0.0f;
+#pragma unroll
+        for (int g = 0; g < RPI; ++g) {
+            const int bg = m ? (int)__builtin_ctzll(m) : -1;
+            m &= m - 1;  // stays 0 once empty
+            const float vg = bg >= 0 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ar), bg))
+                                     : 0.0f;
+            if (g == grp) {
+                b = bg;
+                v = vg;
+            }
+        }
+        bit[u] = b;
+        av[u] = v;
+    }
+}
+
+// Column slice of y for the XCD-contiguous order of the down grids: the blocks
+// dispatched to one XCD (block index mod 8) take consecutive slices.
+__device__ inline int xcd_slice(int bx, int nslices) {
+    const int per_xcd = (nslices + 7) / 8;
+    return (bx & 7) * per_xcd + (bx >> 3);
 }
 
 // Down projection for one token: y[slice] = sum_i a_i W2T[i, slice].
-// Grid = (column slices, remapped XCD-contiguous) x (row splits S). Every
-// thread first loads its share of a (one round trip for the whole vector),
-// the nonzero a_i are compacted into LDS with a ballot + prefix, and the W2T
-// row slices of all of them are loaded UF at a time per lane. With S > 1 each
-// block covers H/S units and adds its partial slice to y (cleared by the gate
-// pass); with S == 1 it stores. dense != 0 keeps every unit.
+// Grid = (column slices of 256 columns: 32 lanes x 8 bf16, XCD-contiguous) x
+// (row splits S). Wave w of a block owns the 64 * PMAX consecutive units
+// h0 + 64 * (w * PMAX + p) + lane of its split; all of its products are loaded
+// in one round, then its nonzero ones (every unit when dense) are visited by
+// next_live_round, two W2T row slices per wave instruction and 8 per lane in
+// flight. The 8 waves' slices are summed in LDS; with S > 1 the block adds its
+// slice to y (cleared by the gate pass), with S == 1 it stores.
 constexpr int KD_THREADS = 512;
 constexpr int KD_WAVES = KD_THREADS / WAVE;
-constexpr int KD_LCAP = 4096;  // compacted entries held in LDS at once
-template <int LPR, int PMAX>
+template <int PMAX>
 __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict__ a,
                                                         const uint16_t* __restrict__ W2T,
                                                         float* __restrict__ y, int D, int H,
                                                         int splits, int dense) {
+    constexpr int LPR = 32;
     constexpr int VEC = 8;
     constexpr int CB = LPR * VEC;
     constexpr int RPI = WAVE / LPR;
     constexpr int UF = 8;
-    __shared__ int list[KD_LCAP];
-    __shared__ float av[KD_LCAP];
-    __shared__ int wcount[PMAX * KD_WAVES];   // kept entries per (row group p, wave)
-    __shared__ int woff[PMAX * KD_WAVES + 1]; // exclusive prefix of wcount in (p, wave) order
     __shared__ float red[KD_WAVES][CB];
 
-    const int nslices = (D + CB - 1) / CB;
-    const int per_xcd = (nslices + 7) / 8;
-    const int bx = blockIdx.x;
-    const int slice = (bx & 7) * per_xcd + (bx >> 3);
-    if (slice >= nslices) return;
+    const int slice = xcd_slice(blockIdx.x, (D + CB - 1) / CB);
+    if (slice * CB >= D) return;
     const int col0 = slice * CB;
     const int hs = (H + splits - 1) / splits;
     const int h0 = blockIdx.y * hs;
@@ -859,69 +867,34 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
     const int sub = lane % LPR, grp = lane / LPR;
     const int col = col0 + sub * VEC;
     const bool col_ok = col < D;
-    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
 
     float ar[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        ar[p] = (p < P && row < h1) ? a[row] : 0.0f;
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        ar[p] = row < h1 ? a[row] : 0.0f;
     }
-    uint64_t mk[PMAX];
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
-        mk[p] = __ballot(keep);
-        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
-    }
-    __syncthreads();
-    // exclusive prefix of the (p, wave) counts, by wave 0
-    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
-    __syncthreads();
-
     float acc[VEC];
 #pragma unroll
     for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
-
-    int p0 = 0;
-    while (p0 < P) {
-        // greedy chunk of row groups whose entries fit the LDS list
-        int p1 = p0 + 1;
-        while (p1 < P && woff[p1 * KD_WAVES] - woff[p0 * KD_WAVES] + 
-                         (woff[(p1 + 1) * KD_WAVES] - woff[p1 * KD_WAVES]) <= KD_LCAP)
-            ++p1;
-        const int ebase = woff[p0 * KD_WAVES];
-        const int n = woff[p1 * KD_WAVES] - ebase;
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
-                const int pos = woff[p * KD_WAVES + wave] - ebase +
-                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-                av[pos] = ar[p];
-            }
-        }
-        __syncthreads();
-        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
+        while (m) {
+            int bit[UF];
+            float av[UF];
+            next_live_round<RPI, UF>(m, ar[p], grp, bit, av);
             u32x4 wv[UF];
 #pragma unroll
-            for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)list[e] * D + col)
-                                          : u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int u = 0; u < UF; ++u)
+                wv[u] = (bit[u] >= 0 && col_ok) ? load_stream(W2T + (size_t)(base + bit[u]) * D + col)
+                                                : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const float aval = e < n ? av[e] : 0.0f;
+            for (int u = 0; u < UF; ++u)
 #pragma unroll
-                for (int k = 0; k < VEC; ++k) acc[k] = fmaf(aval, Elem<uint16_t>::get(wv[u], k), acc[k]);
-            }
+                for (int k = 0; k < VEC; ++k) acc[k] = fmaf(av[u], Elem<uint16_t>::get(wv[u], k), acc[k]);
         }
-        __syncthreads();
-        p0 = p1;
     }
 #pragma unroll
     for (int k = 0; k < VEC; ++k) {
@@ -936,6 +909,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
     __syncthreads();
     for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
         float s = 0.0f;
+#pragma unroll
         for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
         if (col0 + c < D) {
             if (splits > 1)
@@ -947,18 +921,14 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Batch-1 fused pass: gate, compaction, gathered W3 dot and W2T accumulation
-// in one block per group of consecutive units (about one block per CU).
-//
-// Each of the 8 waves owns up to RW units and issues all of their W1 loads
-// before any arithmetic. The live units of the block (z > 0 on the fp32
-// accumulator) are compacted into LDS by wave 0 (ballot + mbcnt); the waves
-// then take them two at a time and load the W3 row and the W2T row of each
-// together, so the up and down reads of a live unit cost one round trip. Each
-// lane keeps the slice of y that matches its slice of x in registers; the
-// waves' slices are summed into LDS and the block writes one partial y of D
-// floats. k_reduce_partials adds the partials. DENSE visits every unit (the
-// dense comparator: W1, W3 and W2T rows of every unit, one pass).
+// Batch-1 dense comparator in one pass: one block per group of consecutive
+// units (about one block per two CUs). Each wave reads the W1, W3 and W2T rows
+// of its units together (the merged gate/up pass of the FFN tutorial, section
+// 9.2 case 3, with the down rows in the same round), so the dense FFN costs one
+// streaming pass over its 3HD weights. Each lane keeps the slice of y that
+// matches its slice of x in registers; the waves' slices are summed in LDS and
+// the block writes one partial y of D floats; k_reduce_partials adds the
+// partials.
 constexpr int KF_THREADS = 512;
 constexpr int KF_WAVES = KF_THREADS / WAVE;
 constexpr int KF_DMAX = 4096;
@@ -988,16 +958,12 @@ __device__ inline float dot_row(const u32x4 (&w)[NC], const u32x4 (&xv)[NC]) {
     return s;
 }
 
-template <int NC, int RW, bool DENSE>
-__global__ __launch_bounds__(KF_THREADS) void k_ffn_t1(
+template <int NC, int RW>
+__global__ __launch_bounds__(KF_THREADS) void k_ffn_dense_t1(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W3, const uint16_t* __restrict__ W2T,
-    float* __restrict__ part, uint8_t* __restrict__ live_out, int D, int H, int rows_per_block,
-    int act) {
+    float* __restrict__ part, int D, int H, int rows_per_block, int act) {
     extern __shared__ float ywave[];  // [KF_WAVES][D]: each wave's slice of y
-    __shared__ float zs[KF_WAVES * RW];
-    __shared__ int list[KF_WAVES * RW];
-    __shared__ int nlist;
     const int lane = threadIdx.x & (WAVE - 1);
     const int wave = threadIdx.x / WAVE;
     const int row0 = blockIdx.x * rows_per_block;
@@ -1015,86 +981,36 @@ __global__ __launch_bounds__(KF_THREADS) void k_ffn_t1(
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[c][k] = 0.0f;
 
-    int nwaves_acc;  // waves 0 .. nwaves_acc-1 hold a y slice
-    if constexpr (DENSE) {
-        // every unit: W1, W3 and W2T rows together, one unit at a time per wave
-        for (int r = 0; r < RW; ++r) {
-            const int rl = wave * RW + r;
-            const bool ok = rl < nrows;
-            const size_t off = (size_t)(row0 + rl) * D;
-            u32x4 w1[NC], w3[NC], w2[NC];
-            load_row<NC>(w1, W1 + off, D, lane, ok);
-            load_row<NC>(w3, W3 + off, D, lane, ok);
-            load_row<NC>(w2, W2T + off, D, lane, ok);
-            const float z = wave_sum_dpp(dot_row<NC>(w1, xv));
-            const float u = wave_sum_dpp(dot_row<NC>(w3, xv));
-            const float a = ok ? activation(act, z) * u : 0.0f;
-            axpy_chunks<NC>(acc, a, w2);
-        }
-        nwaves_acc = KF_WAVES;
-    } else {
-        u32x4 w[RW][NC];
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int rl = wave * RW + r;
-            load_row<NC>(w[r], W1 + (size_t)(row0 + rl) * D, D, lane, rl < nrows);
-        }
-#pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const float z = wave_sum_dpp(dot_row<NC>(w[r], xv));
-            const int rl = wave * RW + r;
-            if (lane == 0 && rl < nrows) zs[rl] = z;
-        }
-        __syncthreads();
-        if (wave == 0) {
-            const bool in = lane < nrows;
-            const bool live = in && zs[lane] > 0.0f;
-            const uint64_t m = __ballot(live);
-            const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
-            if (live) list[pos] = lane;
-            if (lane == 0) nlist = __popcll(m);
-            if (in && live_out) live_out[row0 + lane] = live ? 1 : 0;
-        }
-        __syncthreads();
-        const int n = nlist;
-        // live units two at a time per wave: W3 and W2T rows of both in flight together
-        for (int e = wave; e < n; e += 2 * KF_WAVES) {
-            const int e2 = e + KF_WAVES;
-            const bool ok2 = e2 < n;
-            const int ra = list[e], rb = ok2 ? list[e2] : ra;
-            u32x4 w3a[NC], w2a[NC], w3b[NC], w2b[NC];
-            load_row<NC>(w3a, W3 + (size_t)(row0 + ra) * D, D, lane, true);
-            load_row<NC>(w2a, W2T + (size_t)(row0 + ra) * D, D, lane, true);
-            load_row<NC>(w3b, W3 + (size_t)(row0 + rb) * D, D, lane, ok2);
-            load_row<NC>(w2b, W2T + (size_t)(row0 + rb) * D, D, lane, ok2);
-            const float ua = wave_sum_dpp(dot_row<NC>(w3a, xv));
-            const float ub = wave_sum_dpp(dot_row<NC>(w3b, xv));
-            const float aa = activation(act, zs[ra]) * ua;
-            const float ab = ok2 ? activation(act, zs[rb]) * ub : 0.0f;
-            axpy_chunks<NC>(acc, aa, w2a);
-            axpy_chunks<NC>(acc, ab, w2b);
-        }
-        nwaves_acc = min(n, KF_WAVES);
+    // every unit: W1, W3 and W2T rows together, one unit at a time per wave
+    for (int r = 0; r < RW; ++r) {
+        const int rl = wave * RW + r;
+        const bool ok = rl < nrows;
+        const size_t off = (size_t)(row0 + rl) * D;
+        u32x4 w1[NC], w3[NC], w2[NC];
+        load_row<NC>(w1, W1 + off, D, lane, ok);
+        load_row<NC>(w3, W3 + off, D, lane, ok);
+        load_row<NC>(w2, W2T + off, D, lane, ok);
+        const float z = wave_sum_dpp(dot_row<NC>(w1, xv));
+        const float u = wave_sum_dpp(dot_row<NC>(w3, xv));
+        const float a = ok ? activation(act, z) * u : 0.0f;
+        axpy_chunks<NC>(acc, a, w2);
     }
-    // waves with a y slice store it to LDS (16-byte stores, conflict-free),
-    // then every thread sums 8 columns over those waves and writes the partial
-    if (wave < nwaves_acc) {
+    // each wave stores its y slice to LDS (16-byte stores, conflict-free), then
+    // every thread sums 8 columns over the waves and writes the partial
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-            const int col = c * WAVE * 8 + lane * 8;
-            if (col < D) {
-                float4* dst = reinterpret_cast<float4*>(ywave + (size_t)wave * D + col);
-                dst[0] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
-                dst[1] = make_float4(acc[c][4], acc[c][5], acc[c][6], acc[c][7]);
-            }
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * WAVE * 8 + lane * 8;
+        if (col < D) {
+            float4* dst = reinterpret_cast<float4*>(ywave + (size_t)wave * D + col);
+            dst[0] = make_float4(acc[c][0], acc[c][1], acc[c][2], acc[c][3]);
+            dst[1] = make_float4(acc[c][4], acc[c][5], acc[c][6], acc[c][7]);
         }
     }
     __syncthreads();
     float* pb = part + (size_t)blockIdx.x * D;
     for (int j = threadIdx.x * 8; j < D; j += KF_THREADS * 8) {
         float4 s0 = make_float4(0.f, 0.f, 0.f, 0.f), s1 = s0;
-        for (int w2 = 0; w2 < nwaves_acc; ++w2) {
+        for (int w2 = 0; w2 < KF_WAVES; ++w2) {
             const float4* src = reinterpret_cast<const float4*>(ywave + (size_t)w2 * D + j);
             const float4 a0 = src[0], a1 = src[1];
             s0.x += a0.x; s0.y += a0.y; s0.z += a0.z; s0.w += a0.w;
@@ -1412,108 +1328,11 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
     }
 }
 
-// Down projection, int8 W2T rows: y[slice] = sum_i a'_i q2[i, slice] with
-// a'_i = a_i s2_i from the gate pass. As k_down_t1: grid = (column slices of
-// 16 lanes x 16 columns = 256 columns, XCD-contiguous order) x (row splits);
-// each block loads its share of a' in one round, compacts the nonzero entries
-// in LDS (all units when dense) and accumulates 8 row slices in flight per
-// lane; with splits > 1 it adds its slice into y (cleared by the gate pass).
-template <int PMAX>
-__global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restrict__ a,
-                                                           const int8_t* __restrict__ W2T,
-                                                           float* __restrict__ y, int D, int H,
-                                                           int splits, int dense) {
-    constexpr int LPR = 16;
-    constexpr int CB = LPR * 16;
-    constexpr int RPI = WAVE / LPR;
-    constexpr int UF = 8;
-    __shared__ int list[KD_LCAP];
-    __shared__ float av[KD_LCAP];
-    __shared__ int wcount[PMAX * KD_WAVES];
-    __shared__ int woff[PMAX * KD_WAVES + 1];
-    __shared__ float red[KD_WAVES][CB];
-
-    const int nslices = (D + CB - 1) / CB;
-    const int per_xcd = (nslices + 7) / 8;
-    const int bx = blockIdx.x;
-    const int slice = (bx & 7) * per_xcd + (bx >> 3);
-    if (slice >= nslices) return;
-    const int col0 = slice * CB;
-    const int hs = (H + splits - 1) / splits;
-    const int h0 = blockIdx.y * hs;
-    const int h1 = min(H, h0 + hs);
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int wave = threadIdx.x / WAVE;
-    const int sub = lane % LPR, grp = lane / LPR;
-    const int col = col0 + sub * 16;
-    const bool col_ok = col < D;
-    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
-
-    float ar[PMAX];
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        ar[p] = (p < P && row < h1) ? a[row] : 0.0f;
-    }
-    uint64_t mk[PMAX];
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
-        mk[p] = __ballot(keep);
-        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
-    }
-    __syncthreads();
-    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
-    __syncthreads();
-
-    float acc[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-    int p0 = 0;
-    while (p0 < P) {
-        int p1 = p0 + 1;
-        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
-        const int ebase = woff[p0 * KD_WAVES];
-        const int n = woff[p1 * KD_WAVES] - ebase;
-#pragma unroll
-        for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
-                const int pos = woff[p * KD_WAVES + wave] - ebase +
-                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-                av[pos] = ar[p];
-            }
-        }
-        __syncthreads();
-        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
-            u32x4 wv[UF];
-#pragma unroll
-            for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)list[e] * D + col)
-                                          : u32x4{0u, 0u, 0u, 0u};
-            }
-#pragma unroll
-            for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const float aval = e < n ? av[e] : 0.0f;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wq = wv[u][q];
-#pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        acc[4 * q + b] = fmaf(aval, (float)((int)(wq << (24 - 8 * b)) >> 24), acc[4 * q + b]);
-                }
-            }
-        }
-        __syncthreads();
-        p0 = p1;
-    }
-    // sum over the 4 row groups of a wave as a reduce-scatter (lanes 32 and 16
-    // apart): each lane ends with 4 whole columns of its 16 (12 shuffles, not 32)
-    static_assert(LPR == 16, "two halving exchanges over 4 row groups");
+// Sum over the 4 row groups (16 lanes each) of a wave as a reduce-scatter
+// (lanes 32 and 16 apart): each lane ends with 4 whole columns of its 16 in
+// acc[0..3] (12 shuffles instead of 32), then stores them to its wave's row of
+// red at the columns it owns.
+__device__ inline void rowgroup4_reduce_scatter(float (&acc)[16], float* red_row, int lane) {
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
         const int o = 32 >> st, half = 8 >> st;
@@ -1525,12 +1344,79 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
             acc[k] = keep + __shfl_xor(upper ? lo : hi, o, WAVE);
         }
     }
+    const int sub = lane % 16;
     const int cpart = 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) red[wave][sub * 16 + cpart + k] = acc[k];
+    for (int k = 0; k < 4; ++k) red_row[sub * 16 + cpart + k] = acc[k];
+}
+
+// Down projection, int8 W2T rows: y[slice] = sum_i a'_i q2[i, slice] with
+// a'_i = a_i s2_i from the gate pass. As k_down_t1 (wave-local compaction),
+// with column slices of 16 lanes x 16 int8 columns = 256 columns, so a wave
+// instruction covers 4 rows and a lane keeps 8 rows in flight.
+template <int PMAX>
+__global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restrict__ a,
+                                                           const int8_t* __restrict__ W2T,
+                                                           float* __restrict__ y, int D, int H,
+                                                           int splits, int dense) {
+    constexpr int LPR = 16;
+    constexpr int CB = LPR * 16;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 8;
+    __shared__ float red[KD_WAVES][CB];
+
+    const int slice = xcd_slice(blockIdx.x, (D + CB - 1) / CB);
+    if (slice * CB >= D) return;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * 16;
+    const bool col_ok = col < D;
+
+    float ar[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        ar[p] = row < h1 ? a[row] : 0.0f;
+    }
+    float acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
+        while (m) {
+            int bit[UF];
+            float av[UF];
+            next_live_round<RPI, UF>(m, ar[p], grp, bit, av);
+            u32x4 wv[UF];
+#pragma unroll
+            for (int u = 0; u < UF; ++u)
+                wv[u] = (bit[u] >= 0 && col_ok) ? load_stream(W2T + (size_t)(base + bit[u]) * D + col)
+                                                : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const uint32_t wq = wv[u][q];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+                        acc[4 * q + b] = fmaf(av[u], (float)((int)(wq << (24 - 8 * b)) >> 24), acc[4 * q + b]);
+                }
+            }
+        }
+    }
+    static_assert(LPR == 16, "two halving exchanges over 4 row groups");
+    rowgroup4_reduce_scatter(acc, red[wave], lane);
     __syncthreads();
     for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
         float s = 0.0f;
+#pragma unroll
         for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
         if (col0 + c < D) {
             if (splits > 1)
@@ -1760,17 +1646,10 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
     constexpr int CB = LPR * 16;
     constexpr int RPI = WAVE / LPR;
     constexpr int UF = 8;
-    __shared__ int list[KD_LCAP];
-    __shared__ float av[KD_LCAP];
-    __shared__ int wcount[PMAX * KD_WAVES];
-    __shared__ int woff[PMAX * KD_WAVES + 1];
     __shared__ float red[KD_WAVES][CB];
 
-    const int nslices = (D + CB - 1) / CB;
-    const int per_xcd = (nslices + 7) / 8;
-    const int bx = blockIdx.x;
-    const int slice = (bx & 7) * per_xcd + (bx >> 3);
-    if (slice >= nslices) return;
+    const int slice = xcd_slice(blockIdx.x, (D + CB - 1) / CB);
+    if (slice * CB >= D) return;
     const int col0 = slice * CB;
     const int hs = (H + splits - 1) / splits;
     const int h0 = blockIdx.y * hs;
@@ -1782,62 +1661,37 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
     const bool col_ok = col < D;
     const int G = D / I4_GROUP;
     const size_t rb = (size_t)D / 2;
-    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
 
     float ar[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        ar[p] = (p < P && row < h1) ? a[row] : 0.0f;
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        ar[p] = row < h1 ? a[row] : 0.0f;
     }
-    uint64_t mk[PMAX];
-#pragma unroll
-    for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        const bool keep = p < P && row < h1 && (dense || ar[p] != 0.0f);
-        mk[p] = __ballot(keep);
-        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
-    }
-    __syncthreads();
-    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
-    __syncthreads();
-
     float acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
-    int p0 = 0;
-    while (p0 < P) {
-        int p1 = p0 + 1;
-        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
-        const int ebase = woff[p0 * KD_WAVES];
-        const int n = woff[p1 * KD_WAVES] - ebase;
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
-                const int pos = woff[p * KD_WAVES + wave] - ebase +
-                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-                av[pos] = ar[p];
-            }
-        }
-        __syncthreads();
-        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
+        while (m) {
+            int bit[UF];
+            float av[UF];
+            next_live_round<RPI, UF>(m, ar[p], grp, bit, av);
             u32x2 wv[UF];
             float sg[UF];
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const bool ok = e < n && col_ok;
-                const int row = ok ? list[e] : 0;
-                wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + (size_t)row * rb + col / 2))
+                const bool ok = bit[u] >= 0 && col_ok;
+                const size_t row = (size_t)(base + (ok ? bit[u] : 0));
+                wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + row * rb + col / 2))
                            : u32x2{0u, 0u};
-                sg[u] = ok ? s2[(size_t)row * G + col / I4_GROUP] : 0.0f;
+                sg[u] = ok ? s2[row * G + col / I4_GROUP] : 0.0f;
             }
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const float aval = (e < n ? av[e] : 0.0f) * sg[u];
+                const float aval = av[u] * sg[u];
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     const uint32_t wq = wv[u][q];
@@ -1847,29 +1701,13 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
                 }
             }
         }
-        __syncthreads();
-        p0 = p1;
     }
-    // sum over the 4 row groups of a wave as a reduce-scatter (lanes 32 and 16
-    // apart): each lane ends with 4 whole columns of its 16 (12 shuffles)
     static_assert(LPR == 16, "two halving exchanges over 4 row groups");
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-        const int o = 32 >> st, half = 8 >> st;
-        const bool upper = (lane & o) != 0;
-#pragma unroll
-        for (int k = 0; k < half; ++k) {
-            const float lo = acc[k], hi = acc[k + half];
-            const float keep = upper ? hi : lo;
-            acc[k] = keep + __shfl_xor(upper ? lo : hi, o, WAVE);
-        }
-    }
-    const int cpart = 8 * ((lane >> 5) & 1) + 4 * ((lane >> 4) & 1);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) red[wave][sub * 16 + cpart + k] = acc[k];
+    rowgroup4_reduce_scatter(acc, red[wave], lane);
     __syncthreads();
     for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
         float s = 0.0f;
+#pragma unroll
         for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
         if (col0 + c < D) {
             if (splits > 1)
@@ -2624,9 +2462,6 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
     constexpr int CB = LPR * VEC;
     constexpr int RPI = WAVE / LPR;
     constexpr int UF = 4;
-    __shared__ int list[KD_LCAP];
-    __shared__ int wcount[PMAX * KD_WAVES];
-    __shared__ int woff[PMAX * KD_WAVES + 1];
     __shared__ float red[TT < 4 ? TT : 4][KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
@@ -2643,19 +2478,12 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
     const int sub = lane % LPR, grp = lane / LPR;
     const int col = col0 + sub * VEC;
     const bool col_ok = col < D;
-    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;
-
     uint64_t mk[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        const bool keep = p < P && row < h1 && umask[row] != 0ull;
-        mk[p] = __ballot(keep);
-        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        mk[p] = __ballot(row < h1 && umask[row] != 0ull);
     }
-    __syncthreads();
-    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
-    __syncthreads();
 
     float acc[TT][VEC];
 #pragma unroll
@@ -2663,36 +2491,26 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[t][k] = 0.0f;
 
-    int p0 = 0;
-    while (p0 < P) {
-        int p1 = p0 + 1;
-        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
-        const int ebase = woff[p0 * KD_WAVES];
-        const int n = woff[p1 * KD_WAVES] - ebase;
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
-                const int pos = woff[p * KD_WAVES + wave] - ebase +
-                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-            }
-        }
-        __syncthreads();
-        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = mk[p];
+        while (m) {
+            int bit[UF];
+            next_live_bits<RPI, UF>(m, grp, bit);
             u32x4 wv[UF];
             float av[UF][TT];
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const int row = e < n ? list[e] : 0;
-                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)row * D + col)
+                const bool e_ok = bit[u] >= 0;
+                const int row = e_ok ? (base + bit[u]) : 0;
+                wv[u] = (e_ok && col_ok) ? load_stream(W2T + (size_t)row * D + col)
                                           : u32x4{0u, 0u, 0u, 0u};
                 // TT <= 16 <= tp, and padded token slots of a_rm hold 0
                 const float* ar = a_rm + (size_t)row * tp;
 #pragma unroll
                 for (int t = 0; t < TT; t += 2) {
-                    const float2 v2 = e < n ? *reinterpret_cast<const float2*>(ar + t)
+                    const float2 v2 = e_ok ? *reinterpret_cast<const float2*>(ar + t)
                                             : make_float2(0.0f, 0.0f);
                     av[u][t] = v2.x;
                     av[u][t + 1] = v2.y;
@@ -2707,8 +2525,6 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb(const float* __restrict_
                     for (int t = 0; t < TT; ++t) acc[t][k] = fmaf(av[u][t], w, acc[t][k]);
                 }
         }
-        __syncthreads();
-        p0 = p1;
     }
     tb_down_epilogue<TT, (TT < 4 ? TT : 4), VEC, LPR, CB>(acc, red, y, D, T, col0, splits, wave, sub, grp);
 }
@@ -2853,9 +2669,6 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
     constexpr int CB = LPR * VEC;
     constexpr int RPI = WAVE / LPR;
     constexpr int UF = 4;
-    __shared__ int list[KD_LCAP];
-    __shared__ int wcount[PMAX * KD_WAVES];
-    __shared__ int woff[PMAX * KD_WAVES + 1];
     __shared__ float red[TT < 4 ? TT : 4][KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
@@ -2872,19 +2685,12 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
     const int sub = lane % LPR, grp = lane / LPR;
     const int col = col0 + sub * VEC;
     const bool col_ok = col < D;
-    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
-
     uint64_t mk[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        const bool keep = p < P && row < h1 && umask[row] != 0ull;
-        mk[p] = __ballot(keep);
-        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        mk[p] = __ballot(row < h1 && umask[row] != 0ull);
     }
-    __syncthreads();
-    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
-    __syncthreads();
 
     float acc[TT][VEC];
 #pragma unroll
@@ -2892,36 +2698,26 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[t][k] = 0.0f;
 
-    int p0 = 0;
-    while (p0 < P) {
-        int p1 = p0 + 1;
-        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
-        const int ebase = woff[p0 * KD_WAVES];
-        const int n = woff[p1 * KD_WAVES] - ebase;
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
-                const int pos = woff[p * KD_WAVES + wave] - ebase +
-                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-            }
-        }
-        __syncthreads();
-        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = mk[p];
+        while (m) {
+            int bit[UF];
+            next_live_bits<RPI, UF>(m, grp, bit);
             u32x4 wv[UF];
             float av[UF][TT];
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const int row = e < n ? list[e] : 0;
-                wv[u] = (e < n && col_ok) ? load_stream(W2T + (size_t)row * D + col)
+                const bool e_ok = bit[u] >= 0;
+                const int row = e_ok ? (base + bit[u]) : 0;
+                wv[u] = (e_ok && col_ok) ? load_stream(W2T + (size_t)row * D + col)
                                           : u32x4{0u, 0u, 0u, 0u};
                 // TT <= 16 <= tp, and padded token slots of a_rm hold 0
                 const float* ar = a_rm + (size_t)row * tp;
 #pragma unroll
                 for (int t = 0; t < TT; t += 2) {
-                    const float2 v2 = e < n ? *reinterpret_cast<const float2*>(ar + t)
+                    const float2 v2 = e_ok ? *reinterpret_cast<const float2*>(ar + t)
                                             : make_float2(0.0f, 0.0f);
                     av[u][t] = v2.x;
                     av[u][t + 1] = v2.y;
@@ -2940,8 +2736,6 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i8(const float* __restri
                     }
                 }
         }
-        __syncthreads();
-        p0 = p1;
     }
     tb_down_epilogue<TT, (TT < 4 ? TT : 4), VEC, LPR, CB>(acc, red, y, D, T, col0, splits, wave, sub, grp);
 }
@@ -3063,9 +2857,6 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
     constexpr int CB = LPR * VEC;
     constexpr int RPI = WAVE / LPR;
     constexpr int UF = 4;
-    __shared__ int list[KD_LCAP];
-    __shared__ int wcount[PMAX * KD_WAVES];
-    __shared__ int woff[PMAX * KD_WAVES + 1];
     __shared__ float red[TT < 4 ? TT : 4][KD_WAVES][CB];
 
     const int nslices = (D + CB - 1) / CB;
@@ -3084,19 +2875,12 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
     const bool col_ok = col < D;
     const int G = D / I4_GROUP;
     const size_t rb = (size_t)D / 2;
-    const int P = (h1 - h0 + KD_THREADS - 1) / KD_THREADS;  // <= PMAX (host-checked)
-
     uint64_t mk[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
-        const int row = h0 + p * KD_THREADS + threadIdx.x;
-        const bool keep = p < P && row < h1 && umask[row] != 0ull;
-        mk[p] = __ballot(keep);
-        if (lane == 0) wcount[p * KD_WAVES + wave] = __popcll(mk[p]);
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        mk[p] = __ballot(row < h1 && umask[row] != 0ull);
     }
-    __syncthreads();
-    if (wave == 0) counts_exclusive_prefix<PMAX * KD_WAVES>(wcount, woff, lane);
-    __syncthreads();
 
     float acc[TT][VEC];
 #pragma unroll
@@ -3104,30 +2888,20 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
 #pragma unroll
         for (int k = 0; k < VEC; ++k) acc[t][k] = 0.0f;
 
-    int p0 = 0;
-    while (p0 < P) {
-        int p1 = p0 + 1;
-        while (p1 < P && woff[(p1 + 1) * KD_WAVES] - woff[p0 * KD_WAVES] <= KD_LCAP) ++p1;
-        const int ebase = woff[p0 * KD_WAVES];
-        const int n = woff[p1 * KD_WAVES] - ebase;
 #pragma unroll
-        for (int p = 0; p < PMAX; ++p) {
-            if (p >= p0 && p < p1 && ((mk[p] >> lane) & 1ull)) {
-                const int pos = woff[p * KD_WAVES + wave] - ebase +
-                                __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
-                                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
-                list[pos] = h0 + p * KD_THREADS + threadIdx.x;
-            }
-        }
-        __syncthreads();
-        for (int e0 = wave * RPI + grp; e0 < n; e0 += KD_WAVES * RPI * UF) {
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = mk[p];
+        while (m) {
+            int bit[UF];
+            next_live_bits<RPI, UF>(m, grp, bit);
             u32x2 wv[UF];
             float av[UF][TT];
 #pragma unroll
             for (int u = 0; u < UF; ++u) {
-                const int e = e0 + u * KD_WAVES * RPI;
-                const bool ok = e < n && col_ok;
-                const int row = e < n ? list[e] : 0;
+                const bool e_ok = bit[u] >= 0;
+                const bool ok = e_ok && col_ok;
+                const int row = e_ok ? (base + bit[u]) : 0;
                 wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + (size_t)row * rb + col / 2))
                            : u32x2{0u, 0u};
                 const float sg = ok ? s2[(size_t)row * G + col / I4_GROUP] : 0.0f;
@@ -3135,7 +2909,7 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
                 const float* ar = a_rm + (size_t)row * tp;
 #pragma unroll
                 for (int t = 0; t < TT; t += 2) {
-                    const float2 v2 = e < n ? *reinterpret_cast<const float2*>(ar + t)
+                    const float2 v2 = e_ok ? *reinterpret_cast<const float2*>(ar + t)
                                             : make_float2(0.0f, 0.0f);
                     av[u][t] = v2.x * sg;
                     av[u][t + 1] = v2.y * sg;
@@ -3154,8 +2928,6 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_tb_i4(const float* __restri
                     }
                 }
         }
-        __syncthreads();
-        p0 = p1;
     }
     tb_down_epilogue<TT, (TT < 4 ? TT : 4), VEC, LPR, CB>(acc, red, y, D, T, col0, splits, wave, sub, grp);
 }

@@ -132,38 +132,15 @@ sffn_status sffn_create(sffn_handle **out, int D, int H, int r, int max_tokens, 
                         int dtype, unsigned flags);
 
 /*
- * Launch-plan overrides. sffn_create reads these environment variables once,
- * for measurement sweeps; unset (the normal case) each takes the measured
- * default given in brackets, and a value outside the accepted set is ignored.
- * They choose launch shapes and which kernels run, never the mathematics: the
- * result changes only by rounding (summation order, and where a path rounds
- * the unit products for its MFMA operands, as described under Requirements).
- *   batch 1:  SFFN_T1_ROWS_PER_WAVE [1] and SFFN_T1_LOPA_ROWS_PER_WAVE [2]
- *             (units per wave of the gate pass: 1, 2, 4), SFFN_T1_LOPA_I8_UPW [2]
- *             (units per wave of the int8 LoPA gate: 2 for r <= 1024, or 4),
- *             SFFN_T1_LANES_PER_ROW
- *             [32] (lanes per W2T row slice of the down pass: 4, 8, 16, 32),
- *             SFFN_T1_SPLITS_SPARSE [16] and SFFN_T1_SPLITS_DENSE [16] (unit
- *             ranges of the down pass), SFFN_T1_FUSED_SPARSE [0] and
- *             SFFN_T1_FUSED_DENSE [1] (one fused pass plus a partial-sum
- *             reduction instead of gate + down), SFFN_T1_BLOCKS [128] (blocks
- *             of that fused pass).
- *   2..64 tokens (bf16): SFFN_TBV_MAX [4] (largest batch on the VALU gate
- *             pass), SFFN_TBV_RW2 [2] and SFFN_TBV_RW4 [4] (its units per wave),
- *             SFFN_TB_MAX [4] (largest batch on the VALU down pass, <= 8),
- *             SFFN_TB_SPLITS [16] and SFFN_MFMA_SPLITS [16] (unit ranges of the
- *             VALU and MFMA down passes), SFFN_MFMA_UT1 [1], SFFN_MFMA_UT2 [2],
- *             SFFN_MFMA_UT4 [2] (16-unit tiles per MFMA gate block for up to
- *             16, 32 and 64 tokens).
- *   int8 and int4 groups of 2..4 tokens: SFFN_TB_RW_I8 [2] (units per wave
- *             of the union gate pass: 1, 2, 4 for int8; 1 or 2 for int4);
- *             SFFN_TB_SPLITS also sets the unit ranges of their down passes.
- *   above 64 tokens (bf16, r == 0): SFFN_GEMM_MIN_T [65] (smallest batch on the
- *             GEMM path), SFFN_GEMM_SPLITS [chosen per call] (unit ranges of the
- *             down GEMM), SFFN_GEMM_WIDE_MIN [200] (256 x 128 gate tiles from
- *             this many tiles on, else 256 x 64).
- *   fp32 and per-token lists: SFFN_GATE_ROWS_PER_WAVE [up to 4],
- *             SFFN_DOWN_LANES_PER_ROW [8].
+ * Launch plan. sffn_create fixes it from the shape alone (no environment
+ * variable or other outside input takes part): the kernel of each step, its
+ * block shape and the unit-range splits of the down passes, with the constants
+ * chosen from measured sweeps on MI355X. It chooses data movement only, never
+ * the mathematics: results differ between plans only by rounding (summation
+ * order, and where a path rounds the unit products for its MFMA operands, as
+ * described under Requirements). sffn_create also clears the scratch that must
+ * start zeroed, on a private stream it waits for; it never synchronises the
+ * whole device.
  */
 
 /* Frees the handle and its scratch. NULL is ignored. The caller must make sure

@@ -298,32 +298,3 @@ int orc_ffn_lopa_full(int D, int H, int r, int act, int dtype, unsigned flags, c
     free(z);
     return k;
 }
-
-int orc_ffn_standard_batch(int T, int D, int H, int act, int dtype, const void *x,
-                           const void *W1, const void *W3, const void *W2T, int dense,
-                           double *y, double *z_out, int32_t *live_idx, int32_t *live_count) {
-    size_t esz = dtype == ORC_BF16 ? 2 : (dtype == ORC_F32 ? 4 : 8);
-    for (int t = 0; t < T; ++t) {
-        int k = orc_ffn_standard(D, H, act, dtype, (const char *)x + (size_t)t * D * esz, W1, W3,
-                                 W2T, dense, y + (size_t)t * D,
-                                 z_out ? z_out + (size_t)t * H : NULL, NULL,
-                                 live_idx ? live_idx + (size_t)t * H : NULL);
-        if (k < 0) return k;
-        if (live_count) live_count[t] = k;
-    }
-    return 0;
-}
-
-int orc_ffn_lopa_batch(int T, int D, int H, int r, int act, int dtype, const void *x,
-                       const void *V, const void *U, const void *W3, const void *W2T, int dense,
-                       double *y, double *z_out, int32_t *live_idx, int32_t *live_count) {
-    size_t esz = dtype == ORC_BF16 ? 2 : (dtype == ORC_F32 ? 4 : 8);
-    for (int t = 0; t < T; ++t) {
-        int k = orc_ffn_lopa(D, H, r, act, dtype, (const char *)x + (size_t)t * D * esz, V, U, W3,
-                             W2T, dense, y + (size_t)t * D, z_out ? z_out + (size_t)t * H : NULL,
-                             NULL, NULL, live_idx ? live_idx + (size_t)t * H : NULL);
-        if (k < 0) return k;
-        if (live_count) live_count[t] = k;
-    }
-    return 0;
-}
