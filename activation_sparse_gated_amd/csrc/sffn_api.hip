@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -1242,6 +1243,104 @@ sffn_status sffn_forward_sparse(sffn_handle* h, const void* x, const void* W1, c
         return dispatch_sparse(h, x, W1, W3, W2T, y, T, mode, live_count, live_idx, s);
     } catch (...) {
         return fail(h, SFFN_INTERNAL, "exception in sffn_forward_sparse");
+    }
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ no-allocation variant
+// Unit products of the batch-1 pass (the gate kernel's output, the down
+// kernel's input) for sffn_forward_sparse_noalloc. Each GPU the library runs
+// on holds one copy until the process ends; every call on that GPU uses it.
+constexpr int NOALLOC_MAX_H = 16384;
+static __device__ __align__(256) float scratch[NOALLOC_MAX_H];
+
+namespace {
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_dev[NOALLOC_MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device, looked up once per device
+// (the host-side name is only a stand-in for the symbol, not a device address).
+sffn_status scratch_address(int dev, float** out) {
+    if (dev < 0 || dev >= NOALLOC_MAX_DEVICES)
+        return fail(nullptr, SFFN_UNSUPPORTED, "device index beyond the no-allocation table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_dev[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(nullptr, SFFN_HIP_ERROR,
+                        std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+        g_scratch_dev[dev] = static_cast<float*>(p);
+    }
+    *out = g_scratch_dev[dev];
+    return SFFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+sffn_status sffn_forward_sparse_noalloc(const void* x, const void* W1, const void* W3,
+                                        const void* W2T, float* y, int D, int H, int T, int act,
+                                        void* stream) {
+    try {
+        if (!x || !W1 || !W3 || !W2T || !y)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "null tensor pointer");
+        if (!aligned16(x) || !aligned16(W1) || !aligned16(W3) || !aligned16(W2T) || !aligned16(y))
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "tensor pointers must be 16-byte aligned");
+        if (act != SFFN_ACT_RELU && act != SFFN_ACT_RSPLUS)
+            return fail(nullptr, SFFN_UNSUPPORTED, "unknown activation " + std::to_string(act));
+        if (D <= 0 || D % 8 != 0 || D > 64 * 8 * 8)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT, "D must be a positive multiple of 8, at most 4096");
+        if (H <= 0 || H > NOALLOC_MAX_H)
+            return fail(nullptr, SFFN_INVALID_ARGUMENT,
+                        "H=" + std::to_string(H) + " outside [1, " + std::to_string(NOALLOC_MAX_H) +
+                            "]: the static scratch holds the unit products of at most " +
+                            std::to_string(NOALLOC_MAX_H) + " units");
+        if (T < 0) return fail(nullptr, SFFN_INVALID_ARGUMENT, "T must be >= 0");
+        if (T == 0) return SFFN_OK;
+        int dev = -1;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return fail(nullptr, SFFN_HIP_ERROR, std::string("hipGetDevice: ") + hipGetErrorString(e));
+        float* a = nullptr;
+        sffn_status st = scratch_address(dev, &a);
+        if (st != SFFN_OK) return st;
+        hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+        const int nc = pick(kNC_T1, 7, chunks_needed(D, SFFN_BF16));
+        const int nb = (H + K1_WAVES - 1) / K1_WAVES;
+        constexpr int splits = 16;
+        const int nbx = (((D + 255) / 256 + 7) / 8) * 8;
+        const int hs = (H + splits - 1) / splits;  // <= 1024 units: PMAX 1 or 2
+        const size_t xb = (size_t)D * sizeof(uint16_t);
+        for (int t = 0; t < T; ++t) {
+            const void* xt = (const char*)x + t * xb;
+            float* yt = y + (size_t)t * D;
+            switch (nc) {
+                case 1: hipLaunchKernelGGL(k_gate_up_t1<1>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                case 2: hipLaunchKernelGGL(k_gate_up_t1<2>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                case 3: hipLaunchKernelGGL(k_gate_up_t1<3>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                case 4: hipLaunchKernelGGL(k_gate_up_t1<4>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                case 5: hipLaunchKernelGGL(k_gate_up_t1<5>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                case 6: hipLaunchKernelGGL(k_gate_up_t1<6>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                case 8: hipLaunchKernelGGL(k_gate_up_t1<8>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
+                default: return fail(nullptr, SFFN_INTERNAL, "no batch-1 kernel for this width");
+            }
+            if (hs <= KD_THREADS)
+                hipLaunchKernelGGL(k_down_t1<1>, dim3(nbx, splits), dim3(KD_THREADS), 0, s,
+                                   (const float*)a, (const uint16_t*)W2T, yt, D, H, splits, 0);
+            else
+                hipLaunchKernelGGL(k_down_t1<2>, dim3(nbx, splits), dim3(KD_THREADS), 0, s,
+                                   (const float*)a, (const uint16_t*)W2T, yt, D, H, splits, 0);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return fail(nullptr, SFFN_HIP_ERROR, std::string("launch: ") + hipGetErrorString(e));
+        }
+        return SFFN_OK;
+    } catch (...) {
+        return fail(nullptr, SFFN_INTERNAL, "exception in sffn_forward_sparse_noalloc");
     }
 }
 

@@ -31,7 +31,7 @@ EXPORTED = (
     "sffn_timing_enable", "sffn_timing_read", "sffn_kernel_kinds", "sffn_kernel_name",
     "sffn_forward_sparse_i8", "sffn_forward_dense_i8", "sffn_forward_moe",
     "sffn_forward_lopa_i8", "sffn_forward_sparse_i4", "sffn_forward_dense_i4",
-    "sffn_forward_lopa_i4",
+    "sffn_forward_lopa_i4", "sffn_forward_sparse_noalloc",
 )
 
 _lib = None
@@ -66,6 +66,8 @@ def load() -> ctypes.CDLL:
     lib.sffn_forward_dense.argtypes = [P, P, P, P, P, P, I, P]
     lib.sffn_forward_sparse.restype = I
     lib.sffn_forward_sparse.argtypes = [P, P, P, P, P, P, I, I, P, P, P]
+    lib.sffn_forward_sparse_noalloc.restype = I
+    lib.sffn_forward_sparse_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, P]
     lib.sffn_forward_lopa.restype = I
     lib.sffn_forward_lopa.argtypes = [P, P, P, P, P, P, P, I, I, P, P, P]
     lib.sffn_forward_sparse_i8.restype = I
@@ -171,6 +173,15 @@ def sffn_forward_sparse(handle, x, W1, W3, W2T, y, T: int, mode: int = SFFN_MODE
                                     mode, _ptr(live_count), _ptr(live_idx), _stream(stream))
     if check:
         _check(st, handle)
+    return st
+
+
+def sffn_forward_sparse_noalloc(x, W1, W3, W2T, y, D: int, H: int, T: int, act: int,
+                                stream=None, check: bool = True) -> int:
+    st = load().sffn_forward_sparse_noalloc(_ptr(x), _ptr(W1), _ptr(W3), _ptr(W2T), _ptr(y), D, H,
+                                            T, act, _stream(stream))
+    if check:
+        _check(st, None)
     return st
 
 

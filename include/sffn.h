@@ -173,6 +173,30 @@ sffn_status sffn_forward_sparse(sffn_handle *h, const void *x, const void *W1, c
                                 int32_t *live_idx, void *stream);
 
 /*
+ * The batch-1 sparse forward of sffn_forward_sparse (standard gating, bf16
+ * weights, fp32 accumulation) for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. It takes no handle and allocates nothing: the unit products
+ * handed from the gate kernel to the down kernel live in a static device array
+ * of the library (16384 floats, 64 KiB, one per GPU until the process ends).
+ * The T tokens of x run one after another through the same kernels as the
+ * handle path, each on its own live set; the output is the same up to the
+ * summation order of the down pass.
+ *   x [T x D] bf16, W1, W3, W2T [H x D] bf16 (W2 stored transposed), y [T x D]
+ *   fp32 (overwritten): device pointers, 16-byte aligned, owned by the caller.
+ *   D a positive multiple of 8, at most 4096; H in [1, 16384]; T >= 0 (0 is a
+ *   no-op); act SFFN_ACT_RELU or SFFN_ACT_RSPLUS; stream a hipStream_t.
+ * Errors: SFFN_INVALID_ARGUMENT for a size beyond these limits (H above 16384
+ * says so) or a bad pointer, SFFN_UNSUPPORTED for an unknown activation, both
+ * before any launch; sffn_last_error(NULL) gives the message. Calls that
+ * overlap on one GPU (concurrent streams, or host threads) share the static
+ * array and race: serialise them.
+ */
+sffn_status sffn_forward_sparse_noalloc(const void *x, const void *W1, const void *W3,
+                                        const void *W2T, float *y, int D, int H, int T, int act,
+                                        void *stream);
+
+/*
  * Gate-first sparse forward, LoPA gating without the fixed G term:
  * z = U (V x), then the same skip as sffn_forward_sparse. The rank vector
  * V x is kept in fp32 up to the live test. LoPA handles (r > 0) only.
