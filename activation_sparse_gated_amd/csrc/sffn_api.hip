@@ -29,7 +29,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_LOPA_T1_I8, KIND_GATE_UP_TB, KIND_GATE_UP_T1_I4,
             KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4,
             KIND_RANK_PROJ_MFMA, KIND_GATE_UP_TB_I8, KIND_DOWN_TB_I8, KIND_GATE_UP_TB_I4,
-            KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_COUNT };
+            KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_DOWN_PT, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -44,7 +44,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_dense_t1_i4", "k_down_t1_i4",
                                             "k_gate_up_lopa_t1_i4", "k_rank_proj_mfma",
                                             "k_gate_up_tb_i8", "k_down_tb_i8", "k_gate_up_tb_i4",
-                                            "k_down_tb_i4", "k_rank_proj_tb_i8", "k_gate_up_lopa_tb_q"};
+                                            "k_down_tb_i4", "k_rank_proj_tb_i8", "k_gate_up_lopa_tb_q",
+                                            "k_down_pt"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -356,10 +357,12 @@ inline int token_tiles(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 
 // LOPA: W1 is U, V the rank factor; the batch's rank vectors go through m_t
 // (bf16 hi and lo parts) into the MFMA gate, the rest is the standard plan.
+// per_token: the down pass gathers each token's own live W2T rows (per-token
+// lists) instead of the union's rows once for all tokens.
 template <bool DENSE, bool LOPA = false>
 sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* W3,
                      const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
-                     hipStream_t s, const void* V = nullptr) {
+                     hipStream_t s, const void* V = nullptr, bool per_token = false) {
     const int nt = token_tiles(T);
     uint8_t* live = live_count ? h->live_buf : nullptr;
     sffn_status st = SFFN_OK;
@@ -375,7 +378,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     const int ut = nt == 1 ? 1 : 2;  // unit tiles per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const bool small_down = T <= 4;
-    const int splits = small_down ? h->tb_splits : h->m_splits;
+    const int splits = per_token ? h->t1_splits : (small_down ? h->tb_splits : h->m_splits);
     float* yz = splits > 1 ? y : nullptr;
     if (!LOPA && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once; units
@@ -407,7 +410,17 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     }
 #undef SFFN_GATE_MFMA
     if (st != SFFN_OK) return st;
-    if (small_down) {
+    if (per_token) {
+        // per-token lists: one block row per token, 512-byte row slices
+        const int cb = 32 * 8;
+        const int nbx = (((h->D + cb - 1) / cb + 7) / 8) * 8;
+        const int hs = (h->H + splits - 1) / splits;
+        const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_PT, k_down_pt<PMAX>, dim3(nbx, splits, T),
+                                           dim3(KD_THREADS), s, (const float*)h->m_a,
+                                           (const uint64_t*)h->m_mask, (const uint16_t*)W2T, y,
+                                           h->D, h->H, 16 * nt, splits));
+    } else if (small_down) {
         // 512-byte row slices (32 lanes x 16 B), XCD-contiguous slice order
         const int cb = 32 * 8;
         const int nslices = (h->D + cb - 1) / cb;
@@ -526,11 +539,11 @@ sffn_status run_lopa_t1(sffn_handle* h, const void* x, const void* V, const void
                                      dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)V,
                                      h->t_buf, yz, h->D, h->r));
     if (st != SFFN_OK) return st;
-    // two units per wave: a U row of r <= 512 bf16 fills at most 64 lanes once
-    const int nb = (h->H + K1_WAVES * 2 - 1) / (K1_WAVES * 2);
+    // one unit per wave (measured ahead of two once only live waves read x)
+    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
     uint8_t* live = live_count ? h->live_buf : nullptr;
     SFFN_NCT1_SWITCH(nc, SFFN_NRT1_SWITCH(nr,
-        st = launch(h, KIND_GATE_UP_LOPA_T1, k_gate_up_lopa_t1<NC, NR, 2>, dim3(nb),
+        st = launch(h, KIND_GATE_UP_LOPA_T1, k_gate_up_lopa_t1<NC, NR, 1>, dim3(nb),
                     dim3(K1_THREADS), s, (const uint16_t*)x, (const float*)h->t_buf,
                     (const uint16_t*)U, (const uint16_t*)W3, h->a_buf, live, h->D, h->H, h->r,
                     h->act, h->flags)));
@@ -881,8 +894,13 @@ sffn_status dispatch_sparse(sffn_handle* h, const void* x, const void* W1, const
     sffn_status st = SFFN_OK;
     if (T == 0) return SFFN_OK;
     if (t1_ok(h, T)) return run_sparse_t1(h, x, W1, W3, W2T, y, live_count, live_idx, s);
+    if (mode == SFFN_MODE_PER_TOKEN && mfma_ok(h, T) && T <= MAXT && t1_ok(h, 1))
+        // per-token lists: one batched gate and up pass (W1 read once for the batch),
+        // then each token gathers the W2T rows of its own live list
+        return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s, nullptr, true);
     if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1)) {
-        // per-token lists: every token runs the whole batch-1 pass on its own live set
+        // per-token lists above 64 tokens: every token runs the whole batch-1 pass on its
+        // own live set
         const size_t xb = (size_t)h->D * sizeof(uint16_t);
         for (int t = 0; t < T; ++t) {
             st = run_sparse_t1(h, (const char*)x + t * xb, W1, W3, W2T, y + (size_t)t * h->D,
@@ -1636,6 +1654,9 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
             return run_lopa_t1(h, x, V, U, W3, W2T, y, live_count, live_idx, s);
         // bf16 union batches: rank projection, U gate and W3 gather on MFMA (RMSNorm of
         // the rank vectors excepted: it needs each token's whole t before the gate)
+        if (mfma_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM) && t1_ok(h, 1))
+            return run_mfma<false, true>(h, x, U, W3, W2T, y, T, live_count, live_idx, s, V,
+                                         mode == SFFN_MODE_PER_TOKEN);
         if (mode == SFFN_MODE_UNION && mfma_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
             return run_mfma<false, true>(h, x, U, W3, W2T, y, T, live_count, live_idx, s, V);
         // other bf16 batches: each token runs the batch-1 pass on its own live set (the

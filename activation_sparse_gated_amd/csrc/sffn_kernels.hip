@@ -683,8 +683,9 @@ __global__ __launch_bounds__(K1_THREADS) void k_rank_proj_t1(const uint16_t* __r
 
 // LoPA batch-1 bf16 gate: z_i = U_i . t with t in fp32 (U rows widened exactly
 // from bf16), then, as in k_gate_up_t1, each wave reads the W3 rows of its own
-// live units.
-// NR = 16-byte register chunks of a U row (r <= NR * 512).
+// live units. x is read only by waves with a live unit, together with their W3
+// rows (the gate itself needs only t), which keeps the L2 free for the U stream.
+// NR = 16-byte register chunks of a U row (r <= NR * 512); RW units per wave.
 template <int NC, int NR, int RW>
 __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
     const uint16_t* __restrict__ x, const float* __restrict__ t_in,
@@ -719,12 +720,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
             for (int k = 0; k < 8; ++k) tv[c][k] = 0.0f;
         }
     }
-    u32x4 xv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 8;
-        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
-    }
     float inv = 1.0f;  // RMSNorm of t: every wave sees all of t
     if (flags & LOPA_RMSNORM) {
         float ss = 0.0f;
@@ -736,6 +731,7 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
     }
     float z[RW];
     bool live[RW];
+    bool any = false;
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
         const int unit = unit0 + q;
@@ -749,12 +745,20 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1(
         const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
         z[q] = wave_sum_dpp(s) * inv + gx;
         live[q] = in && z[q] > 0.0f;
+        any = any || live[q];
         if (lane == 0 && in) {
             if (live_out) live_out[unit] = live[q] ? 1 : 0;
             if (!live[q]) a_out[unit] = 0.0f;
         }
     }
-    // the wave's live units: all W3 loads first (wave-uniform branches)
+    if (!any) return;  // wave-uniform
+    // the wave's live units: x and all W3 loads first (wave-uniform branches)
+    u32x4 xv[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int col = c * CW + lane * 8;
+        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
+    }
     u32x4 w3[RW][NC];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
@@ -917,6 +921,91 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1(const float* __restrict_
             else
                 y[col0 + c] = s;
         }
+    }
+}
+
+// Down projection of a batch with per-token live lists: y_t[slice] =
+// sum_{i in L_t} a[i][t] W2T[i, slice]. Grid = (column slices, row splits,
+// tokens): the blocks of token t compact the units of their split that are
+// live for t (bit t of umask, wave-local as in k_down_t1) and gather only those
+// W2T row slices, with the products a[i][t] from the unit-major batch buffer
+// (row stride tp); a row live for several tokens is fetched by each of their
+// blocks (from HBM the first time, from the caches after). y (T x D) is
+// cleared by the gate pass.
+template <int PMAX>
+__global__ __launch_bounds__(KD_THREADS) void k_down_pt(const float* __restrict__ a_rm,
+                                                        const uint64_t* __restrict__ umask,
+                                                        const uint16_t* __restrict__ W2T,
+                                                        float* __restrict__ y, int D, int H, int tp,
+                                                        int splits) {
+    constexpr int LPR = 32;
+    constexpr int VEC = 8;
+    constexpr int CB = LPR * VEC;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 8;
+    __shared__ float red[KD_WAVES][CB];
+
+    const int slice = xcd_slice(blockIdx.x, (D + CB - 1) / CB);
+    if (slice * CB >= D) return;
+    const int t = blockIdx.z;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * VEC;
+    const bool col_ok = col < D;
+
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        mk[p] = __ballot(row < h1 && ((umask[row] >> t) & 1ull));
+    }
+    float acc[VEC];
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) acc[k] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = mk[p];
+        while (m) {
+            int bit[UF];
+            next_live_bits<RPI, UF>(m, grp, bit);
+            u32x4 wv[UF];
+            float av[UF];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const bool ok = bit[u] >= 0;
+                const size_t row = (size_t)(base + (ok ? bit[u] : 0));
+                wv[u] = (ok && col_ok) ? load_stream(W2T + row * D + col) : u32x4{0u, 0u, 0u, 0u};
+                av[u] = ok ? a_rm[row * tp + t] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u)
+#pragma unroll
+                for (int k = 0; k < VEC; ++k) acc[k] = fmaf(av[u], Elem<uint16_t>::get(wv[u], k), acc[k]);
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < VEC; ++k) {
+        float v = acc[k];
+        for (int o = LPR; o < WAVE; o <<= 1) v += __shfl_xor(v, o, WAVE);
+        acc[k] = v;
+    }
+    if (grp == 0) {
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) red[wave][sub * VEC + k] = acc[k];
+    }
+    __syncthreads();
+    float* yt = y + (size_t)t * D;
+    for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+        if (col0 + c < D) atomicAdd(yt + col0 + c, s);
     }
 }
 
