@@ -88,7 +88,9 @@ struct sffn_handle {
     int32_t* g_list = nullptr;     // [H + 32] units live for some token, then the count
 
     // instrumentation
-    bool timing = false;
+    int timing_every = 0;   // 0: off; N: the launches of every Nth forward call are timed
+    int64_t call_seq = 0;   // forward calls checked since timing was enabled
+    bool timed_call = false; // the launches of the current call are timed
     struct Rec { int kind; hipEvent_t start, stop; };
     std::vector<Rec> pending;
     std::vector<hipEvent_t> pool;
@@ -127,7 +129,7 @@ template <typename... KArgs, typename... Args>
 sffn_status launch_shm(sffn_handle* h, int kind, void (*kern)(KArgs...), dim3 grid, dim3 block,
                        size_t shm, hipStream_t s, Args... args) {
     if (grid.x == 0) return SFFN_OK;
-    if (h->timing) {
+    if (h->timed_call) {
         hipEvent_t e0 = take_event(h), e1 = take_event(h);
         if (!e0 || !e1) return fail(h, SFFN_HIP_ERROR, "hipEventCreate failed");
         hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)shm, s, e0, e1, 0,
@@ -145,7 +147,7 @@ template <typename... KArgs, typename... Args>
 sffn_status launch(sffn_handle* h, int kind, void (*kern)(KArgs...), dim3 grid, dim3 block,
                    hipStream_t s, Args... args) {
     if (grid.x == 0) return SFFN_OK;
-    if (h->timing) {
+    if (h->timed_call) {
         hipEvent_t e0 = take_event(h), e1 = take_event(h);
         if (!e0 || !e1) return fail(h, SFFN_HIP_ERROR, "hipEventCreate failed");
         hipExtLaunchKernelGGL(kern, grid, block, 0, s, e0, e1, 0, static_cast<KArgs>(args)...);
@@ -952,6 +954,7 @@ sffn_status check_common(sffn_handle* h, const void* x, const void* W3, const vo
     if (dev != h->device)
         return fail(h, SFFN_INVALID_ARGUMENT, "current device differs from the handle's device");
     *stream_out = reinterpret_cast<hipStream_t>(stream);
+    h->timed_call = h->timing_every > 0 && (h->call_seq++ % h->timing_every) == 0;
     return SFFN_OK;
 }
 
@@ -1681,7 +1684,10 @@ sffn_status sffn_forward_lopa(sffn_handle* h, const void* x, const void* V, cons
 
 sffn_status sffn_timing_enable(sffn_handle* h, int enable) {
     if (!h) return fail(nullptr, SFFN_INVALID_ARGUMENT, "null handle");
-    h->timing = enable != 0;
+    if (enable < 0) return fail(h, SFFN_INVALID_ARGUMENT, "enable must be >= 0");
+    h->timing_every = enable;
+    h->call_seq = 0;
+    h->timed_call = false;
     return SFFN_OK;
 }
 

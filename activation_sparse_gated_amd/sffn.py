@@ -279,8 +279,9 @@ def sffn_forward_moe(handle, x, W1s, W3s, W2Ts, route, gate, y, T: int, dense: b
     return st
 
 
-def sffn_timing_enable(handle, enable: bool) -> None:
-    _check(load().sffn_timing_enable(handle, int(bool(enable))), handle)
+def sffn_timing_enable(handle, enable) -> None:
+    """enable: False/0 off, True/1 every forward call, N > 1 every Nth call."""
+    _check(load().sffn_timing_enable(handle, int(enable)), handle)
 
 
 def sffn_timing_read(handle, kind: int, reset: bool = False):

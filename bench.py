@@ -44,6 +44,20 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def read_graph_durations(name: str):
+    """Mean duration (us) per kernel over the timed graph replays, from the committed
+    rocprofv3 kernel trace of the bench command, if it was taken on the current kernel
+    sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != kernel_source_hash():
+        return None
+    return d.get("graph_replay_mean_us")
+
+
 def read_traffic(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources (else None)."""
@@ -68,22 +82,55 @@ def _rocpd_rows(db_dir, query):
     return rows
 
 
+# bench.py launches this one-byte fill right before the warmup of the timed graph
+# replays and right after them, so a kernel trace can be cut to the timed region
+MARKER_KERNEL = "FillFunctor<unsigned char>"
+
+
 def summarize_trace(db_dir: str, out: str, command: str) -> None:
-    """Kernel-trace summary (count, mean/min/max duration) of a rocprofv3 run as markdown."""
-    rows = _rocpd_rows(db_dir, "select name, count(*), avg(duration), min(duration), max(duration), "
-                               "sum(duration) from kernels group by name order by sum(duration) desc")
+    """Kernel-trace summary (count, mean/min/max duration) of a rocprofv3 run as markdown,
+    for the whole run and, when bench.py's markers are present, for the dispatches of the
+    timed graph replays alone; the graph-replay means also go to a JSON file beside it
+    (with the kernel source hash) for bench.py's roofline."""
+    rows = _rocpd_rows(db_dir, "select name, start, end from kernels order by start")
+    short = [r[0].split("(")[0].replace("void ", "") for r in rows]
+    marks = [i for i, n in enumerate(short) if MARKER_KERNEL in n]
+
+    def table(idx):
+        acc = {}
+        for i in idx:
+            d = (rows[i][2] - rows[i][1]) / 1e3
+            a = acc.setdefault(short[i], [])
+            a.append(d)
+        out_rows = sorted(acc.items(), key=lambda kv: -sum(kv[1]))
+        lines = ["| kernel | launches | mean us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
+        for name, ds in out_rows:
+            lines.append(f"| `{name}` | {len(ds)} | {sum(ds) / len(ds):.3f} | {min(ds):.3f} | "
+                         f"{max(ds):.3f} | {sum(ds) / 1e3:.3f} |")
+        return lines, {name: sum(ds) / len(ds) for name, ds in out_rows}
+
     lines = [f"# rocprofv3 kernel trace: {os.path.basename(out)}", "", "Command (from the repo root):",
-             "", "```", command, "```", "",
-             "| kernel | launches | mean us | min us | max us | total ms |", "|---|---|---|---|---|---|"]
-    for name, cnt, avg, mn, mx, tot in rows:
-        short = name.split("(")[0].replace("void ", "")
-        lines.append(f"| `{short}` | {cnt} | {avg / 1e3:.3f} | {mn / 1e3:.3f} | {mx / 1e3:.3f} | "
-                     f"{tot / 1e6:.3f} |")
+             "", "```", command, "```", ""]
+    graph = None
+    if len(marks) >= 2:
+        idx = [i for i in range(marks[0] + 1, marks[1]) if MARKER_KERNEL not in short[i]]
+        t, graph = table(idx)
+        span_us = (rows[marks[1]][1] - rows[marks[0]][2]) / 1e3
+        lines += ["## Timed graph replays (warmup and timed steps, between the markers)", "",
+                  f"{len(idx)} dispatches over {span_us:,.1f} us.", ""] + t + [""]
+    t, _ = table(range(len(rows)))
+    lines += ["## Whole run (graph replays, eager passes, set-up)", ""] + t
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
+    if graph is not None:
+        with open(os.path.splitext(out)[0] + ".json", "w") as f:
+            json.dump({"source_hash": kernel_source_hash(), "command": command,
+                       "graph_replay_mean_us": {k: round(v, 4) for k, v in graph.items()}}, f,
+                      indent=2)
 
 
-def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command: str) -> None:
+def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command: str,
+                  workload: str = "decode") -> None:
     """HBM bytes per launch of `kernel` from FETCH_SIZE and WRITE_SIZE runs, each scaled by
     what the same counter reads for the calibration copy of CALIB_BYTES in the same run."""
     q = ("select kernel_name, counter_name, avg(value), count(*) from counters_collection "
@@ -100,7 +147,7 @@ def summarize_pmc(fetch_dir: str, write_dir: str, kernel: str, out: str, command
         scale = CALIB_BYTES / (max(calib) * 1024.0)
         res[counter] = {"kib_per_dispatch": kern[0], "calib_kib": max(calib), "scale": scale,
                         "bytes_per_launch": kern[0] * 1024.0 * scale}
-    d = {"kernel": kernel, "workload": "decode", "source_hash": kernel_source_hash(),
+    d = {"kernel": kernel, "workload": workload, "source_hash": kernel_source_hash(),
          "command": command, "calibration_copy_bytes": CALIB_BYTES,
          "fetch": res["FETCH_SIZE"], "write": res["WRITE_SIZE"],
          "hbm_bytes_per_launch": round(res["FETCH_SIZE"]["bytes_per_launch"]
@@ -345,19 +392,48 @@ def bench_moe(torch, sffn, gen, to_dev, act, args):
     return out
 
 
+def _device_layer(torch, D, H, sparsity, gen, layer, seed_base):
+    """One FFN layer of the stack workload drawn on the device: W1, W3, W2T ~ N(0, 1/D)
+    from a generator seeded per layer, W1[:, 0] = -Phi^-1(s) (the recipe of the
+    inputs module, drawn by torch so that 32 layers of the wide shape take seconds)."""
+    g = torch.Generator(device="cuda")
+    out = {}
+    for i, k in enumerate(("W1", "W3", "W2T")):
+        g.manual_seed(seed_base + 1000 * layer + i)
+        w = torch.randn(H, D, generator=g, device="cuda", dtype=torch.float32) / np.sqrt(D)
+        if k == "W1":
+            w[:, 0] = float(gen.gate_offset(sparsity))
+        out[k] = w.to(torch.bfloat16).view(torch.int16)
+        del w
+    return out
+
+
 def bench_stacks(torch, sffn, gen, to_dev, act, args):
     """32-layer stacks at s = 0.895, batch-1 decode of 256 tokens through all layers.
-    The 32 layers are byte-identical copies of one generated layer at distinct addresses
-    (2.4 GB and 9.7 GB): the weights stream from HBM exactly as 32 independent layers."""
+    Each layer has its own independently drawn weights (2.4 GB and 9.7 GB per stack);
+    every (token, layer) pair gets its own input (layers are not chained), so each
+    layer sees the workload's sparsity. Per-layer sparsity is measured outside the
+    timed region."""
     out = {}
     for (D, H) in ((2048, 6144), (4096, 12288)):
-        w = gen.standard_weights(D, H, 0.895, cfg=5, dtype="bf16")
-        W = {k: to_dev(w[k]) for k in ("W1", "W3", "W2T")}
-        layers = [{k: (W[k] if l == 0 else W[k].clone()) for k in W} for l in range(32)]
+        s = 0.895
+        layers = [_device_layer(torch, D, H, s, gen, l, 2026 * 7919 + D) for l in range(32)]
         ntok = 256
         xs = to_dev(gen.tokens(D, ntok * 32, cfg=5, dtype="bf16"))
         h = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_BF16)
         y = torch.zeros(ntok * 32, D, dtype=torch.float32, device="cuda")
+        cnt = torch.zeros(ntok * 32, dtype=torch.int32, device="cuda")
+        idx = torch.zeros(1, H, dtype=torch.int32, device="cuda")
+        # live counts of the first 8 tokens through every layer (outside the timed region)
+        for t in range(8):
+            for l in range(32):
+                i = t * 32 + l
+                L = layers[l]
+                sffn.sffn_forward_sparse(h.ptr, xs[i], L["W1"], L["W3"], L["W2T"], y[i], 1,
+                                         sffn.SFFN_MODE_PER_TOKEN, cnt[i:i + 1], idx[0])
+        torch.cuda.synchronize()
+        kl = cnt[:8 * 32].view(8, 32).cpu().numpy().astype(np.float64)
+        layer_sparsity = 1.0 - kl.mean(axis=0) / H
         res = {}
         for name, dense in (("sparse", False), ("dense", True)):
             def fn():
@@ -373,10 +449,15 @@ def bench_stacks(torch, sffn, gen, to_dev, act, args):
             res[name + "_stack_tokens_per_s"] = round(ntok / (ms * 1e-3), 1)
             res[name + "_layer_tokens_per_s"] = round(ntok * 32 / (ms * 1e-3), 1)
         res["sparse_vs_dense"] = round(res["sparse_stack_tokens_per_s"] / res["dense_stack_tokens_per_s"], 3)
+        res["layers"] = "32 independent draws, inputs not chained"
+        res["layer_sparsity_min"] = round(float(layer_sparsity.min()), 4)
+        res["layer_sparsity_mean"] = round(float(layer_sparsity.mean()), 4)
+        res["layer_sparsity_max"] = round(float(layer_sparsity.max()), 4)
         out[f"D{D}_H{H}"] = res
-        log(f"stack D={D} H={H}: " + ", ".join(f"{k} {v:,}" for k, v in res.items()))
+        log(f"stack D={D} H={H}: " + ", ".join(f"{k} {v:,}" if not isinstance(v, str) else f"{k} {v}"
+                                               for k, v in res.items()))
         h.close()
-        del layers, W
+        del layers
         torch.cuda.empty_cache()
     return out
 
@@ -389,7 +470,7 @@ def main() -> int:
         summarize_counters(sys.argv[2], sys.argv[3], sys.argv[4])
         return 0
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-pmc":
-        summarize_pmc(sys.argv[2], sys.argv[3], sys.argv[4], sys.argv[5], sys.argv[6])
+        summarize_pmc(*sys.argv[2:7], *(sys.argv[7:8] or ["decode"]))
         return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -401,6 +482,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall-clock budget of the CPU oracle baseline sample")
     ap.add_argument("--no-extras", action="store_true", help="skip the dense and LoPA streams")
+    ap.add_argument("--only-lopa", action="store_true",
+                    help="of the extra lines run only the LoPA streams (for counter collection)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--only-batched", action="store_true",
                     help="run only the batched-decode lines (for counter collection)")
@@ -454,27 +537,6 @@ def main() -> int:
         print(json.dumps({"prefill": res}), flush=True)
         return 0
 
-    # ---------------------------------------------------------------- streaming ceiling
-    # a 4 GiB -> 4 GiB device copy (torch's vectorised copy kernel), median of 5; bytes read
-    # plus written per second: what a plain streaming kernel reaches on this GPU in this process
-    src = torch.ones(2**30, dtype=torch.float32, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    st_ms = []
-    for _ in range(5):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        dst.copy_(src)
-        e1.record()
-        torch.cuda.synchronize()
-        st_ms.append(e0.elapsed_time(e1))
-    stream_gbps = 2 * src.numel() * 4 / (sorted(st_ms)[2] * 1e-3) / 1e9
-    del src, dst
-    torch.cuda.empty_cache()
-    log(f"streaming ceiling: {stream_gbps:,.0f} GB/s (4 GiB device copy, read + write)")
-
     hs = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_BF16)
 
     # live counts of every token (outside the timed region)
@@ -519,19 +581,25 @@ def main() -> int:
                                      sffn.SFFN_MODE_PER_TOKEN)
 
     g_sparse = capture(sparse_stream)
+    marker = torch.empty(1, dtype=torch.uint8, device="cuda")
+    marker.fill_(1)   # trace marker: the timed graph replays start
     ms_step = time_graph(g_sparse, args.steps, args.warmup)
+    marker.fill_(2)   # trace marker: they end
+    torch.cuda.synchronize()
     tok_s = n / (ms_step * 1e-3)
     bytes_tok = 2 * (H * D + 2 * k * D) + 6 * D          # weights read + x in + y out
     touched_gbps = bytes_tok.sum() / (ms_step * 1e-3) / 1e9
     log(f"sparse: {ms_step:.3f} ms/step, {tok_s:,.0f} tokens/s, {touched_gbps:,.0f} GB/s touched")
 
-    # per-kernel durations, measured at each kernel's own begin/end on the same stream
-    sffn.sffn_timing_enable(hs.ptr, True)
+    # per-kernel durations, measured with HIP events at each kernel's own begin and end on
+    # the stream it runs on; every 8th call of four passes over the token stream is timed,
+    # so the calls between keep the GPU as busy as in the graph replay
+    sffn.sffn_timing_enable(hs.ptr, 8)
     sffn.sffn_timing_read(hs.ptr, 0, reset=True)
-    for _ in range(2):
+    for _ in range(4):
         sparse_stream()
     torch.cuda.synchronize()
-    sffn.sffn_timing_enable(hs.ptr, False)
+    sffn.sffn_timing_enable(hs.ptr, 0)
     kt = {}
     for kd in range(sffn.sffn_kernel_kinds()):
         ms, launches = sffn.sffn_timing_read(hs.ptr, kd)
@@ -544,11 +612,27 @@ def main() -> int:
     algo_bytes = {
         "k_gate_up_t1": 2 * (H * D + kmean * D) + 2 * D + 4 * H,     # W1, live W3 rows, x, a out
         "k_down_t1": 2 * kmean * D + 4 * H + 4 * D,                  # live W2T rows, a in, y out
-        "k_ffn_t1": 2 * (H * D + 2 * kmean * D) + 2 * D + 4 * D * 0,  # W1, live W3 + W2T rows, x
-        "k_reduce_partials": 0.0,
     }
     gate_bytes = algo_bytes.get(dom, float("nan"))
-    achieved = gate_bytes / (kt[dom] * 1e-6) / 1e9
+    # durations of the same kernels inside the timed graph replays, from the committed kernel
+    # trace of this command when it was taken on the current sources (eager launches run
+    # slower: the host cannot keep the GPU busy between them)
+    gdur = read_graph_durations("decode_headline_kernel_trace") or {}
+
+    def graph_us(kind):
+        for name, us in gdur.items():
+            if name.startswith(f"sffn::{kind}<") or name == f"sffn::{kind}":
+                return us
+        return None
+
+    kt_graph = {kk: graph_us(kk) for kk in kt}
+    if all(v is not None for v in kt_graph.values()):
+        dom_us, dur_src = kt_graph[dom], ("rocprofv3 kernel trace of this command, timed graph "
+                                          "replays (profiles/decode_headline_kernel_trace.json)")
+    else:
+        kt_graph = None
+        dom_us, dur_src = kt[dom], "HIP events at the kernel's begin and end, eager pass"
+    achieved = gate_bytes / (dom_us * 1e-6) / 1e9
     log("kernels (us/launch): " + ", ".join(f"{n_} {v:.2f}" for n_, v in kt.items()))
     log(f"dominant {dom}: {gate_bytes / 1e6:.2f} MB algorithmic per launch, {achieved:,.0f} GB/s")
 
@@ -560,7 +644,7 @@ def main() -> int:
     del calib, calib_out
 
     extras = {}
-    if not args.no_extras:
+    if not args.no_extras and not args.only_lopa:
         def dense_stream():
             for t in range(n):
                 rp = reps[t % R]
@@ -621,6 +705,7 @@ def main() -> int:
                 f"measured {other[f's{s_o}']['measured_sparsity']}, {tok_o / dense_tok_s:.2f}x dense")
         extras["other_sparsities"] = other
 
+    if not args.no_extras or args.only_lopa:
         # LoPA at constant parameter count: D = 2560, H' = 9787, r = 400
         Hp, r = 9787, 400
         wl = gen.lopa_weights(D, Hp, r, s, cfg=3, dtype="bf16")
@@ -645,13 +730,27 @@ def main() -> int:
 
         g_lopa = capture(lopa_stream)
         ms_lopa = time_graph(g_lopa, args.steps, args.warmup)
+        sffn.sffn_timing_enable(hl.ptr, 8)
+        sffn.sffn_timing_read(hl.ptr, 0, reset=True)
+        for _ in range(4):
+            lopa_stream()
+        torch.cuda.synchronize()
+        sffn.sffn_timing_enable(hl.ptr, 0)
+        lopa_kt = {}
+        for kd in range(sffn.sffn_kernel_kinds()):
+            ms_, l_ = sffn.sffn_timing_read(hl.ptr, kd)
+            if l_:
+                lopa_kt[sffn.sffn_kernel_name(kd)] = round(ms_ * 1e3 / l_, 3)
+        sffn.sffn_timing_read(hl.ptr, 0, reset=True)
         lopa_tok_s = n / (ms_lopa * 1e-3)
         lopa_gbps = (2 * (r * (D + Hp) + 2 * kl * D) + 6 * D).sum() / (ms_lopa * 1e-3) / 1e9
         log(f"lopa: {ms_lopa:.3f} ms/step, {lopa_tok_s:,.0f} tokens/s, {lopa_gbps:,.0f} GB/s touched")
         extras.update({"lopa_tokens_per_s": round(lopa_tok_s, 1),
                        "lopa_touched_GBps": round(lopa_gbps, 1),
                        "lopa_measured_sparsity": round(float(1 - kl.mean() / Hp), 4),
-                       "lopa_speedup_vs_dense": round(lopa_tok_s / extras["dense_tokens_per_s"], 3)})
+                       "lopa_kernel_us": lopa_kt,
+                       "lopa_speedup_vs_dense": (round(lopa_tok_s / extras["dense_tokens_per_s"], 3)
+                                                 if "dense_tokens_per_s" in extras else None)})
         del g_lopa
         hl.close()
 
@@ -691,12 +790,13 @@ def main() -> int:
             "touched_GBps": round(float(full_gbps), 1),
             "measured_sparsity": round(float(1 - kf.mean() / Hp), 4),
             "w2_rows_mean": round(float(k2f.mean()), 1),
-            "speedup_vs_dense": round(full_tok_s / extras["dense_tokens_per_s"], 3)}
+            "speedup_vs_dense": (round(full_tok_s / extras["dense_tokens_per_s"], 3)
+                                 if "dense_tokens_per_s" in extras else None)}
         del g_full
         hf.close()
 
     # ---------------------------------------------------------------- weight-only int8 decode
-    if not args.no_extras:
+    if not args.no_extras and not args.only_lopa:
         # the decode workload's fp64 draws quantized per row to int8 (same streams and offset)
         wq = gen.standard_weights_int8(D, H, s, cfg=2)
         WQ = {kk: torch.from_numpy(np.ascontiguousarray(wq[kk])).cuda()
@@ -955,7 +1055,7 @@ def main() -> int:
             del replq, WLQ
 
     # ---------------------------------------------------------------- batched decode and stacks
-    if not args.no_extras:
+    if not args.no_extras and not args.only_lopa:
         extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
         extras["lopa_batched"] = bench_lopa_batched(torch, sffn, gen, to_dev, act, args)
         extras["stacks"] = bench_stacks(torch, sffn, gen, to_dev, act, args)
@@ -1002,8 +1102,9 @@ def main() -> int:
         log(f"cpu oracle: {cpu['value']} tokens/s on {threads} threads ({done} tokens), "
             f"{cpu['one_thread_value']} tokens/s on 1 thread; {cpu_model}")
         if not args.no_extras:
-            # the 32-layer stacks: the first 8 stack tokens through all 32 layers (the
-            # layers are copies of one generated layer, as on the GPU), extrapolated
+            # the 32-layer stacks: the first 8 stack tokens through all 32 layers,
+            # extrapolated (the oracle's time does not depend on the weight values, so one
+            # drawn layer stands for each of the 32)
             stk = {}
             for (Ds, Hs) in ((2048, 6144), (4096, 12288)):
                 ws = gen.standard_weights(Ds, Hs, 0.895, cfg=5, dtype="bf16")
@@ -1042,14 +1143,16 @@ def main() -> int:
                    "replicas": R, "parallelism": "single GPU"},
         "touched_GBps": round(float(touched_gbps), 1),
         "touched_frac_of_peak": round(float(touched_gbps) / HBM_PEAK_GBPS, 4),
-        "stream_copy_GBps": round(float(stream_gbps), 1),
-        "touched_frac_of_stream": round(float(touched_gbps) / stream_gbps, 4),
         "measured_sparsity": round(float(meas_sparsity), 4),
         "k_mean": round(float(k.mean()), 1),
         "k_std": round(float(k.std()), 1),
         "us_per_token": round(ms_step * 1e3 / n, 3),
         "kernel_us": {kk: round(v, 3) for kk, v in kt.items()},
         "kernels_per_token": len(kt),
+        "kernel_us_graph_replay": ({kk: round(v, 3) for kk, v in kt_graph.items()}
+                                   if kt_graph else None),
+        # time per token that no kernel of the token covers (graph-replay durations when known)
+        "per_token_gap_us": round(ms_step * 1e3 / n - sum((kt_graph or kt).values()), 3),
         **extras,
         "roofline": {"bound": "hbm", "achieved": round(float(achieved), 1),
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -1057,7 +1160,8 @@ def main() -> int:
                      "traffic": traffic,
                      "kernel": dom,
                      "bytes_per_launch": round(float(gate_bytes), 0),
-                     "avg_launch_us": round(kt[dom], 3)},
+                     "avg_launch_us": round(dom_us, 3),
+                     "duration_source": dur_src},
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
     }

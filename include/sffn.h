@@ -314,9 +314,12 @@ const char *sffn_status_string(sffn_status s);
 int sffn_abi_version(void);
 
 /*
- * Instrumentation, for measuring the kernels' own durations. While enabled,
- * every kernel the forward calls enqueue is launched with a start/stop event
- * pair recorded at the kernel's own begin and end. sffn_timing_read
+ * Instrumentation, for measuring the kernels' own durations. enable = 0 turns
+ * it off; enable = N > 0 times the forward calls 0, N, 2N, ... counted from
+ * this call (N = 1: every call): each kernel such a call enqueues is launched
+ * with a start/stop event pair recorded at the kernel's own begin and end, and
+ * the other calls launch as usual, so a long stream of calls keeps the GPU as
+ * busy as it is untimed. sffn_timing_read
  * synchronises with those events and returns, for kernel kind `kind`, the
  * summed duration in milliseconds and the number of launches since the last
  * reset (reset != 0 clears the totals of every kind after reading). Kinds are
