@@ -221,10 +221,11 @@ sffn_status run_live_list(sffn_handle* h, int T, int32_t* live_count, int32_t* l
 constexpr int kNC_T1[] = {1, 2, 3, 4, 5, 6, 8};
 constexpr int kPMAX[] = {1, 2, 4, 8, 16, 32};
 
+// The batch-1 bf16 kernels hold a row of D in registers (at most 8 chunks of 512
+// bf16); any H works, since the down pass splits the units into ranges of at most
+// 32 x 512 (t1_splits is raised at create when H needs it).
 bool t1_ok(const sffn_handle* h, int T) {
-    return T == 1 && h->dtype == SFFN_BF16 &&
-           chunks_needed(h->D, h->dtype) <= 8 &&
-           (h->H + KD_THREADS - 1) / KD_THREADS <= 32;
+    return T == 1 && h->dtype == SFFN_BF16 && chunks_needed(h->D, h->dtype) <= 8;
 }
 
 #define SFFN_NCT1_SWITCH(NCV, BODY)                       \

@@ -462,6 +462,84 @@ def bench_stacks(torch, sffn, gen, to_dev, act, args):
     return out
 
 
+def _device_lopa_layer(torch, D, Hp, r, sparsity, gen, replica, seed_base):
+    """One LoPA layer drawn on the device with the recipe of the inputs module:
+    V ~ N(0, 1/D) with V[0] = e_0, U ~ N(0, 1/r) with U[:, 0] = c, W3 ~ N(0, 1/D),
+    W2T ~ N(0, 1/H')."""
+    g = torch.Generator(device="cuda")
+    out = {}
+    for i, (k, shape, std) in enumerate((("V", (r, D), D), ("U", (Hp, r), r), ("W3", (Hp, D), D),
+                                         ("W2T", (Hp, D), Hp))):
+        g.manual_seed(seed_base + 1000 * replica + i)
+        w = torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32) / np.sqrt(std)
+        if k == "V":
+            w[0].zero_()
+            w[0, 0] = 1.0
+        if k == "U":
+            w[:, 0] = float(gen.gate_offset(sparsity))
+        out[k] = w.to(torch.bfloat16).view(torch.int16)
+        del w
+    return out
+
+
+def bench_wide_lopa(torch, sffn, gen, act, args):
+    """Standard gating against LoPA at one parameter count on the wide shape: D = 4096,
+    H = 12288 against r = 640, H' = 16799, s = 0.9, batch-1 decode of 256 tokens over
+    4 independently drawn replicas of each layer (and the dense comparator)."""
+    D, H, r, s, R, n = 4096, 12288, 640, 0.9, 4, 256
+    Hp = 16799
+    std = [_device_layer(torch, D, H, s, gen, q, 4096 * 31 + q) for q in range(R)]
+    lop = [_device_lopa_layer(torch, D, Hp, r, s, gen, q, 4096 * 37) for q in range(R)]
+    xs = torch.from_numpy(gen.tokens(D, n, cfg=7, dtype="bf16").view(np.int16)).cuda()
+    y = torch.zeros(n, D, dtype=torch.float32, device="cuda")
+    cnt = torch.zeros(n, dtype=torch.int32, device="cuda")
+    hs = sffn.Handle(D, H, 0, 1, act, sffn.SFFN_BF16)
+    hl = sffn.Handle(D, Hp, r, 1, act, sffn.SFFN_BF16)
+    idx = torch.zeros(Hp, dtype=torch.int32, device="cuda")
+    out = {"shape": f"D={D}, H={H} against r={r}, H'={Hp}", "sparsity_target": s}
+    for t in range(n):
+        L = std[t % R]
+        sffn.sffn_forward_sparse(hs.ptr, xs[t], L["W1"], L["W3"], L["W2T"], y[t], 1,
+                                 sffn.SFFN_MODE_PER_TOKEN, cnt[t:t + 1], idx[:H])
+    torch.cuda.synchronize()
+    out["standard_measured_sparsity"] = round(float(1 - cnt.double().mean().item() / H), 4)
+    for t in range(n):
+        L = lop[t % R]
+        sffn.sffn_forward_lopa(hl.ptr, xs[t], L["V"], L["U"], L["W3"], L["W2T"], y[t], 1,
+                               sffn.SFFN_MODE_PER_TOKEN, cnt[t:t + 1], idx)
+    torch.cuda.synchronize()
+    out["lopa_measured_sparsity"] = round(float(1 - cnt.double().mean().item() / Hp), 4)
+
+    def f_std():
+        for t in range(n):
+            L = std[t % R]
+            sffn.sffn_forward_sparse(hs.ptr, xs[t], L["W1"], L["W3"], L["W2T"], y[t], 1)
+
+    def f_dense():
+        for t in range(n):
+            L = std[t % R]
+            sffn.sffn_forward_dense(hs.ptr, xs[t], L["W1"], L["W3"], L["W2T"], y[t], 1)
+
+    def f_lopa():
+        for t in range(n):
+            L = lop[t % R]
+            sffn.sffn_forward_lopa(hl.ptr, xs[t], L["V"], L["U"], L["W3"], L["W2T"], y[t], 1,
+                                   sffn.SFFN_MODE_PER_TOKEN)
+
+    for name, fn in (("standard", f_std), ("dense", f_dense), ("lopa", f_lopa)):
+        ms = _graph_time(torch, fn, max(2, args.steps // 4), 1)
+        out[name + "_tokens_per_s"] = round(n / (ms * 1e-3), 1)
+    out["lopa_vs_standard"] = round(out["lopa_tokens_per_s"] / out["standard_tokens_per_s"], 3)
+    out["standard_vs_dense"] = round(out["standard_tokens_per_s"] / out["dense_tokens_per_s"], 3)
+    out["lopa_vs_dense"] = round(out["lopa_tokens_per_s"] / out["dense_tokens_per_s"], 3)
+    log("wide lopa: " + ", ".join(f"{k} {v}" for k, v in out.items()))
+    hs.close()
+    hl.close()
+    del std, lop
+    torch.cuda.empty_cache()
+    return out
+
+
 def main() -> int:
     if len(sys.argv) > 1 and sys.argv[1] == "--summarize-trace":
         summarize_trace(sys.argv[2], sys.argv[3], sys.argv[4])
@@ -1058,6 +1136,7 @@ def main() -> int:
     if not args.no_extras and not args.only_lopa:
         extras["batched"] = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
         extras["lopa_batched"] = bench_lopa_batched(torch, sffn, gen, to_dev, act, args)
+        extras["lopa_wide"] = bench_wide_lopa(torch, sffn, gen, act, args)
         extras["stacks"] = bench_stacks(torch, sffn, gen, to_dev, act, args)
         extras["moe_top2_8x"] = bench_moe(torch, sffn, gen, to_dev, act, args)
         extras["prefill"] = bench_prefill(torch, sffn, gen, to_dev, reps, D, H, act, args)
