@@ -2493,6 +2493,495 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
     }
 }
 
+// ---- weight-only int8 batches on MFMA (5..64 tokens)
+// The plan of the bf16 batches with int8 codes: the codes are staged as they are
+// (half the bytes of bf16 rows) and decoded exactly into bf16 where an MFMA operand
+// is formed (an int8 value has at most 8 significant bits), and each row's scale
+// multiplies its fp32 sums. Products and sums as in the bf16 batches.
+
+// 8 int8 codes (two dwords, ascending columns) -> 8 bf16 values, exact: each code
+// q goes through the offset byte q + 128 (byte ^ 0x80, read as unsigned), so the
+// conversion never sees a sign-extended byte. (A signed bit-field extract feeding
+// the int-to-float conversion was lowered to an unsigned byte conversion with a
+// sign-extend modifier, which gave 2^32 + q for negative codes.)
+__device__ inline u32x4 decode_i8x8(uint32_t w0, uint32_t w1) {
+    u32x4 o;
+    const uint32_t w[2] = {w0 ^ 0x80808080u, w1 ^ 0x80808080u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t f0 = __float_as_uint((float)((w[h] >> (16 * p)) & 0xffu) - 128.0f);
+            const uint32_t f1 = __float_as_uint((float)((w[h] >> (16 * p + 8)) & 0xffu) - 128.0f);
+            o[2 * h + p] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);  // bf16 of f0, f1
+        }
+    }
+    return o;
+}
+
+// Chunks of 256 columns: a weight row gives 256 bytes of codes (16 pieces of 16 B)
+// and a token row of x 512 bytes, staged as two 256-byte rows (chunk columns
+// 0..127 and 128..255). In a weight row r, LDS slot j holds piece j ^ (r % 16); in
+// the two rows of token t, piece j ^ (t % 16): the 16-row fragment reads of one
+// column hit 16 different slots.
+constexpr int KQ_KC = 256;
+// Wave w multiplies unit tile w % UT against all NT token tiles over the k-steps
+// ks = w / UT (mod KG) of every chunk, so each weight operand is decoded once per
+// block; the KG partial sums are added in LDS.
+template <int NT, int UT>
+struct GateTilesI8 {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    static_assert(UT == 1 || UT == 2, "unit tiles: 1 or 2");
+    static constexpr int TP = 16 * NT;
+    static constexpr int UB = 16 * UT;
+    static constexpr int KG = 4 / UT;                      // K groups
+    static constexpr int TPW = NT;                         // tiles per wave (one unit tile)
+    static constexpr int ROWS = UB + 2 * TP;               // staged 256-byte rows per chunk
+    static constexpr int IPW = ROWS / 16;                  // 1 KB load instructions per wave per chunk
+    static constexpr int STAGE = ROWS * 256;
+    static constexpr int NS = STAGE <= 24576 ? 4 : 3;
+    static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
+};
+
+// 8 int8 codes (two dwords) -> the 8 bf16 values q + 128 (exact: 0..255 has at most 8
+// significant bits): byte ^ 0x80 is q + 128 read as unsigned, one conversion each.
+__device__ inline u32x4 decode_i8x8_offset(uint32_t w0, uint32_t w1) {
+    u32x4 o;
+    const uint32_t w[2] = {w0 ^ 0x80808080u, w1 ^ 0x80808080u};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) {
+            const uint32_t f0 = __float_as_uint((float)((w[h] >> (16 * p)) & 0xffu));
+            const uint32_t f1 = __float_as_uint((float)((w[h] >> (16 * p + 8)) & 0xffu));
+            o[2 * h + p] = __builtin_amdgcn_perm(f1, f0, 0x07060302u);
+        }
+    }
+    return o;
+}
+
+// acc[i] (tiles of this wave) = int8 rows[] of W x tokens of x, over K columns (K a
+// multiple of 16). Each weight operand is decoded as q + 128 and a second MFMA with
+// the constant operand -128 takes the offset off in the same accumulator, so the
+// sum is that of q x. The k-steps of every chunk are spread over the K groups of
+// waves (all four waves decode and multiply every chunk). The LDS ring and its waits
+// as in mfma_gate_pass.
+template <int NT, int UT>
+__device__ inline void mfma_gate_pass_i8(f32x4* acc, const int8_t* __restrict__ W,
+                                         const int* rows, const uint16_t* __restrict__ x,
+                                         const uint16_t* __restrict__ zeros, int K, int T,
+                                         uint8_t* ring) {
+    using G = GateTilesI8<NT, UT>;
+    constexpr int NS = G::NS, IPW = G::IPW;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15, pq = lane >> 4;
+    const int ut = wave % UT, kgroup = wave / UT;
+    const int nchunks = (K + KQ_KC - 1) / KQ_KC;
+#pragma unroll
+    for (int i = 0; i < G::TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // per load instruction: source of this lane's piece, its first column in the
+    // chunk, and the bytes one chunk advances (a row of 4 staged rows is either a
+    // weight row or half a token row in every lane)
+    const uint8_t* src[IPW];
+    bool rok[IPW];
+    int pcol[IPW], cstep[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int r = 4 * (wave * IPW + i) + pq;  // staged row
+        if (r < G::UB) {
+            const int p = r16 ^ (r & 15);
+            const int row = rows[r];
+            rok[i] = row >= 0;
+            pcol[i] = 16 * p;
+            cstep[i] = KQ_KC;
+            src[i] = reinterpret_cast<const uint8_t*>(W) + (rok[i] ? (size_t)row * K + 16 * p : 0);
+        } else {
+            const int xr = r - G::UB, tok = xr >> 1, half = xr & 1;
+            const int p = r16 ^ (tok & 15);
+            rok[i] = tok < T;
+            pcol[i] = 128 * half + 8 * p;
+            cstep[i] = 2 * KQ_KC;
+            src[i] = reinterpret_cast<const uint8_t*>(x + (rok[i] ? (size_t)tok * K + pcol[i] : 0));
+        }
+    }
+    auto issue = [&](int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const bool ok = rok[i] && c * KQ_KC + pcol[i] < K;
+            const void* g = ok ? (const void*)(src[i] + (size_t)c * cstep[i]) : (const void*)zeros;
+            load_lds16(g, ring + stage * G::STAGE + 1024 * (wave * IPW + i));
+        }
+    };
+    const u32x4 neg128 = u32x4{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
+    auto compute = [&](int stage) {
+        const uint8_t* wt = ring + stage * G::STAGE;
+        const uint8_t* xt = wt + G::UB * 256;
+#pragma unroll
+        for (int kk = 0; kk < KQ_KC / 32 / G::KG; ++kk) {
+            const int ks = kk * G::KG + kgroup;
+            // A: unit row 16 ut + r16, codes of columns 32 ks + 8 pq .. + 7
+            const int pa = 2 * ks + (pq >> 1);
+            const uint2 wv = *reinterpret_cast<const uint2*>(wt + (ut * 16 + r16) * 256 +
+                                                             16 * (pa ^ r16) + 8 * (pq & 1));
+            const u32x4 af = decode_i8x8_offset(wv.x, wv.y);
+            // B: token 16 nt + r16, x of the same columns (half ks / 4 of the token row)
+            const int pb = 4 * (ks & 3) + pq;
+#pragma unroll
+            for (int i = 0; i < G::TPW; ++i) {
+                const int tok = i * 16 + r16;
+                const u32x4 bf = *reinterpret_cast<const u32x4*>(xt + (2 * tok + (ks >> 2)) * 256 +
+                                                                 16 * (pb ^ r16));
+                acc[i] = mfma_bf16(af, bf, acc[i]);
+                acc[i] = mfma_bf16(neg128, bf, acc[i]);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + NS - 1) / NS * NS;
+    for (int c0 = 0; c0 < niter; c0 += NS) {
+#pragma unroll
+        for (int d = 0; d < NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((NS - 2) * IPW);  // this wave's pieces of chunk c have landed
+            __syncthreads();                // ... and every wave's; chunk c - 1 is consumed
+            issue((d + NS - 1) % NS, c + NS - 1);
+            if (c < nchunks) compute(d);
+        }
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+}
+
+// Gate and gathered up projection of a batch, int8 weights (the plan of
+// k_gate_up_mfma): z = s1_i (q1_i . x) (LoPA: W1 is U with K = r, z = sU_i (qU_i .
+// t) over the two bf16 parts of t, plus (G x)_i when asked); for the units live for
+// some token u = s3_i (q3_i . x) (through A under double activation), and the
+// unit product is stored pre-multiplied by the W2T row scale, a_i s2_i, so the
+// down pass reads only the codes of W2T.
+template <int NT, int UT, bool DENSE, bool LOPA>
+__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ W1, const float* __restrict__ s1,
+    const int8_t* __restrict__ W3, const float* __restrict__ s3, const float* __restrict__ s2,
+    const uint16_t* __restrict__ zeros, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act,
+    const uint16_t* __restrict__ t_hi, const uint16_t* __restrict__ t_lo, int r, unsigned flags) {
+    using G = GateTilesI8<NT, UT>;
+    constexpr int TP = G::TP, UB = G::UB;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
+    __shared__ float part[G::KG][UB][TP + 1];
+    __shared__ float zf[UB][TP + 1];
+    __shared__ unsigned long long tmask[UB];
+    __shared__ int rows_g[UB];
+    __shared__ int rows_u[UB];
+    __shared__ int upos[UB];
+    __shared__ int nu_s;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15;
+    const int u0 = blockIdx.x * UB;
+    const int ut = wave % UT, kgroup = wave / UT;
+
+    if (y_zero) {
+        for (int j = blockIdx.x * KM_THREADS + threadIdx.x; j < T * D; j += gridDim.x * KM_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    if (threadIdx.x < UB) {
+        tmask[threadIdx.x] = 0ull;
+        rows_g[threadIdx.x] = (u0 + (int)threadIdx.x < H) ? u0 + (int)threadIdx.x : -1;
+    }
+    __syncthreads();
+
+    auto store_tiles = [&](const f32x4 (&acc)[G::TPW]) {
+#pragma unroll
+        for (int i = 0; i < G::TPW; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part[kgroup][ut * 16 + 4 * (lane >> 4) + j][i * 16 + r16] = acc[i][j];
+        }
+    };
+
+    {
+        f32x4 acc[G::TPW];
+        if (LOPA) {
+            f32x4 acc2[G::TPW];
+            mfma_gate_pass_i8<NT, UT>(acc, W1, rows_g, t_hi, zeros, r, T, ring);
+            mfma_gate_pass_i8<NT, UT>(acc2, W1, rows_g, t_lo, zeros, r, T, ring);
+#pragma unroll
+            for (int i = 0; i < G::TPW; ++i) acc[i] += acc2[i];
+        } else {
+            mfma_gate_pass_i8<NT, UT>(acc, W1, rows_g, x, zeros, D, T, ring);
+        }
+        store_tiles(acc);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        const bool ok = (u0 + i < H) && t < T;
+        float z = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G::KG; ++g) z += part[g][i][t];
+        if (ok) {
+            z *= s1[u0 + i];
+            if (LOPA && (flags & LOPA_G_TILED)) z += Elem<uint16_t>::get1(x[(size_t)t * D + (u0 + i) % D]);
+        }
+        zf[i][t] = z;
+        const bool live = ok && (DENSE || z > 0.0f);
+        if (live) atomicOr(&tmask[i], 1ull << t);
+        if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool any = lane < UB && tmask[lane] != 0ull;
+        const uint64_t m = __ballot(any);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (lane < UB) {
+            upos[lane] = any ? pos : -1;
+            rows_u[lane] = -1;
+            if (u0 + lane < H) umask[u0 + lane] = tmask[lane];
+        }
+        if (lane == 0) nu_s = __popcll(m);
+    }
+    __syncthreads();
+    if (threadIdx.x < UB && upos[threadIdx.x] >= 0) rows_u[upos[threadIdx.x]] = u0 + threadIdx.x;
+    const int nu = nu_s;
+    __syncthreads();
+
+    if (nu > 0) {
+        f32x4 acc[G::TPW];
+        mfma_gate_pass_i8<NT, UT>(acc, W3, rows_u, x, zeros, D, T, ring);
+        store_tiles(acc);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        if (u0 + i >= H) continue;
+        const int p = upos[i];
+        float av = 0.0f;
+        if (p >= 0 && t < T && ((tmask[i] >> t) & 1ull)) {
+            float u = 0.0f;
+#pragma unroll
+            for (int g = 0; g < G::KG; ++g) u += part[g][p][t];
+            u *= s3[u0 + i];
+            if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
+            av = activation(act, zf[i][t]) * u * s2[u0 + i];
+        }
+        a_rm[(size_t)(u0 + i) * TP + t] = av;
+    }
+}
+
+// LoPA rank projection for a batch, int8 V: t[token][m] = sV_m (qV_m . x_token),
+// 16 rank rows per block, stored token-major as bf16 hi and lo parts (as
+// k_rank_proj_mfma).
+template <int NT>
+__global__ __launch_bounds__(KM_THREADS) void k_rank_proj_mfma_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ V, const float* __restrict__ sV,
+    const uint16_t* __restrict__ zeros, uint16_t* __restrict__ t_hi, uint16_t* __restrict__ t_lo,
+    int D, int r, int T) {
+    using G = GateTilesI8<NT, 1>;
+    constexpr int TP = G::TP;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
+    __shared__ float part[G::KG][16][TP + 1];
+    __shared__ int rows[16];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int m0 = blockIdx.x * 16;
+    const int kgroup = wave;  // one unit tile: the four waves split the k-steps
+    if (threadIdx.x < 16) rows[threadIdx.x] = m0 + (int)threadIdx.x < r ? m0 + (int)threadIdx.x : -1;
+    __syncthreads();
+    f32x4 acc[G::TPW];
+    mfma_gate_pass_i8<NT, 1>(acc, V, rows, x, zeros, D, T, ring);
+#pragma unroll
+    for (int i = 0; i < G::TPW; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) part[kgroup][4 * (lane >> 4) + j][i * 16 + (lane & 15)] = acc[i][j];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < 16 * TP; e += KM_THREADS) {
+        const int m = e % 16, t = e / 16;
+        if (m0 + m >= r) continue;
+        float v = 0.0f;
+#pragma unroll
+        for (int g = 0; g < G::KG; ++g) v += part[g][m][t];
+        v = t < T ? v * sV[m0 + m] : 0.0f;
+        const uint32_t hi = bf16_rne(v);
+        const uint32_t lo = bf16_rne(v - __uint_as_float(hi << 16));
+        t_hi[(size_t)t * r + m0 + m] = (uint16_t)hi;
+        t_lo[(size_t)t * r + m0 + m] = (uint16_t)lo;
+    }
+}
+
+// Down pass of an int8 batch: k_down_mfma with the codes of W2T (16 columns per
+// 16-byte piece, two pieces per thread per chunk of 64 units x 128 columns)
+// decoded exactly into the bf16 staging layout; the unit products already carry
+// the W2T row scales. D a multiple of 16.
+template <int NT>
+__global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
+    const float* __restrict__ a_rm, const uint64_t* __restrict__ umask,
+    const int8_t* __restrict__ W2T, float* __restrict__ y, int D, int H, int T, int splits) {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    constexpr int TP = 16 * NT;
+    constexpr int APT = KDM_KC * TP / 4 / KDM_THREADS;            // float4 product pieces per thread
+    constexpr int WPT = KDM_KC * KDM_NB / 16 / KDM_THREADS;       // 16-byte code pieces per thread
+    constexpr int NCW = 2 * NT;
+    constexpr int DEPTH = NT == 1 ? 6 : (NT == 2 ? 5 : 4);
+    constexpr int WPART = 32 * 256;
+    constexpr int APART = 32 * 128;
+    constexpr int STAGE = 2 * WPART + 4 * APART;
+    constexpr int PM = KDM_LCAP / KDM_THREADS;
+    static_assert(WPT == 2 && KDM_KC == 64, "staging plan: 64 units x 128 columns");
+    __shared__ int list[KDM_LCAP];
+    __shared__ int wcnt[PM][KDM_THREADS / WAVE];
+    __shared__ __attribute__((aligned(256))) uint8_t stg[2][STAGE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int col0 = blockIdx.x * KDM_NB;
+    const int hs = (H + splits - 1) / splits;  // <= KDM_LCAP (host-checked)
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+
+    bool keep[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        const int row = h0 + p * KDM_THREADS + threadIdx.x;
+        keep[p] = row < h1 && umask[row] != 0ull;
+    }
+    uint64_t mk[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        mk[p] = __ballot(keep[p]);
+        if (lane == 0) wcnt[p][wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    int n = 0;
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        int off = n;
+        for (int w = 0; w < KDM_THREADS / WAVE; ++w) {
+            const int c = wcnt[p][w];
+            if (w < wave) off += c;
+            n += c;
+        }
+        if (keep[p]) {
+            const int pos = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+            list[pos] = h0 + p * KDM_THREADS + threadIdx.x;
+        }
+    }
+    __syncthreads();
+    const int nchunks = (n + KDM_KC - 1) / KDM_KC;
+
+    const int tt = wave / (4 / NT);
+    const int cb = (wave % (4 / NT)) * NCW;
+    f32x4 acc[NCW];
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // code piece g = tid + 256 k: unit row g / 8 of the chunk, 16 columns at 16 (g % 8)
+    u32x4 wv[DEPTH][WPT];
+    float4 av[DEPTH][APT];
+    bool wok[DEPTH][WPT], aok[DEPTH][APT];
+    auto fetch = [&](int slot, int c) {
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) {
+            const int g = threadIdx.x + k * KDM_THREADS;
+            const int e = c * KDM_KC + (g >> 3), col = col0 + 16 * (g & 7);
+            const bool ok = e < n && col < D;
+            wv[slot][k] = load_stream(W2T + (ok ? (size_t)list[e] * D + col : 0));
+            wok[slot][k] = ok;
+        }
+#pragma unroll
+        for (int q = 0; q < APT; ++q) {
+            const int idx = threadIdx.x + q * KDM_THREADS;
+            const int e = c * KDM_KC + idx / (TP / 4);
+            const bool ok = e < n;
+            av[slot][q] = *reinterpret_cast<const float4*>(
+                a_rm + (ok ? (size_t)list[e] * TP + 4 * (idx % (TP / 4)) : 0));
+            aok[slot][q] = ok;
+        }
+    };
+    auto stage_write = [&](int stage, int d) {
+        uint8_t* st = stg[stage];
+#pragma unroll
+        for (int k = 0; k < WPT; ++k) {
+            const int g = threadIdx.x + k * KDM_THREADS;
+            const int row = g >> 3, r = row & 31, p0 = 2 * (g & 7);
+            const u32x4 w = wok[d][k] ? wv[d][k] : u32x4{0u, 0u, 0u, 0u};
+            uint8_t* base = st + (row >> 5) * WPART + r * 256;
+            *reinterpret_cast<u32x4*>(base + 16 * swz256(r, p0)) = decode_i8x8(w[0], w[1]);
+            *reinterpret_cast<u32x4*>(base + 16 * swz256(r, p0 + 1)) = decode_i8x8(w[2], w[3]);
+        }
+#pragma unroll
+        for (int q = 0; q < APT; ++q) {
+            const int idx = threadIdx.x + q * KDM_THREADS;
+            const int row = idx / (TP / 4), r = row & 31, t0 = 4 * (idx % (TP / 4));
+            const float4 f = aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float fv[4] = {f.x, f.y, f.z, f.w};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hi[j] = bf16_rne(fv[j]);
+                lo[j] = bf16_rne(fv[j] - __uint_as_float(hi[j] << 16));
+            }
+            const int off = 2 * WPART + (row >> 5) * APART + r * 128 + 16 * swz128(r, t0 >> 3) + 8 * ((t0 >> 2) & 1);
+            *reinterpret_cast<uint2*>(st + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+            *reinterpret_cast<uint2*>(st + off + 2 * APART) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        }
+    };
+    auto compute = [&](int stage) {
+        const uint8_t* st = stg[stage];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint8_t* ah = st + 2 * WPART + ks * APART;
+            const u32x4 fh = frag_tr128(ah, tt * 16, lane);
+            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane);
+#pragma unroll
+            for (int i = 0; i < NCW; ++i) {
+                const u32x4 b = frag_tr(st + ks * WPART, (cb + i) * 16, lane);
+                acc[i] = mfma_bf16(fh, b, acc[i]);
+                acc[i] = mfma_bf16(fl, b, acc[i]);
+            }
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) fetch(d, d);
+    stage_write(0, 0);
+    __syncthreads();
+    fetch(0, DEPTH);
+    const int niter = (nchunks + DEPTH - 1) / DEPTH * DEPTH;
+    for (int c0 = 0; c0 < niter; c0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int c = c0 + d;
+            const int nslot = (d + 1) % DEPTH;
+            stage_write((c + 1) & 1, nslot);
+            if (c < nchunks) compute(c & 1);
+            __syncthreads();
+            fetch(nslot, c + 1 + DEPTH);
+        }
+    }
+    if (n == 0 && splits > 1) return;
+    const int r16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+        const int col = col0 + (cb + i) * 16 + r16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = tt * 16 + 4 * (lane >> 4) + j;
+            if (t < T && col < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + col, acc[i][j]);
+                else
+                    y[(size_t)t * D + col] = acc[i][j];
+            }
+        }
+    }
+}
+
 // Epilogue of the small-batch down passes: each lane's TT x VEC column sums are
 // reduced over the wave's lane groups (shuffles), the wave sums of up to TR
 // tokens at a time are staged in LDS (red[TR][KD_WAVES][CB]), and after one

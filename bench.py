@@ -952,20 +952,40 @@ def main() -> int:
         b4["union_vs_dense"] = round(b4["union_tokens_per_s"] / b4["dense_tokens_per_s"], 3)
         res_q["batch4"] = b4
         hq4.close()
-        # union batches of 16 tokens (four groups of 4 through the same kernels)
-        hq16 = sffn.Handle(D, H, 0, 16, act, sffn.SFFN_I8)
-
-        def fn16():
-            for c in range(n // 16):
-                rp = repq[c % R]
-                sffn.sffn_forward_sparse_i8(hq16.ptr, x[16 * c:16 * c + 16], rp["W1"], rp["W1_scale"],
-                                            rp["W3"], rp["W3_scale"], rp["W2T"], rp["W2T_scale"],
-                                            y[16 * c:16 * c + 16], 16, sffn.SFFN_MODE_UNION)
-        g16 = capture(fn16)
-        ms16 = time_graph(g16, args.steps, args.warmup)
-        del g16
-        res_q["batch16_union_tokens_per_s"] = round(16 * (n // 16) / (ms16 * 1e-3), 1)
-        hq16.close()
+        # union and dense batches of 16 and 64 tokens (one MFMA pass over the codes per call)
+        hq64 = sffn.Handle(D, H, 0, 64, act, sffn.SFFN_I8)
+        bq = {}
+        for TB in (16, 64):
+            rq = {}
+            for name, dense in (("union", False), ("dense", True)):
+                def fnT(TB=TB, dense=dense):
+                    for c in range(n // TB):
+                        rp = repq[c % R]
+                        a_ = (hq64.ptr, x[TB * c:TB * c + TB], rp["W1"], rp["W1_scale"], rp["W3"],
+                              rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[TB * c:TB * c + TB], TB)
+                        if dense:
+                            sffn.sffn_forward_dense_i8(*a_)
+                        else:
+                            sffn.sffn_forward_sparse_i8(*a_, sffn.SFFN_MODE_UNION)
+                gT = capture(fnT)
+                msT = time_graph(gT, args.steps, args.warmup)
+                del gT
+                rq[name + "_tokens_per_s"] = round(TB * (n // TB) / (msT * 1e-3), 1)
+                if not dense:
+                    sffn.sffn_timing_enable(hq64.ptr, True)
+                    fnT()
+                    torch.cuda.synchronize()
+                    sffn.sffn_timing_enable(hq64.ptr, False)
+                    kb = {}
+                    for kd in range(nk):
+                        ms_k, launches = sffn.sffn_timing_read(hq64.ptr, kd, reset=(kd == nk - 1))
+                        if launches:
+                            kb[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
+                    rq["union_kernel_us"] = kb
+            rq["union_vs_dense"] = round(rq["union_tokens_per_s"] / rq["dense_tokens_per_s"], 3)
+            bq[f"T{TB}"] = rq
+        res_q["batched"] = bq
+        hq64.close()
         extras["int8"] = res_q
         log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items() if not isinstance(v, dict))
             + f", kernels (us/launch) {ktq}, batch of 4 {b4}")
