@@ -30,7 +30,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_DENSE_T1_I4, KIND_DOWN_T1_I4, KIND_GATE_UP_LOPA_T1_I4,
             KIND_RANK_PROJ_MFMA, KIND_GATE_UP_TB_I8, KIND_DOWN_TB_I8, KIND_GATE_UP_TB_I4,
             KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_DOWN_PT,
-            KIND_GATE_UP_MFMA_I8, KIND_DOWN_MFMA_I8, KIND_RANK_PROJ_MFMA_I8, KIND_COUNT };
+            KIND_GATE_UP_MFMA_I8, KIND_DOWN_MFMA_I8, KIND_RANK_PROJ_MFMA_I8,
+            KIND_GATE_UP_MFMA_I4, KIND_DOWN_MFMA_I4, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -47,7 +48,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_gate_up_tb_i8", "k_down_tb_i8", "k_gate_up_tb_i4",
                                             "k_down_tb_i4", "k_rank_proj_tb_i8", "k_gate_up_lopa_tb_q",
                                             "k_down_pt", "k_gate_up_mfma_i8", "k_down_mfma_i8",
-                                            "k_rank_proj_mfma_i8"};
+                                            "k_rank_proj_mfma_i8", "k_gate_up_mfma_i4",
+                                            "k_down_mfma_i4"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -692,6 +694,48 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
                                    dim3(KDM_THREADS), s, (const float*)h->m_a,
                                    (const uint64_t*)h->m_mask, (const int8_t*)W2T, y, h->D, h->H,
                                    T, splits));
+    if (st != SFFN_OK) return st;
+    if (!DENSE) return run_live_list(h, T, live_count, live_idx, s);
+    return SFFN_OK;
+}
+
+// int4 union (and dense) batches of 5..64 tokens on MFMA: every code read once for
+// the batch. LOPA: W1 is U (int8 rows, scales s1 = U's), V int8 with sV.
+bool mfma_i4_ok(const sffn_handle* h, int T) {
+    return T > 4 && h->dtype == SFFN_I4 && h->m_a != nullptr && T <= h->max_tokens;
+}
+
+template <bool DENSE, bool LOPA = false>
+sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const float* s1,
+                        const void* W3, const float* s3, const void* W2T, const float* s2,
+                        float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s,
+                        const void* V = nullptr, const float* sV = nullptr) {
+    const int nt = token_tiles(T);
+    uint8_t* live = live_count ? h->live_buf : nullptr;
+    sffn_status st = SFFN_OK;
+    uint16_t* t_hi = h->m_t;
+    uint16_t* t_lo = h->m_t ? h->m_t + (size_t)h->m_tp * h->r : nullptr;
+    if (LOPA) {
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA_I8, k_rank_proj_mfma_i8<NT>,
+                                       dim3((h->r + 15) / 16), dim3(KM_THREADS), s,
+                                       (const uint16_t*)x, (const int8_t*)V, sV,
+                                       (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
+        if (st != SFFN_OK) return st;
+    }
+    const int nb = (h->H + 31) / 32;
+    const int splits = h->m_splits;
+    float* yz = splits > 1 ? y : nullptr;
+    SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_I4, k_gate_up_mfma_i4<NT, DENSE, LOPA>,
+                                   dim3(nb), dim3(KM_THREADS), s, (const uint16_t*)x, W1, s1,
+                                   (const uint8_t*)W3, s3, (const uint16_t*)h->m_zero, h->m_a,
+                                   h->m_mask, live, yz, h->D, h->H, T, h->act,
+                                   (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r, h->flags));
+    if (st != SFFN_OK) return st;
+    const int ntile = (h->D + KDM_NB - 1) / KDM_NB;
+    SFFN_NT_SWITCH(nt, st = launch(h, KIND_DOWN_MFMA_I4, k_down_mfma_i4<NT>, dim3(ntile, splits),
+                                   dim3(KDM_THREADS), s, (const float*)h->m_a,
+                                   (const uint64_t*)h->m_mask, (const uint8_t*)W2T, s2, y, h->D,
+                                   h->H, T, splits));
     if (st != SFFN_OK) return st;
     if (!DENSE) return run_live_list(h, T, live_count, live_idx, s);
     return SFFN_OK;
@@ -1440,12 +1484,14 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     if (!s1 || !s3 || !s2) return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // int8 union (and dense) batches above 4 tokens: one MFMA pass over the weights
+    // int8 and int4 union (and dense) batches above 4 tokens: one MFMA pass over the weights
     if (bits == 8 && mfma_i8_ok(h, T) && (dense || mode == SFFN_MODE_UNION))
         return dense ? run_mfma_i8<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
                      : run_mfma_i8<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
-    // union (and dense) batches of 2..4 tokens read the weights once for the batch;
-    // larger int4 ones go as groups of 2..4 consecutive tokens (sizes as equal as can be)
+    if (bits == 4 && mfma_i4_ok(h, T) && (dense || mode == SFFN_MODE_UNION))
+        return dense ? run_mfma_i4<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
+                     : run_mfma_i4<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
+    // union (and dense) batches of 2..4 tokens read the weights once for the batch
     if (T >= 2 && h->m_a && (dense || mode == SFFN_MODE_UNION)) {
         const int ng = (T + 3) / 4;
         for (int g = 0, t0 = 0; g < ng; ++g) {
@@ -1618,12 +1664,16 @@ static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, 
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(sV) || !al4(sU) || !al4(s3) || !al4(s2))
         return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // int8 union batches above 4 tokens: one MFMA pass over V, U, the W3 rows of the
+    // int8 and int4 union batches above 4 tokens: one MFMA pass over V, U, the W3 rows of the
     // union and their W2T rows (RMSNorm of t excepted: it needs each token's whole t
     // before the gate)
     if (bits == 8 && mode == SFFN_MODE_UNION && mfma_i8_ok(h, T) && h->m_t &&
         !(h->flags & SFFN_FLAG_RMSNORM))
         return run_mfma_i8<false, true>(h, x, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx,
+                                        s, V, sV);
+    if (bits == 4 && mode == SFFN_MODE_UNION && mfma_i4_ok(h, T) && h->m_t &&
+        !(h->flags & SFFN_FLAG_RMSNORM))
+        return run_mfma_i4<false, true>(h, x, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx,
                                         s, V, sV);
     // union batches of 2..4 tokens read the weights once for the batch; larger ones
     // go as groups of 2..4 consecutive tokens (sizes as equal as can be)

@@ -2982,6 +2982,481 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
     }
 }
 
+// ---- weight-only int4 batches on MFMA (5..64 tokens)
+// As the int8 batches, with codes packed two per byte (column 2j in the low
+// nibble) and one fp32 scale per 128 columns of a row. A 256-column chunk holds
+// two scale groups, so each wave sums a group's k-steps in a separate tile and
+// adds it into its accumulator times the group scale of each row.
+
+// 8 int4 codes (one dword: columns 2b, 2b + 1 in byte b) -> the 8 bf16 values
+// n + 136 in column order: the offset nibble n + 8 goes into the low mantissa bits
+// of 128.0 (bf16 0x4300), one byte permute per pair of columns.
+__device__ inline u32x4 decode_i4x8_offset(uint32_t w) {
+    const uint32_t wq = w ^ 0x88888888u;
+    const uint32_t lo = wq & 0x0F0F0F0Fu;         // byte b: column 2b
+    const uint32_t hi = (wq >> 4) & 0x0F0F0F0Fu;  // byte b: column 2b + 1
+    u32x4 o;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        // bytes: lo.b, 0, hi.b, 0 (selector 0x0c gives a zero byte)
+        const uint32_t sel = (uint32_t)b | (0x0cu << 8) | ((4u + b) << 16) | (0x0cu << 24);
+        o[b] = __builtin_amdgcn_perm(hi, lo, sel) | 0x43004300u;
+    }
+    return o;
+}
+
+// Staging of the int4 gate pass (32 units per block): per 256-column chunk a
+// weight row gives 128 bytes of codes (8 pieces of 32 codes; in row r, LDS slot j
+// holds piece j ^ ((r >> 1) % 8), so the 4-byte fragment reads of 16 rows at one
+// k-step spread over the banks) and a token row of x 512 bytes, staged as in the
+// int8 pass. Wave w multiplies unit tile w % 2 against all token tiles over the
+// k-steps ks = w / 2 (mod 2) of each chunk.
+constexpr int I4_GMAX = 64;  // scale groups per row (D <= 8192)
+template <int NT>
+struct GateTilesI4 {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    static constexpr int TP = 16 * NT;
+    static constexpr int UB = 32;
+    static constexpr int KG = 2;
+    static constexpr int TPW = NT;
+    static constexpr int WI = UB / 8;                   // weight load instructions per chunk (1 KB each)
+    static constexpr int IPW = (WI + TP / 2) / 4;       // load instructions per wave per chunk
+    static constexpr int STAGE = UB * 128 + 2 * TP * 256;
+    static constexpr int NS = STAGE <= 24576 ? 4 : 3;
+    static constexpr int SPT = UB * I4_GMAX / KM_THREADS;  // scale entries per thread
+    static_assert((WI + TP / 2) % 4 == 0, "whole load instructions per wave");
+    static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
+};
+
+// acc[i] (tiles of this wave) = sum over the K columns (a multiple of 128) of
+// scale(row, group) * (codes of rows[] x tokens of x). Each weight operand is
+// decoded as n + 136 and a second MFMA with the constant -136 takes the offset
+// off. `sc` (LDS, UB x I4_GMAX) receives the rows' group scales, loaded ahead of
+// the ring and stored while chunk 0 lands.
+template <int NT>
+__device__ inline void mfma_gate_pass_i4(f32x4* acc, const uint8_t* __restrict__ W,
+                                         const float* __restrict__ scales, const int* rows,
+                                         const uint16_t* __restrict__ x,
+                                         const uint16_t* __restrict__ zeros, int K, int T,
+                                         uint8_t* ring, float (*sc)[I4_GMAX]) {
+    using G = GateTilesI4<NT>;
+    constexpr int NS = G::NS, IPW = G::IPW;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15, pq = lane >> 4;
+    const int ut = wave % 2, kgroup = wave / 2;
+    const int nchunks = (K + KQ_KC - 1) / KQ_KC;
+    const int ng = K / I4_GROUP;
+#pragma unroll
+    for (int i = 0; i < G::TPW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // group scales of the block's rows (issued before the ring loads)
+    float sv[G::SPT];
+#pragma unroll
+    for (int m = 0; m < G::SPT; ++m) {
+        const int e = threadIdx.x + m * KM_THREADS;
+        const int rl = e / I4_GMAX, g = e % I4_GMAX;
+        const int row = rows[rl];
+        sv[m] = (g < ng && row >= 0) ? scales[(size_t)row * ng + g] : 0.0f;
+    }
+
+    const uint8_t* src[IPW];
+    bool rok[IPW];
+    int pcol[IPW], cstep[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;  // load instruction of the chunk
+        if (q < G::WI) {
+            const int rl = 8 * q + (lane >> 3);
+            const int p = (lane & 7) ^ ((rl >> 1) & 7);
+            const int row = rows[rl];
+            rok[i] = row >= 0;
+            pcol[i] = 32 * p;
+            cstep[i] = KQ_KC / 2;
+            src[i] = W + (rok[i] ? (size_t)row * (K / 2) + 16 * p : 0);
+        } else {
+            const int xr = 4 * (q - G::WI) + pq, tok = xr >> 1, half = xr & 1;
+            const int p = r16 ^ (tok & 15);
+            rok[i] = tok < T;
+            pcol[i] = 128 * half + 8 * p;
+            cstep[i] = 2 * KQ_KC;
+            src[i] = reinterpret_cast<const uint8_t*>(x + (rok[i] ? (size_t)tok * K + pcol[i] : 0));
+        }
+    }
+    auto issue = [&](int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const bool ok = rok[i] && c * KQ_KC + pcol[i] < K;
+            const void* g = ok ? (const void*)(src[i] + (size_t)c * cstep[i]) : (const void*)zeros;
+            load_lds16(g, ring + stage * G::STAGE + 1024 * (wave * IPW + i));
+        }
+    };
+    const u32x4 neg136 = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+    const int arow = ut * 16 + r16;
+    auto compute = [&](int stage, int c) {
+        const uint8_t* wt = ring + stage * G::STAGE;
+        const uint8_t* xt = wt + G::UB * 128;
+#pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {  // the chunk's two scale groups
+            f32x4 tmp[G::TPW];
+#pragma unroll
+            for (int i = 0; i < G::TPW; ++i) tmp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                const int ks = 4 * gh + 2 * kk + kgroup;
+                // A: codes of columns 32 ks + 8 pq .. + 7 (piece ks, bytes 4 pq .. + 3)
+                const uint32_t wv = *reinterpret_cast<const uint32_t*>(
+                    wt + arow * 128 + 16 * (ks ^ ((arow >> 1) & 7)) + 4 * pq);
+                const u32x4 af = decode_i4x8_offset(wv);
+                const int pb = 4 * (ks & 3) + pq;
+#pragma unroll
+                for (int i = 0; i < G::TPW; ++i) {
+                    const int tok = i * 16 + r16;
+                    const u32x4 bf = *reinterpret_cast<const u32x4*>(
+                        xt + (2 * tok + (ks >> 2)) * 256 + 16 * (pb ^ r16));
+                    tmp[i] = mfma_bf16(af, bf, tmp[i]);
+                    tmp[i] = mfma_bf16(neg136, bf, tmp[i]);
+                }
+            }
+            // C rows of this lane: 4 (lane / 16) + j of the unit tile
+            const int g = 2 * c + gh;
+            float s4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s4[j] = sc[ut * 16 + 4 * pq + j][g < I4_GMAX ? g : 0];
+#pragma unroll
+            for (int i = 0; i < G::TPW; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(s4[j], tmp[i][j], acc[i][j]);
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + NS - 1) / NS * NS;
+    for (int c0 = 0; c0 < niter; c0 += NS) {
+#pragma unroll
+        for (int d = 0; d < NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((NS - 2) * IPW);  // this wave's pieces of chunk c (and the scales) have landed
+            if (c == 0) {
+#pragma unroll
+                for (int m = 0; m < G::SPT; ++m) {
+                    const int e = threadIdx.x + m * KM_THREADS;
+                    sc[e / I4_GMAX][e % I4_GMAX] = sv[m];
+                }
+            }
+            __syncthreads();                // ... and every wave's; chunk c - 1 is consumed
+            issue((d + NS - 1) % NS, c + NS - 1);
+            if (c < nchunks) compute(d, c);
+        }
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+}
+
+// Gate and gathered up projection of a batch, int4 up (and gate) weights:
+// z = sum_g s1_ig (q1_i,g . x_g) over the int4 W1 (LoPA: z = sU_i (qU_i . t) over
+// the int8 U and the two bf16 parts of t, plus (G x)_i when asked); for the units
+// live for some token u = sum_g s3_ig (q3_i,g . x_g) (through A under double
+// activation); a_i = A(z_i) u_i is stored unscaled (the W2T group scales vary
+// along D, so the down pass applies them).
+template <int NT, bool DENSE, bool LOPA>
+__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
+    const uint16_t* __restrict__ x, const void* __restrict__ W1, const float* __restrict__ s1,
+    const uint8_t* __restrict__ W3, const float* __restrict__ s3,
+    const uint16_t* __restrict__ zeros, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act,
+    const uint16_t* __restrict__ t_hi, const uint16_t* __restrict__ t_lo, int r, unsigned flags) {
+    using G4 = GateTilesI4<NT>;
+    using G8 = GateTilesI8<NT, 2>;
+    constexpr int TP = G4::TP, UB = G4::UB, KG = G4::KG;
+    static_assert(G8::UB == UB && G8::KG == KG, "one tile plan for both passes");
+    constexpr int RING = (LOPA && G8::NS * G8::STAGE > G4::NS * G4::STAGE) ? G8::NS * G8::STAGE
+                                                                         : G4::NS * G4::STAGE;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[RING];
+    __shared__ float part[KG][UB][TP + 1];
+    __shared__ float zf[UB][TP + 1];
+    __shared__ float sc[UB][I4_GMAX];
+    __shared__ unsigned long long tmask[UB];
+    __shared__ int rows_g[UB];
+    __shared__ int rows_u[UB];
+    __shared__ int upos[UB];
+    __shared__ int nu_s;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15;
+    const int u0 = blockIdx.x * UB;
+    const int ut = wave % 2, kgroup = wave / 2;
+
+    if (y_zero) {
+        for (int j = blockIdx.x * KM_THREADS + threadIdx.x; j < T * D; j += gridDim.x * KM_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    if (threadIdx.x < UB) {
+        tmask[threadIdx.x] = 0ull;
+        rows_g[threadIdx.x] = (u0 + (int)threadIdx.x < H) ? u0 + (int)threadIdx.x : -1;
+    }
+    __syncthreads();
+
+    auto store_tiles = [&](const f32x4 (&acc)[NT]) {
+#pragma unroll
+        for (int i = 0; i < NT; ++i) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                part[kgroup][ut * 16 + 4 * (lane >> 4) + j][i * 16 + r16] = acc[i][j];
+        }
+    };
+
+    {
+        f32x4 acc[NT];
+        if (LOPA) {
+            f32x4 acc2[NT];
+            mfma_gate_pass_i8<NT, 2>(acc, (const int8_t*)W1, rows_g, t_hi, zeros, r, T, ring);
+            mfma_gate_pass_i8<NT, 2>(acc2, (const int8_t*)W1, rows_g, t_lo, zeros, r, T, ring);
+#pragma unroll
+            for (int i = 0; i < NT; ++i) acc[i] += acc2[i];
+        } else {
+            mfma_gate_pass_i4<NT>(acc, (const uint8_t*)W1, s1, rows_g, x, zeros, D, T, ring, sc);
+        }
+        store_tiles(acc);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        const bool ok = (u0 + i < H) && t < T;
+        float z = 0.0f;
+#pragma unroll
+        for (int g = 0; g < KG; ++g) z += part[g][i][t];
+        if (ok && LOPA) {
+            z *= s1[u0 + i];
+            if (flags & LOPA_G_TILED) z += Elem<uint16_t>::get1(x[(size_t)t * D + (u0 + i) % D]);
+        }
+        zf[i][t] = z;
+        const bool live = ok && (DENSE || z > 0.0f);
+        if (live) atomicOr(&tmask[i], 1ull << t);
+        if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        const bool any = lane < UB && tmask[lane] != 0ull;
+        const uint64_t m = __ballot(any);
+        const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0));
+        if (lane < UB) {
+            upos[lane] = any ? pos : -1;
+            rows_u[lane] = -1;
+            if (u0 + lane < H) umask[u0 + lane] = tmask[lane];
+        }
+        if (lane == 0) nu_s = __popcll(m);
+    }
+    __syncthreads();
+    if (threadIdx.x < UB && upos[threadIdx.x] >= 0) rows_u[upos[threadIdx.x]] = u0 + threadIdx.x;
+    const int nu = nu_s;
+    __syncthreads();
+
+    if (nu > 0) {
+        f32x4 acc[NT];
+        mfma_gate_pass_i4<NT>(acc, W3, s3, rows_u, x, zeros, D, T, ring, sc);
+        store_tiles(acc);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        if (u0 + i >= H) continue;
+        const int p = upos[i];
+        float av = 0.0f;
+        if (p >= 0 && t < T && ((tmask[i] >> t) & 1ull)) {
+            float u = 0.0f;
+#pragma unroll
+            for (int g = 0; g < KG; ++g) u += part[g][p][t];
+            if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
+            av = activation(act, zf[i][t]) * u;
+        }
+        a_rm[(size_t)(u0 + i) * TP + t] = av;
+    }
+}
+
+// Down pass of an int4 batch: k_down_mfma with the codes of W2T (32 columns per
+// 16-byte piece, one piece per thread per chunk of 64 units x 128 columns)
+// decoded exactly into the bf16 staging layout; the block's 128 columns are one
+// scale group, so each unit's product is multiplied by its group scale as it is
+// staged. D a multiple of 128.
+template <int NT>
+__global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i4(
+    const float* __restrict__ a_rm, const uint64_t* __restrict__ umask,
+    const uint8_t* __restrict__ W2T, const float* __restrict__ s2, float* __restrict__ y, int D,
+    int H, int T, int splits) {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    static_assert(KDM_NB == I4_GROUP, "one scale group per column tile");
+    constexpr int TP = 16 * NT;
+    constexpr int APT = KDM_KC * TP / 4 / KDM_THREADS;
+    constexpr int NCW = 2 * NT;
+    constexpr int DEPTH = NT == 1 ? 6 : (NT == 2 ? 5 : 4);
+    constexpr int WPART = 32 * 256;
+    constexpr int APART = 32 * 128;
+    constexpr int STAGE = 2 * WPART + 4 * APART;
+    constexpr int PM = KDM_LCAP / KDM_THREADS;
+    static_assert(KDM_KC * KDM_NB / 32 == KDM_THREADS, "one code piece per thread per chunk");
+    __shared__ int list[KDM_LCAP];
+    __shared__ int wcnt[PM][KDM_THREADS / WAVE];
+    __shared__ __attribute__((aligned(256))) uint8_t stg[2][STAGE];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int col0 = blockIdx.x * KDM_NB;
+    const int ng = D / I4_GROUP;
+    const int grp = col0 / I4_GROUP;
+    const int hs = (H + splits - 1) / splits;  // <= KDM_LCAP (host-checked)
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+
+    bool keep[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        const int row = h0 + p * KDM_THREADS + threadIdx.x;
+        keep[p] = row < h1 && umask[row] != 0ull;
+    }
+    uint64_t mk[PM];
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        mk[p] = __ballot(keep[p]);
+        if (lane == 0) wcnt[p][wave] = __popcll(mk[p]);
+    }
+    __syncthreads();
+    int n = 0;
+#pragma unroll
+    for (int p = 0; p < PM; ++p) {
+        int off = n;
+        for (int w = 0; w < KDM_THREADS / WAVE; ++w) {
+            const int c = wcnt[p][w];
+            if (w < wave) off += c;
+            n += c;
+        }
+        if (keep[p]) {
+            const int pos = off + __builtin_amdgcn_mbcnt_hi((uint32_t)(mk[p] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mk[p], 0));
+            list[pos] = h0 + p * KDM_THREADS + threadIdx.x;
+        }
+    }
+    __syncthreads();
+    const int nchunks = (n + KDM_KC - 1) / KDM_KC;
+
+    const int tt = wave / (4 / NT);
+    const int cb = (wave % (4 / NT)) * NCW;
+    f32x4 acc[NCW];
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // code piece tid: unit row tid / 4 of the chunk, 32 columns at 32 (tid % 4)
+    u32x4 wv[DEPTH];
+    float4 av[DEPTH][APT];
+    float sa[DEPTH][APT];
+    bool wok[DEPTH], aok[DEPTH][APT];
+    auto fetch = [&](int slot, int c) {
+        {
+            const int e = c * KDM_KC + (threadIdx.x >> 2), col = col0 + 32 * (threadIdx.x & 3);
+            const bool ok = e < n && col < D;
+            wv[slot] = load_stream(W2T + (ok ? (size_t)list[e] * (D / 2) + col / 2 : 0));
+            wok[slot] = ok;
+        }
+#pragma unroll
+        for (int q = 0; q < APT; ++q) {
+            const int idx = threadIdx.x + q * KDM_THREADS;
+            const int e = c * KDM_KC + idx / (TP / 4);
+            const bool ok = e < n;
+            const size_t unit = ok ? (size_t)list[e] : 0;
+            av[slot][q] = *reinterpret_cast<const float4*>(a_rm + unit * TP + (ok ? 4 * (idx % (TP / 4)) : 0));
+            sa[slot][q] = ok ? s2[unit * ng + grp] : 0.0f;
+            aok[slot][q] = ok;
+        }
+    };
+    auto stage_write = [&](int stage, int d) {
+        uint8_t* st = stg[stage];
+        {
+            const int row = threadIdx.x >> 2, r = row & 31, p0 = 4 * (threadIdx.x & 3);
+            const u32x4 w = wok[d] ? wv[d] : u32x4{0u, 0u, 0u, 0u};  // codes 0
+            uint8_t* base = st + (row >> 5) * WPART + r * 256;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // value n + 136 minus 136, exact in fp32; bf16 of the integer n
+                const u32x4 o = decode_i4x8_offset(w[k]);
+                u32x4 v;
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const float f0 = __uint_as_float(o[h] << 16) - 136.0f;
+                    const float f1 = __uint_as_float(o[h] & 0xffff0000u) - 136.0f;
+                    v[h] = __builtin_amdgcn_perm(__float_as_uint(f1), __float_as_uint(f0), 0x07060302u);
+                }
+                *reinterpret_cast<u32x4*>(base + 16 * swz256(r, p0 + k)) = v;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < APT; ++q) {
+            const int idx = threadIdx.x + q * KDM_THREADS;
+            const int row = idx / (TP / 4), r = row & 31, t0 = 4 * (idx % (TP / 4));
+            const float4 f = aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float sg = sa[d][q];
+            const float fv[4] = {f.x * sg, f.y * sg, f.z * sg, f.w * sg};
+            uint32_t hi[4], lo[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hi[j] = bf16_rne(fv[j]);
+                lo[j] = bf16_rne(fv[j] - __uint_as_float(hi[j] << 16));
+            }
+            const int off = 2 * WPART + (row >> 5) * APART + r * 128 + 16 * swz128(r, t0 >> 3) + 8 * ((t0 >> 2) & 1);
+            *reinterpret_cast<uint2*>(st + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
+            *reinterpret_cast<uint2*>(st + off + 2 * APART) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+        }
+    };
+    auto compute = [&](int stage) {
+        const uint8_t* st = stg[stage];
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const uint8_t* ah = st + 2 * WPART + ks * APART;
+            const u32x4 fh = frag_tr128(ah, tt * 16, lane);
+            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane);
+#pragma unroll
+            for (int i = 0; i < NCW; ++i) {
+                const u32x4 b = frag_tr(st + ks * WPART, (cb + i) * 16, lane);
+                acc[i] = mfma_bf16(fh, b, acc[i]);
+                acc[i] = mfma_bf16(fl, b, acc[i]);
+            }
+        }
+    };
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) fetch(d, d);
+    stage_write(0, 0);
+    __syncthreads();
+    fetch(0, DEPTH);
+    const int niter = (nchunks + DEPTH - 1) / DEPTH * DEPTH;
+    for (int c0 = 0; c0 < niter; c0 += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            const int c = c0 + d;
+            const int nslot = (d + 1) % DEPTH;
+            stage_write((c + 1) & 1, nslot);
+            if (c < nchunks) compute(c & 1);
+            __syncthreads();
+            fetch(nslot, c + 1 + DEPTH);
+        }
+    }
+    if (n == 0 && splits > 1) return;
+    const int r16 = lane & 15;
+#pragma unroll
+    for (int i = 0; i < NCW; ++i) {
+        const int col = col0 + (cb + i) * 16 + r16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int t = tt * 16 + 4 * (lane >> 4) + j;
+            if (t < T && col < D) {
+                if (splits > 1)
+                    atomicAdd(y + (size_t)t * D + col, acc[i][j]);
+                else
+                    y[(size_t)t * D + col] = acc[i][j];
+            }
+        }
+    }
+}
+
 // Epilogue of the small-batch down passes: each lane's TT x VEC column sums are
 // reduced over the wave's lane groups (shuffles), the wave sums of up to TR
 // tokens at a time are staged in LDS (red[TR][KD_WAVES][CB]), and after one
