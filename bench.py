@@ -174,6 +174,16 @@ def summarize_counters(db_dir: str, out: str, command: str) -> None:
         f.write("\n".join(lines) + "\n")
 
 
+def _calibration_copy(torch):
+    """A plain copy of known size (one scalar multiply of CALIB_BYTES of floats), for
+    scaling the HBM byte counters of a profile of this run."""
+    calib = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
+    calib_out = torch.empty_like(calib)
+    torch.mul(calib, 1.0, out=calib_out)
+    torch.cuda.synchronize()
+    del calib, calib_out
+
+
 def _graph_time(torch, fn, steps, warmup):
     """Capture fn once into a HIP graph; ms per replay."""
     g = torch.cuda.CUDAGraph()
@@ -193,6 +203,43 @@ def _graph_time(torch, fn, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) / steps
+
+
+def _quant_batches(torch, sffn, h, fwd_sparse, fwd_dense, reps, x, y, n, args, sizes=(16, 64)):
+    """Union (and, with fwd_dense, dense) calls of T tokens through a quantised forward;
+    the weight tuple of each call is reps[c % len(reps)], x and y hold n tokens."""
+    out = {}
+    nk = sffn.sffn_kernel_kinds()
+    for TB in sizes:
+        rq = {}
+        for name, fwd in (("union", fwd_sparse), ("dense", fwd_dense)):
+            if fwd is None:
+                continue
+
+            def fn(TB=TB, fwd=fwd, name=name):
+                for c in range(n // TB):
+                    a_ = (h.ptr, x[TB * c:TB * c + TB]) + reps[c % len(reps)] + (y[TB * c:TB * c + TB], TB)
+                    if name == "union":
+                        fwd(*a_, sffn.SFFN_MODE_UNION)
+                    else:
+                        fwd(*a_)
+            ms = _graph_time(torch, fn, max(2, args.steps // 2), 1)
+            rq[name + "_tokens_per_s"] = round(TB * (n // TB) / (ms * 1e-3), 1)
+            if name == "union":
+                sffn.sffn_timing_enable(h.ptr, True)
+                fn()
+                torch.cuda.synchronize()
+                sffn.sffn_timing_enable(h.ptr, False)
+                kb = {}
+                for kd in range(nk):
+                    ms_k, launches = sffn.sffn_timing_read(h.ptr, kd, reset=(kd == nk - 1))
+                    if launches:
+                        kb[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
+                rq["union_kernel_us"] = kb
+        if "dense_tokens_per_s" in rq:
+            rq["union_vs_dense"] = round(rq["union_tokens_per_s"] / rq["dense_tokens_per_s"], 3)
+        out[f"T{TB}"] = rq
+    return out
 
 
 def bench_lopa_batched(torch, sffn, gen, to_dev, act, args):
@@ -607,6 +654,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     if args.only_batched:
+        _calibration_copy(torch)
         res = bench_batched(torch, sffn, gen, to_dev, x, reps, D, H, act, args)
         print(json.dumps({"batched": res}), flush=True)
         return 0
@@ -714,12 +762,7 @@ def main() -> int:
     log("kernels (us/launch): " + ", ".join(f"{n_} {v:.2f}" for n_, v in kt.items()))
     log(f"dominant {dom}: {gate_bytes / 1e6:.2f} MB algorithmic per launch, {achieved:,.0f} GB/s")
 
-    # a plain copy of known size, for scaling the HBM byte counters of a profile of this run
-    calib = torch.ones(CALIB_BYTES // 4, dtype=torch.float32, device="cuda")
-    calib_out = torch.empty_like(calib)
-    torch.mul(calib, 1.0, out=calib_out)
-    torch.cuda.synchronize()
-    del calib, calib_out
+    _calibration_copy(torch)
 
     extras = {}
     if not args.no_extras and not args.only_lopa:
@@ -954,37 +997,10 @@ def main() -> int:
         hq4.close()
         # union and dense batches of 16 and 64 tokens (one MFMA pass over the codes per call)
         hq64 = sffn.Handle(D, H, 0, 64, act, sffn.SFFN_I8)
-        bq = {}
-        for TB in (16, 64):
-            rq = {}
-            for name, dense in (("union", False), ("dense", True)):
-                def fnT(TB=TB, dense=dense):
-                    for c in range(n // TB):
-                        rp = repq[c % R]
-                        a_ = (hq64.ptr, x[TB * c:TB * c + TB], rp["W1"], rp["W1_scale"], rp["W3"],
-                              rp["W3_scale"], rp["W2T"], rp["W2T_scale"], y[TB * c:TB * c + TB], TB)
-                        if dense:
-                            sffn.sffn_forward_dense_i8(*a_)
-                        else:
-                            sffn.sffn_forward_sparse_i8(*a_, sffn.SFFN_MODE_UNION)
-                gT = capture(fnT)
-                msT = time_graph(gT, args.steps, args.warmup)
-                del gT
-                rq[name + "_tokens_per_s"] = round(TB * (n // TB) / (msT * 1e-3), 1)
-                if not dense:
-                    sffn.sffn_timing_enable(hq64.ptr, True)
-                    fnT()
-                    torch.cuda.synchronize()
-                    sffn.sffn_timing_enable(hq64.ptr, False)
-                    kb = {}
-                    for kd in range(nk):
-                        ms_k, launches = sffn.sffn_timing_read(hq64.ptr, kd, reset=(kd == nk - 1))
-                        if launches:
-                            kb[sffn.sffn_kernel_name(kd)] = round(ms_k * 1e3 / launches, 3)
-                    rq["union_kernel_us"] = kb
-            rq["union_vs_dense"] = round(rq["union_tokens_per_s"] / rq["dense_tokens_per_s"], 3)
-            bq[f"T{TB}"] = rq
-        res_q["batched"] = bq
+        res_q["batched"] = _quant_batches(
+            torch, sffn, hq64, sffn.sffn_forward_sparse_i8, sffn.sffn_forward_dense_i8,
+            [tuple(rp[k] for k in ("W1", "W1_scale", "W3", "W3_scale", "W2T", "W2T_scale"))
+             for rp in repq], x, y, n, args)
         hq64.close()
         extras["int8"] = res_q
         log("int8: " + ", ".join(f"{kk} {v:,}" for kk, v in res_q.items() if not isinstance(v, dict))
@@ -1062,6 +1078,12 @@ def main() -> int:
         b44["union_vs_dense"] = round(b44["union_tokens_per_s"] / b44["dense_tokens_per_s"], 3)
         res4["batch4"] = b44
         h44.close()
+        h464 = sffn.Handle(D, H, 0, 64, act, sffn.SFFN_I4)
+        res4["batched"] = _quant_batches(
+            torch, sffn, h464, sffn.sffn_forward_sparse_i4, sffn.sffn_forward_dense_i4,
+            [tuple(rp[k] for k in ("W1", "W1_scale", "W3", "W3_scale", "W2T", "W2T_scale"))
+             for rp in rep4], x, y, n, args)
+        h464.close()
         extras["int4_group128"] = res4
         log("int4: " + ", ".join(f"{kk} {v:,}" for kk, v in res4.items() if not isinstance(v, dict))
             + f", kernels (us/launch) {kt4}, batch of 4 {b44}")
@@ -1147,6 +1169,12 @@ def main() -> int:
             bq4["union_vs_per_token"] = round(bq4["union_tokens_per_s"] / bq4["per_token_tokens_per_s"], 3)
             extras["lopa_int8" if bits == 8 else "lopa_int4_up_down"]["batch4"] = bq4
             hlq4.close()
+            hlq64 = sffn.Handle(D, Hp, r, 64, act, sffn.SFFN_I8 if bits == 8 else sffn.SFFN_I4)
+            extras["lopa_int8" if bits == 8 else "lopa_int4_up_down"]["batched_union"] = _quant_batches(
+                torch, sffn, hlq64, fwd, None,
+                [tuple(rp[k] for k in ("V", "V_scale", "U", "U_scale", "W3", "W3_scale", "W2T",
+                                       "W2T_scale")) for rp in replq], xl, y, n, args)
+            hlq64.close()
             log(f"lopa int{bits}: {ms_lq:.3f} ms/step, {lq_tok_s:,.0f} tokens/s, "
                 f"kernels (us/launch) {ktl}, batch of 4 {bq4}")
             hlq.close()
