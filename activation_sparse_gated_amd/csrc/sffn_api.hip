@@ -31,7 +31,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_RANK_PROJ_MFMA, KIND_GATE_UP_TB_I8, KIND_DOWN_TB_I8, KIND_GATE_UP_TB_I4,
             KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_DOWN_PT,
             KIND_GATE_UP_MFMA_I8, KIND_DOWN_MFMA_I8, KIND_RANK_PROJ_MFMA_I8,
-            KIND_GATE_UP_MFMA_I4, KIND_DOWN_MFMA_I4, KIND_COUNT };
+            KIND_GATE_UP_MFMA_I4, KIND_DOWN_MFMA_I4, KIND_DOWN_PT_I8, KIND_DOWN_PT_I4,
+            KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
@@ -49,7 +50,7 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_down_tb_i4", "k_rank_proj_tb_i8", "k_gate_up_lopa_tb_q",
                                             "k_down_pt", "k_gate_up_mfma_i8", "k_down_mfma_i8",
                                             "k_rank_proj_mfma_i8", "k_gate_up_mfma_i4",
-                                            "k_down_mfma_i4"};
+                                            "k_down_mfma_i4", "k_down_pt_i8", "k_down_pt_i4"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -646,6 +647,31 @@ sffn_status run_i8_t1(sffn_handle* h, const void* x, const void* W1, const float
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
+// Per-token down pass of a quantised batch (int8 or int4 W2T rows): each token's
+// own live W2T rows from the unit-major products and token masks the batch gate
+// wrote (row stride tp); y is cleared by that gate.
+sffn_status run_down_pt_q(sffn_handle* h, const void* W2T, const float* s2, float* y, int T,
+                          int tp, int bits, hipStream_t s) {
+    const int cb = 16 * 16;
+    const int nbx = (((h->D + cb - 1) / cb + 7) / 8) * 8;
+    const int splits = h->t1_splits;
+    const int hs = (h->H + splits - 1) / splits;
+    const int pmax = pick(kPMAX, 6, (hs + KD_THREADS - 1) / KD_THREADS);
+    sffn_status st = SFFN_OK;
+    if (bits == 8) {
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_PT_I8, k_down_pt_q<PMAX, 8>,
+                                           dim3(nbx, splits, T), dim3(KD_THREADS), s,
+                                           (const float*)h->m_a, (const uint64_t*)h->m_mask,
+                                           (const uint8_t*)W2T, s2, y, h->D, h->H, tp, splits));
+    } else {
+        SFFN_PMAX_SWITCH(pmax, st = launch(h, KIND_DOWN_PT_I4, k_down_pt_q<PMAX, 4>,
+                                           dim3(nbx, splits, T), dim3(KD_THREADS), s,
+                                           (const float*)h->m_a, (const uint64_t*)h->m_mask,
+                                           (const uint8_t*)W2T, s2, y, h->D, h->H, tp, splits));
+    }
+    return st;
+}
+
 // int8 union (and dense) batches of 5..64 tokens on MFMA: every weight code read
 // once for the batch (W1 or U, V, the W3 rows of the union, their W2T rows).
 // LOPA: W1 is U (scales s1 = U's), V with its scales sV gives the rank vectors.
@@ -657,7 +683,7 @@ template <bool DENSE, bool LOPA = false>
 sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const float* s1,
                         const void* W3, const float* s3, const void* W2T, const float* s2,
                         float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s,
-                        const void* V = nullptr, const float* sV = nullptr) {
+                        const void* V = nullptr, const float* sV = nullptr, bool per_token = false) {
     const int nt = token_tiles(T);
     uint8_t* live = live_count ? h->live_buf : nullptr;
     sffn_status st = SFFN_OK;
@@ -673,7 +699,7 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
     const int ut = 2;  // 32 units per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const int splits = h->m_splits;
-    float* yz = splits > 1 ? y : nullptr;
+    float* yz = (per_token || splits > 1) ? y : nullptr;
 #define SFFN_GATE_MFMA_I8(NTV)                                                                 \
     st = launch(h, KIND_GATE_UP_MFMA_I8, k_gate_up_mfma_i8<NTV, 2, DENSE, LOPA>, dim3(nb),     \
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const int8_t*)W1, s1,                \
@@ -690,10 +716,13 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
 #undef SFFN_GATE_MFMA_I8
     if (st != SFFN_OK) return st;
     const int ntile = (h->D + KDM_NB - 1) / KDM_NB;
-    SFFN_NT_SWITCH(nt, st = launch(h, KIND_DOWN_MFMA_I8, k_down_mfma_i8<NT>, dim3(ntile, splits),
-                                   dim3(KDM_THREADS), s, (const float*)h->m_a,
-                                   (const uint64_t*)h->m_mask, (const int8_t*)W2T, y, h->D, h->H,
-                                   T, splits));
+    if (per_token)
+        st = run_down_pt_q(h, W2T, s2, y, T, 16 * nt, 8, s);
+    else
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_DOWN_MFMA_I8, k_down_mfma_i8<NT>, dim3(ntile, splits),
+                                       dim3(KDM_THREADS), s, (const float*)h->m_a,
+                                       (const uint64_t*)h->m_mask, (const int8_t*)W2T, y, h->D,
+                                       h->H, T, splits));
     if (st != SFFN_OK) return st;
     if (!DENSE) return run_live_list(h, T, live_count, live_idx, s);
     return SFFN_OK;
@@ -709,7 +738,7 @@ template <bool DENSE, bool LOPA = false>
 sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const float* s1,
                         const void* W3, const float* s3, const void* W2T, const float* s2,
                         float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s,
-                        const void* V = nullptr, const float* sV = nullptr) {
+                        const void* V = nullptr, const float* sV = nullptr, bool per_token = false) {
     const int nt = token_tiles(T);
     uint8_t* live = live_count ? h->live_buf : nullptr;
     sffn_status st = SFFN_OK;
@@ -724,7 +753,7 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
     }
     const int nb = (h->H + 31) / 32;
     const int splits = h->m_splits;
-    float* yz = splits > 1 ? y : nullptr;
+    float* yz = (per_token || splits > 1) ? y : nullptr;
     SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_I4, k_gate_up_mfma_i4<NT, DENSE, LOPA>,
                                    dim3(nb), dim3(KM_THREADS), s, (const uint16_t*)x, W1, s1,
                                    (const uint8_t*)W3, s3, (const uint16_t*)h->m_zero, h->m_a,
@@ -732,10 +761,13 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
                                    (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r, h->flags));
     if (st != SFFN_OK) return st;
     const int ntile = (h->D + KDM_NB - 1) / KDM_NB;
-    SFFN_NT_SWITCH(nt, st = launch(h, KIND_DOWN_MFMA_I4, k_down_mfma_i4<NT>, dim3(ntile, splits),
-                                   dim3(KDM_THREADS), s, (const float*)h->m_a,
-                                   (const uint64_t*)h->m_mask, (const uint8_t*)W2T, s2, y, h->D,
-                                   h->H, T, splits));
+    if (per_token)
+        st = run_down_pt_q(h, W2T, s2, y, T, 16 * nt, 4, s);
+    else
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_DOWN_MFMA_I4, k_down_mfma_i4<NT>, dim3(ntile, splits),
+                                       dim3(KDM_THREADS), s, (const float*)h->m_a,
+                                       (const uint64_t*)h->m_mask, (const uint8_t*)W2T, s2, y,
+                                       h->D, h->H, T, splits));
     if (st != SFFN_OK) return st;
     if (!DENSE) return run_live_list(h, T, live_count, live_idx, s);
     return SFFN_OK;
@@ -746,7 +778,8 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
 template <bool DENSE>
 sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float* s1,
                       const void* W3, const float* s3, const void* W2T, const float* s2,
-                      float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
+                      float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s,
+                      bool per_token = false) {
     const int nc = pick(kNC_T1, 7, (h->D + 1023) / 1024);
     const int rw = DENSE ? 1 : 2;  // units per wave: union calls 2, the dense comparator 1 (measured)
     const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
@@ -755,7 +788,7 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
     int splits = h->tb_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
     uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
-    float* yz = splits > 1 ? y : nullptr;
+    float* yz = (per_token || splits > 1) ? y : nullptr;
     sffn_status st = SFFN_OK;
 #define SFFN_TBQ_GATE(TTV, RWV)                                                                   \
     SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_TB_I8, k_gate_up_tb_i8<NC, TTV, DENSE, RWV>,  \
@@ -769,6 +802,11 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
 #undef SFFN_TBQ_RW
 #undef SFFN_TBQ_GATE
     if (st != SFFN_OK) return st;
+    if (per_token) {
+        st = run_down_pt_q(h, W2T, s2, y, T, tp, 8, s);
+        if (st != SFFN_OK) return st;
+        return run_live_list(h, T, live_count, live_idx, s);
+    }
     const int cb = 16 * 16;
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
@@ -790,7 +828,8 @@ sffn_status run_i8_tb(sffn_handle* h, const void* x, const void* W1, const float
 template <bool DENSE>
 sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float* s1,
                       const void* W3, const float* s3, const void* W2T, const float* s2,
-                      float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s) {
+                      float* y, int T, int32_t* live_count, int32_t* live_idx, hipStream_t s,
+                      bool per_token = false) {
     const int nc = (h->D + 2047) / 2048;
     const int rw = DENSE ? 1 : 2;  // as for int8
     const int nb = (h->H + K1_WAVES * rw - 1) / (K1_WAVES * rw);
@@ -799,7 +838,7 @@ sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float
     int splits = h->tb_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
     uint8_t* live = (!DENSE && live_count) ? h->live_buf : nullptr;
-    float* yz = splits > 1 ? y : nullptr;
+    float* yz = (per_token || splits > 1) ? y : nullptr;
     sffn_status st = SFFN_OK;
 #define SFFN_TB4_GATE(NCV, TTV)                                                                   \
     if (rw == 2)                                                                                  \
@@ -822,6 +861,11 @@ sffn_status run_i4_tb(sffn_handle* h, const void* x, const void* W1, const float
 #undef SFFN_TB4_NC
 #undef SFFN_TB4_GATE
     if (st != SFFN_OK) return st;
+    if (per_token) {
+        st = run_down_pt_q(h, W2T, s2, y, T, tp, 4, s);
+        if (st != SFFN_OK) return st;
+        return run_live_list(h, T, live_count, live_idx, s);
+    }
     const int cb = 16 * 16;
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
@@ -1484,15 +1528,20 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     if (!s1 || !s3 || !s2) return fail(h, SFFN_INVALID_ARGUMENT, "null scale pointer");
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // int8 and int4 union (and dense) batches above 4 tokens: one MFMA pass over the weights
-    if (bits == 8 && mfma_i8_ok(h, T) && (dense || mode == SFFN_MODE_UNION))
+    // batches above 4 tokens: one MFMA gate pass over the weights for the batch, then
+    // the union's W2T rows once (union, dense) or each token's own live rows (per-token
+    // lists)
+    const bool pt = !dense && mode == SFFN_MODE_PER_TOKEN;
+    if (bits == 8 && mfma_i8_ok(h, T))
         return dense ? run_mfma_i8<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
-                     : run_mfma_i8<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
-    if (bits == 4 && mfma_i4_ok(h, T) && (dense || mode == SFFN_MODE_UNION))
+                     : run_mfma_i8<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx,
+                                          s, nullptr, nullptr, pt);
+    if (bits == 4 && mfma_i4_ok(h, T))
         return dense ? run_mfma_i4<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
-                     : run_mfma_i4<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx, s);
-    // union (and dense) batches of 2..4 tokens read the weights once for the batch
-    if (T >= 2 && h->m_a && (dense || mode == SFFN_MODE_UNION)) {
+                     : run_mfma_i4<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx,
+                                          s, nullptr, nullptr, pt);
+    // batches of 2..4 tokens: one pass over the weights on the VALU, the same two ways
+    if (T >= 2 && h->m_a) {
         const int ng = (T + 3) / 4;
         for (int g = 0, t0 = 0; g < ng; ++g) {
             const int tg = T / ng + (g < T % ng ? 1 : 0);
@@ -1502,10 +1551,10 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
             int32_t* li = live_idx ? live_idx + (size_t)t0 * h->H : nullptr;
             if (bits == 4)
                 st = dense ? run_i4_tb<true>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, nullptr, nullptr, s)
-                           : run_i4_tb<false>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, lc, li, s);
+                           : run_i4_tb<false>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, lc, li, s, pt);
             else
                 st = dense ? run_i8_tb<true>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, nullptr, nullptr, s)
-                           : run_i8_tb<false>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, lc, li, s);
+                           : run_i8_tb<false>(h, xg, W1, s1, W3, s3, W2T, s2, yg, tg, lc, li, s, pt);
             if (st != SFFN_OK) return st;
             t0 += tg;
         }
@@ -1566,12 +1615,12 @@ bool lopa_q_tb_ok(const sffn_handle* h, int T, int bits) {
 sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const float* sV,
                           const void* U, const float* sU, const void* W3, const float* s3,
                           const void* W2T, const float* s2, float* y, int T, int32_t* live_count,
-                          int32_t* live_idx, hipStream_t s, int bits) {
+                          int32_t* live_idx, hipStream_t s, int bits, bool per_token = false) {
     const int tt = T <= 2 ? 2 : 4;
     const int tp = 16 * token_tiles(T);
     int splits = h->tb_splits;
     while ((h->H + splits - 1) / splits > 32 * KD_THREADS) ++splits;
-    float* yz = splits > 1 ? y : nullptr;
+    float* yz = (per_token || splits > 1) ? y : nullptr;
     uint8_t* live = live_count ? h->live_buf : nullptr;
     sffn_status st = SFFN_OK;
     const int nc8 = (h->D + 1023) / 1024;
@@ -1617,6 +1666,11 @@ sffn_status run_lopa_q_tb(sffn_handle* h, const void* x, const void* V, const fl
 #undef SFFN_LQTB_NC
 #undef SFFN_LQTB
     if (st != SFFN_OK) return st;
+    if (per_token) {
+        st = run_down_pt_q(h, W2T, s2, y, T, tp, bits, s);
+        if (st != SFFN_OK) return st;
+        return run_live_list(h, T, live_count, live_idx, s);
+    }
     const int cb = 16 * 16;
     const int nslices = (h->D + cb - 1) / cb;
     const int nbx = ((nslices + 7) / 8) * 8;
@@ -1664,27 +1718,26 @@ static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, 
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(sV) || !al4(sU) || !al4(s3) || !al4(s2))
         return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // int8 and int4 union batches above 4 tokens: one MFMA pass over V, U, the W3 rows of the
-    // union and their W2T rows (RMSNorm of t excepted: it needs each token's whole t
-    // before the gate)
-    if (bits == 8 && mode == SFFN_MODE_UNION && mfma_i8_ok(h, T) && h->m_t &&
-        !(h->flags & SFFN_FLAG_RMSNORM))
+    // batches above 4 tokens: one MFMA pass over V, U and the W3 rows of the union, then
+    // the union's W2T rows once or each token's own (RMSNorm of t excepted: it needs
+    // each token's whole t before the gate)
+    const bool pt = mode == SFFN_MODE_PER_TOKEN;
+    if (bits == 8 && mfma_i8_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
         return run_mfma_i8<false, true>(h, x, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx,
-                                        s, V, sV);
-    if (bits == 4 && mode == SFFN_MODE_UNION && mfma_i4_ok(h, T) && h->m_t &&
-        !(h->flags & SFFN_FLAG_RMSNORM))
+                                        s, V, sV, pt);
+    if (bits == 4 && mfma_i4_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
         return run_mfma_i4<false, true>(h, x, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx,
-                                        s, V, sV);
-    // union batches of 2..4 tokens read the weights once for the batch; larger ones
-    // go as groups of 2..4 consecutive tokens (sizes as equal as can be)
-    if (mode == SFFN_MODE_UNION && T >= 2 && lopa_q_tb_ok(h, 2, bits)) {
+                                        s, V, sV, pt);
+    // batches of 2..4 tokens read the weights once for the batch; larger ones (with
+    // RMSNorm) go as groups of 2..4 consecutive tokens (sizes as equal as can be)
+    if (T >= 2 && lopa_q_tb_ok(h, 2, bits)) {
         const int ng = (T + 3) / 4;
         for (int g = 0, t0 = 0; g < ng; ++g) {
             const int tg = T / ng + (g < T % ng ? 1 : 0);
             st = run_lopa_q_tb(h, (const char*)x + (size_t)t0 * h->D * sizeof(uint16_t), V, sV, U,
                                sU, W3, s3, W2T, s2, y + (size_t)t0 * h->D, tg,
                                live_count ? live_count + t0 : nullptr,
-                               live_idx ? live_idx + (size_t)t0 * h->H : nullptr, s, bits);
+                               live_idx ? live_idx + (size_t)t0 * h->H : nullptr, s, bits, pt);
             if (st != SFFN_OK) return st;
             t0 += tg;
         }

@@ -1807,6 +1807,109 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
     }
 }
 
+// Down projection of a quantised batch with per-token live lists: y_t[slice] =
+// sum_{i in L_t} a'[i][t] q2[i, slice] (int8 rows; a' carries the row scale) or
+// sum_{i in L_t} a[i][t] s2_ig q2[i, slice] (int4 rows, group scales). Grid =
+// (column slices of 256 columns, unit-range splits, tokens); the blocks of token
+// t walk the units of their split whose token mask has bit t (wave-local, as in
+// k_down_pt) and gather only those W2T row slices, with the products from the
+// unit-major batch buffer (row stride tp). y (T x D) is cleared by the gate pass.
+template <int PMAX, int BITS>
+__global__ __launch_bounds__(KD_THREADS) void k_down_pt_q(const float* __restrict__ a_rm,
+                                                          const uint64_t* __restrict__ umask,
+                                                          const uint8_t* __restrict__ W2T,
+                                                          const float* __restrict__ s2,
+                                                          float* __restrict__ y, int D, int H,
+                                                          int tp, int splits) {
+    static_assert(BITS == 8 || BITS == 4, "int8 or int4 rows");
+    constexpr int LPR = 16;
+    constexpr int CB = LPR * 16;
+    constexpr int RPI = WAVE / LPR;
+    constexpr int UF = 8;
+    __shared__ float red[KD_WAVES][CB];
+
+    const int slice = xcd_slice(blockIdx.x, (D + CB - 1) / CB);
+    if (slice * CB >= D) return;
+    const int t = blockIdx.z;
+    const int col0 = slice * CB;
+    const int hs = (H + splits - 1) / splits;
+    const int h0 = blockIdx.y * hs;
+    const int h1 = min(H, h0 + hs);
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int sub = lane % LPR, grp = lane / LPR;
+    const int col = col0 + sub * 16;
+    const bool col_ok = col < D;
+    const int G = D / I4_GROUP;
+    const size_t rb = BITS == 8 ? (size_t)D : (size_t)D / 2;
+
+    uint64_t mk[PMAX];
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int row = h0 + (wave * PMAX + p) * WAVE + lane;
+        mk[p] = __ballot(row < h1 && ((umask[row] >> t) & 1ull));
+    }
+    float acc[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+#pragma unroll
+    for (int p = 0; p < PMAX; ++p) {
+        const int base = h0 + (wave * PMAX + p) * WAVE;
+        uint64_t m = mk[p];
+        while (m) {
+            int bit[UF];
+            next_live_bits<RPI, UF>(m, grp, bit);
+            u32x4 wv[UF];
+            float av[UF];
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                const bool ok = bit[u] >= 0;
+                const size_t row = (size_t)(base + (ok ? bit[u] : 0));
+                if (BITS == 8) {
+                    wv[u] = (ok && col_ok) ? load_stream(W2T + row * rb + col) : u32x4{0u, 0u, 0u, 0u};
+                    av[u] = ok ? a_rm[row * tp + t] : 0.0f;
+                } else {
+                    const u32x2 w2 = (ok && col_ok)
+                        ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + row * rb + col / 2))
+                        : u32x2{0u, 0u};
+                    wv[u] = u32x4{w2[0], w2[1], 0u, 0u};
+                    av[u] = (ok && col_ok) ? a_rm[row * tp + t] * s2[row * G + col / I4_GROUP] : 0.0f;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < UF; ++u) {
+                if (BITS == 8) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const uint32_t wq = wv[u][q];
+#pragma unroll
+                        for (int b = 0; b < 4; ++b)
+                            acc[4 * q + b] = fmaf(av[u], (float)((int)(wq << (24 - 8 * b)) >> 24), acc[4 * q + b]);
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const uint32_t wq = wv[u][q];
+#pragma unroll
+                        for (int b = 0; b < 8; ++b)
+                            acc[8 * q + b] = fmaf(av[u], (float)((int)(wq << (28 - 4 * b)) >> 28), acc[8 * q + b]);
+                    }
+                }
+            }
+        }
+    }
+    static_assert(LPR == 16, "two halving exchanges over 4 row groups");
+    rowgroup4_reduce_scatter(acc, red[wave], lane);
+    __syncthreads();
+    float* yt = y + (size_t)t * D;
+    for (int c = threadIdx.x; c < CB; c += KD_THREADS) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w2 = 0; w2 < KD_WAVES; ++w2) s += red[w2][c];
+        if (col0 + c < D) atomicAdd(yt + col0 + c, s);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Small batches (2 <= T <= TT <= 4), bf16, on the VALU.
 //

@@ -206,13 +206,14 @@ def _graph_time(torch, fn, steps, warmup):
 
 
 def _quant_batches(torch, sffn, h, fwd_sparse, fwd_dense, reps, x, y, n, args, sizes=(16, 64)):
-    """Union (and, with fwd_dense, dense) calls of T tokens through a quantised forward;
-    the weight tuple of each call is reps[c % len(reps)], x and y hold n tokens."""
+    """Per-token-list, union (and, with fwd_dense, dense) calls of T tokens through a
+    quantised forward; the weight tuple of each call is reps[c % len(reps)], x and y hold
+    n tokens."""
     out = {}
     nk = sffn.sffn_kernel_kinds()
     for TB in sizes:
         rq = {}
-        for name, fwd in (("union", fwd_sparse), ("dense", fwd_dense)):
+        for name, fwd in (("per_token", fwd_sparse), ("union", fwd_sparse), ("dense", fwd_dense)):
             if fwd is None:
                 continue
 
@@ -221,6 +222,8 @@ def _quant_batches(torch, sffn, h, fwd_sparse, fwd_dense, reps, x, y, n, args, s
                     a_ = (h.ptr, x[TB * c:TB * c + TB]) + reps[c % len(reps)] + (y[TB * c:TB * c + TB], TB)
                     if name == "union":
                         fwd(*a_, sffn.SFFN_MODE_UNION)
+                    elif name == "per_token":
+                        fwd(*a_, sffn.SFFN_MODE_PER_TOKEN)
                     else:
                         fwd(*a_)
             ms = _graph_time(torch, fn, max(2, args.steps // 2), 1)
