@@ -210,22 +210,22 @@ sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, cons
  * weights (SFFN_I8 handles): as sffn_forward_sparse / sffn_forward_dense, with
  * W1, W3, W2T int8 [H x D] row-major (16-byte aligned) and W1_scale, W3_scale,
  * W2T_scale fp32 [H] (4-byte aligned): weight (i, j) of each matrix is
- * q[i][j] * scale[i]. x is bf16 [T x D], y fp32 [T x D]. Union and dense calls
- * with 2..4 tokens read the weights once for the batch (the union of the
- * tokens' live sets); larger union and dense batches go as groups of 2..4
- * consecutive tokens, each reading the weights once; per-token calls run token
- * by token. Errors as for the other forward calls; a non-int8 handle gives
- * SFFN_INVALID_ARGUMENT.
+ * q[i][j] * scale[i]. x is bf16 [T x D], y fp32 [T x D]. Calls with 2..64
+ * tokens, in either mode and dense, read every weight code once for the batch:
+ * one gate pass (VALU for 2..4 tokens, MFMA on exactly decoded codes above)
+ * gathers the W3 rows of the union of the live sets; then the union's W2T rows
+ * are read once (union, dense) or each token's own live rows are gathered
+ * (per-token lists). Errors as for the other forward calls; a non-int8 handle
+ * gives SFFN_INVALID_ARGUMENT.
  */
 /*
  * Gate-first sparse forward and the dense comparator with weight-only int4
  * weights (SFFN_I4 handles): as the _i8 calls, with W1, W3, W2T packed int4
  * [H x D/2] bytes (16-byte aligned) and W1_scale, W3_scale, W2T_scale fp32
  * [H x D/128] (4-byte aligned): weight (i, j) is code(i, j) * scale[i][j / 128].
- * x bf16 [T x D], y fp32 [T x D]; union and dense calls read the weights once
- * per group of 2..4 tokens (as for int8), per-token calls run token by token.
- * Errors as for the other forward calls; a non-int4 handle gives
- * SFFN_INVALID_ARGUMENT.
+ * x bf16 [T x D], y fp32 [T x D]; batches of 2..64 tokens read every code
+ * once per call, as for int8. Errors as for the other forward calls; a non-int4
+ * handle gives SFFN_INVALID_ARGUMENT.
  */
 sffn_status sffn_forward_sparse_i4(sffn_handle *h, const void *x, const void *W1,
                                    const float *W1_scale, const void *W3, const float *W3_scale,
@@ -244,9 +244,11 @@ sffn_status sffn_forward_dense_i4(sffn_handle *h, const void *x, const void *W1,
  * stored row of each (V_scale [r], U_scale [H], W3_scale [H], W2T_scale [H],
  * 4-byte aligned): t = V x is exact in fp32 on the dequantised rows, the gate
  * options of the handle (G, RMSNorm, double activation) apply as for bf16.
- * Union calls (D <= 4096) read the weights once per group of 2..4 consecutive
- * tokens; per-token calls, and one-token calls, run token by token. Errors as for the other
- * forward calls; a non-int8 or r == 0 handle gives SFFN_INVALID_ARGUMENT.
+ * Batches of 5..64 tokens (without RMSNorm) read every code once per call on
+ * MFMA, in either mode; batches of 2..4 tokens (D <= 4096), and larger ones
+ * with RMSNorm, read the weights once per group of 2..4 consecutive tokens;
+ * other calls run token by token. Errors as for the other forward calls; a
+ * non-int8 or r == 0 handle gives SFFN_INVALID_ARGUMENT.
  */
 sffn_status sffn_forward_lopa_i8(sffn_handle *h, const void *x, const void *V,
                                  const float *V_scale, const void *U, const float *U_scale,
@@ -260,9 +262,8 @@ sffn_status sffn_forward_lopa_i8(sffn_handle *h, const void *x, const void *V,
  * [H x r] with one fp32 scale per stored row (V_scale [r], U_scale [H]), and
  * W3, W2T packed int4 [H x D/2] bytes with W3_scale, W2T_scale fp32
  * [H x D/128] as for sffn_forward_sparse_i4. The gate options of the handle
- * apply as for bf16; union calls (D <= 4096) read the weights once per group
- * of 2..4 consecutive tokens, per-token calls run token by token. Errors as for
- * the other forward calls; a non-int4 or r == 0 handle gives
+ * apply as for bf16; batches are planned as for sffn_forward_lopa_i8. Errors as
+ * for the other forward calls; a non-int4 or r == 0 handle gives
  * SFFN_INVALID_ARGUMENT.
  */
 sffn_status sffn_forward_lopa_i4(sffn_handle *h, const void *x, const void *V,
