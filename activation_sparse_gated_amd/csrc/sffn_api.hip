@@ -21,7 +21,7 @@ using namespace sffn;
 namespace {
 
 enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GATE_UP_DENSE,
-            KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_GATE_UP_DENSE_T1, KIND_DOWN_T1,
+            KIND_DOWN, KIND_LIVE_LIST, KIND_GATE_UP_T1, KIND_DOWN_T1,
             KIND_FFN_DENSE_T1, KIND_REDUCE, KIND_RANK_PROJ_T1, KIND_GATE_UP_LOPA_T1,
             KIND_GATE_UP_MFMA, KIND_DOWN_MFMA, KIND_DOWN_TB, KIND_GATE_UP_T1_I8,
             KIND_GATE_UP_DENSE_T1_I8, KIND_DOWN_T1_I8, KIND_MOE_GATHER, KIND_MOE_COMBINE,
@@ -35,7 +35,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
-                                            "k_gate_up_t1", "k_gate_up_dense_t1", "k_down_t1",
+                                            "k_gate_up_t1", "k_down_t1",
                                             "k_ffn_dense_t1", "k_reduce_partials",
                                             "k_rank_proj_t1", "k_gate_up_lopa_t1",
                                             "k_gate_up_mfma", "k_down_mfma", "k_down_tb",
@@ -70,7 +70,6 @@ struct sffn_handle {
     // launch plan (fixed per shape at create; the constants come from measured sweeps)
     int gate_rows_per_wave = 4;    // units per wave of the general (fp32) gate kernels
     int t1_splits = 16;            // unit-range splits of the batch-1 down passes
-    int t1_fused = 1;              // the batch-1 dense comparator runs as one fused pass
     int f_rows_per_block = 0;      // units per block of that pass
     int f_rw = 0;                  // units per wave of that pass
     int f_blocks = 0;              // its blocks (= partial outputs)
@@ -330,21 +329,11 @@ sffn_status run_sparse_t1(sffn_handle* h, const void* x, const void* W1, const v
     return run_live_list(h, 1, live_count, live_idx, s);
 }
 
-// Batch-1 dense comparator: the fused pass where its per-wave LDS slices fit
-// (D <= KF_DMAX), else a dense gate/up pass and the down kernel over every unit.
+// Batch-1 dense comparator: the fused pass (the batch-1 plan takes bf16 rows of
+// at most 4096 = KF_DMAX columns, where its per-wave LDS slices always fit).
 sffn_status run_dense_t1(sffn_handle* h, const void* x, const void* W1, const void* W3,
                          const void* W2T, float* y, hipStream_t s) {
-    if (h->t1_fused) return run_fused_dense_t1(h, x, W1, W3, W2T, y, s);
-    const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
-    const int nb = (h->H + K1_WAVES - 1) / K1_WAVES;
-    const int splits = h->t1_splits;
-    float* yz = splits > 1 ? y : nullptr;
-    sffn_status st = SFFN_OK;
-    SFFN_NCT1_SWITCH(nc, st = launch(h, KIND_GATE_UP_DENSE_T1, k_gate_up_dense_t1<NC>, dim3(nb),
-                                     dim3(K1_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,
-                                     (const uint16_t*)W3, h->a_buf, yz, h->D, h->H, h->act));
-    if (st != SFFN_OK) return st;
-    return run_down_t1(h, W2T, y, splits, 1, s);
+    return run_fused_dense_t1(h, x, W1, W3, W2T, y, s);
 }
 
 // ---- batched bf16 path on MFMA
@@ -1215,8 +1204,6 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
                 sffn_destroy(h);
                 return fail(nullptr, SFFN_HIP_ERROR, m);
             }
-        } else {
-            h->t1_fused = 0;
         }
         // scratch that must start zeroed is cleared on a private stream of the
         // handle's own, which create waits for (no device-wide synchronisation)

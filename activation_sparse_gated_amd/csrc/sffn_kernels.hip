@@ -606,45 +606,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_t1(
     const float u = wave_sum_dpp(su);
     if (lane == 0) a_out[unit] = activation(act, z) * u;
 }
-// Dense gate and up projection for one token (the unfused batch-1 dense
-// comparator): the W1 and W3 rows of the wave's unit read together.
-template <int NC>
-__global__ __launch_bounds__(K1_THREADS) void k_gate_up_dense_t1(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
-    const uint16_t* __restrict__ W3, float* __restrict__ a_out, float* __restrict__ y_zero,
-    int D, int H, int act) {
-    constexpr int CW = WAVE * 8;
-    const int lane = threadIdx.x & (WAVE - 1);
-    const int wave = threadIdx.x / WAVE;
-    const int row = blockIdx.x * K1_WAVES + wave;
-    u32x4 w1[NC], w3[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 8;
-        const bool ok = row < H && col < D;
-        w1[c] = ok ? load_stream(W1 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
-        w3[c] = ok ? load_stream(W3 + (size_t)row * D + col) : u32x4{0u, 0u, 0u, 0u};
-    }
-    u32x4 xv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        const int col = c * CW + lane * 8;
-        xv[c] = col < D ? load_cached(x + col) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (y_zero) {
-        for (int j = blockIdx.x * K1_THREADS + threadIdx.x; j < D; j += gridDim.x * K1_THREADS)
-            y_zero[j] = 0.0f;
-    }
-    float sz = 0.0f, su = 0.0f;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-        sz = dot2_chunk(w1[c], xv[c], sz);
-        su = dot2_chunk(w3[c], xv[c], su);
-    }
-    sz = wave_sum_dpp(sz);
-    su = wave_sum_dpp(su);
-    if (lane == 0 && row < H) a_out[row] = activation(act, sz) * su;
-}
 
 // LoPA batch-1 bf16: rank projection t = V x (fp32 out), one V row per wave,
 // products of bf16 pairs accumulated in fp32. Also clears y for a down pass
