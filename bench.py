@@ -1251,6 +1251,21 @@ def main() -> int:
             cpu["stacks_extrapolated"] = stk
             log("cpu oracle stacks (extrapolated from 8 tokens): " + ", ".join(
                 f"{k} {v['stack_tokens_per_s']} stack tokens/s" for k, v in stk.items()))
+            # LoPA (D = 2560, H' = 9787, r = 400): the LoPA workload's tokens through the fp64
+            # LoPA oracle for about a quarter of the decode sample's time
+            wlo = gen.lopa_weights(D, 9787, 400, s, cfg=3, dtype="bf16")
+            xlo = gen.tokens(D, 256, cfg=3, dtype="bf16")
+            donel, t3 = 0, time.time()
+            while time.time() - t3 < args.cpu_seconds / 4:
+                ref.ffn_lopa(xlo[donel % 256], wlo["V"], wlo["U"], wlo["W3"], wlo["W2T"],
+                             act=ref.ACT_RSPLUS)
+                donel += 1
+            dtl = time.time() - t3
+            cpu["lopa"] = {"tokens_per_s": round(donel / dtl, 2),
+                           "sample": f"{donel} LoPA tokens through the fp64 LoPA oracle on "
+                                     f"{threads} threads: {dtl:.1f} s"}
+            log(f"cpu oracle lopa: {cpu['lopa']['tokens_per_s']} tokens/s")
+            del wlo
 
     traffic = read_traffic(dom, "decode")
     out = {
