@@ -1177,8 +1177,13 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         int rpw = 4;
         while (rpw > 1 && (H + rpw * K1_WAVES - 1) / (rpw * K1_WAVES) < 1024) rpw /= 2;
         h->gate_rows_per_wave = rpw;
-        // batch-1 down passes: 16 unit ranges, more when a range would exceed what
-        // one block's waves hold (32 x 512 units)
+        // batch-1 (and per-token) down passes: 16 unit ranges, more when a range would
+        // exceed what one block's waves hold (32 x 512 units); bf16 ranges of at most
+        // 512 units (one group of 64 per wave, one round of row loads) up to 64 ranges
+        // (more ranges add same-address atomics to y)
+        if (dtype == SFFN_BF16)
+            while ((H + h->t1_splits - 1) / h->t1_splits > KD_THREADS && h->t1_splits < 64)
+                ++h->t1_splits;
         while ((H + h->t1_splits - 1) / h->t1_splits > 32 * KD_THREADS) ++h->t1_splits;
         // fused batch-1 dense comparator: about one block per two CUs (128 blocks),
         // at most 8 units per wave
@@ -1463,9 +1468,10 @@ sffn_status sffn_forward_sparse_noalloc(const void* x, const void* W1, const voi
         hipStream_t s = reinterpret_cast<hipStream_t>(stream);
         const int nc = pick(kNC_T1, 7, chunks_needed(D, SFFN_BF16));
         const int nb = (H + K1_WAVES - 1) / K1_WAVES;
-        constexpr int splits = 16;
+        // unit ranges of at most 512 units (one group of 64 per wave), at least 16 ranges;
+        // H <= 16384 gives at most 32
+        const int splits = std::max(16, (H + KD_THREADS - 1) / KD_THREADS);
         const int nbx = (((D + 255) / 256 + 7) / 8) * 8;
-        const int hs = (H + splits - 1) / splits;  // <= 1024 units: PMAX 1 or 2
         const size_t xb = (size_t)D * sizeof(uint16_t);
         for (int t = 0; t < T; ++t) {
             const void* xt = (const char*)x + t * xb;
@@ -1480,12 +1486,8 @@ sffn_status sffn_forward_sparse_noalloc(const void* x, const void* W1, const voi
                 case 8: hipLaunchKernelGGL(k_gate_up_t1<8>, dim3(nb), dim3(K1_THREADS), 0, s, (const uint16_t*)xt, (const uint16_t*)W1, (const uint16_t*)W3, a, (uint8_t*)nullptr, yt, D, H, act); break;
                 default: return fail(nullptr, SFFN_INTERNAL, "no batch-1 kernel for this width");
             }
-            if (hs <= KD_THREADS)
-                hipLaunchKernelGGL(k_down_t1<1>, dim3(nbx, splits), dim3(KD_THREADS), 0, s,
-                                   (const float*)a, (const uint16_t*)W2T, yt, D, H, splits, 0);
-            else
-                hipLaunchKernelGGL(k_down_t1<2>, dim3(nbx, splits), dim3(KD_THREADS), 0, s,
-                                   (const float*)a, (const uint16_t*)W2T, yt, D, H, splits, 0);
+            hipLaunchKernelGGL(k_down_t1<1>, dim3(nbx, splits), dim3(KD_THREADS), 0, s,
+                               (const float*)a, (const uint16_t*)W2T, yt, D, H, splits, 0);
             e = hipGetLastError();
             if (e != hipSuccess)
                 return fail(nullptr, SFFN_HIP_ERROR, std::string("launch: ") + hipGetErrorString(e));

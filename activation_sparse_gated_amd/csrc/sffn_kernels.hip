@@ -792,6 +792,51 @@ __device__ inline void next_live_round(uint64_t& m, float ar, int grp, int (&bit
     }
 }
 
+// next_live_round over the PMAX groups of 64 units a wave holds (products ar[p],
+// marks m[p]), taken in ascending order across the groups, so a round's row loads
+// span group boundaries and a wave with several groups pays one round trip per
+// RPI * UF units rather than one per group (used by the int8 and int4 downs, whose
+// rounds take 32 units; the bf16 plan splits the units so that a wave holds one
+// group). off[u] = 64 p + bit (the unit's offset within the wave's units), -1 once
+// they run out.
+template <int PMAX, int RPI, int UF>
+__device__ inline void next_live_round_multi(uint64_t (&m)[PMAX], const float (&ar)[PMAX],
+                                             int grp, int (&off)[UF], float (&av)[UF]) {
+#pragma unroll
+    for (int u = 0; u < UF; ++u) {
+        int o = -1;
+        float v = 0.0f;
+#pragma unroll
+        for (int g = 0; g < RPI; ++g) {
+            int og = -1;
+            float vg = 0.0f;
+#pragma unroll
+            for (int q = 0; q < PMAX; ++q) {
+                if (og < 0 && m[q]) {
+                    const int b = (int)__builtin_ctzll(m[q]);
+                    m[q] &= m[q] - 1;
+                    og = q * WAVE + b;
+                    vg = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ar[q]), b));
+                }
+            }
+            if (g == grp) {
+                o = og;
+                v = vg;
+            }
+        }
+        off[u] = o;
+        av[u] = v;
+    }
+}
+
+template <int PMAX>
+__device__ inline bool any_bits(const uint64_t (&m)[PMAX]) {
+    uint64_t a = 0;
+#pragma unroll
+    for (int q = 0; q < PMAX; ++q) a |= m[q];
+    return a != 0;
+}
+
 // Column slice of y for the XCD-contiguous order of the down grids: the blocks
 // dispatched to one XCD (block index mod 8) take consecutive slices.
 __device__ inline int xcd_slice(int bx, int nslices) {
@@ -1436,28 +1481,30 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i8(const float* __restri
     float acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    uint64_t mk[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
         const int base = h0 + (wave * PMAX + p) * WAVE;
-        uint64_t m = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
-        while (m) {
-            int bit[UF];
-            float av[UF];
-            next_live_round<RPI, UF>(m, ar[p], grp, bit, av);
-            u32x4 wv[UF];
+        mk[p] = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
+    }
+    const int wbase = h0 + wave * PMAX * WAVE;
+    while (any_bits(mk)) {
+        int off[UF];
+        float av[UF];
+        next_live_round_multi<PMAX, RPI, UF>(mk, ar, grp, off, av);
+        u32x4 wv[UF];
 #pragma unroll
-            for (int u = 0; u < UF; ++u)
-                wv[u] = (bit[u] >= 0 && col_ok) ? load_stream(W2T + (size_t)(base + bit[u]) * D + col)
-                                                : u32x4{0u, 0u, 0u, 0u};
+        for (int u = 0; u < UF; ++u)
+            wv[u] = (off[u] >= 0 && col_ok) ? load_stream(W2T + (size_t)(wbase + off[u]) * D + col)
+                                            : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int u = 0; u < UF; ++u) {
+        for (int u = 0; u < UF; ++u) {
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const uint32_t wq = wv[u][q];
+            for (int q = 0; q < 4; ++q) {
+                const uint32_t wq = wv[u][q];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
-                        acc[4 * q + b] = fmaf(av[u], (float)((int)(wq << (24 - 8 * b)) >> 24), acc[4 * q + b]);
-                }
+                for (int b = 0; b < 4; ++b)
+                    acc[4 * q + b] = fmaf(av[u], (float)((int)(wq << (24 - 8 * b)) >> 24), acc[4 * q + b]);
             }
         }
     }
@@ -1721,34 +1768,36 @@ __global__ __launch_bounds__(KD_THREADS) void k_down_t1_i4(const float* __restri
     float acc[16];
 #pragma unroll
     for (int k = 0; k < 16; ++k) acc[k] = 0.0f;
+    uint64_t mk[PMAX];
 #pragma unroll
     for (int p = 0; p < PMAX; ++p) {
         const int base = h0 + (wave * PMAX + p) * WAVE;
-        uint64_t m = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
-        while (m) {
-            int bit[UF];
-            float av[UF];
-            next_live_round<RPI, UF>(m, ar[p], grp, bit, av);
-            u32x2 wv[UF];
-            float sg[UF];
+        mk[p] = __ballot(base + lane < h1 && (dense || ar[p] != 0.0f));
+    }
+    const int wbase = h0 + wave * PMAX * WAVE;
+    while (any_bits(mk)) {
+        int off[UF];
+        float av[UF];
+        next_live_round_multi<PMAX, RPI, UF>(mk, ar, grp, off, av);
+        u32x2 wv[UF];
+        float sg[UF];
 #pragma unroll
-            for (int u = 0; u < UF; ++u) {
-                const bool ok = bit[u] >= 0 && col_ok;
-                const size_t row = (size_t)(base + (ok ? bit[u] : 0));
-                wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + row * rb + col / 2))
-                           : u32x2{0u, 0u};
-                sg[u] = ok ? s2[row * G + col / I4_GROUP] : 0.0f;
-            }
+        for (int u = 0; u < UF; ++u) {
+            const bool ok = off[u] >= 0 && col_ok;
+            const size_t row = (size_t)(wbase + (ok ? off[u] : 0));
+            wv[u] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(W2T + row * rb + col / 2))
+                       : u32x2{0u, 0u};
+            sg[u] = ok ? s2[row * G + col / I4_GROUP] : 0.0f;
+        }
 #pragma unroll
-            for (int u = 0; u < UF; ++u) {
-                const float aval = av[u] * sg[u];
+        for (int u = 0; u < UF; ++u) {
+            const float aval = av[u] * sg[u];
 #pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    const uint32_t wq = wv[u][q];
+            for (int q = 0; q < 2; ++q) {
+                const uint32_t wq = wv[u][q];
 #pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        acc[8 * q + b] = fmaf(aval, (float)((int)(wq << (28 - 4 * b)) >> 28), acc[8 * q + b]);
-                }
+                for (int b = 0; b < 8; ++b)
+                    acc[8 * q + b] = fmaf(aval, (float)((int)(wq << (28 - 4 * b)) >> 28), acc[8 * q + b]);
             }
         }
     }
