@@ -1228,6 +1228,10 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if ((dtype == SFFN_BF16 || dtype == SFFN_I8 || dtype == SFFN_I4) && max_tokens >= 2) {
             h->m_tp = 16 * token_tiles(max_tokens);
             while ((H + h->m_splits - 1) / h->m_splits > KDM_LCAP) ++h->m_splits;
+            // bf16: ranges of at most 512 units, as for the batch-1 pass (up to 64)
+            if (dtype == SFFN_BF16)
+                while ((H + h->tb_splits - 1) / h->tb_splits > KD_THREADS && h->tb_splits < 64)
+                    ++h->tb_splits;
             while ((H + h->tb_splits - 1) / h->tb_splits > 32 * KD_THREADS) ++h->tb_splits;
             e = hipMalloc(&h->m_a, (size_t)H * h->m_tp * sizeof(float));
             if (e == hipSuccess) e = hipMalloc(&h->m_mask, (size_t)H * sizeof(uint64_t));
