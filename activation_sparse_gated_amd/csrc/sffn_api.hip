@@ -32,7 +32,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_DOWN_PT,
             KIND_GATE_UP_MFMA_I8, KIND_DOWN_MFMA_I8, KIND_RANK_PROJ_MFMA_I8,
             KIND_GATE_UP_MFMA_I4, KIND_DOWN_MFMA_I4, KIND_DOWN_PT_I8, KIND_DOWN_PT_I4,
-            KIND_COUNT };
+            KIND_GATE_UP_MFMA_FUSED, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_down_t1",
@@ -50,7 +50,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_down_tb_i4", "k_rank_proj_tb_i8", "k_gate_up_lopa_tb_q",
                                             "k_down_pt", "k_gate_up_mfma_i8", "k_down_mfma_i8",
                                             "k_rank_proj_mfma_i8", "k_gate_up_mfma_i4",
-                                            "k_down_mfma_i4", "k_down_pt_i8", "k_down_pt_i4"};
+                                            "k_down_mfma_i4", "k_down_pt_i8", "k_down_pt_i4",
+                                            "k_gate_up_mfma_fused"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -390,6 +391,22 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
             16 * nt, h->act))
         if (tt == 2) { SFFN_TBV(2); } else { SFFN_TBV(4); }
 #undef SFFN_TBV
+    } else if (!LOPA && (DENSE || nt == 4)) {
+        // the union covers nearly every unit (or every unit, dense): W1 and W3 rows of
+        // the block in one pass, x staged once for both
+#define SFFN_GATE_FUSED(NTV, UTV)                                                              \
+    st = launch(h, KIND_GATE_UP_MFMA_FUSED, k_gate_up_mfma_fused<NTV, UTV, DENSE>, dim3(nb),   \
+                dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
+                (const uint16_t*)W3, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, yz,   \
+                h->D, h->H, T, h->act)
+        if (nt == 1) {
+            SFFN_GATE_FUSED(1, 1);
+        } else if (nt == 2) {
+            SFFN_GATE_FUSED(2, 2);
+        } else {
+            SFFN_GATE_FUSED(4, 2);
+        }
+#undef SFFN_GATE_FUSED
     } else {
 #define SFFN_GATE_MFMA(NTV, UTV)                                                               \
     st = launch(h, KIND_GATE_UP_MFMA, k_gate_up_mfma<NTV, UTV, DENSE, LOPA>, dim3(nb),         \
