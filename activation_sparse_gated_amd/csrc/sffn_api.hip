@@ -77,7 +77,8 @@ struct sffn_handle {
     float* part_buf = nullptr;     // [f_blocks x D] partial outputs of the dense comparator
     // batched bf16 path on MFMA (union of live sets, dense)
     int m_tp = 0;                  // padded token count (16 * token tiles) the buffers hold
-    int m_splits = 16;             // row splits of the MFMA down pass
+    int m_splits = 16;             // unit ranges of the MFMA down pass above 32 tokens
+    int m_splits_s = 12;           // ... up to 32 tokens: column tiles x ranges <= CUs
     void* m_zero = nullptr;        // 4 KB of zeros (source of the staged pieces outside the operands)
     // mixture of experts: tokens gathered per expert, expert outputs per slot
     uint16_t* moe_x = nullptr;     // [2 * max_tokens x D] bf16
@@ -357,6 +358,11 @@ inline int token_tiles(int T) { return T <= 16 ? 1 : (T <= 32 ? 2 : 4); }
 // (bf16 hi and lo parts) into the MFMA gate, the rest is the standard plan.
 // per_token: the down pass gathers each token's own live W2T rows (per-token
 // lists) instead of the union's rows once for all tokens.
+// unit ranges of the MFMA down pass for a batch of nt token tiles
+inline int mfma_down_splits(const sffn_handle* h, int nt) {
+    return nt <= 2 ? h->m_splits_s : h->m_splits;
+}
+
 template <bool DENSE, bool LOPA = false>
 sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* W3,
                      const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
@@ -376,7 +382,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     const int ut = nt == 1 ? 1 : 2;  // unit tiles per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const bool small_down = T <= 4;
-    const int splits = per_token ? h->t1_splits : (small_down ? h->tb_splits : h->m_splits);
+    const int splits = per_token ? h->t1_splits : (small_down ? h->tb_splits : mfma_down_splits(h, nt));
     float* yz = splits > 1 ? y : nullptr;
     if (!LOPA && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once; units
@@ -705,7 +711,7 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
     }
     const int ut = 2;  // 32 units per gate block
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
-    const int splits = h->m_splits;
+    const int splits = mfma_down_splits(h, nt);
     float* yz = (per_token || splits > 1) ? y : nullptr;
 #define SFFN_GATE_MFMA_I8(NTV)                                                                 \
     st = launch(h, KIND_GATE_UP_MFMA_I8, k_gate_up_mfma_i8<NTV, 2, DENSE, LOPA>, dim3(nb),     \
@@ -759,7 +765,7 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
         if (st != SFFN_OK) return st;
     }
     const int nb = (h->H + 31) / 32;
-    const int splits = h->m_splits;
+    const int splits = mfma_down_splits(h, nt);
     float* yz = (per_token || splits > 1) ? y : nullptr;
     SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_I4, k_gate_up_mfma_i4<NT, DENSE, LOPA>,
                                    dim3(nb), dim3(KM_THREADS), s, (const uint16_t*)x, W1, s1,
@@ -1246,6 +1252,15 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if ((dtype == SFFN_BF16 || dtype == SFFN_I8 || dtype == SFFN_I4) && max_tokens >= 2) {
             h->m_tp = 16 * token_tiles(max_tokens);
             while ((H + h->m_splits - 1) / h->m_splits > KDM_LCAP) ++h->m_splits;
+            // up to 32 tokens the down pass runs at one block per CU (measured ahead of
+            // the 16 ranges that put two blocks on some CUs: union of 8 / 17 / 32 tokens
+            // 272k / 455k / 814k -> 292k / 504k / 885k tokens/s at D=2560, H=7168); above
+            // that the 16 ranges stay ahead
+            int ncu = 256;
+            if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, h->device) != hipSuccess || ncu < 1)
+                ncu = 256;
+            h->m_splits_s = std::max(1, ncu / ((D + KDM_NB - 1) / KDM_NB));
+            while ((H + h->m_splits_s - 1) / h->m_splits_s > KDM_LCAP) ++h->m_splits_s;
             // bf16: ranges of at most 512 units, as for the batch-1 pass (up to 64)
             if (dtype == SFFN_BF16)
                 while ((H + h->tb_splits - 1) / h->tb_splits > KD_THREADS && h->tb_splits < 64)
