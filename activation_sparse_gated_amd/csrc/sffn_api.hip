@@ -384,6 +384,9 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     const bool small_down = T <= 4;
     const int splits = per_token ? h->t1_splits : (small_down ? h->tb_splits : mfma_down_splits(h, nt));
     float* yz = splits > 1 ? y : nullptr;
+    // the MFMA down pass takes the products split into bf16 hi and lo parts; the
+    // per-token and small-batch down passes take them in fp32
+    const int split = (!per_token && !small_down) ? 1 : 0;
     if (!LOPA && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once; units
         // per wave = token slots (2 or 4)
@@ -405,7 +408,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     st = launch(h, KIND_GATE_UP_MFMA_FUSED, k_gate_up_mfma_fused<NTV, UTV, DENSE>, dim3(nb),   \
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
                 (const uint16_t*)W3, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, yz,   \
-                h->D, h->H, T, h->act)
+                h->D, h->H, T, h->act, split)
         if (nt == 1) {
             SFFN_GATE_FUSED(1, 1);
         } else if (nt == 2) {
@@ -420,7 +423,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
                 (const uint16_t*)W3, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, yz,   \
                 h->D, h->H, T, h->act, (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r,      \
-                h->flags)
+                h->flags, split)
     if (nt == 1) {
         SFFN_GATE_MFMA(1, 1);
     } else if (nt == 2) {
@@ -718,7 +721,7 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const int8_t*)W1, s1,                \
                 (const int8_t*)W3, s3, s2, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, \
                 yz, h->D, h->H, T, h->act, (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r,  \
-                h->flags)
+                h->flags, per_token ? 0 : 1)
     if (nt == 1) {
         SFFN_GATE_MFMA_I8(1);
     } else if (nt == 2) {

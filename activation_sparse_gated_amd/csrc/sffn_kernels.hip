@@ -2066,6 +2066,24 @@ __device__ inline uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Unit product v of (unit row, token t) in a_rm, whose rows hold TP tokens in 4 TP
+// bytes: fp32 a_rm[row][t] (split == 0), or the bf16 parts hi = rne(v) and
+// lo = rne(v - hi) (about 16 significant bits together), the hi parts of the
+// row's TP tokens first and then their lo parts (split != 0). The split form is
+// what the MFMA down passes stage: splitting once here replaces a split of every
+// product in each of the down pass's column tiles.
+__device__ inline void store_product(float* __restrict__ a_rm, size_t row, int TP, int t, float v,
+                                     int split) {
+    if (split) {
+        uint16_t* r = reinterpret_cast<uint16_t*>(a_rm + row * TP);
+        const uint32_t hi = bf16_rne(v);
+        r[t] = (uint16_t)hi;
+        r[TP + t] = (uint16_t)bf16_rne(v - __uint_as_float(hi << 16));
+    } else {
+        a_rm[row * TP + t] = v;
+    }
+}
+
 // Stage 1: gate and up projection of UB = 16*UT units for T <= 16*NT tokens,
 // as [UB x D] x [D x TP] products on MFMA tiles (see mfma_gate_pass for the
 // staging of the operands). The (unit tile, token tile) pairs are spread over the 4 waves;
@@ -2223,7 +2241,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
     const uint16_t* __restrict__ W3, const uint16_t* __restrict__ zeros, float* __restrict__ a_rm,
     uint64_t* __restrict__ umask, uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D,
     int H, int T, int act, const uint16_t* __restrict__ t_hi, const uint16_t* __restrict__ t_lo,
-    int r, unsigned flags) {
+    int r, unsigned flags, int split) {
     using G = GateTiles<NT, UT>;
     constexpr int TP = G::TP, UB = G::UB;
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
@@ -2328,7 +2346,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
             if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
             av = activation(act, zf[i][t]) * u;
         }
-        a_rm[(size_t)(u0 + i) * TP + t] = av;
+        store_product(a_rm, (size_t)(u0 + i), TP, t, av, split);
     }
 }
 
@@ -2439,7 +2457,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ W1,
     const uint16_t* __restrict__ W3, const uint16_t* __restrict__ zeros, float* __restrict__ a_rm,
     uint64_t* __restrict__ umask, uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D,
-    int H, int T, int act) {
+    int H, int T, int act, int split) {
     using G = FusedTiles<NT, UT>;
     constexpr int TP = G::TP, UB = G::UB;
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
@@ -2490,7 +2508,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused(
         const bool live = ok && (DENSE || z > 0.0f);
         if (live) atomicOr(&tmask[i], 1ull << t);
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
-        a_rm[(size_t)(u0 + i) * TP + t] = live ? activation(act, z) * u : 0.0f;
+        store_product(a_rm, (size_t)(u0 + i), TP, t, live ? activation(act, z) * u : 0.0f, split);
     }
     __syncthreads();
     if (threadIdx.x < UB && u0 + (int)threadIdx.x < H) umask[u0 + threadIdx.x] = tmask[threadIdx.x];
@@ -2593,9 +2611,9 @@ __global__ __launch_bounds__(KM_THREADS) void k_rank_proj_mfma(
 // its split in one round and compacts the live units into an ascending list in
 // LDS, then runs through them in chunks of 64 with the global loads of the next
 // 4..6 chunks in flight in registers. A chunk is staged without reshaping: each
-// W2T row slice goes to LDS as it is (256-byte K-rows), the unit products as
-// bf16 hi and lo parts (about 16 significant bits together, rounded once per
-// block) in 128-byte K-rows [unit][token]. Both MFMA operands are read with the
+// W2T row slice goes to LDS as it is (256-byte K-rows), the unit products as the
+// bf16 hi and lo parts the gate pass stored (store_product, split form) in
+// 128-byte K-rows [unit][token]. Both MFMA operands are read with the
 // transposing LDS read, which hands a lane the 8 consecutive units of one token
 // or one column. Each wave owns 2*NT of the block's NT x 8 output tiles (one
 // token tile) and adds them to y with fp32 atomics (one add per split per
@@ -2671,7 +2689,7 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
 
     // W2T piece g = tid + 256 k: unit row g / 16 of the chunk, 8 columns at 8 (g % 16)
     u32x4 wv[DEPTH][WPT];
-    float4 av[DEPTH][APT];
+    u32x4 av[DEPTH][APT];
     bool wok[DEPTH][WPT], aok[DEPTH][APT];
     auto fetch = [&](int slot, int c) {
 #pragma unroll
@@ -2687,7 +2705,7 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
             const int idx = threadIdx.x + q * KDM_THREADS;
             const int e = c * KDM_KC + idx / (TP / 4);
             const bool ok = e < n;
-            av[slot][q] = *reinterpret_cast<const float4*>(
+            av[slot][q] = *reinterpret_cast<const u32x4*>(
                 a_rm + (ok ? (size_t)list[e] * TP + 4 * (idx % (TP / 4)) : 0));
             aok[slot][q] = ok;
         }
@@ -2703,19 +2721,13 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
         }
 #pragma unroll
         for (int q = 0; q < APT; ++q) {
+            // piece p of a unit's row: the hi parts of tokens 8p .. 8p + 7 for p < TP / 8,
+            // else the lo parts of tokens 8 (p - TP / 8) .. + 7
             const int idx = threadIdx.x + q * KDM_THREADS;
-            const int row = idx / (TP / 4), r = row & 31, t0 = 4 * (idx % (TP / 4));
-            const float4 f = aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float fv[4] = {f.x, f.y, f.z, f.w};
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hi[j] = bf16_rne(fv[j]);
-                lo[j] = bf16_rne(fv[j] - __uint_as_float(hi[j] << 16));
-            }
-            const int off = 2 * WPART + (row >> 5) * APART + r * 128 + 16 * swz128(r, t0 >> 3) + 8 * ((t0 >> 2) & 1);
-            *reinterpret_cast<uint2*>(st + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-            *reinterpret_cast<uint2*>(st + off + 2 * APART) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+            const int row = idx / (TP / 4), r = row & 31, p = idx % (TP / 4);
+            const int part = p >= TP / 8 ? 1 : 0, tg = p - part * (TP / 8);
+            const int off = 2 * WPART + (2 * part + (row >> 5)) * APART + r * 128 + 16 * swz128(r, tg);
+            *reinterpret_cast<u32x4*>(st + off) = aok[d][q] ? av[d][q] : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto compute = [&](int stage) {
@@ -2945,7 +2957,8 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
     const int8_t* __restrict__ W3, const float* __restrict__ s3, const float* __restrict__ s2,
     const uint16_t* __restrict__ zeros, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
     uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act,
-    const uint16_t* __restrict__ t_hi, const uint16_t* __restrict__ t_lo, int r, unsigned flags) {
+    const uint16_t* __restrict__ t_hi, const uint16_t* __restrict__ t_lo, int r, unsigned flags,
+    int split) {
     using G = GateTilesI8<NT, UT>;
     constexpr int TP = G::TP, UB = G::UB;
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
@@ -3047,7 +3060,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
             if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
             av = activation(act, zf[i][t]) * u * s2[u0 + i];
         }
-        a_rm[(size_t)(u0 + i) * TP + t] = av;
+        store_product(a_rm, (size_t)(u0 + i), TP, t, av, split);
     }
 }
 
@@ -3160,7 +3173,7 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
 
     // code piece g = tid + 256 k: unit row g / 8 of the chunk, 16 columns at 16 (g % 8)
     u32x4 wv[DEPTH][WPT];
-    float4 av[DEPTH][APT];
+    u32x4 av[DEPTH][APT];
     bool wok[DEPTH][WPT], aok[DEPTH][APT];
     auto fetch = [&](int slot, int c) {
 #pragma unroll
@@ -3176,7 +3189,7 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
             const int idx = threadIdx.x + q * KDM_THREADS;
             const int e = c * KDM_KC + idx / (TP / 4);
             const bool ok = e < n;
-            av[slot][q] = *reinterpret_cast<const float4*>(
+            av[slot][q] = *reinterpret_cast<const u32x4*>(
                 a_rm + (ok ? (size_t)list[e] * TP + 4 * (idx % (TP / 4)) : 0));
             aok[slot][q] = ok;
         }
@@ -3194,19 +3207,13 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
         }
 #pragma unroll
         for (int q = 0; q < APT; ++q) {
+            // piece p of a unit's row: the hi parts of tokens 8p .. 8p + 7 for p < TP / 8,
+            // else the lo parts of tokens 8 (p - TP / 8) .. + 7
             const int idx = threadIdx.x + q * KDM_THREADS;
-            const int row = idx / (TP / 4), r = row & 31, t0 = 4 * (idx % (TP / 4));
-            const float4 f = aok[d][q] ? av[d][q] : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float fv[4] = {f.x, f.y, f.z, f.w};
-            uint32_t hi[4], lo[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hi[j] = bf16_rne(fv[j]);
-                lo[j] = bf16_rne(fv[j] - __uint_as_float(hi[j] << 16));
-            }
-            const int off = 2 * WPART + (row >> 5) * APART + r * 128 + 16 * swz128(r, t0 >> 3) + 8 * ((t0 >> 2) & 1);
-            *reinterpret_cast<uint2*>(st + off) = make_uint2(hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16));
-            *reinterpret_cast<uint2*>(st + off + 2 * APART) = make_uint2(lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16));
+            const int row = idx / (TP / 4), r = row & 31, p = idx % (TP / 4);
+            const int part = p >= TP / 8 ? 1 : 0, tg = p - part * (TP / 8);
+            const int off = 2 * WPART + (2 * part + (row >> 5)) * APART + r * 128 + 16 * swz128(r, tg);
+            *reinterpret_cast<u32x4*>(st + off) = aok[d][q] ? av[d][q] : u32x4{0u, 0u, 0u, 0u};
         }
     };
     auto compute = [&](int stage) {
