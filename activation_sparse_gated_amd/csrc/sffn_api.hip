@@ -400,10 +400,12 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
             16 * nt, h->act))
         if (tt == 2) { SFFN_TBV(2); } else { SFFN_TBV(4); }
 #undef SFFN_TBV
-    } else if (!LOPA && (DENSE || nt >= 2)) {
-        // above 16 tokens the union covers most units (1 - 0.9^17 = 83 %; dense: every
+    } else if (!LOPA && (DENSE || T > 10)) {
+        // above 10 tokens the union covers most units (1 - 0.9^11 = 69 %; dense: every
         // unit): W1 and W3 rows of the block in one pass, x staged once for both
-        // (measured ahead of the gathered W3 pass from 17 tokens on)
+        // (measured ahead of the gathered W3 pass from 12 tokens on, level at 10,
+        // behind up to 8: union of 12 / 14 / 16 tokens 395k / 448k / 498k -> 400k /
+        // 460k / 520k tokens/s, of 8 297k -> 295k)
 #define SFFN_GATE_FUSED(NTV, UTV)                                                              \
     st = launch(h, KIND_GATE_UP_MFMA_FUSED, k_gate_up_mfma_fused<NTV, UTV, DENSE>, dim3(nb),   \
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const uint16_t*)W1,                  \
