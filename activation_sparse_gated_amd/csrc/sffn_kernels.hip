@@ -3064,6 +3064,169 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
     }
 }
 
+// Gate and up projection of an int8 batch in one pass (standard gating, batches
+// above 10 tokens and the dense comparator), as k_gate_up_mfma_fused does for bf16:
+// each 256-column chunk stages the block's 32 W1 code rows, its 32 W3 code rows and
+// the token rows of x (two 256-byte rows per token) together, so x is staged once
+// for both products. Wave w owns unit tile w & 1 of matrix w >> 1 (W1, then W3)
+// against every token tile and runs every k-step of the chunk, so no partial sums
+// are combined across waves; the codes are decoded exactly as in mfma_gate_pass_i8
+// (bf16 q + 128, the offset taken off by a second MFMA against a constant -128).
+template <int NT>
+struct FusedTilesI8 {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    static constexpr int TP = 16 * NT;
+    static constexpr int UB = 32;                          // units per block
+    static constexpr int ROWS = 2 * UB + 2 * TP;           // W1 rows, W3 rows, token half rows
+    static constexpr int IPW = ROWS / 16;                  // 1 KB load instructions per wave per chunk
+    static constexpr int STAGE = ROWS * 256;
+    static constexpr int NS = STAGE <= 32768 ? 4 : 3;
+    static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
+    static_assert(NS * STAGE <= 147456, "LDS ring");
+    static_assert(2 * UB * (TP + 1) * 4 <= NS * STAGE, "z and u tiles fit the ring");
+};
+
+template <int NT>
+__device__ inline void mfma_fused_pass_i8(f32x4 (&acc)[NT], const int8_t* __restrict__ W1,
+                                          const int8_t* __restrict__ W3, int u0, int H,
+                                          const uint16_t* __restrict__ x,
+                                          const uint16_t* __restrict__ zeros, int K, int T,
+                                          uint8_t* ring) {
+    using G = FusedTilesI8<NT>;
+    constexpr int NS = G::NS, IPW = G::IPW, UB = G::UB;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15, pq = lane >> 4;
+    const int ut = wave & 1, mat = wave >> 1;
+    const int nchunks = (K + KQ_KC - 1) / KQ_KC;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* src[IPW];
+    bool rok[IPW];
+    int pcol[IPW], cstep[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int r = 4 * (wave * IPW + i) + pq;  // staged row
+        if (r < 2 * UB) {
+            const int row = u0 + (r & (UB - 1));
+            const int8_t* W = r < UB ? W1 : W3;
+            const int p = r16 ^ (r & 15);
+            rok[i] = row < H;
+            pcol[i] = 16 * p;
+            cstep[i] = KQ_KC;
+            src[i] = reinterpret_cast<const uint8_t*>(W) + (rok[i] ? (size_t)row * K + 16 * p : 0);
+        } else {
+            const int xr = r - 2 * UB, tok = xr >> 1, half = xr & 1;
+            const int p = r16 ^ (tok & 15);
+            rok[i] = tok < T;
+            pcol[i] = 128 * half + 8 * p;
+            cstep[i] = 2 * KQ_KC;
+            src[i] = reinterpret_cast<const uint8_t*>(x + (rok[i] ? (size_t)tok * K + pcol[i] : 0));
+        }
+    }
+    auto issue = [&](int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const bool ok = rok[i] && c * KQ_KC + pcol[i] < K;
+            const void* g = ok ? (const void*)(src[i] + (size_t)c * cstep[i]) : (const void*)zeros;
+            load_lds16(g, ring + stage * G::STAGE + 1024 * (wave * IPW + i));
+        }
+    };
+    const u32x4 neg128 = u32x4{0xC300C300u, 0xC300C300u, 0xC300C300u, 0xC300C300u};  // bf16 -128
+    auto compute = [&](int stage) {
+        const uint8_t* wt = ring + stage * G::STAGE;
+        const uint8_t* xt = wt + 2 * UB * 256;
+        const int arow = mat * UB + ut * 16 + r16;  // arow & 15 == r16
+#pragma unroll
+        for (int ks = 0; ks < KQ_KC / 32; ++ks) {
+            // A: codes of columns 32 ks + 8 pq .. + 7 of the wave's unit row
+            const int pa = 2 * ks + (pq >> 1);
+            const uint2 wv = *reinterpret_cast<const uint2*>(wt + arow * 256 + 16 * (pa ^ r16) +
+                                                             8 * (pq & 1));
+            const u32x4 af = decode_i8x8_offset(wv.x, wv.y);
+            // B: token 16 i + r16, x of the same columns (half ks / 4 of the token row)
+            const int pb = 4 * (ks & 3) + pq;
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const int tok = i * 16 + r16;
+                const u32x4 bf = *reinterpret_cast<const u32x4*>(xt + (2 * tok + (ks >> 2)) * 256 +
+                                                                 16 * (pb ^ r16));
+                acc[i] = mfma_bf16(af, bf, acc[i]);
+                acc[i] = mfma_bf16(neg128, bf, acc[i]);
+            }
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + NS - 1) / NS * NS;
+    for (int c0 = 0; c0 < niter; c0 += NS) {
+#pragma unroll
+        for (int d = 0; d < NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((NS - 2) * IPW);  // this wave's pieces of chunk c have landed
+            __syncthreads();                // ... and every wave's; chunk c - 1 is consumed
+            issue((d + NS - 1) % NS, c + NS - 1);
+            if (c < nchunks) compute(d);
+        }
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+}
+
+template <int NT, bool DENSE>
+__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused_i8(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ W1, const float* __restrict__ s1,
+    const int8_t* __restrict__ W3, const float* __restrict__ s3, const float* __restrict__ s2,
+    const uint16_t* __restrict__ zeros, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act,
+    int split) {
+    using G = FusedTilesI8<NT>;
+    constexpr int TP = G::TP, UB = G::UB;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
+    __shared__ unsigned long long tmask[UB];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15;
+    const int u0 = blockIdx.x * UB;
+    const int ut = wave & 1, mat = wave >> 1;
+
+    if (y_zero) {
+        for (int j = blockIdx.x * KM_THREADS + threadIdx.x; j < T * D; j += gridDim.x * KM_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    if (threadIdx.x < UB) tmask[threadIdx.x] = 0ull;  // first read after the pass's barriers
+
+    f32x4 acc[NT];
+    mfma_fused_pass_i8<NT>(acc, W1, W3, u0, H, x, zeros, D, T, ring);
+    // the ring is free after the pass (its loads have landed, every wave is past it):
+    // z sums of the block's units in zu[0], u sums in zu[1]
+    float (*zu)[UB][TP + 1] = reinterpret_cast<float (*)[UB][TP + 1]>(ring);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zu[mat][ut * 16 + 4 * (lane >> 4) + j][i * 16 + r16] = acc[i][j];
+    __syncthreads();
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        if (u0 + i >= H) continue;
+        const bool ok = t < T;
+        const float z = zu[0][i][t] * s1[u0 + i];
+        const bool live = ok && (DENSE || z > 0.0f);
+        if (live) atomicOr(&tmask[i], 1ull << t);
+        if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
+        float av = 0.0f;
+        if (live) {
+            const float u = zu[1][i][t] * s3[u0 + i];
+            av = activation(act, z) * u * s2[u0 + i];
+        }
+        store_product(a_rm, (size_t)(u0 + i), TP, t, av, split);
+    }
+    __syncthreads();
+    if (threadIdx.x < UB && u0 + (int)threadIdx.x < H) umask[u0 + threadIdx.x] = tmask[threadIdx.x];
+}
+
 // LoPA rank projection for a batch, int8 V: t[token][m] = sV_m (qV_m . x_token),
 // 16 rank rows per block, stored token-major as bf16 hi and lo parts (as
 // k_rank_proj_mfma).
