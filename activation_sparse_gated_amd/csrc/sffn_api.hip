@@ -32,7 +32,8 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_DOWN_TB_I4, KIND_RANK_PROJ_TB_I8, KIND_GATE_UP_LOPA_TB_Q, KIND_DOWN_PT,
             KIND_GATE_UP_MFMA_I8, KIND_DOWN_MFMA_I8, KIND_RANK_PROJ_MFMA_I8,
             KIND_GATE_UP_MFMA_I4, KIND_DOWN_MFMA_I4, KIND_DOWN_PT_I8, KIND_DOWN_PT_I4,
-            KIND_GATE_UP_MFMA_FUSED, KIND_GATE_UP_MFMA_FUSED_I8, KIND_COUNT };
+            KIND_GATE_UP_MFMA_FUSED, KIND_GATE_UP_MFMA_FUSED_I8, KIND_GATE_UP_MFMA_FUSED_I4,
+            KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_down_t1",
@@ -51,7 +52,8 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_down_pt", "k_gate_up_mfma_i8", "k_down_mfma_i8",
                                             "k_rank_proj_mfma_i8", "k_gate_up_mfma_i4",
                                             "k_down_mfma_i4", "k_down_pt_i8", "k_down_pt_i4",
-                                            "k_gate_up_mfma_fused", "k_gate_up_mfma_fused_i8"};
+                                            "k_gate_up_mfma_fused", "k_gate_up_mfma_fused_i8",
+                                            "k_gate_up_mfma_fused_i4"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
@@ -782,11 +784,21 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
     const int nb = (h->H + 31) / 32;
     const int splits = mfma_down_splits(h, nt);
     float* yz = (per_token || splits > 1) ? y : nullptr;
-    SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_I4, k_gate_up_mfma_i4<NT, DENSE, LOPA>,
-                                   dim3(nb), dim3(KM_THREADS), s, (const uint16_t*)x, W1, s1,
-                                   (const uint8_t*)W3, s3, (const uint16_t*)h->m_zero, h->m_a,
-                                   h->m_mask, live, yz, h->D, h->H, T, h->act,
-                                   (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r, h->flags));
+    if (!LOPA && (DENSE || T > 10)) {
+        // W1 and W3 codes of the block and x staged together, x once for both
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_FUSED_I4,
+                                       k_gate_up_mfma_fused_i4<NT, DENSE>, dim3(nb),
+                                       dim3(KM_THREADS), s, (const uint16_t*)x, (const uint8_t*)W1,
+                                       s1, (const uint8_t*)W3, s3, (const uint16_t*)h->m_zero,
+                                       h->m_a, h->m_mask, live, yz, h->D, h->H, T, h->act));
+    } else {
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_I4, k_gate_up_mfma_i4<NT, DENSE, LOPA>,
+                                       dim3(nb), dim3(KM_THREADS), s, (const uint16_t*)x, W1, s1,
+                                       (const uint8_t*)W3, s3, (const uint16_t*)h->m_zero, h->m_a,
+                                       h->m_mask, live, yz, h->D, h->H, T, h->act,
+                                       (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r,
+                                       h->flags));
+    }
     if (st != SFFN_OK) return st;
     const int ntile = (h->D + KDM_NB - 1) / KDM_NB;
     if (per_token)

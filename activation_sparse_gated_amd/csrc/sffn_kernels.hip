@@ -3723,6 +3723,200 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
     }
 }
 
+// Gate and up projection of an int4 batch in one pass (standard gating, batches
+// above 10 tokens and the dense comparator), as k_gate_up_mfma_fused_i8 does for
+// int8: each 256-column chunk stages the block's 32 W1 code rows and 32 W3 code rows
+// (128 bytes each) and the token rows of x together. Wave w owns unit tile w & 1 of
+// matrix w >> 1 over every k-step; each 128-column group is summed in its own
+// accumulators and added with the row's group scale (both matrices' scales of the
+// block in LDS), the same steps as mfma_gate_pass_i4.
+template <int NT>
+struct FusedTilesI4 {
+    static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
+    static constexpr int TP = 16 * NT;
+    static constexpr int UB = 32;
+    static constexpr int WI = 2 * UB / 8;                  // weight load instructions per chunk (1 KB each)
+    static constexpr int IPW = (WI + TP / 2) / 4;          // load instructions per wave per chunk
+    static constexpr int STAGE = 2 * UB * 128 + 2 * TP * 256;
+    static constexpr int NS = STAGE <= 24576 ? 4 : 3;
+    static constexpr int SPT = 2 * UB * I4_GMAX / KM_THREADS;  // scale entries per thread
+    static_assert((WI + TP / 2) % 4 == 0, "whole load instructions per wave");
+    static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
+    static_assert(2 * UB * (TP + 1) * 4 <= NS * STAGE, "z and u tiles fit the ring");
+};
+
+template <int NT>
+__device__ inline void mfma_fused_pass_i4(f32x4 (&acc)[NT], const uint8_t* __restrict__ W1,
+                                          const float* __restrict__ s1,
+                                          const uint8_t* __restrict__ W3,
+                                          const float* __restrict__ s3, int u0, int H,
+                                          const uint16_t* __restrict__ x,
+                                          const uint16_t* __restrict__ zeros, int K, int T,
+                                          uint8_t* ring, float (*sc)[I4_GMAX]) {
+    using G = FusedTilesI4<NT>;
+    constexpr int NS = G::NS, IPW = G::IPW, UB = G::UB;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15, pq = lane >> 4;
+    const int ut = wave & 1, mat = wave >> 1;
+    const int nchunks = (K + KQ_KC - 1) / KQ_KC;
+    const int ng = K / I4_GROUP;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // group scales of the block's W1 rows (sc rows 0 .. UB - 1) and W3 rows (UB ..),
+    // issued before the ring loads
+    float sv[G::SPT];
+#pragma unroll
+    for (int m = 0; m < G::SPT; ++m) {
+        const int e = threadIdx.x + m * KM_THREADS;
+        const int rl = e / I4_GMAX, g = e % I4_GMAX;
+        const int row = u0 + (rl & (UB - 1));
+        const float* scales = rl < UB ? s1 : s3;
+        sv[m] = (g < ng && row < H) ? scales[(size_t)row * ng + g] : 0.0f;
+    }
+
+    const uint8_t* src[IPW];
+    bool rok[IPW];
+    int pcol[IPW], cstep[IPW];
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+        const int q = wave * IPW + i;  // load instruction of the chunk
+        if (q < G::WI) {
+            const int rl = 8 * q + (lane >> 3);  // staged weight row: W1 rows, then W3 rows
+            const int p = (lane & 7) ^ ((rl >> 1) & 7);
+            const int row = u0 + (rl & (UB - 1));
+            const uint8_t* W = rl < UB ? W1 : W3;
+            rok[i] = row < H;
+            pcol[i] = 32 * p;
+            cstep[i] = KQ_KC / 2;
+            src[i] = W + (rok[i] ? (size_t)row * (K / 2) + 16 * p : 0);
+        } else {
+            const int xr = 4 * (q - G::WI) + pq, tok = xr >> 1, half = xr & 1;
+            const int p = r16 ^ (tok & 15);
+            rok[i] = tok < T;
+            pcol[i] = 128 * half + 8 * p;
+            cstep[i] = 2 * KQ_KC;
+            src[i] = reinterpret_cast<const uint8_t*>(x + (rok[i] ? (size_t)tok * K + pcol[i] : 0));
+        }
+    }
+    auto issue = [&](int stage, int c) {
+#pragma unroll
+        for (int i = 0; i < IPW; ++i) {
+            const bool ok = rok[i] && c * KQ_KC + pcol[i] < K;
+            const void* g = ok ? (const void*)(src[i] + (size_t)c * cstep[i]) : (const void*)zeros;
+            load_lds16(g, ring + stage * G::STAGE + 1024 * (wave * IPW + i));
+        }
+    };
+    const u32x4 neg136 = u32x4{0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};  // bf16 -136
+    const int arow = mat * UB + ut * 16 + r16;
+    auto compute = [&](int stage, int c) {
+        const uint8_t* wt = ring + stage * G::STAGE;
+        const uint8_t* xt = wt + 2 * UB * 128;
+#pragma unroll
+        for (int gh = 0; gh < 2; ++gh) {  // the chunk's two scale groups
+            f32x4 tmp[NT];
+#pragma unroll
+            for (int i = 0; i < NT; ++i) tmp[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int ks = 4 * gh + kk;
+                // A: codes of columns 32 ks + 8 pq .. + 7 (piece ks, bytes 4 pq .. + 3)
+                const uint32_t wv = *reinterpret_cast<const uint32_t*>(
+                    wt + arow * 128 + 16 * (ks ^ ((arow >> 1) & 7)) + 4 * pq);
+                const u32x4 af = decode_i4x8_offset(wv);
+                const int pb = 4 * (ks & 3) + pq;
+#pragma unroll
+                for (int i = 0; i < NT; ++i) {
+                    const int tok = i * 16 + r16;
+                    const u32x4 bf = *reinterpret_cast<const u32x4*>(
+                        xt + (2 * tok + (ks >> 2)) * 256 + 16 * (pb ^ r16));
+                    tmp[i] = mfma_bf16(af, bf, tmp[i]);
+                    tmp[i] = mfma_bf16(neg136, bf, tmp[i]);
+                }
+            }
+            // C rows of this lane: 4 (lane / 16) + j of the unit tile
+            const int g = 2 * c + gh;
+            float s4[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) s4[j] = sc[mat * UB + ut * 16 + 4 * pq + j][g < I4_GMAX ? g : 0];
+#pragma unroll
+            for (int i = 0; i < NT; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(s4[j], tmp[i][j], acc[i][j]);
+        }
+    };
+
+#pragma unroll
+    for (int d = 0; d < NS - 1; ++d) issue(d, d);
+    const int niter = (nchunks + NS - 1) / NS * NS;
+    for (int c0 = 0; c0 < niter; c0 += NS) {
+#pragma unroll
+        for (int d = 0; d < NS; ++d) {
+            const int c = c0 + d;
+            wait_vmcnt((NS - 2) * IPW);  // this wave's pieces of chunk c (and the scales) have landed
+            if (c == 0) {
+#pragma unroll
+                for (int m = 0; m < G::SPT; ++m) {
+                    const int e = threadIdx.x + m * KM_THREADS;
+                    sc[e / I4_GMAX][e % I4_GMAX] = sv[m];
+                }
+            }
+            __syncthreads();                // ... and every wave's; chunk c - 1 is consumed
+            issue((d + NS - 1) % NS, c + NS - 1);
+            if (c < nchunks) compute(d, c);
+        }
+    }
+    wait_vmcnt(0);
+    __syncthreads();
+}
+
+template <int NT, bool DENSE>
+__global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused_i4(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ W1, const float* __restrict__ s1,
+    const uint8_t* __restrict__ W3, const float* __restrict__ s3,
+    const uint16_t* __restrict__ zeros, float* __restrict__ a_rm, uint64_t* __restrict__ umask,
+    uint8_t* __restrict__ live_out, float* __restrict__ y_zero, int D, int H, int T, int act) {
+    using G = FusedTilesI4<NT>;
+    constexpr int TP = G::TP, UB = G::UB;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
+    __shared__ float sc[2 * UB][I4_GMAX];
+    __shared__ unsigned long long tmask[UB];
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int wave = threadIdx.x / WAVE;
+    const int r16 = lane & 15;
+    const int u0 = blockIdx.x * UB;
+    const int ut = wave & 1, mat = wave >> 1;
+
+    if (y_zero) {
+        for (int j = blockIdx.x * KM_THREADS + threadIdx.x; j < T * D; j += gridDim.x * KM_THREADS)
+            y_zero[j] = 0.0f;
+    }
+    if (threadIdx.x < UB) tmask[threadIdx.x] = 0ull;  // first read after the pass's barriers
+
+    f32x4 acc[NT];
+    mfma_fused_pass_i4<NT>(acc, W1, s1, W3, s3, u0, H, x, zeros, D, T, ring, sc);
+    // the ring is free after the pass: z sums in zu[0], u sums in zu[1]
+    float (*zu)[UB][TP + 1] = reinterpret_cast<float (*)[UB][TP + 1]>(ring);
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) zu[mat][ut * 16 + 4 * (lane >> 4) + j][i * 16 + r16] = acc[i][j];
+    __syncthreads();
+    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+        const int i = e / TP, t = e % TP;
+        if (u0 + i >= H) continue;
+        const bool ok = t < T;
+        const float z = zu[0][i][t];
+        const bool live = ok && (DENSE || z > 0.0f);
+        if (live) atomicOr(&tmask[i], 1ull << t);
+        if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
+        a_rm[(size_t)(u0 + i) * TP + t] = live ? activation(act, z) * zu[1][i][t] : 0.0f;
+    }
+    __syncthreads();
+    if (threadIdx.x < UB && u0 + (int)threadIdx.x < H) umask[u0 + threadIdx.x] = tmask[threadIdx.x];
+}
+
 // Down pass of an int4 batch: k_down_mfma with the codes of W2T (32 columns per
 // 16-byte piece, one piece per thread per chunk of 64 units x 128 columns)
 // decoded exactly into the bf16 staging layout; the block's 128 columns are one
