@@ -21,7 +21,7 @@ FLAGS = [
 
 def build(verbose: bool = False) -> str:
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *SOURCES,
-           "-o", LIB + ".tmp"]
+           "-lhipblaslt", "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

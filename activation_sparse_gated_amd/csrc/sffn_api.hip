@@ -3,6 +3,7 @@
 // forward call. All arithmetic runs in the kernels of sffn_kernels.hip.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
+#include <hipblaslt/hipblaslt.h>
 
 #include <algorithm>
 #include <cstdio>
@@ -33,7 +34,7 @@ enum Kind { KIND_GATE_UP_SPARSE = 0, KIND_GATE_UP_LOPA, KIND_RANK_PROJ, KIND_GAT
             KIND_GATE_UP_MFMA_I8, KIND_DOWN_MFMA_I8, KIND_RANK_PROJ_MFMA_I8,
             KIND_GATE_UP_MFMA_I4, KIND_DOWN_MFMA_I4, KIND_DOWN_PT_I8, KIND_DOWN_PT_I4,
             KIND_GATE_UP_MFMA_FUSED, KIND_GATE_UP_MFMA_FUSED_I8, KIND_GATE_UP_MFMA_FUSED_I4,
-            KIND_COUNT };
+            KIND_DOWN_GEMM_BLT, KIND_COUNT };
 const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa", "k_rank_proj",
                                             "k_gate_up_dense", "k_down", "k_live_list",
                                             "k_gate_up_t1", "k_down_t1",
@@ -53,10 +54,18 @@ const char* const kKindNames[KIND_COUNT] = {"k_gate_up_sparse", "k_gate_up_lopa"
                                             "k_rank_proj_mfma_i8", "k_gate_up_mfma_i4",
                                             "k_down_mfma_i4", "k_down_pt_i8", "k_down_pt_i4",
                                             "k_gate_up_mfma_fused", "k_gate_up_mfma_fused_i8",
-                                            "k_gate_up_mfma_fused_i4"};
+                                            "k_gate_up_mfma_fused_i4", "down_gemm_hipblaslt"};
 
 // Largest batch of a bf16 standard-gating handle (batches above MAXT run as GEMMs).
 constexpr int MAXT_GEMM = 8192;
+// From this many tokens the down pass runs as one library GEMM over every unit: against
+// k_down_gemm (D=2560, H=7168, weights rotating through HBM) the union of 1280 / 1536 /
+// 1792 / 2048 tokens 4.95M / 5.90M / 5.80M / 6.58M -> 5.17M / 6.49M / 6.85M / 7.62M
+// tokens/s, level at 1024 (union +1 %, dense -3 %). Its workspace is allocated with the
+// handle; plans are cached per handle.
+constexpr int BLT_MIN_T = 1025;
+constexpr size_t BLT_WS = size_t(64) << 20;
+constexpr size_t BLT_MAX_PLANS = 16;
 
 thread_local std::string g_thread_error = "no error";
 
@@ -94,6 +103,17 @@ struct sffn_handle {
     uint16_t* g_a = nullptr;       // [H x g_tp] bf16 unit products, unit-major
     uint64_t* g_any = nullptr;     // [g_tp / 256 x 2 ceil(H / 128)] 64-unit live masks per token tile
     int32_t* g_list = nullptr;     // [H + 32] units live for some token, then the count
+    // the down pass of batches of BLT_MIN_T tokens and more: y = a W2 over every unit as
+    // one hipBLASLt GEMM (bf16 in, fp32 out), plans cached per token count
+    struct BltPlan {
+        int T = 0;
+        hipblasLtMatmulDesc_t desc = nullptr;
+        hipblasLtMatrixLayout_t la = nullptr, lb = nullptr, ly = nullptr;
+        hipblasLtMatmulAlgo_t algo{};
+    };
+    hipblasLtHandle_t blt = nullptr;
+    void* blt_ws = nullptr;        // workspace of the library GEMM
+    std::vector<BltPlan> blt_plans;
 
     // instrumentation
     int timing_every = 0;   // 0: off; N: the launches of every Nth forward call are timed
@@ -498,6 +518,87 @@ sffn_status run_gate_gemm(sffn_handle* h, const void* x, const void* W1, const v
                   (const uint64_t*)h->g_any, ntt, nut * (UN / 64), h->g_list, count);
 }
 
+void blt_plan_free(sffn_handle::BltPlan& p) {
+    if (p.la) (void)hipblasLtMatrixLayoutDestroy(p.la);
+    if (p.lb) (void)hipblasLtMatrixLayoutDestroy(p.lb);
+    if (p.ly) (void)hipblasLtMatrixLayoutDestroy(p.ly);
+    if (p.desc) (void)hipblasLtMatmulDescDestroy(p.desc);
+    p = sffn_handle::BltPlan{};
+}
+
+// Plan of y[T x D] = sum over units u of a[u][t] W2T[u][:], in the library's
+// column-major terms Y (D x T) = A (W2T as D x H, ld D) . B^T (the unit-major products
+// as T x H, ld g_tp), fp32 accumulation and output.
+sffn_status blt_plan(sffn_handle* h, int T, const sffn_handle::BltPlan** out) {
+    for (const auto& p : h->blt_plans)
+        if (p.T == T) {
+            *out = &p;
+            return SFFN_OK;
+        }
+    sffn_handle::BltPlan p;
+    p.T = T;
+    hipblasStatus_t st = hipblasLtMatmulDescCreate(&p.desc, HIPBLAS_COMPUTE_32F, HIP_R_32F);
+    const hipblasOperation_t opn = HIPBLAS_OP_N, opt = HIPBLAS_OP_T;
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSA, &opn, sizeof(opn));
+    if (st == HIPBLAS_STATUS_SUCCESS)
+        st = hipblasLtMatmulDescSetAttribute(p.desc, HIPBLASLT_MATMUL_DESC_TRANSB, &opt, sizeof(opt));
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&p.la, HIP_R_16BF, h->D, h->H, h->D);
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&p.lb, HIP_R_16BF, T, h->H, h->g_tp);
+    if (st == HIPBLAS_STATUS_SUCCESS) st = hipblasLtMatrixLayoutCreate(&p.ly, HIP_R_32F, h->D, T, h->D);
+    int n = 0;
+    if (st == HIPBLAS_STATUS_SUCCESS) {
+        hipblasLtMatmulPreference_t pref = nullptr;
+        st = hipblasLtMatmulPreferenceCreate(&pref);
+        const uint64_t ws = BLT_WS;
+        if (st == HIPBLAS_STATUS_SUCCESS)
+            st = hipblasLtMatmulPreferenceSetAttribute(pref, HIPBLASLT_MATMUL_PREF_MAX_WORKSPACE_BYTES,
+                                                       &ws, sizeof(ws));
+        hipblasLtMatmulHeuristicResult_t res[1];
+        if (st == HIPBLAS_STATUS_SUCCESS)
+            st = hipblasLtMatmulAlgoGetHeuristic(h->blt, p.desc, p.la, p.lb, p.ly, p.ly, pref, 1, res, &n);
+        if (pref) (void)hipblasLtMatmulPreferenceDestroy(pref);
+        if (st == HIPBLAS_STATUS_SUCCESS && n > 0) p.algo = res[0].algo;
+    }
+    if (st != HIPBLAS_STATUS_SUCCESS || n == 0) {
+        blt_plan_free(p);
+        return fail(h, SFFN_INTERNAL, "hipBLASLt has no plan for the down GEMM at T=" + std::to_string(T) +
+                                          " (status " + std::to_string((int)st) + ")");
+    }
+    if (h->blt_plans.size() >= BLT_MAX_PLANS) {
+        blt_plan_free(h->blt_plans.front());
+        h->blt_plans.erase(h->blt_plans.begin());
+    }
+    h->blt_plans.push_back(p);
+    *out = &h->blt_plans.back();
+    return SFFN_OK;
+}
+
+sffn_status run_down_blt(sffn_handle* h, const void* W2T, float* y, int T, hipStream_t s) {
+    const sffn_handle::BltPlan* p = nullptr;
+    sffn_status st = blt_plan(h, T, &p);
+    if (st != SFFN_OK) return st;
+    const float alpha = 1.0f, beta = 0.0f;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (h->timed_call) {
+        e0 = take_event(h);
+        e1 = take_event(h);
+        if (!e0 || !e1) return fail(h, SFFN_HIP_ERROR, "hipEventCreate failed");
+        hipError_t e = hipEventRecord(e0, s);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    }
+    const hipblasStatus_t bs = hipblasLtMatmul(h->blt, p->desc, &alpha, W2T, p->la, h->g_a, p->lb, &beta,
+                                               y, p->ly, y, p->ly, &p->algo, h->blt_ws, BLT_WS, s);
+    if (h->timed_call) {
+        hipError_t e = hipEventRecord(e1, s);
+        if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+        h->pending.push_back({KIND_DOWN_GEMM_BLT, e0, e1});
+    }
+    if (bs != HIPBLAS_STATUS_SUCCESS)
+        return fail(h, SFFN_HIP_ERROR, "hipblasLtMatmul (down GEMM): status " + std::to_string((int)bs));
+    return SFFN_OK;
+}
+
 template <bool DENSE>
 sffn_status run_gemm(sffn_handle* h, const void* x, const void* W1, const void* W3,
                      const void* W2T, float* y, int T, int32_t* live_count, int32_t* live_idx,
@@ -514,6 +615,16 @@ sffn_status run_gemm(sffn_handle* h, const void* x, const void* W1, const void* 
     int32_t* count = h->g_list + h->H + 32;
     // 256 x 128 gate tiles once there are 200 of them, else 256 x 64 (more blocks)
     const bool wide = (long)((T + 255) / 256) * ((h->H + 127) / 128) >= 200;
+    if (T >= BLT_MIN_T && h->blt) {
+        // the down pass over every unit (the products of units dead for every token are
+        // exact zeros: A(z) = 0 for z <= 0), so the gate writes no union masks, and y is
+        // written by the GEMM (no clear)
+        sffn_status st = wide ? run_gate_gemm<256, 128, true>(h, x, W1, W3, live, nullptr, T, s)
+                              : run_gate_gemm<256, 64, true>(h, x, W1, W3, live, nullptr, T, s);
+        if (st == SFFN_OK) st = run_down_blt(h, W2T, y, T, s);
+        if (st != SFFN_OK || DENSE) return st;
+        return run_live_list(h, T, live_count, live_idx, s);
+    }
     sffn_status st = wide ? run_gate_gemm<256, 128, DENSE>(h, x, W1, W3, live, yz, T, s)
                           : run_gate_gemm<256, 64, DENSE>(h, x, W1, W3, live, yz, T, s);
     if (st != SFFN_OK) return st;
@@ -1315,10 +1426,20 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
             if (e == hipSuccess) e = hipMalloc(&h->g_any, (size_t)ntt * nm * sizeof(uint64_t));
             if (e == hipSuccess) e = hipMalloc(&h->g_list, ((size_t)H + 33) * sizeof(int32_t));
             if (e == hipSuccess) e = hipMemsetAsync(h->g_list, 0, ((size_t)H + 33) * sizeof(int32_t), init);
+            if (e == hipSuccess && max_tokens >= BLT_MIN_T) e = hipMalloc(&h->blt_ws, BLT_WS);
             if (e != hipSuccess) {
                 (void)finish_init(e);
                 sffn_destroy(h);
                 return fail(nullptr, SFFN_OUT_OF_MEMORY, std::string("scratch allocation: ") + hipGetErrorString(e));
+            }
+            if (max_tokens >= BLT_MIN_T) {
+                const hipblasStatus_t bs = hipblasLtCreate(&h->blt);
+                if (bs != HIPBLAS_STATUS_SUCCESS) {
+                    h->blt = nullptr;
+                    (void)finish_init(hipSuccess);
+                    sffn_destroy(h);
+                    return fail(nullptr, SFFN_HIP_ERROR, "hipblasLtCreate: status " + std::to_string((int)bs));
+                }
             }
         }
         e = finish_init(hipSuccess);
@@ -1362,6 +1483,10 @@ void sffn_destroy(sffn_handle* h) {
     if (h->g_a) (void)hipFree(h->g_a);
     if (h->g_any) (void)hipFree(h->g_any);
     if (h->g_list) (void)hipFree(h->g_list);
+    for (auto& p : h->blt_plans) blt_plan_free(p);
+    h->blt_plans.clear();
+    if (h->blt) (void)hipblasLtDestroy(h->blt);
+    if (h->blt_ws) (void)hipFree(h->blt_ws);
 
     delete h;
 }

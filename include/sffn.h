@@ -30,7 +30,9 @@
  * Requirements: D % 8 == 0, D <= 8192; 1 <= H <= 1<<20; LoPA: r % 8 == 0 and
  * 8 <= r <= 2048; 0 <= T <= max_tokens (at most 64, or 8192 for bf16
  * standard-gating handles: union and dense calls with T > 64 run as MFMA
- * GEMMs with the unit products rounded to bf16, and those with 5..64 tokens
+ * GEMMs with the unit products rounded to bf16 (above 1024 tokens the down
+ * projection is one hipBLASLt GEMM over every unit: the products of units
+ * dead for every token are exact zeros), and those with 5..64 tokens
  * multiply them as two bf16 parts, about 16 significant bits, on MFMA); every
  * pointer 16-byte aligned and a device pointer (hipMalloc or torch CUDA
  * tensors). T == 0 is a no-op.
@@ -126,7 +128,8 @@ enum { SFFN_FLAG_G_TILED = 1u, SFFN_FLAG_RMSNORM = 2u, SFFN_FLAG_DOUBLE_ACT = 4u
  * On success *out receives the handle. Allocates device scratch on the
  * current device: about min(max_tokens, 64) * (H + r) floats plus
  * max_tokens * H bytes, and for max_tokens > 64 also H * 256 ceil(max_tokens /
- * 256) bf16 unit products.
+ * 256) bf16 unit products; for max_tokens > 1024 also a hipBLASLt handle and its
+ * 64 MiB workspace (SFFN_HIP_ERROR if the library cannot create the handle).
  */
 sffn_status sffn_create(sffn_handle **out, int D, int H, int r, int max_tokens, int act,
                         int dtype, unsigned flags);
