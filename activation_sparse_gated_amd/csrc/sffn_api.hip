@@ -1195,9 +1195,14 @@ sffn_status dispatch_sparse(sffn_handle* h, const void* x, const void* W1, const
         // per-token lists: one batched gate and up pass (W1 read once for the batch),
         // then each token gathers the W2T rows of its own live list
         return run_mfma<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s, nullptr, true);
+    if (mode == SFFN_MODE_PER_TOKEN && gemm_ok(h, T))
+        // above 64 tokens every unit is live for some token in practice (1 - s^T), so
+        // per-token gathers would read nearly every row once per token: the batch takes
+        // the union GEMMs (same result; the live lists are still per token)
+        return run_gemm<false>(h, x, W1, W3, W2T, y, T, live_count, live_idx, s);
     if (mode == SFFN_MODE_PER_TOKEN && t1_ok(h, 1)) {
-        // per-token lists above 64 tokens: every token runs the whole batch-1 pass on its
-        // own live set
+        // per-token lists above 64 tokens on handles without the GEMM path (standard
+        // gating in fp32): every token runs the whole batch-1 pass on its own live set
         const size_t xb = (size_t)h->D * sizeof(uint16_t);
         for (int t = 0; t < T; ++t) {
             st = run_sparse_t1(h, (const char*)x + t * xb, W1, W3, W2T, y + (size_t)t * h->D,

@@ -88,7 +88,10 @@ enum { SFFN_ACT_RELU = 0, SFFN_ACT_RSPLUS = 1 };
  * the _i4 ones. */
 enum { SFFN_BF16 = 0, SFFN_F32 = 1, SFFN_I8 = 2, SFFN_I4 = 3 };
 /* How a batch of T tokens moves data; never changes the result.
- * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set.
+ * PER_TOKEN: each token reads the W3 rows and W2T rows of its own live set
+ *            (bf16 standard-gating batches above 64 tokens, where nearly every
+ *            unit is live for some token, run as UNION; live lists stay per
+ *            token).
  * UNION:     the union of the tokens' live sets is read once and each row is
  *            applied to the tokens for which it is live (batched decode: the
  *            pages note the speedup is quoted at batch size 1 and erodes as
