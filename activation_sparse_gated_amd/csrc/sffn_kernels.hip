@@ -1379,9 +1379,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
             for (int k = 0; k < 16; ++k) tv[c][k] = 0.0f;
         }
     }
-    X16 xv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) xv[c] = load_x16(x, c * CW + lane * 16, D);
     const float su_ = in ? sU[unit] : 0.0f;
     const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
     float inv = 1.0f;  // RMSNorm of t: every lane group sees all of t
@@ -1403,6 +1400,13 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i8(
         if (!live) a_out[unit] = 0.0f;
     }
     uint64_t m = __ballot(live && sub == 0);
+    // x only for waves with a live unit (about a fifth of them): its loads go out with
+    // the first W3 row's
+    X16 xv[NC];
+    if (m) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) xv[c] = load_x16(x, c * CW + lane * 16, D);
+    }
     while (m) {
         const int g = __builtin_ctzll(m) / LPU;
         m &= m - 1;
@@ -1683,9 +1687,6 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i4(
             for (int k = 0; k < 16; ++k) tv[c][k] = 0.0f;
         }
     }
-    X32 xv[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) xv[c] = load_x32(x, c * CW + lane * 32, D);
     const float su_ = in ? sU[unit] : 0.0f;
     const float gx = ((flags & LOPA_G_TILED) && in) ? Elem<uint16_t>::get1(x[unit % D]) : 0.0f;
     float inv = 1.0f;  // RMSNorm of t: every lane group sees all of t
@@ -1707,6 +1708,12 @@ __global__ __launch_bounds__(K1_THREADS) void k_gate_up_lopa_t1_i4(
         if (!live) a_out[unit] = 0.0f;
     }
     uint64_t m = __ballot(live && sub == 0);
+    // x only for waves with a live unit: its loads go out with the first W3 row's
+    X32 xv[NC];
+    if (m) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) xv[c] = load_x32(x, c * CW + lane * 32, D);
+    }
     while (m) {
         const int g = __builtin_ctzll(m) >> 4;
         m &= m - 1;
