@@ -395,8 +395,12 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     uint16_t* t_hi = h->m_t;
     uint16_t* t_lo = h->m_t ? h->m_t + (size_t)h->m_tp * h->r : nullptr;
     if (LOPA) {
-        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA, k_rank_proj_mfma<NT>,
-                                       dim3((h->r + 15) / 16), dim3(KM_THREADS), s,
+        // 16 rank rows x 16 tokens per block (grid: rank tiles x token tiles): x is staged
+        // once per token tile, V read once per token tile (from L2 after the first); at
+        // 64 tokens 100 blocks instead of 25 (LoPA union of 40 / 64 tokens 490k / 755k ->
+        // 508k / 788k tokens/s, int8 417k / 652k -> 441k / 691k)
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA, k_rank_proj_mfma<1>,
+                                       dim3((h->r + 15) / 16, NT), dim3(KM_THREADS), s,
                                        (const uint16_t*)x, (const uint16_t*)V,
                                        (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
         if (st != SFFN_OK) return st;
@@ -821,8 +825,8 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
     uint16_t* t_hi = h->m_t;
     uint16_t* t_lo = h->m_t ? h->m_t + (size_t)h->m_tp * h->r : nullptr;
     if (LOPA) {
-        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA_I8, k_rank_proj_mfma_i8<NT>,
-                                       dim3((h->r + 15) / 16), dim3(KM_THREADS), s,
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA_I8, k_rank_proj_mfma_i8<1>,
+                                       dim3((h->r + 15) / 16, NT), dim3(KM_THREADS), s,
                                        (const uint16_t*)x, (const int8_t*)V, sV,
                                        (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
         if (st != SFFN_OK) return st;
@@ -886,8 +890,8 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
     uint16_t* t_hi = h->m_t;
     uint16_t* t_lo = h->m_t ? h->m_t + (size_t)h->m_tp * h->r : nullptr;
     if (LOPA) {
-        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA_I8, k_rank_proj_mfma_i8<NT>,
-                                       dim3((h->r + 15) / 16), dim3(KM_THREADS), s,
+        SFFN_NT_SWITCH(nt, st = launch(h, KIND_RANK_PROJ_MFMA_I8, k_rank_proj_mfma_i8<1>,
+                                       dim3((h->r + 15) / 16, NT), dim3(KM_THREADS), s,
                                        (const uint16_t*)x, (const int8_t*)V, sV,
                                        (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
         if (st != SFFN_OK) return st;

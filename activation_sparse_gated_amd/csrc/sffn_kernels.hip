@@ -2580,6 +2580,14 @@ __global__ __launch_bounds__(KM_THREADS) void k_rank_proj_mfma(
     int D, int r, int T) {
     using G = GateTiles<NT, 1>;
     constexpr int TP = G::TP;
+    {
+        // token tile of this block (grid y): its TP tokens of x and rows of t
+        const int t0 = (int)blockIdx.y * TP;
+        x += (size_t)t0 * D;
+        t_hi += (size_t)t0 * r;
+        t_lo += (size_t)t0 * r;
+        T = min(TP, T - t0);
+    }
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
     __shared__ float part[G::KG][16][TP + 1];
     __shared__ int rows[16];
@@ -3245,6 +3253,14 @@ __global__ __launch_bounds__(KM_THREADS) void k_rank_proj_mfma_i8(
     int D, int r, int T) {
     using G = GateTilesI8<NT, 1>;
     constexpr int TP = G::TP;
+    {
+        // token tile of this block (grid y): its TP tokens of x and rows of t
+        const int t0 = (int)blockIdx.y * TP;
+        x += (size_t)t0 * D;
+        t_hi += (size_t)t0 * r;
+        t_lo += (size_t)t0 * r;
+        T = min(TP, T - t0);
+    }
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
     __shared__ float part[G::KG][16][TP + 1];
     __shared__ int rows[16];
