@@ -2102,6 +2102,24 @@ __device__ inline void store_product(float* __restrict__ a_rm, size_t row, int T
 // live; DENSE: all tokens), live flags [T x H] when requested, and clears y
 // (T x D) for a down pass that accumulates. `zeros`: at least 16 zero bytes.
 constexpr int KM_THREADS = 256;
+
+// Token mask of one unit in the batched gate epilogues, which walk the (unit,
+// token) entries e = i TP + t of a block in strides of KM_THREADS: the TP
+// entries of unit i are TP consecutive lanes of one wave (TP divides 64), so
+// one ballot gives bit t = "live for token t" to every lane of the unit, with
+// no LDS atomics (64 lanes or-ing one word serialise). Every lane of the wave
+// must call it.
+template <int TP>
+__device__ inline uint64_t unit_token_mask(bool live) {
+    static_assert(TP == 16 || TP == 32 || TP == 64, "token tile rows");
+    const uint64_t b = __ballot(live);
+    if constexpr (TP == 64) {
+        return b;
+    } else {
+        const int lane = threadIdx.x & (WAVE - 1);
+        return (b >> (lane & ~(TP - 1))) & ((1ull << TP) - 1);
+    }
+}
 constexpr int KM_KC = 128;        // columns per chunk (4 MFMA steps of 32): 256 B per row
 
 template <int NT, int UT>
@@ -2312,7 +2330,8 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
         zf[i][t] = z;
         const bool ok = (u0 + i < H) && t < T;
         const bool live = ok && (DENSE || z > 0.0f);
-        if (live) atomicOr(&tmask[i], 1ull << t);
+        const uint64_t tm = unit_token_mask<TP>(live);
+        if (t == 0) tmask[i] = tm;
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
     }
     __syncthreads();
@@ -2505,16 +2524,18 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused(
     __syncthreads();
     for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
         const int i = e / TP, t = e % TP;
-        if (u0 + i >= H) continue;
         float z = 0.0f, u = 0.0f;
 #pragma unroll
         for (int g = 0; g < G::KG; ++g) {
             z += pz[g][i][t];
             u += pu[g][i][t];
         }
-        const bool ok = t < T;
+        const bool in = u0 + i < H;
+        const bool ok = in && t < T;
         const bool live = ok && (DENSE || z > 0.0f);
-        if (live) atomicOr(&tmask[i], 1ull << t);
+        const uint64_t tm = unit_token_mask<TP>(live);  // before the wave's lanes part
+        if (!in) continue;
+        if (t == 0) tmask[i] = tm;
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
         store_product(a_rm, (size_t)(u0 + i), TP, t, live ? activation(act, z) * u : 0.0f, split);
     }
@@ -3036,7 +3057,8 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
         }
         zf[i][t] = z;
         const bool live = ok && (DENSE || z > 0.0f);
-        if (live) atomicOr(&tmask[i], 1ull << t);
+        const uint64_t tm = unit_token_mask<TP>(live);
+        if (t == 0) tmask[i] = tm;
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
     }
     __syncthreads();
@@ -3226,11 +3248,13 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused_i8(
     __syncthreads();
     for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
         const int i = e / TP, t = e % TP;
-        if (u0 + i >= H) continue;
-        const bool ok = t < T;
-        const float z = zu[0][i][t] * s1[u0 + i];
+        const bool in = u0 + i < H;
+        const bool ok = in && t < T;
+        const float z = in ? zu[0][i][t] * s1[u0 + i] : 0.0f;
         const bool live = ok && (DENSE || z > 0.0f);
-        if (live) atomicOr(&tmask[i], 1ull << t);
+        const uint64_t tm = unit_token_mask<TP>(live);  // before the wave's lanes part
+        if (!in) continue;
+        if (t == 0) tmask[i] = tm;
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
         float av = 0.0f;
         if (live) {
@@ -3704,7 +3728,8 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
         }
         zf[i][t] = z;
         const bool live = ok && (DENSE || z > 0.0f);
-        if (live) atomicOr(&tmask[i], 1ull << t);
+        const uint64_t tm = unit_token_mask<TP>(live);
+        if (t == 0) tmask[i] = tm;
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
     }
     __syncthreads();
@@ -3929,11 +3954,13 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_fused_i4(
     __syncthreads();
     for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
         const int i = e / TP, t = e % TP;
-        if (u0 + i >= H) continue;
-        const bool ok = t < T;
+        const bool in = u0 + i < H;
+        const bool ok = in && t < T;
         const float z = zu[0][i][t];
         const bool live = ok && (DENSE || z > 0.0f);
-        if (live) atomicOr(&tmask[i], 1ull << t);
+        const uint64_t tm = unit_token_mask<TP>(live);  // before the wave's lanes part
+        if (!in) continue;
+        if (t == 0) tmask[i] = tm;
         if (ok && live_out) live_out[(size_t)t * H + u0 + i] = (z > 0.0f) ? 1 : 0;
         a_rm[(size_t)(u0 + i) * TP + t] = live ? activation(act, z) * zu[1][i][t] : 0.0f;
     }
