@@ -2575,15 +2575,23 @@ __device__ inline u32x4 frag_tr(const uint8_t* part, int col0, int lane) {
 // different 32-byte slot pairs.
 __device__ inline int swz128(int r, int p) { return p ^ (2 * ((r >> 1) & 1) + 4 * ((r >> 3) & 1)); }
 
-// frag_tr over a part of 32 K-rows of 128 bytes (up to 64 bf16 columns).
-__device__ inline u32x4 frag_tr128(const uint8_t* part, int col0, int lane) {
+// Extra slot permutation of the lo parts of split products staged next to their
+// hi parts: with 16 or 32 tokens a unit's hi and lo pieces of one token group are
+// written by lanes of one 128-byte write group, and without it they would share banks
+// (with 64 tokens the two parts fill separate write groups).
+template <int TP>
+constexpr int lo_slot_xor() { return TP == 16 ? 2 : (TP == 32 ? 4 : 0); }
+
+// frag_tr over a part of 32 K-rows of 128 bytes (up to 64 bf16 columns); sx permutes
+// the slots of the part as staged (0, or lo_slot_xor for the lo parts).
+__device__ inline u32x4 frag_tr128(const uint8_t* part, int col0, int lane, int sx = 0) {
     typedef __attribute__((address_space(3))) i16x4* lds_v4;
     const int g = lane >> 4, s = lane & 15;
     const int col = col0 + 4 * (s & 3);
     const int p = col >> 3, half = (col >> 2) & 1;
     const int r0 = 8 * g + (s >> 2), r1 = r0 + 4;
-    const uint8_t* a0 = part + r0 * 128 + 16 * swz128(r0, p) + 8 * half;
-    const uint8_t* a1 = part + r1 * 128 + 16 * swz128(r1, p) + 8 * half;
+    const uint8_t* a0 = part + r0 * 128 + 16 * (swz128(r0, p) ^ sx) + 8 * half;
+    const uint8_t* a1 = part + r1 * 128 + 16 * (swz128(r1, p) ^ sx) + 8 * half;
     const i16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a0));
     const i16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(a1));
     const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
@@ -2763,7 +2771,8 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
             const int idx = threadIdx.x + q * KDM_THREADS;
             const int row = idx / (TP / 4), r = row & 31, p = idx % (TP / 4);
             const int part = p >= TP / 8 ? 1 : 0, tg = p - part * (TP / 8);
-            const int off = 2 * WPART + (2 * part + (row >> 5)) * APART + r * 128 + 16 * swz128(r, tg);
+            const int off = 2 * WPART + (2 * part + (row >> 5)) * APART + r * 128 +
+                            16 * (swz128(r, tg) ^ (part ? lo_slot_xor<TP>() : 0));
             *reinterpret_cast<u32x4*>(st + off) = aok[d][q] ? av[d][q] : u32x4{0u, 0u, 0u, 0u};
         }
     };
@@ -2773,7 +2782,7 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma(
         for (int ks = 0; ks < 2; ++ks) {
             const uint8_t* ah = st + 2 * WPART + ks * APART;
             const u32x4 fh = frag_tr128(ah, tt * 16, lane);
-            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane);
+            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane, lo_slot_xor<TP>());
 #pragma unroll
             for (int i = 0; i < NCW; ++i) {
                 const u32x4 b = frag_tr(st + ks * WPART, (cb + i) * 16, lane);
@@ -3423,7 +3432,8 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
             const int idx = threadIdx.x + q * KDM_THREADS;
             const int row = idx / (TP / 4), r = row & 31, p = idx % (TP / 4);
             const int part = p >= TP / 8 ? 1 : 0, tg = p - part * (TP / 8);
-            const int off = 2 * WPART + (2 * part + (row >> 5)) * APART + r * 128 + 16 * swz128(r, tg);
+            const int off = 2 * WPART + (2 * part + (row >> 5)) * APART + r * 128 +
+                            16 * (swz128(r, tg) ^ (part ? lo_slot_xor<TP>() : 0));
             *reinterpret_cast<u32x4*>(st + off) = aok[d][q] ? av[d][q] : u32x4{0u, 0u, 0u, 0u};
         }
     };
@@ -3433,7 +3443,7 @@ __global__ __launch_bounds__(KDM_THREADS) void k_down_mfma_i8(
         for (int ks = 0; ks < 2; ++ks) {
             const uint8_t* ah = st + 2 * WPART + ks * APART;
             const u32x4 fh = frag_tr128(ah, tt * 16, lane);
-            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane);
+            const u32x4 fl = frag_tr128(ah + 2 * APART, tt * 16, lane, lo_slot_xor<TP>());
 #pragma unroll
             for (int i = 0; i < NCW; ++i) {
                 const u32x4 b = frag_tr(st + ks * WPART, (cb + i) * 16, lane);
