@@ -834,7 +834,9 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
                                        (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
         if (st != SFFN_OK) return st;
     }
-    const int ut = 2;  // 32 units per gate block
+    // 32 units per gate block; LoPA above 32 tokens 64 (H' = 9787: 153 blocks in one
+    // round against 306 in 1.2 rounds, x staged half as often)
+    const int ut = (LOPA && nt == 4) ? 4 : 2;
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const int splits = mfma_down_splits(h, nt);
     float* yz = (per_token || splits > 1) ? y : nullptr;
@@ -847,18 +849,18 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
                                        h->m_a, h->m_mask, live, yz, h->D, h->H, T, h->act,
                                        per_token ? 0 : 1));
     } else {
-#define SFFN_GATE_MFMA_I8(NTV)                                                                 \
-    st = launch(h, KIND_GATE_UP_MFMA_I8, k_gate_up_mfma_i8<NTV, 2, DENSE, LOPA>, dim3(nb),     \
+#define SFFN_GATE_MFMA_I8(NTV, UTV)                                                            \
+    st = launch(h, KIND_GATE_UP_MFMA_I8, k_gate_up_mfma_i8<NTV, UTV, DENSE, LOPA>, dim3(nb),   \
                 dim3(KM_THREADS), s, (const uint16_t*)x, (const int8_t*)W1, s1,                \
                 (const int8_t*)W3, s3, s2, (const uint16_t*)h->m_zero, h->m_a, h->m_mask, live, \
                 yz, h->D, h->H, T, h->act, (const uint16_t*)t_hi, (const uint16_t*)t_lo, h->r,  \
                 h->flags, per_token ? 0 : 1)
     if (nt == 1) {
-        SFFN_GATE_MFMA_I8(1);
+        SFFN_GATE_MFMA_I8(1, 2);
     } else if (nt == 2) {
-        SFFN_GATE_MFMA_I8(2);
+        SFFN_GATE_MFMA_I8(2, 2);
     } else {
-        SFFN_GATE_MFMA_I8(4);
+        SFFN_GATE_MFMA_I8(4, LOPA ? 4 : 2);
     }
 #undef SFFN_GATE_MFMA_I8
     }

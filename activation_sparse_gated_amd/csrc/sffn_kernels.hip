@@ -2866,7 +2866,7 @@ constexpr int KQ_KC = 256;
 template <int NT, int UT>
 struct GateTilesI8 {
     static_assert(NT == 1 || NT == 2 || NT == 4, "token tiles: 1, 2 or 4");
-    static_assert(UT == 1 || UT == 2, "unit tiles: 1 or 2");
+    static_assert(UT == 1 || UT == 2 || UT == 4, "unit tiles: 1, 2 or 4");
     static constexpr int TP = 16 * NT;
     static constexpr int UB = 16 * UT;
     static constexpr int KG = 4 / UT;                      // K groups
@@ -2874,7 +2874,10 @@ struct GateTilesI8 {
     static constexpr int ROWS = UB + 2 * TP;               // staged 256-byte rows per chunk
     static constexpr int IPW = ROWS / 16;                  // 1 KB load instructions per wave per chunk
     static constexpr int STAGE = ROWS * 256;
-    static constexpr int NS = STAGE <= 24576 ? 4 : 3;
+    // 3 stages from 24 KB on: at 17-32 tokens (24 KB stages) two blocks then share a CU
+    // (LDS within 80 KB), so the 306 blocks of a LoPA gate over H' = 9787 run in one
+    // round (int8 LoPA union of 17 / 32 tokens 263k / 476k -> 361k / 642k tokens/s)
+    static constexpr int NS = STAGE <= 16384 ? 4 : 3;
     static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
 };
 
@@ -3007,9 +3010,12 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
     int split) {
     using G = GateTilesI8<NT, UT>;
     constexpr int TP = G::TP, UB = G::UB;
+    constexpr int EPT = UB * TP / KM_THREADS;  // (unit, token) entries per thread
+    static_assert(EPT * KM_THREADS == UB * TP, "entries per thread");
+    static_assert(G::KG * UB * (TP + 1) * 4 <= G::NS * G::STAGE, "partial sums fit the ring");
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
-    __shared__ float part[G::KG][UB][TP + 1];
-    __shared__ float zf[UB][TP + 1];
+    // the partial sums of a pass go through the ring once the pass has drained it
+    float (*part)[UB][TP + 1] = reinterpret_cast<float (*)[UB][TP + 1]>(ring);
     __shared__ unsigned long long tmask[UB];
     __shared__ int rows_g[UB];
     __shared__ int rows_u[UB];
@@ -3054,7 +3060,12 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
         store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+    // z of this thread's entries e = threadIdx.x + k KM_THREADS, kept in registers
+    // through the W3 pass (the ring is reused by it)
+    float zr[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = threadIdx.x + k * KM_THREADS;
         const int i = e / TP, t = e % TP;
         const bool ok = (u0 + i < H) && t < T;
         float z = 0.0f;
@@ -3064,7 +3075,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
             z *= s1[u0 + i];
             if (LOPA && (flags & LOPA_G_TILED)) z += Elem<uint16_t>::get1(x[(size_t)t * D + (u0 + i) % D]);
         }
-        zf[i][t] = z;
+        zr[k] = z;
         const bool live = ok && (DENSE || z > 0.0f);
         const uint64_t tm = unit_token_mask<TP>(live);
         if (t == 0) tmask[i] = tm;
@@ -3094,7 +3105,9 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
         store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = threadIdx.x + k * KM_THREADS;
         const int i = e / TP, t = e % TP;
         if (u0 + i >= H) continue;
         const int p = upos[i];
@@ -3105,7 +3118,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i8(
             for (int g = 0; g < G::KG; ++g) u += part[g][p][t];
             u *= s3[u0 + i];
             if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
-            av = activation(act, zf[i][t]) * u * s2[u0 + i];
+            av = activation(act, zr[k]) * u * s2[u0 + i];
         }
         store_product(a_rm, (size_t)(u0 + i), TP, t, av, split);
     }
