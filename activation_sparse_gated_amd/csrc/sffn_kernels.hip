@@ -3540,7 +3540,8 @@ struct GateTilesI4 {
     static constexpr int WI = UB / 8;                   // weight load instructions per chunk (1 KB each)
     static constexpr int IPW = (WI + TP / 2) / 4;       // load instructions per wave per chunk
     static constexpr int STAGE = UB * 128 + 2 * TP * 256;
-    static constexpr int NS = STAGE <= 24576 ? 4 : 3;
+    // 3 stages from 20 KB on: at 17-32 tokens the LoPA gate then fits two blocks per CU
+    static constexpr int NS = STAGE <= 16384 ? 4 : 3;
     static constexpr int SPT = UB * I4_GMAX / KM_THREADS;  // scale entries per thread
     static_assert((WI + TP / 2) % 4 == 0, "whole load instructions per wave");
     static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
@@ -3689,12 +3690,20 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
     using G8 = GateTilesI8<NT, 2>;
     constexpr int TP = G4::TP, UB = G4::UB, KG = G4::KG;
     static_assert(G8::UB == UB && G8::KG == KG, "one tile plan for both passes");
-    constexpr int RING = (LOPA && G8::NS * G8::STAGE > G4::NS * G4::STAGE) ? G8::NS * G8::STAGE
-                                                                         : G4::NS * G4::STAGE;
+    // LDS: the int4 ring with the group scales of its pass behind it (they are written
+    // and read only while an int4 pass runs), or the int8 ring of the LoPA U pass if
+    // larger; the partial sums of a pass go through the drained ring, and each thread
+    // keeps the z of its (unit, token) entries in registers through the W3 pass
+    constexpr int G4RING = G4::NS * G4::STAGE;
+    constexpr int RING = (LOPA && G8::NS * G8::STAGE > G4RING + UB * I4_GMAX * 4)
+                             ? G8::NS * G8::STAGE
+                             : G4RING + UB * I4_GMAX * 4;
+    constexpr int EPT = UB * TP / KM_THREADS;  // (unit, token) entries per thread
+    static_assert(EPT * KM_THREADS == UB * TP, "entries per thread");
+    static_assert(KG * UB * (TP + 1) * 4 <= G4RING, "partial sums fit the ring");
     __shared__ __attribute__((aligned(16))) uint8_t ring[RING];
-    __shared__ float part[KG][UB][TP + 1];
-    __shared__ float zf[UB][TP + 1];
-    __shared__ float sc[UB][I4_GMAX];
+    float (*part)[UB][TP + 1] = reinterpret_cast<float (*)[UB][TP + 1]>(ring);
+    float (*sc)[I4_GMAX] = reinterpret_cast<float (*)[I4_GMAX]>(ring + G4RING);
     __shared__ unsigned long long tmask[UB];
     __shared__ int rows_g[UB];
     __shared__ int rows_u[UB];
@@ -3739,7 +3748,10 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
         store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+    float zr[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = threadIdx.x + k * KM_THREADS;
         const int i = e / TP, t = e % TP;
         const bool ok = (u0 + i < H) && t < T;
         float z = 0.0f;
@@ -3749,7 +3761,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
             z *= s1[u0 + i];
             if (flags & LOPA_G_TILED) z += Elem<uint16_t>::get1(x[(size_t)t * D + (u0 + i) % D]);
         }
-        zf[i][t] = z;
+        zr[k] = z;
         const bool live = ok && (DENSE || z > 0.0f);
         const uint64_t tm = unit_token_mask<TP>(live);
         if (t == 0) tmask[i] = tm;
@@ -3779,7 +3791,9 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
         store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = threadIdx.x + k * KM_THREADS;
         const int i = e / TP, t = e % TP;
         if (u0 + i >= H) continue;
         const int p = upos[i];
@@ -3789,7 +3803,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma_i4(
 #pragma unroll
             for (int g = 0; g < KG; ++g) u += part[g][p][t];
             if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
-            av = activation(act, zf[i][t]) * u;
+            av = activation(act, zr[k]) * u;
         }
         a_rm[(size_t)(u0 + i) * TP + t] = av;
     }
