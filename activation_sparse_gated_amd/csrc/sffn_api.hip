@@ -405,10 +405,11 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
                                        (const uint16_t*)h->m_zero, t_hi, t_lo, h->D, h->r, T));
         if (st != SFFN_OK) return st;
     }
-    // unit tiles per gate block: LoPA above 32 tokens takes 64 units (H' = 9787: 153 blocks in
-    // one round, x staged half as often, against 306 blocks in 1.2 rounds; union of 40 / 64
-    // tokens 508k / 789k -> 570k / 889k tokens/s; of 24 / 32 tokens 32 units stay ahead)
-    const int ut = nt == 1 ? 1 : ((LOPA && nt == 4) ? 4 : 2);
+    // unit tiles per gate block: 32 units from 17 tokens on; at 33-64 tokens the 32-unit
+    // block of the LoPA gate takes 74 KB of LDS, so its 306 blocks over H' = 9787 run two
+    // per CU in one round (ahead of 153 blocks of 64 units: union of 40 / 64 tokens 573k /
+    // 893k -> 596k / 898k tokens/s)
+    const int ut = nt == 1 ? 1 : 2;
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const bool small_down = T <= 4;
     const int splits = per_token ? h->t1_splits : (small_down ? h->tb_splits : mfma_down_splits(h, nt));
@@ -460,7 +461,7 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     } else if (nt == 2) {
         SFFN_GATE_MFMA(2, 2);
     } else {
-        SFFN_GATE_MFMA(4, LOPA ? 4 : 2);
+        SFFN_GATE_MFMA(4, 2);
     }
     }
 #undef SFFN_GATE_MFMA

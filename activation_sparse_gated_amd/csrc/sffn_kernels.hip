@@ -2134,7 +2134,9 @@ struct GateTiles {
     static constexpr int ROWS = UB + TP;                   // staged rows per chunk
     static constexpr int IPW = ROWS / 16;                  // 1 KB load instructions per wave per chunk
     static constexpr int STAGE = ROWS * 256;               // bytes per LDS stage
-    static constexpr int NS = STAGE <= 24576 ? 4 : 3;      // LDS stages (deeper rings measured slower)
+    // LDS stages (deeper rings measured slower); 3 from 24 KB on, so that at 33-64 tokens a
+    // 32-unit block takes 74 KB and two share a CU
+    static constexpr int NS = STAGE <= 16384 ? 4 : 3;
     static_assert((NS - 2) * IPW <= 24, "vmcnt wait table");
 };
 
@@ -2269,9 +2271,13 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
     int r, unsigned flags, int split) {
     using G = GateTiles<NT, UT>;
     constexpr int TP = G::TP, UB = G::UB;
+    constexpr int EPT = UB * TP / KM_THREADS;  // (unit, token) entries per thread
+    static_assert(EPT * KM_THREADS == UB * TP, "entries per thread");
+    static_assert(G::KG * UB * (TP + 1) * 4 <= G::NS * G::STAGE, "partial sums fit the ring");
     __shared__ __attribute__((aligned(16))) uint8_t ring[G::NS * G::STAGE];
-    __shared__ float part[G::KG][UB][TP + 1];
-    __shared__ float zf[UB][TP + 1];
+    // the partial sums of a pass go through the ring once the pass has drained it; each
+    // thread keeps the z of its (unit, token) entries in registers through the W3 pass
+    float (*part)[UB][TP + 1] = reinterpret_cast<float (*)[UB][TP + 1]>(ring);
     __shared__ unsigned long long tmask[UB];
     __shared__ int rows_g[UB];
     __shared__ int rows_u[UB];
@@ -2320,14 +2326,17 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
         store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+    float zr[EPT];
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = threadIdx.x + k * KM_THREADS;
         const int i = e / TP, t = e % TP;
         float z = 0.0f;
 #pragma unroll
         for (int g = 0; g < G::KG; ++g) z += part[g][i][t];
         if (LOPA && (flags & LOPA_G_TILED) && t < T && u0 + i < H)
             z += Elem<uint16_t>::get1(x[(size_t)t * D + (u0 + i) % D]);
-        zf[i][t] = z;
+        zr[k] = z;
         const bool ok = (u0 + i < H) && t < T;
         const bool live = ok && (DENSE || z > 0.0f);
         const uint64_t tm = unit_token_mask<TP>(live);
@@ -2360,7 +2369,9 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
         store_tiles(acc);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < UB * TP; e += KM_THREADS) {
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+        const int e = threadIdx.x + k * KM_THREADS;
         const int i = e / TP, t = e % TP;
         if (u0 + i >= H) continue;
         const int p = upos[i];
@@ -2370,7 +2381,7 @@ __global__ __launch_bounds__(KM_THREADS) void k_gate_up_mfma(
 #pragma unroll
             for (int g = 0; g < G::KG; ++g) u += part[g][p][t];
             if (LOPA && (flags & LOPA_DOUBLE_ACT)) u = activation(act, u);
-            av = activation(act, zf[i][t]) * u;
+            av = activation(act, zr[k]) * u;
         }
         store_product(a_rm, (size_t)(u0 + i), TP, t, av, split);
     }
