@@ -101,7 +101,7 @@ struct sffn_handle {
     // large batches as GEMMs on MFMA (T > MAXT)
     int g_tp = 0;                  // padded token count of g_a (multiple of 256)
     uint16_t* g_a = nullptr;       // [H x g_tp] bf16 unit products, unit-major
-    uint64_t* g_any = nullptr;     // [g_tp / 256 x 2 ceil(H / 128)] 64-unit live masks per token tile
+    uint64_t* g_any = nullptr;     // [g_tp / 128 x 2 ceil(H / 128)] 64-unit live masks per token tile
     int32_t* g_list = nullptr;     // [H + 32] units live for some token, then the count
     // the down pass of batches of BLT_MIN_T tokens and more: y = a W2 over every unit as
     // one hipBLASLt GEMM (bf16 in, fp32 out), plans cached per token count
@@ -621,8 +621,11 @@ sffn_status run_gemm(sffn_handle* h, const void* x, const void* W1, const void* 
     uint8_t* live = live_count ? h->live_buf : nullptr;
     float* yz = splits > 1 ? y : nullptr;
     int32_t* count = h->g_list + h->H + 32;
-    // 256 x 128 gate tiles once there are 200 of them, else 256 x 64 (more blocks)
+    // 256 x 128 gate tiles once there are 200 of them, else 256 x 64 (more blocks); up to
+    // 256 tokens 128 x 64 (twice the blocks at 64 KB of LDS, two per CU: union of 128 / 256
+    // tokens 1.44M / 2.67M -> 1.46M / 2.73M tokens/s)
     const bool wide = (long)((T + 255) / 256) * ((h->H + 127) / 128) >= 200;
+    const bool small = !wide && T <= 256;
     if (T >= BLT_MIN_T && h->blt) {
         // the down pass over every unit (the products of units dead for every token are
         // exact zeros: A(z) = 0 for z <= 0), so the gate writes no union masks, and y is
@@ -634,7 +637,8 @@ sffn_status run_gemm(sffn_handle* h, const void* x, const void* W1, const void* 
         return run_live_list(h, T, live_count, live_idx, s);
     }
     sffn_status st = wide ? run_gate_gemm<256, 128, DENSE>(h, x, W1, W3, live, yz, T, s)
-                          : run_gate_gemm<256, 64, DENSE>(h, x, W1, W3, live, yz, T, s);
+                          : (small ? run_gate_gemm<128, 64, DENSE>(h, x, W1, W3, live, yz, T, s)
+                                   : run_gate_gemm<256, 64, DENSE>(h, x, W1, W3, live, yz, T, s));
     if (st != SFFN_OK) return st;
     st = launch(h, KIND_DOWN_GEMM, k_down_gemm, dim3(nmt * nnt * splits), dim3(KDG_THREADS), s,
                 (const uint16_t*)h->g_a, DENSE ? (const int32_t*)nullptr : (const int32_t*)h->g_list,
@@ -1434,7 +1438,7 @@ sffn_status sffn_create(sffn_handle** out, int D, int H, int r, int max_tokens, 
         if (dtype == SFFN_BF16 && r == 0 && h->m_zero && max_tokens > MAXT) {
             // large batches as GEMMs: bf16 unit products for up to g_tp tokens
             h->g_tp = 256 * ((max_tokens + 255) / 256);
-            const int ntt = h->g_tp / 256;
+            const int ntt = h->g_tp / 128;  // token tiles of 128 (batches up to 256) or 256
             e = hipMalloc(&h->g_a, (size_t)H * h->g_tp * sizeof(uint16_t));
             // one 64-bit mask per 64 units of each gate tile (tiles of 64 or 128 units)
             const size_t nm = 2 * (((size_t)H + 127) / 128);
