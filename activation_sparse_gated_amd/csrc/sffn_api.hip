@@ -411,13 +411,16 @@ sffn_status run_mfma(sffn_handle* h, const void* x, const void* W1, const void* 
     // 893k -> 596k / 898k tokens/s)
     const int ut = nt == 1 ? 1 : 2;
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
-    const bool small_down = T <= 4;
+    // VALU kernels up to 4 tokens (the dense comparator up to 2: from 3 tokens its MFMA
+    // passes are ahead, dense of 3 / 4 tokens 95.8k / 126k -> 101k / 134k tokens/s)
+    const int valu_max = DENSE ? 2 : 4;
+    const bool small_down = T <= valu_max;
     const int splits = per_token ? h->t1_splits : (small_down ? h->tb_splits : mfma_down_splits(h, nt));
     float* yz = splits > 1 ? y : nullptr;
     // the MFMA down pass takes the products split into bf16 hi and lo parts; the
     // per-token and small-batch down passes take them in fp32
     const int split = (!per_token && !small_down) ? 1 : 0;
-    if (!LOPA && T <= 4 && chunks_needed(h->D, h->dtype) <= 8) {
+    if (!LOPA && T <= valu_max && chunks_needed(h->D, h->dtype) <= 8) {
         // gate/up on the VALU: x of the batch in registers, W1 streamed once; units
         // per wave = token slots (2 or 4)
         const int nc = pick(kNC_T1, 7, chunks_needed(h->D, h->dtype));
