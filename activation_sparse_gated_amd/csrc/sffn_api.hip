@@ -821,8 +821,9 @@ sffn_status run_down_pt_q(sffn_handle* h, const void* W2T, const float* s2, floa
 // int8 union (and dense) batches of 5..64 tokens on MFMA: every weight code read
 // once for the batch (W1 or U, V, the W3 rows of the union, their W2T rows).
 // LOPA: W1 is U (scales s1 = U's), V with its scales sV gives the rank vectors.
-bool mfma_i8_ok(const sffn_handle* h, int T) {
-    return T > 4 && h->dtype == SFFN_I8 && h->m_a != nullptr && T <= h->max_tokens;
+// min_t: the smallest batch taken on MFMA (5 unless the caller's plan says otherwise)
+bool mfma_i8_ok(const sffn_handle* h, int T, int min_t = 5) {
+    return T >= min_t && h->dtype == SFFN_I8 && h->m_a != nullptr && T <= h->max_tokens;
 }
 
 template <bool DENSE, bool LOPA = false>
@@ -888,8 +889,8 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
 
 // int4 union (and dense) batches of 5..64 tokens on MFMA: every code read once for
 // the batch. LOPA: W1 is U (int8 rows, scales s1 = U's), V int8 with sV.
-bool mfma_i4_ok(const sffn_handle* h, int T) {
-    return T > 4 && h->dtype == SFFN_I4 && h->m_a != nullptr && T <= h->max_tokens;
+bool mfma_i4_ok(const sffn_handle* h, int T, int min_t = 5) {
+    return T >= min_t && h->dtype == SFFN_I4 && h->m_a != nullptr && T <= h->max_tokens;
 }
 
 template <bool DENSE, bool LOPA = false>
@@ -1730,13 +1731,16 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
     // batches above 4 tokens: one MFMA gate pass over the weights for the batch, then
     // the union's W2T rows once (union, dense) or each token's own live rows (per-token
-    // lists)
+    // lists). From 3 tokens the int4 batches in every mode and the int8 dense comparator
+    // are ahead on MFMA too (T = 4: int4 union 139k -> 151k, per-token 140k -> 152k, dense
+    // 109k -> 148k; int8 dense 133k -> 147k tokens/s), while the int8 union and per-token
+    // lists stay level or ahead on the VALU kernels up to 4 tokens
     const bool pt = !dense && mode == SFFN_MODE_PER_TOKEN;
-    if (bits == 8 && mfma_i8_ok(h, T))
+    if (bits == 8 && mfma_i8_ok(h, T, dense ? 3 : 5))
         return dense ? run_mfma_i8<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
                      : run_mfma_i8<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx,
                                           s, nullptr, nullptr, pt);
-    if (bits == 4 && mfma_i4_ok(h, T))
+    if (bits == 4 && mfma_i4_ok(h, T, 3))
         return dense ? run_mfma_i4<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
                      : run_mfma_i4<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx,
                                           s, nullptr, nullptr, pt);
