@@ -1922,14 +1922,15 @@ static sffn_status forward_lopa_q(sffn_handle* h, const void* x, const void* V, 
     auto al4 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; };
     if (!al4(sV) || !al4(sU) || !al4(s3) || !al4(s2))
         return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
-    // batches above 4 tokens: one MFMA pass over V, U and the W3 rows of the union, then
+    // batches above 2 tokens: one MFMA pass over V, U and the W3 rows of the union, then
     // the union's W2T rows once or each token's own (RMSNorm of t excepted: it needs
-    // each token's whole t before the gate)
+    // each token's whole t before the gate); at 3 / 4 tokens ahead of the VALU kernels
+    // (union, int8: 82k / 96k -> 92k / 121k tokens/s; int4: 79k / 92k -> 91k / 119k)
     const bool pt = mode == SFFN_MODE_PER_TOKEN;
-    if (bits == 8 && mfma_i8_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
+    if (bits == 8 && mfma_i8_ok(h, T, 3) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
         return run_mfma_i8<false, true>(h, x, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx,
                                         s, V, sV, pt);
-    if (bits == 4 && mfma_i4_ok(h, T) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
+    if (bits == 4 && mfma_i4_ok(h, T, 3) && h->m_t && !(h->flags & SFFN_FLAG_RMSNORM))
         return run_mfma_i4<false, true>(h, x, U, sU, W3, s3, W2T, s2, y, T, live_count, live_idx,
                                         s, V, sV, pt);
     // batches of 2..4 tokens read the weights once for the batch; larger ones (with
