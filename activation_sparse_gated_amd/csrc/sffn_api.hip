@@ -849,8 +849,10 @@ sffn_status run_mfma_i8(sffn_handle* h, const void* x, const void* W1, const flo
     const int nb = (h->H + 16 * ut - 1) / (16 * ut);
     const int splits = mfma_down_splits(h, nt);
     float* yz = (per_token || splits > 1) ? y : nullptr;
-    if (!LOPA && (DENSE || T > 10)) {
-        // W1 and W3 codes of the block and x staged together, x once for both
+    if (!LOPA) {
+        // W1 and W3 codes of the block and x staged together, x once for both; ahead of
+        // the gathered W3 pass at every batch size (union of 5 / 10 tokens, int8 196k /
+        // 348k -> 211k / 372k tokens/s, int4 186k / 329k -> 220k / 382k)
         SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_FUSED_I8,
                                        k_gate_up_mfma_fused_i8<NT, DENSE>, dim3(nb),
                                        dim3(KM_THREADS), s, (const uint16_t*)x, (const int8_t*)W1,
@@ -913,8 +915,10 @@ sffn_status run_mfma_i4(sffn_handle* h, const void* x, const void* W1, const flo
     const int nb = (h->H + 31) / 32;
     const int splits = mfma_down_splits(h, nt);
     float* yz = (per_token || splits > 1) ? y : nullptr;
-    if (!LOPA && (DENSE || T > 10)) {
-        // W1 and W3 codes of the block and x staged together, x once for both
+    if (!LOPA) {
+        // W1 and W3 codes of the block and x staged together, x once for both; ahead of
+        // the gathered W3 pass at every batch size (union of 5 / 10 tokens, int8 196k /
+        // 348k -> 211k / 372k tokens/s, int4 186k / 329k -> 220k / 382k)
         SFFN_NT_SWITCH(nt, st = launch(h, KIND_GATE_UP_MFMA_FUSED_I4,
                                        k_gate_up_mfma_fused_i4<NT, DENSE>, dim3(nb),
                                        dim3(KM_THREADS), s, (const uint16_t*)x, (const uint8_t*)W1,
