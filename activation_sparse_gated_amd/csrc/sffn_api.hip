@@ -1735,12 +1735,11 @@ static sffn_status forward_i8(sffn_handle* h, const void* x, const void* W1, con
     if (!al4(s1) || !al4(s3) || !al4(s2)) return fail(h, SFFN_INVALID_ARGUMENT, "scales must be 4-byte aligned");
     // batches above 4 tokens: one MFMA gate pass over the weights for the batch, then
     // the union's W2T rows once (union, dense) or each token's own live rows (per-token
-    // lists). From 3 tokens the int4 batches in every mode and the int8 dense comparator
-    // are ahead on MFMA too (T = 4: int4 union 139k -> 151k, per-token 140k -> 152k, dense
-    // 109k -> 148k; int8 dense 133k -> 147k tokens/s), while the int8 union and per-token
-    // lists stay level or ahead on the VALU kernels up to 4 tokens
+    // lists). From 3 tokens every mode is ahead on the fused MFMA pass (T = 4, against the
+    // VALU kernels: int8 union 158k -> 172k, per-token 162k -> 175k, dense 133k -> 147k;
+    // int4 union 139k -> 180k, per-token 140k -> 182k, dense 109k -> 148k tokens/s)
     const bool pt = !dense && mode == SFFN_MODE_PER_TOKEN;
-    if (bits == 8 && mfma_i8_ok(h, T, dense ? 3 : 5))
+    if (bits == 8 && mfma_i8_ok(h, T, 3))
         return dense ? run_mfma_i8<true>(h, x, W1, s1, W3, s3, W2T, s2, y, T, nullptr, nullptr, s)
                      : run_mfma_i8<false>(h, x, W1, s1, W3, s3, W2T, s2, y, T, live_count, live_idx,
                                           s, nullptr, nullptr, pt);
