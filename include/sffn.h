@@ -218,8 +218,9 @@ sffn_status sffn_forward_lopa(sffn_handle *h, const void *x, const void *V, cons
  * W2T_scale fp32 [H] (4-byte aligned): weight (i, j) of each matrix is
  * q[i][j] * scale[i]. x is bf16 [T x D], y fp32 [T x D]. Calls with 2..64
  * tokens, in either mode and dense, read every weight code once for the batch:
- * one gate pass (VALU for 2..4 tokens, MFMA on exactly decoded codes above)
- * gathers the W3 rows of the union of the live sets; then the union's W2T rows
+ * one gate pass (VALU for 2 tokens; from 3 tokens MFMA on exactly decoded codes,
+ * with the W1 and W3 rows staged together) computes the W3 dots of the units live
+ * for some token; then the union's W2T rows
  * are read once (union, dense) or each token's own live rows are gathered
  * (per-token lists). Errors as for the other forward calls; a non-int8 handle
  * gives SFFN_INVALID_ARGUMENT.
